@@ -1,0 +1,266 @@
+/*
+ * sgl_attn.h -- C ABI of the paged prefix-shared attention library for
+ * MI355X (gfx950).
+ *
+ * The library holds the data-parallel hot path behind prefix-shared
+ * ("radix") attention: attention over a token-granular paged KV pool whose
+ * rows are found through a req_to_token table that a longest-prefix match on
+ * a radix tree fills, so a cached shared prefix is read rather than
+ * recomputed.  The operations follow the statement of the problem on the
+ * pages:
+ *   - "SGLang 深度解读" (luoboask.github.io), module 5 "Attention 层 --
+ *     RadixAttention 实现": store the current K/V at the slots given by
+ *     req_to_token, then run paged attention over the pool;
+ *   - "SGLang 深度拆解" (chenxutan.com) section 3.2: the PagedPrefill and
+ *     PagedDecode kernels take Q, the paged K/V caches, a page table,
+ *     context lengths and cached-prefix lengths;
+ *   - the same page, section 2.3: match_prefix / insert / evict / pin on the
+ *     radix tree, with reference counts and LRU stamps per node.
+ *
+ * Conventions for every call
+ *   - Plain C types only.  "device" pointers point to GPU memory (any HIP
+ *     allocation, e.g. a torch tensor's data_ptr); "host" pointers to CPU
+ *     memory.  Streams are hipStream_t passed as void* (NULL = the default
+ *     stream).
+ *   - The caller owns all device memory: Q/K/V, the pools, req_to_token,
+ *     outputs and workspaces.  The library allocates no device memory and
+ *     keeps no pointer after a call returns.  Host objects (sgl_kv_pool,
+ *     sgl_radix) belong to their handle until *_destroy.
+ *   - Device operations only enqueue work on the given stream and return;
+ *     their results are ready when the stream is.  Host operations are
+ *     synchronous and not thread-safe on one handle.
+ *   - Every call returns an sgl_status; no C++ exception crosses the ABI.
+ *     Argument checks run before any GPU work is enqueued; a failed call
+ *     enqueues nothing.
+ *   - Layouts are row-major and dense:  Q/O [tokens, Hq, D];  new K/V
+ *     [tokens, Hkv, D];  pools [num_slots, Hkv, D];  req_to_token
+ *     [num_rows, row_stride] int32 slot ids;  LSE [tokens, Hq] float32.
+ *   - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention with
+ *     contiguous groups).  Key j is visible to a query at absolute position
+ *     t iff j <= t: the whole cached prefix and the new tokens up to and
+ *     including itself.
+ *   - Supported: dtype SGL_F32 or SGL_BF16 (outputs in the input dtype,
+ *     arithmetic accumulates in fp32), D in {64, 128}, Hq / Hkv in
+ *     {1, 2, 4, 8}, Hkv <= 16.  Anything else -> SGL_ERR_UNSUPPORTED.
+ *   - Index safety: device kernels never access memory outside the arrays
+ *     the arguments describe.  A slot id outside [0, num_slots) read from
+ *     req_to_token is replaced by slot 0 (its result is then meaningless but
+ *     no fault occurs).  With the environment variable SGL_ATTN_VALIDATE=1
+ *     the device calls first copy the index metadata to the host (a
+ *     synchronising step), check it, and return SGL_ERR_INVALID on any
+ *     out-of-range slot, row or length, enqueuing nothing.
+ */
+#ifndef SGL_ATTN_H
+#define SGL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SGL_OK = 0,
+    SGL_ERR_INVALID = 1,      /* bad shape, length, index, handle or pointer */
+    SGL_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype, D, group size) */
+    SGL_ERR_OOM = 3,          /* slot pool exhausted; the pool is unchanged */
+    SGL_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+    SGL_ERR_WORKSPACE = 5     /* workspace missing or smaller than required */
+} sgl_status;
+
+typedef enum { SGL_F32 = 0, SGL_BF16 = 1 } sgl_dtype;
+
+typedef struct sgl_kv_pool sgl_kv_pool;
+typedef struct sgl_radix sgl_radix;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *sgl_status_string(int status);
+
+/* ABI version of this header (bumped on any signature change). */
+int sgl_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * KV slot pool (host).  The pool shares one set of slots between the prefix
+ * cache and running requests ("SGLang：从前端 DSL 到 SRT 服务运行时"
+ * (oripoin.cn), section "用基数树实现前缀复用", third bullet).  A page is
+ * page_size consecutive slots page*page_size .. +page_size-1 (pages of one
+ * or more tokens, same section; vLLM's 16-token pages, chenxutan.com section
+ * 2.2).  The free list is FIFO: alloc pops whole pages from its head, free
+ * appends them to its tail.
+ * ---------------------------------------------------------------------- */
+
+/* num_slots: multiple of page_size, 1 <= page_size <= 1024, num_slots < 2^31.
+ * init_order: host [num_slots / page_size] permutation of the page ids giving
+ * the initial free-list order, or NULL for 0, 1, 2, ...  (copied).
+ * *out receives the handle.  INVALID if init_order is not a permutation. */
+int sgl_kv_pool_create(int64_t num_slots, int32_t page_size, const int32_t *init_order,
+                       sgl_kv_pool **out);
+int sgl_kv_pool_destroy(sgl_kv_pool *pool);
+
+/* Allocate n slots for a request that already holds cur_len tokens whose last
+ * slot is last_slot (ignored when cur_len % page_size == 0).  With
+ * page_size > 1 the rest of last_slot's page is used first, then whole pages
+ * are popped from the free list; the unused tail of the last page stays with
+ * the request.  out_slots: host [n].  OOM (pool unchanged) if not enough
+ * pages are free. */
+int sgl_kv_pool_alloc(sgl_kv_pool *pool, int64_t cur_len, int32_t last_slot, int64_t n,
+                      int32_t *out_slots);
+
+/* Return slots to the pool: every slot in host slots[n] that starts a page
+ * (slot % page_size == 0) returns its page, in array order.  Other slots are
+ * skipped (they belong to a page whose first slot is in the list).  INVALID
+ * (pool unchanged) on an out-of-range slot or a page that is already free. */
+int sgl_kv_pool_free(sgl_kv_pool *pool, const int32_t *slots, int64_t n);
+
+/* Number of free slots (free pages * page_size), or -1 for a NULL pool. */
+int64_t sgl_kv_pool_available(const sgl_kv_pool *pool);
+
+/* ------------------------------------------------------------------------
+ * Prefix cache: a compressed radix tree over token ids whose nodes hold the
+ * slots of their tokens, a reference count and an LRU stamp
+ * (chenxutan.com section 2.3; bhfrc.com news 45689 section 3.1).  Sharing is
+ * in whole pages.  A logical clock ticks once per match and once per insert
+ * and stamps every node on the path.  Node handles are opaque non-zero ids
+ * (0 = the root, i.e. an empty match); a handle stays valid while its node
+ * is locked, and until the next evict otherwise.
+ * ---------------------------------------------------------------------- */
+int sgl_radix_create(int32_t page_size, sgl_radix **out);
+int sgl_radix_destroy(sgl_radix *tree);
+
+/* Longest cached prefix of host tokens[n], in whole pages.  *out_len gets its
+ * length; out_slots (host, capacity n, may be NULL) gets its slots; *out_node
+ * (may be NULL) gets the handle of the node that ends the prefix. */
+int sgl_radix_match(sgl_radix *tree, const int32_t *tokens, int64_t n, int32_t *out_slots,
+                    int64_t *out_len, uint64_t *out_node);
+
+/* Insert the first floor(n / page_size) pages of host tokens[n] with their
+ * host slots[n].  Pages already cached keep the tree's slots; a caller page
+ * whose first slot differs from the cached one is a duplicate and is freed
+ * to `pool` (may be NULL only if no duplicate can occur), in position order.
+ * *out_cached_len (may be NULL) gets how many tokens were already cached.
+ * Within a page the slots must be page*page_size + 0, 1, ... (INVALID
+ * otherwise, tree unchanged). */
+int sgl_radix_insert(sgl_radix *tree, const int32_t *tokens, const int32_t *slots, int64_t n,
+                     sgl_kv_pool *pool, int64_t *out_cached_len);
+
+/* Add delta (+1 or -1) to the reference count of every node on the path
+ * root..node (pin a prefix / release it, chenxutan.com section 2.3
+ * pin_prefix; bhfrc.com news 45689 section 3.2).  INVALID if the handle is
+ * unknown or a count would go negative (tree unchanged). */
+int sgl_radix_lock(sgl_radix *tree, uint64_t node, int32_t delta);
+
+/* Free at least n_tokens cached tokens if possible: repeatedly remove the
+ * last page of the unreferenced leaf with the oldest stamp, returning its
+ * page to `pool`, until enough is freed or no unreferenced leaf is left
+ * (leaf-first LRU guarded by reference counts, oripoin.cn section
+ * "用基数树实现前缀复用").  *out_freed gets the number of tokens freed. */
+int sgl_radix_evict(sgl_radix *tree, int64_t n_tokens, sgl_kv_pool *pool, int64_t *out_freed);
+
+/* Cached tokens, and how many of them are unreferenced (evictable). */
+int sgl_radix_stats(const sgl_radix *tree, int64_t *out_cached, int64_t *out_evictable);
+
+/* ------------------------------------------------------------------------
+ * Device operations.
+ * ---------------------------------------------------------------------- */
+
+/* Build req_to_token rows (GPU scatter).  For request r (0 <= r < batch) the
+ * table row req_rows[r] receives, from column new_col0[r] (or, if new_col0 is
+ * NULL, from column P_r), the slots new_slots[new_off[r] .. new_off[r+1]),
+ * and columns [0, P_r) receive prefix_slots[prefix_off[r] .. prefix_off[r+1])
+ * where P_r = prefix_off[r+1] - prefix_off[r].  prefix_slots / prefix_off
+ * may both be NULL (P_r = 0, columns outside the new range untouched; this
+ * is the decode append).  All arrays are device arrays; offsets are int64
+ * CSR offsets starting at 0.  Writes that would fall outside
+ * [0, num_rows) x [0, row_stride) are dropped by the kernel. */
+int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                           const int32_t *req_rows, int32_t batch,
+                           const int32_t *prefix_slots, const int64_t *prefix_off,
+                           const int32_t *new_slots, const int64_t *new_off,
+                           const int32_t *new_col0, void *stream);
+
+/* Store K/V rows into the pools: token i's K row (Hkv*D elements) goes to
+ * k_pool[slots[i]], likewise V ("token_to_kv_pool.write(cache_loc, k, v)",
+ * luoboask.github.io module 5).  slots: device [n_tokens]; out-of-range slots
+ * are skipped. */
+int sgl_store_kv(int dtype, const void *k_new, const void *v_new, int64_t n_tokens,
+                 const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                 int32_t Hkv, int32_t D, void *stream);
+
+/* Extend (prefix-aware prefill) attention, chenxutan.com section 3.2
+ * PagedPrefill and luoboask.github.io module 5.  Request r has a cached
+ * prefix of P_r = prefix_lens[r] tokens and E_r = q_off[r+1] - q_off[r] new
+ * tokens; its new token i sits at absolute position P_r + i and is query row
+ * q_off[r] + i.  Its K/V row at position j is slot
+ * r2t[req_rows[r] * row_stride + j].
+ *   q: device [n_tokens, Hq, D];  o: device [n_tokens, Hq, D] (dtype).
+ *   k_new / v_new: device [n_tokens, Hkv, D] to be stored first at the slots
+ *     of positions P_r .. P_r+E_r-1, or both NULL if already stored.
+ *   prefix_lens, req_rows: device int32 [batch];  q_off: device int64
+ *     [batch+1], q_off[0] = 0, q_off[batch] = n_tokens.
+ *   max_extend_len: host bound >= every E_r (sizes the grid);
+ *   lse: device float32 [n_tokens, Hq] log-sum-exp of the scaled scores
+ *     (natural log), or NULL.
+ *   workspace: device scratch of sgl_extend_workspace_size(...) bytes (may be
+ *     NULL when that size is 0).
+ * scale multiplies q.k (normally 1/sqrt(D)). */
+int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_new,
+                    void *k_pool, void *v_pool, int64_t num_slots,
+                    const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                    const int32_t *req_rows, const int32_t *prefix_lens, const int64_t *q_off,
+                    int32_t batch, int64_t n_tokens, int32_t max_extend_len,
+                    int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                    void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+size_t sgl_extend_workspace_size(int32_t batch, int64_t n_tokens, int32_t max_extend_len,
+                                 int32_t Hq, int32_t Hkv, int32_t D);
+
+/* Decode attention: one query token per request over its whole context,
+ * chenxutan.com section 3.2 PagedDecode.  seq_lens[r] (device int32)
+ * INCLUDES the current token, whose K/V sits at position seq_lens[r]-1
+ * (stored first from k_new / v_new [batch, Hkv, D] when they are not NULL).
+ *   q, o: device [batch, Hq, D];  lse: device float32 [batch, Hq] or NULL.
+ *   max_seq_len: host bound >= every seq_lens[r] (sizes the split-K grid).
+ *   workspace: sgl_decode_workspace_size(...) bytes. */
+int sgl_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new,
+                    void *k_pool, void *v_pool, int64_t num_slots,
+                    const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                    const int32_t *req_rows, const int32_t *seq_lens,
+                    int32_t batch, int32_t max_seq_len,
+                    int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                    void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+size_t sgl_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq, int32_t Hkv,
+                                 int32_t D);
+
+/* Cascade decode: as sgl_decode_attn, but the requests form G groups that
+ * share a cached prefix (sibling requests of one radix subtree: parallel
+ * samples of one prompt, bhfrc.com news 45689 section 1.3).  Requests
+ * group_ptr[g] .. group_ptr[g+1]-1 form group g (group_ptr: device int32
+ * [G+1], group_ptr[0] = 0, group_ptr[G] = batch) and share their first
+ * group_prefix_len[g] (device int32 [G]) KV positions.  The shared prefix is
+ * read ONCE per group for all its requests' queries, each request's own
+ * suffix is read per request, and the two partial softmax states are merged
+ * with the log-sum-exp rule.  The result equals sgl_decode_attn.
+ * Precondition: within a group all req_to_token rows hold the same slots in
+ * columns [0, group_prefix_len[g]) (the prefix slots are read from the row
+ * of the group's first request) and group_prefix_len[g] <= seq_lens[r] for
+ * its requests.  max_group_size, max_prefix_len: host bounds (grid sizing);
+ * max_group_size * (Hq / Hkv) <= 128.
+ * workspace: sgl_cascade_workspace_size(...) bytes. */
+int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new,
+                            void *k_pool, void *v_pool, int64_t num_slots,
+                            const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                            const int32_t *req_rows, const int32_t *seq_lens,
+                            const int32_t *group_ptr, const int32_t *group_prefix_len,
+                            int32_t batch, int32_t G, int32_t max_seq_len,
+                            int32_t max_group_size, int32_t max_prefix_len,
+                            int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                            void *o, float *lse, void *workspace, size_t workspace_bytes,
+                            void *stream);
+size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
+                                  int32_t max_group_size, int32_t max_prefix_len,
+                                  int32_t Hq, int32_t Hkv, int32_t D);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SGL_ATTN_H */

@@ -53,6 +53,7 @@ typedef struct {
     int32_t n_heads;
     const int64_t *key_lo, *key_hi; /* per query row key range, NULL -> [0, t] */
     int32_t method;
+    int32_t n_threads;
     double *O, *M, *L, *LSE;  /* outputs, indexed [row][head slot] */
     int64_t next;             /* work counter */
     pthread_mutex_t mu;
@@ -132,7 +133,10 @@ static void *worker(void *arg) {
     }
     double *sbuf = (double *)malloc(sizeof(double) * (size_t)maxlen);
     if (!sbuf) return (void *)1;
-    const int64_t chunk = 16;
+    /* work units per grab: small calls still spread over all threads */
+    int64_t chunk = total / ((int64_t)jb->n_threads * 8);
+    if (chunk < 1) chunk = 1;
+    if (chunk > 16) chunk = 16;
     for (;;) {
         pthread_mutex_lock(&jb->mu);
         int64_t start = jb->next;
@@ -185,7 +189,7 @@ int oracle_attention(int64_t n_req, const int64_t *kv_off, const float *K, const
     jb.n_rows = n_rows; jb.row_req = row_req; jb.row_pos = row_pos; jb.kv_off = kv_off;
     jb.K = K; jb.V = V; jb.Q = Q; jb.Hq = Hq; jb.Hkv = Hkv; jb.D = D; jb.scale = scale;
     jb.heads = heads; jb.n_heads = n_heads; jb.key_lo = key_lo; jb.key_hi = key_hi;
-    jb.method = method; jb.O = O; jb.M = M; jb.L = Lsum; jb.LSE = LSE; jb.next = 0;
+    jb.method = method; jb.n_threads = n_threads; jb.O = O; jb.M = M; jb.L = Lsum; jb.LSE = LSE; jb.next = 0;
     pthread_mutex_init(&jb.mu, NULL);
     int rc = 0;
     if (n_threads == 1) {

@@ -36,6 +36,7 @@ Rules (the pages leave the details open; these are the readings used):
     never share a stamp (one operation stamps one root path, which holds at
     most one leaf), so the order is unique.
 """
+from collections import deque
 
 
 class OutOfSlots(Exception):
@@ -51,7 +52,7 @@ class SlotPool:
             init_order = list(range(n_pages))
         init_order = [int(x) for x in init_order]
         assert sorted(init_order) == list(range(n_pages)), "init_order must be a permutation"
-        self.free_pages = list(init_order)   # head = index 0
+        self.free_pages = deque(init_order)  # head = left end
         self.is_free = [True] * n_pages
         self.num_slots = num_slots
 
@@ -69,7 +70,7 @@ class SlotPool:
         if need > len(self.free_pages):
             raise OutOfSlots(f"need {need} pages, {len(self.free_pages)} free")
         for _ in range(need):
-            page = self.free_pages.pop(0)
+            page = self.free_pages.popleft()
             self.is_free[page] = False
             for i in range(p):
                 if len(out) < n:

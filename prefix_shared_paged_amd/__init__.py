@@ -1,0 +1,352 @@
+"""Paged prefix-shared attention for MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over the C ABI of libsgl_attn.so (declared in
+include/sgl_attn.h); every step of the attention path runs in the library's
+HIP kernels.  PyTorch only provides device memory and the current stream.
+The names follow the C functions without the ``sgl_`` prefix.
+
+If the library is missing it is built (hipcc) on first use; if that fails the
+import of the entry points raises -- there is no fallback implementation.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+SGL_OK, SGL_ERR_INVALID, SGL_ERR_UNSUPPORTED, SGL_ERR_OOM, SGL_ERR_HIP, SGL_ERR_WORKSPACE = range(6)
+SGL_F32, SGL_BF16 = 0, 1
+
+_lib = None
+
+
+class SglError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+class OutOfSlots(SglError):
+    pass
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def load():
+    """Load libsgl_attn.so (building it first if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "sgl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "sgl_abi_version": (ctypes.c_int, []),
+        "sgl_kv_pool_create": (ctypes.c_int, [I64, I32, P, P]),
+        "sgl_kv_pool_destroy": (ctypes.c_int, [P]),
+        "sgl_kv_pool_alloc": (ctypes.c_int, [P, I64, I32, I64, P]),
+        "sgl_kv_pool_free": (ctypes.c_int, [P, P, I64]),
+        "sgl_kv_pool_available": (I64, [P]),
+        "sgl_radix_create": (ctypes.c_int, [I32, P]),
+        "sgl_radix_destroy": (ctypes.c_int, [P]),
+        "sgl_radix_match": (ctypes.c_int, [P, P, I64, P, P, P]),
+        "sgl_radix_insert": (ctypes.c_int, [P, P, P, I64, P, P]),
+        "sgl_radix_lock": (ctypes.c_int, [P, ctypes.c_uint64, I32]),
+        "sgl_radix_evict": (ctypes.c_int, [P, I64, P, P]),
+        "sgl_radix_stats": (ctypes.c_int, [P, P, P]),
+        "sgl_build_req_to_token": (ctypes.c_int, [P, I64, I64, P, I32, P, P, P, P, P, P]),
+        "sgl_store_kv": (ctypes.c_int, [ctypes.c_int, P, P, I64, P, P, P, I64, I32, I32, P]),
+        "sgl_extend_attn": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P, P, P,
+                                           I32, I64, I32, I32, I32, I32, F, P, P, P, SZ, P]),
+        "sgl_extend_workspace_size": (SZ, [I32, I64, I32, I32, I32, I32]),
+        "sgl_decode_attn": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P, P,
+                                           I32, I32, I32, I32, I32, F, P, P, P, SZ, P]),
+        "sgl_decode_workspace_size": (SZ, [I32, I32, I32, I32, I32]),
+        "sgl_cascade_decode_attn": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P,
+                                                   P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
+                                                   F, P, P, P, SZ, P]),
+        "sgl_cascade_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, I32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_kv_pool_create", "sgl_kv_pool_destroy",
+           "sgl_kv_pool_alloc", "sgl_kv_pool_free", "sgl_kv_pool_available", "sgl_radix_create",
+           "sgl_radix_destroy", "sgl_radix_match", "sgl_radix_insert", "sgl_radix_lock",
+           "sgl_radix_evict", "sgl_radix_stats", "sgl_build_req_to_token", "sgl_store_kv",
+           "sgl_extend_attn", "sgl_extend_workspace_size", "sgl_decode_attn",
+           "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size"]
+
+
+def status_string(status: int) -> str:
+    return load().sgl_status_string(status).decode()
+
+
+def _check(fn, status):
+    if status == SGL_ERR_OOM:
+        raise OutOfSlots(fn, status)
+    if status != SGL_OK:
+        raise SglError(fn, status)
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# host objects
+# ---------------------------------------------------------------------------
+class KVPool:
+    """Slot pool: FIFO free list of pages (sgl_kv_pool_*)."""
+
+    def __init__(self, num_slots, page_size=1, init_order=None):
+        lib = load()
+        self._h = ctypes.c_void_p()
+        order = None if init_order is None else _i32(init_order)
+        _check("sgl_kv_pool_create", lib.sgl_kv_pool_create(
+            num_slots, page_size, _np_ptr(order) if order is not None else None, ctypes.byref(self._h)))
+        self.num_slots = num_slots
+        self.page_size = page_size
+
+    @property
+    def handle(self):
+        return self._h
+
+    def alloc(self, n, cur_len=0, last_slot=-1):
+        out = np.empty(int(n), np.int32)
+        _check("sgl_kv_pool_alloc", load().sgl_kv_pool_alloc(self._h, cur_len, last_slot, n, _np_ptr(out)))
+        return out
+
+    def free(self, slots):
+        s = _i32(slots)
+        _check("sgl_kv_pool_free", load().sgl_kv_pool_free(self._h, _np_ptr(s), s.size))
+
+    def available(self):
+        return int(load().sgl_kv_pool_available(self._h))
+
+    def close(self):
+        if self._h:
+            load().sgl_kv_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class RadixTree:
+    """Prefix cache: compressed radix tree with ref counts and LRU (sgl_radix_*)."""
+
+    def __init__(self, page_size=1):
+        self._h = ctypes.c_void_p()
+        _check("sgl_radix_create", load().sgl_radix_create(page_size, ctypes.byref(self._h)))
+        self.page_size = page_size
+
+    def match(self, tokens):
+        """Return (matched_len, slots[:matched_len], node_handle)."""
+        t = _i32(tokens)
+        out = np.empty(max(t.size, 1), np.int32)
+        n = ctypes.c_int64()
+        node = ctypes.c_uint64()
+        _check("sgl_radix_match", load().sgl_radix_match(self._h, _np_ptr(t), t.size, _np_ptr(out),
+                                                         ctypes.byref(n), ctypes.byref(node)))
+        return int(n.value), out[:n.value].copy(), int(node.value)
+
+    def insert(self, tokens, slots, pool=None):
+        t, s = _i32(tokens), _i32(slots)
+        if t.size != s.size:
+            raise ValueError("tokens and slots differ in length")
+        cached = ctypes.c_int64()
+        _check("sgl_radix_insert", load().sgl_radix_insert(
+            self._h, _np_ptr(t), _np_ptr(s), t.size, pool.handle if pool is not None else None,
+            ctypes.byref(cached)))
+        return int(cached.value)
+
+    def lock(self, node, delta):
+        _check("sgl_radix_lock", load().sgl_radix_lock(self._h, node, delta))
+
+    def evict(self, n_tokens, pool):
+        freed = ctypes.c_int64()
+        _check("sgl_radix_evict", load().sgl_radix_evict(self._h, n_tokens, pool.handle, ctypes.byref(freed)))
+        return int(freed.value)
+
+    def stats(self):
+        c, e = ctypes.c_int64(), ctypes.c_int64()
+        _check("sgl_radix_stats", load().sgl_radix_stats(self._h, ctypes.byref(c), ctypes.byref(e)))
+        return int(c.value), int(e.value)
+
+    def close(self):
+        if self._h:
+            load().sgl_radix_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------------------
+# device operations (torch tensors on the GPU)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtype=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SGL_F32
+    if t.dtype == torch.bfloat16:
+        return SGL_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def build_req_to_token(r2t, req_rows, new_slots, new_off, prefix_slots=None, prefix_off=None,
+                       new_col0=None, stream=None):
+    torch = _torch()
+    _check("sgl_build_req_to_token", load().sgl_build_req_to_token(
+        _dev_ptr(r2t, "r2t", torch.int32), r2t.shape[0], r2t.shape[1],
+        _dev_ptr(req_rows, "req_rows", torch.int32), req_rows.numel(),
+        _dev_ptr(prefix_slots, "prefix_slots", torch.int32, True),
+        _dev_ptr(prefix_off, "prefix_off", torch.int64, True),
+        _dev_ptr(new_slots, "new_slots", torch.int32), _dev_ptr(new_off, "new_off", torch.int64),
+        _dev_ptr(new_col0, "new_col0", torch.int32, True), _stream(stream)))
+
+
+def store_kv(k_new, v_new, slots, k_pool, v_pool, stream=None):
+    torch = _torch()
+    n, Hkv, D = k_new.shape
+    _check("sgl_store_kv", load().sgl_store_kv(
+        _dtype_code(k_new), _dev_ptr(k_new, "k_new", k_new.dtype), _dev_ptr(v_new, "v_new", k_new.dtype), n,
+        _dev_ptr(slots, "slots", torch.int32), _dev_ptr(k_pool, "k_pool", k_new.dtype),
+        _dev_ptr(v_pool, "v_pool", k_new.dtype), k_pool.shape[0], Hkv, D, _stream(stream)))
+
+
+def extend_workspace_size(batch, n_tokens, max_extend_len, Hq, Hkv, D):
+    return int(load().sgl_extend_workspace_size(batch, n_tokens, max_extend_len, Hq, Hkv, D))
+
+
+def extend_attn(q, k_pool, v_pool, r2t, req_rows, prefix_lens, q_off, max_extend_len, k_new=None,
+                v_new=None, scale=None, o=None, lse=None, workspace=None, stream=None):
+    """Extend attention; q [n_tokens, Hq, D], pools [S, Hkv, D]; returns o."""
+    torch = _torch()
+    n_tokens, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    ws_n = extend_workspace_size(req_rows.numel(), n_tokens, max_extend_len, Hq, Hkv, D)
+    if ws_n and workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    _check("sgl_extend_attn", load().sgl_extend_attn(
+        _dtype_code(q), _dev_ptr(q, "q", q.dtype), _dev_ptr(k_new, "k_new", q.dtype, True),
+        _dev_ptr(v_new, "v_new", q.dtype, True), _dev_ptr(k_pool, "k_pool", q.dtype),
+        _dev_ptr(v_pool, "v_pool", q.dtype), k_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(prefix_lens, "prefix_lens", torch.int32), _dev_ptr(q_off, "q_off", torch.int64),
+        req_rows.numel(), n_tokens, max_extend_len, Hq, Hkv, D, scale, _dev_ptr(o, "o", q.dtype),
+        _dev_ptr(lse, "lse", torch.float32, True), _dev_ptr(workspace, "workspace", None, True),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+    return o
+
+
+def decode_workspace_size(batch, max_seq_len, Hq, Hkv, D):
+    return int(load().sgl_decode_workspace_size(batch, max_seq_len, Hq, Hkv, D))
+
+
+def cascade_workspace_size(batch, G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D):
+    return int(load().sgl_cascade_workspace_size(batch, G, max_seq_len, max_group_size, max_prefix_len,
+                                                 Hq, Hkv, D))
+
+
+def decode_attn(q, k_pool, v_pool, r2t, req_rows, seq_lens, max_seq_len, k_new=None, v_new=None,
+                scale=None, o=None, lse=None, workspace=None, stream=None):
+    """Decode attention; q [batch, Hq, D]; seq_lens include the current token; returns o."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    ws_n = decode_workspace_size(B, max_seq_len, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _check("sgl_decode_attn", load().sgl_decode_attn(
+        _dtype_code(q), _dev_ptr(q, "q", q.dtype), _dev_ptr(k_new, "k_new", q.dtype, True),
+        _dev_ptr(v_new, "v_new", q.dtype, True), _dev_ptr(k_pool, "k_pool", q.dtype),
+        _dev_ptr(v_pool, "v_pool", q.dtype), k_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), B, max_seq_len, Hq, Hkv, D, scale,
+        _dev_ptr(o, "o", q.dtype), _dev_ptr(lse, "lse", torch.float32, True),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+def cascade_decode_attn(q, k_pool, v_pool, r2t, req_rows, seq_lens, group_ptr, group_prefix_len,
+                        max_seq_len, max_group_size, max_prefix_len, k_new=None, v_new=None,
+                        scale=None, o=None, lse=None, workspace=None, stream=None):
+    """Cascade decode: groups share a prefix read once per group; returns o."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = group_prefix_len.numel()
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    ws_n = cascade_workspace_size(B, G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _check("sgl_cascade_decode_attn", load().sgl_cascade_decode_attn(
+        _dtype_code(q), _dev_ptr(q, "q", q.dtype), _dev_ptr(k_new, "k_new", q.dtype, True),
+        _dev_ptr(v_new, "v_new", q.dtype, True), _dev_ptr(k_pool, "k_pool", q.dtype),
+        _dev_ptr(v_pool, "v_pool", q.dtype), k_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(group_ptr, "group_ptr", torch.int32),
+        _dev_ptr(group_prefix_len, "group_prefix_len", torch.int32), B, G, max_seq_len,
+        max_group_size, max_prefix_len, Hq, Hkv, D, scale, _dev_ptr(o, "o", q.dtype),
+        _dev_ptr(lse, "lse", torch.float32, True), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o

@@ -1,0 +1,334 @@
+// api.hip -- C-ABI device entry points of libsgl_attn: argument checks,
+// optional host-side validation of index metadata, workspace layout, and the
+// kernel launches.  See include/sgl_attn.h for the contract.
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kDecodeChunk = 256;   // keys per split (flat decode and cascade suffix)
+constexpr int kPrefixChunk = 256;   // keys per split (cascade prefix)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool validate_on() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = std::getenv("SGL_ATTN_VALIDATE");
+        v = (e && e[0] && e[0] != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+bool shape_ok(int dtype, int32_t Hq, int32_t Hkv, int32_t D) {
+    if (dtype != SGL_F32 && dtype != SGL_BF16) return false;
+    if (D != 64 && D != 128) return false;
+    if (Hkv < 1 || Hkv > 16 || Hq < Hkv || Hq % Hkv != 0) return false;
+    const int g = Hq / Hkv;
+    return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+int elt_size(int dtype) { return dtype == SGL_BF16 ? 2 : 4; }
+
+template <class T>
+bool fetch(std::vector<T> &out, const T *dev, size_t n, hipStream_t st) {
+    out.resize(n);
+    if (n == 0) return true;
+    if (hipStreamSynchronize(st) != hipSuccess) return false;
+    return hipMemcpy(out.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+size_t part_bytes(int64_t B, int64_t S, int64_t Hq, int64_t D) {
+    return align_up((size_t)(B * S * Hq * D) * sizeof(float)) + align_up((size_t)(B * S * Hq * 2) * sizeof(float));
+}
+
+PartialBuf carve(char *&p, int64_t B, int64_t S, int64_t Hq, int64_t D) {
+    PartialBuf pb;
+    pb.o = (float *)p;
+    p += align_up((size_t)(B * S * Hq * D) * sizeof(float));
+    pb.ml = (float *)p;
+    p += align_up((size_t)(B * S * Hq * 2) * sizeof(float));
+    pb.S = (int32_t)S;
+    return pb;
+}
+
+// Check that req_to_token row `row` columns [c0, c1) hold valid slots.
+bool slots_ok(const std::vector<int32_t> &tab, int64_t row_stride, int64_t row, int64_t c0, int64_t c1,
+              int64_t num_slots) {
+    for (int64_t c = c0; c < c1; c++) {
+        const int32_t s = tab[(size_t)(row * row_stride + c)];
+        if (s < 0 || s >= num_slots) return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sgl_status_string(int status) {
+    switch (status) {
+        case SGL_OK: return "SGL_OK";
+        case SGL_ERR_INVALID: return "SGL_ERR_INVALID";
+        case SGL_ERR_UNSUPPORTED: return "SGL_ERR_UNSUPPORTED";
+        case SGL_ERR_OOM: return "SGL_ERR_OOM";
+        case SGL_ERR_HIP: return "SGL_ERR_HIP";
+        case SGL_ERR_WORKSPACE: return "SGL_ERR_WORKSPACE";
+        default: return "SGL_ERR_UNKNOWN";
+    }
+}
+
+int sgl_abi_version(void) { return 1; }
+
+int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                           const int32_t *req_rows, int32_t batch, const int32_t *prefix_slots,
+                           const int64_t *prefix_off, const int32_t *new_slots, const int64_t *new_off,
+                           const int32_t *new_col0, void *stream) {
+    if (batch < 0 || num_rows < 0 || row_stride < 0) return SGL_ERR_INVALID;
+    if (batch == 0) return SGL_OK;
+    if (!r2t || !req_rows || !new_slots || !new_off) return SGL_ERR_INVALID;
+    if ((prefix_slots == nullptr) != (prefix_off == nullptr)) return SGL_ERR_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_on()) {
+        std::vector<int32_t> rows, col0;
+        std::vector<int64_t> poff, noff;
+        if (!fetch(rows, req_rows, batch, st) || !fetch(noff, new_off, batch + 1, st)) return SGL_ERR_HIP;
+        if (prefix_off && !fetch(poff, prefix_off, batch + 1, st)) return SGL_ERR_HIP;
+        if (new_col0 && !fetch(col0, new_col0, batch, st)) return SGL_ERR_HIP;
+        if (noff[0] != 0 || (prefix_off && poff[0] != 0)) return SGL_ERR_INVALID;
+        for (int r = 0; r < batch; r++) {
+            if (rows[r] < 0 || rows[r] >= num_rows) return SGL_ERR_INVALID;
+            if (noff[r + 1] < noff[r]) return SGL_ERR_INVALID;
+            int64_t P = 0;
+            if (prefix_off) {
+                if (poff[r + 1] < poff[r]) return SGL_ERR_INVALID;
+                P = poff[r + 1] - poff[r];
+            }
+            const int64_t c0 = new_col0 ? col0[r] : P;
+            if (P > row_stride || c0 < 0 || c0 + (noff[r + 1] - noff[r]) > row_stride) return SGL_ERR_INVALID;
+        }
+    }
+    return launch_build_req_to_token(r2t, num_rows, row_stride, req_rows, batch, prefix_slots,
+                                     prefix_off, new_slots, new_off, new_col0, st);
+}
+
+int sgl_store_kv(int dtype, const void *k_new, const void *v_new, int64_t n_tokens,
+                 const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                 int32_t Hkv, int32_t D, void *stream) {
+    if (!shape_ok(dtype, Hkv, Hkv, D)) return SGL_ERR_UNSUPPORTED;
+    if (n_tokens < 0 || num_slots < 0) return SGL_ERR_INVALID;
+    if (n_tokens == 0) return SGL_OK;
+    if (!k_new || !v_new || !slots || !k_pool || !v_pool) return SGL_ERR_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_on()) {
+        std::vector<int32_t> s;
+        if (!fetch(s, slots, (size_t)n_tokens, st)) return SGL_ERR_HIP;
+        for (int32_t x : s)
+            if (x < 0 || x >= num_slots) return SGL_ERR_INVALID;
+    }
+    return launch_store_kv(0, elt_size(dtype), k_new, v_new, n_tokens, slots, k_pool, v_pool, num_slots,
+                           Hkv, D, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0, st);
+}
+
+size_t sgl_extend_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,
+                    void *v_pool, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+                    int64_t row_stride, const int32_t *req_rows, const int32_t *prefix_lens,
+                    const int64_t *q_off, int32_t batch, int64_t n_tokens, int32_t max_extend_len,
+                    int32_t Hq, int32_t Hkv, int32_t D, float scale, void *o, float *lse,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!shape_ok(dtype, Hq, Hkv, D)) return SGL_ERR_UNSUPPORTED;
+    if (batch < 0 || n_tokens < 0 || max_extend_len < 0 || num_slots < 1 || num_rows < 0 || row_stride < 0)
+        return SGL_ERR_INVALID;
+    if (batch == 0 || n_tokens == 0) return SGL_OK;
+    if (!q || !k_pool || !v_pool || !r2t || !req_rows || !prefix_lens || !q_off || !o)
+        return SGL_ERR_INVALID;
+    if ((k_new == nullptr) != (v_new == nullptr)) return SGL_ERR_INVALID;
+    if (max_extend_len == 0) return SGL_ERR_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_on()) {
+        std::vector<int32_t> rows, plen, tab;
+        std::vector<int64_t> off;
+        if (!fetch(rows, req_rows, batch, st) || !fetch(plen, prefix_lens, batch, st) ||
+            !fetch(off, q_off, batch + 1, st) || !fetch(tab, r2t, (size_t)(num_rows * row_stride), st))
+            return SGL_ERR_HIP;
+        if (off[0] != 0 || off[batch] != n_tokens) return SGL_ERR_INVALID;
+        for (int r = 0; r < batch; r++) {
+            const int64_t E = off[r + 1] - off[r];
+            if (E < 0 || E > max_extend_len) return SGL_ERR_INVALID;
+            if (rows[r] < 0 || rows[r] >= num_rows || plen[r] < 0) return SGL_ERR_INVALID;
+            if (plen[r] + E > row_stride) return SGL_ERR_INVALID;
+            if (!slots_ok(tab, row_stride, rows[r], 0, plen[r] + E, num_slots)) return SGL_ERR_INVALID;
+        }
+    }
+    int rc = SGL_OK;
+    if (k_new) {
+        rc = launch_store_kv(1, elt_size(dtype), k_new, v_new, n_tokens, nullptr, k_pool, v_pool,
+                             num_slots, Hkv, D, r2t, num_rows, row_stride, req_rows, prefix_lens,
+                             q_off, batch, max_extend_len, st);
+        if (rc != SGL_OK) return rc;
+    }
+    if (dtype == SGL_F32)
+        return launch_extend_f32((const float *)q, (const float *)k_pool, (const float *)v_pool,
+                                 num_slots, r2t, num_rows, row_stride, req_rows, prefix_lens, q_off,
+                                 batch, max_extend_len, Hq, Hkv, D, scale, (float *)o, lse, st);
+    return launch_extend_bf16((const __bf16 *)q, (const __bf16 *)k_pool, (const __bf16 *)v_pool,
+                              num_slots, r2t, num_rows, row_stride, req_rows, prefix_lens, q_off, batch,
+                              max_extend_len, Hq, Hkv, D, scale, (__bf16 *)o, lse, st);
+}
+
+size_t sgl_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D) {
+    (void)Hkv;
+    if (batch <= 0 || max_seq_len <= 0) return 0;
+    const int64_t S = ceil_div64(max_seq_len, kDecodeChunk);
+    return part_bytes(batch, S, Hq, D);
+}
+
+namespace {
+
+int decode_common(bool cascade, int dtype, const void *q, const void *k_new, const void *v_new,
+                  void *k_pool, void *v_pool, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+                  int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens,
+                  const int32_t *group_ptr, const int32_t *group_prefix_len, int32_t batch, int32_t G,
+                  int32_t max_seq_len, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq,
+                  int32_t Hkv, int32_t D, float scale, void *o, float *lse, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    if (!shape_ok(dtype, Hq, Hkv, D)) return SGL_ERR_UNSUPPORTED;
+    if (batch < 0 || max_seq_len < 0 || num_slots < 1 || num_rows < 0 || row_stride < 0)
+        return SGL_ERR_INVALID;
+    if (batch == 0) return SGL_OK;
+    if (!q || !k_pool || !v_pool || !r2t || !req_rows || !seq_lens || !o) return SGL_ERR_INVALID;
+    if ((k_new == nullptr) != (v_new == nullptr)) return SGL_ERR_INVALID;
+    if (max_seq_len < 1) return SGL_ERR_INVALID;
+    const int g = Hq / Hkv;
+    if (cascade) {
+        if (G < 1 || G > batch || !group_ptr || !group_prefix_len) return SGL_ERR_INVALID;
+        if (max_group_size < 1 || max_prefix_len < 0 || max_prefix_len > max_seq_len) return SGL_ERR_INVALID;
+        if ((int64_t)max_group_size * g > 64) return SGL_ERR_UNSUPPORTED;
+    }
+    const size_t need = cascade ? sgl_cascade_workspace_size(batch, G, max_seq_len, max_group_size,
+                                                             max_prefix_len, Hq, Hkv, D)
+                                : sgl_decode_workspace_size(batch, max_seq_len, Hq, Hkv, D);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return SGL_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (validate_on()) {
+        std::vector<int32_t> rows, lens, tab, gptr, gpl;
+        if (!fetch(rows, req_rows, batch, st) || !fetch(lens, seq_lens, batch, st) ||
+            !fetch(tab, r2t, (size_t)(num_rows * row_stride), st))
+            return SGL_ERR_HIP;
+        for (int r = 0; r < batch; r++) {
+            if (rows[r] < 0 || rows[r] >= num_rows) return SGL_ERR_INVALID;
+            if (lens[r] < 1 || lens[r] > max_seq_len || lens[r] > row_stride) return SGL_ERR_INVALID;
+            if (!slots_ok(tab, row_stride, rows[r], 0, lens[r], num_slots)) return SGL_ERR_INVALID;
+        }
+        if (cascade) {
+            if (!fetch(gptr, group_ptr, G + 1, st) || !fetch(gpl, group_prefix_len, G, st)) return SGL_ERR_HIP;
+            if (gptr[0] != 0 || gptr[G] != batch) return SGL_ERR_INVALID;
+            for (int gg = 0; gg < G; gg++) {
+                const int a = gptr[gg], b = gptr[gg + 1];
+                if (b <= a || b - a > max_group_size) return SGL_ERR_INVALID;
+                if (gpl[gg] < 0 || gpl[gg] > max_prefix_len) return SGL_ERR_INVALID;
+                for (int r = a; r < b; r++) {
+                    if (gpl[gg] > lens[r]) return SGL_ERR_INVALID;
+                    if (std::memcmp(&tab[(size_t)rows[r] * row_stride], &tab[(size_t)rows[a] * row_stride],
+                                    sizeof(int32_t) * (size_t)gpl[gg]) != 0)
+                        return SGL_ERR_INVALID;
+                }
+            }
+        }
+    }
+
+    int rc = SGL_OK;
+    if (k_new) {
+        rc = launch_store_kv(2, elt_size(dtype), k_new, v_new, batch, nullptr, k_pool, v_pool, num_slots,
+                             Hkv, D, r2t, num_rows, row_stride, req_rows, seq_lens, nullptr, batch, 0, st);
+        if (rc != SGL_OK) return rc;
+    }
+
+    char *wp = (char *)workspace;
+    SplitArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots; a.r2t = r2t;
+    a.num_rows = num_rows; a.row_stride = row_stride; a.req_rows = req_rows; a.seq_lens = seq_lens;
+    a.group_ptr = group_ptr; a.group_prefix_len = group_prefix_len; a.batch = batch; a.G = G;
+    a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.scale = scale;
+    auto run_split = [&](const SplitArgs &x) {
+        return dtype == SGL_F32 ? launch_split_f32(x, st) : launch_split_bf16(x, st);
+    };
+
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
+    m.batch = batch; m.G = G; m.Hq = Hq; m.D = D; m.out_bf16 = dtype == SGL_BF16; m.o = o; m.lse = lse;
+    m.chunk_flat = kDecodeChunk; m.chunk_prefix = kPrefixChunk;
+
+    if (!cascade) {
+        const int64_t S = ceil_div64(max_seq_len, kDecodeChunk);
+        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)S; a.chunk = kDecodeChunk;
+        a.part = carve(wp, batch, S, Hq, D);
+        if ((rc = run_split(a)) != SGL_OK) return rc;
+        m.kind = 0; m.flat_or_suffix = a.part;
+        return launch_merge(m, st);
+    }
+    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, kPrefixChunk) : 1;
+    const int64_t Ss = ceil_div64(max_seq_len, kDecodeChunk);
+    SplitArgs pa = a;
+    pa.kind = 1; pa.chunk = kPrefixChunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size;
+    pa.part = carve(wp, batch, Sp, Hq, D);
+    // the f32 path walks (request, head, split) for every kind; the bf16 path one wave per group
+    pa.n_sets = dtype == SGL_F32 ? batch : G;
+    SplitArgs sa = a;
+    sa.kind = 2; sa.chunk = kDecodeChunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
+    sa.part = carve(wp, batch, Ss, Hq, D);
+    if (max_prefix_len > 0 && (rc = run_split(pa)) != SGL_OK) return rc;
+    if ((rc = run_split(sa)) != SGL_OK) return rc;
+    m.kind = 3; m.prefix = pa.part; m.flat_or_suffix = sa.part;
+    if (max_prefix_len == 0) m.kind = 0, m.flat_or_suffix = sa.part;
+    return launch_merge(m, st);
+}
+
+}  // namespace
+
+int sgl_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,
+                    void *v_pool, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+                    int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens, int32_t batch,
+                    int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D, float scale, void *o,
+                    float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(false, dtype, q, k_new, v_new, k_pool, v_pool, num_slots, r2t, num_rows,
+                         row_stride, req_rows, seq_lens, nullptr, nullptr, batch, 0, max_seq_len, 0, 0,
+                         Hq, Hkv, D, scale, o, lse, workspace, workspace_bytes, stream);
+}
+
+size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len, int32_t max_group_size,
+                                  int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D) {
+    (void)Hkv;
+    (void)G;
+    (void)max_group_size;
+    if (batch <= 0 || max_seq_len <= 0) return 0;
+    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, kPrefixChunk) : 1;
+    const int64_t Ss = ceil_div64(max_seq_len, kDecodeChunk);
+    return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, Ss, Hq, D);
+}
+
+int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,
+                            void *v_pool, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+                            int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens,
+                            const int32_t *group_ptr, const int32_t *group_prefix_len, int32_t batch,
+                            int32_t G, int32_t max_seq_len, int32_t max_group_size,
+                            int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                            void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(true, dtype, q, k_new, v_new, k_pool, v_pool, num_slots, r2t, num_rows,
+                         row_stride, req_rows, seq_lens, group_ptr, group_prefix_len, batch, G,
+                         max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D, scale, o, lse,
+                         workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// common.h -- internal helpers shared by the HIP sources of libsgl_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sgl_attn.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define SGL_LDS __attribute__((address_space(3)))
+
+static constexpr float kLog2e = 1.4426950408889634f;
+static constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Split key-index range helpers --------------------------------------------
+__host__ __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// A slot read from req_to_token is used only if it lies in the pool.
+__device__ __forceinline__ int32_t safe_slot(int32_t s, int64_t num_slots) {
+    return (s >= 0 && (int64_t)s < num_slots) ? s : 0;
+}
+
+// Wave-wide reductions (wave64) ------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Launch-side status helper.
+static inline int hip_status(hipError_t e) { return e == hipSuccess ? SGL_OK : SGL_ERR_HIP; }
+
+// Partial softmax state layout written by split kernels and read by the merge:
+//   o part  [B][S][Hq][D] fp32: sum_j exp(s_j - m) v_j  (not normalised)
+//   ml part [B][S][Hq][2] fp32: (m, l) with m in log2 units of the scaled
+//            score (m = max_j s_j * scale * log2 e), l = sum_j 2^(s_j*scale*log2e - m).
+// An empty key set is stored as (m = -inf, l = 0, o = 0).
+struct PartialBuf {
+    float *o;
+    float *ml;
+    int32_t S;  // split capacity per request
+};
+
+// Kernel launchers implemented in the .hip files ----------------------------
+int launch_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                              const int32_t *req_rows, int32_t batch, const int32_t *prefix_slots,
+                              const int64_t *prefix_off, const int32_t *new_slots,
+                              const int64_t *new_off, const int32_t *new_col0, hipStream_t st);
+
+// mode 0: slots[i];  mode 1: extend (r2t at prefix_lens[r] + i);  mode 2: decode (r2t at seq_lens[r]-1)
+int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
+                    const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                    int32_t Hkv, int32_t D, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                    const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
+                    int32_t batch, int32_t max_extend_len, hipStream_t st);
+
+int launch_extend_f32(const float *q, const float *k_pool, const float *v_pool, int64_t num_slots,
+                      const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                      const int32_t *req_rows, const int32_t *prefix_lens, const int64_t *q_off,
+                      int32_t batch, int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D,
+                      float scale, float *o, float *lse, hipStream_t st);
+
+int launch_extend_bf16(const __bf16 *q, const __bf16 *k_pool, const __bf16 *v_pool,
+                       int64_t num_slots, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                       const int32_t *req_rows, const int32_t *prefix_lens, const int64_t *q_off,
+                       int32_t batch, int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D,
+                       float scale, __bf16 *o, float *lse, hipStream_t st);
+
+// Which key range a split kernel covers:
+//   kind 0 (flat):   per request r, keys [0, seq_lens[r])
+//   kind 1 (prefix): per group g, keys [0, group_prefix_len[g]) of the group's first row,
+//                    query rows = every member of the group
+//   kind 2 (suffix): per request r, keys [group_prefix_len[group(r)], seq_lens[r])
+struct SplitArgs {
+    int kind;
+    const void *q;
+    const void *k_pool;
+    const void *v_pool;
+    int64_t num_slots;
+    const int32_t *r2t;
+    int64_t num_rows;
+    int64_t row_stride;
+    const int32_t *req_rows;
+    const int32_t *seq_lens;
+    const int32_t *group_ptr;
+    const int32_t *group_prefix_len;
+    int32_t batch;
+    int32_t G;
+    int32_t n_sets;        // grid extent over requests (kind 0/2) or groups (kind 1)
+    int32_t max_splits;    // grid extent over splits
+    int32_t chunk;         // keys per split
+    int32_t max_members;   // kind 1: rows of a group = members * (Hq/Hkv)
+    int32_t Hq, Hkv, D;
+    float scale;
+    PartialBuf part;
+};
+
+int launch_split_f32(const SplitArgs &a, hipStream_t st);
+int launch_split_bf16(const SplitArgs &a, hipStream_t st);
+
+// Merge partial states of (optionally) a prefix buffer and a suffix buffer.
+//   kind 0: parts = flat splits of r;  kind 3: parts = prefix splits of group(r) for r
+//   + suffix splits of r.
+struct MergeArgs {
+    int kind;
+    PartialBuf flat_or_suffix;
+    PartialBuf prefix;
+    const int32_t *seq_lens;
+    const int32_t *group_ptr;
+    const int32_t *group_prefix_len;
+    int32_t batch, G, chunk_flat, chunk_prefix;
+    int32_t Hq, D;
+    int out_bf16;
+    void *o;
+    float *lse;
+};
+int launch_merge(const MergeArgs &a, hipStream_t st);

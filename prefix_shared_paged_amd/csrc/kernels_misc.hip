@@ -1,0 +1,231 @@
+// kernels_misc.hip -- req_to_token build, KV store, and the log-sum-exp merge
+// of partial softmax states.
+#include "common.h"
+
+// ---------------------------------------------------------------------------
+// req_to_token build: one workgroup per request, columns strided over threads.
+// Row r of the batch writes table row req_rows[r]: columns [0, P_r) from the
+// prefix CSR and [c0, c0 + E_r) from the new-slot CSR ("SGLang 深度解读"
+// module 5: req_to_token maps a request's token positions to pool slots).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) r2t_build_kernel(
+    int32_t *__restrict__ r2t, int64_t num_rows, int64_t stride, const int32_t *__restrict__ req_rows,
+    int32_t batch, const int32_t *__restrict__ prefix_slots, const int64_t *__restrict__ prefix_off,
+    const int32_t *__restrict__ new_slots, const int64_t *__restrict__ new_off,
+    const int32_t *__restrict__ new_col0) {
+    const int r = blockIdx.x;
+    const int64_t row = req_rows[r];
+    if (row < 0 || row >= num_rows) return;
+    int32_t *dst = r2t + row * stride;
+    int64_t P = 0;
+    if (prefix_off) {
+        const int64_t a = prefix_off[r], b = prefix_off[r + 1], total = prefix_off[batch];
+        if (a >= 0 && a <= b && b <= total) {
+            P = b - a;
+            for (int64_t j = threadIdx.x; j < P && j < stride; j += blockDim.x) dst[j] = prefix_slots[a + j];
+        }
+    }
+    const int64_t a = new_off[r], b = new_off[r + 1], total = new_off[batch];
+    if (!(a >= 0 && a <= b && b <= total)) return;
+    const int64_t c0 = new_col0 ? (int64_t)new_col0[r] : P;
+    for (int64_t j = threadIdx.x; j < b - a; j += blockDim.x) {
+        const int64_t c = c0 + j;
+        if (c >= 0 && c < stride) dst[c] = new_slots[a + j];
+    }
+}
+
+int launch_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                              const int32_t *req_rows, int32_t batch, const int32_t *prefix_slots,
+                              const int64_t *prefix_off, const int32_t *new_slots,
+                              const int64_t *new_off, const int32_t *new_col0, hipStream_t st) {
+    if (batch == 0) return SGL_OK;
+    hipLaunchKernelGGL(r2t_build_kernel, dim3(batch), dim3(256), 0, st, r2t, num_rows, row_stride,
+                       req_rows, batch, prefix_slots, prefix_off, new_slots, new_off, new_col0);
+    return hip_status(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
+// KV store: copy token rows (Hkv * D elements = row_chunks * 16 bytes) of K and
+// V into the pools at their slots ("SGLang 深度解读" module 5: write the
+// current K, V at cache_loc before attending).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(256) store_kv_kernel(
+    const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_new, uint4 *__restrict__ k_pool,
+    uint4 *__restrict__ v_pool, int64_t num_slots, int32_t row_chunks, int64_t n_tokens,
+    const int32_t *__restrict__ slots, const int32_t *__restrict__ r2t, int64_t num_rows,
+    int64_t stride, const int32_t *__restrict__ req_rows, const int32_t *__restrict__ lens,
+    const int64_t *__restrict__ q_off) {
+    if (MODE == 1) {
+        // extend: blockIdx.y = request; tokens q_off[r] .. q_off[r+1]
+        const int r = blockIdx.y;
+        const int64_t t0 = q_off[r], t1 = q_off[r + 1];
+        const int64_t row = req_rows[r];
+        const int64_t P = lens[r];
+        if (row < 0 || row >= num_rows || t0 < 0 || t1 > n_tokens || t0 > t1 || P < 0) return;
+        const int64_t n = (t1 - t0) * row_chunks;
+        for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+             idx += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t i = idx / row_chunks, c = idx % row_chunks;
+            const int64_t col = P + i;
+            if (col >= stride) continue;
+            const int32_t s = r2t[row * stride + col];
+            if (s < 0 || s >= num_slots) continue;
+            k_pool[(int64_t)s * row_chunks + c] = k_new[(t0 + i) * row_chunks + c];
+            v_pool[(int64_t)s * row_chunks + c] = v_new[(t0 + i) * row_chunks + c];
+        }
+    } else {
+        const int64_t n = n_tokens * row_chunks;
+        for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+             idx += (int64_t)gridDim.x * blockDim.x) {
+            const int64_t i = idx / row_chunks, c = idx % row_chunks;
+            int32_t s;
+            if (MODE == 0) {
+                s = slots[i];
+            } else {  // decode: token i of request i at position seq_lens[i] - 1
+                const int64_t row = req_rows[i];
+                const int64_t col = (int64_t)lens[i] - 1;
+                if (row < 0 || row >= num_rows || col < 0 || col >= stride) continue;
+                s = r2t[row * stride + col];
+            }
+            if (s < 0 || s >= num_slots) continue;
+            k_pool[(int64_t)s * row_chunks + c] = k_new[i * row_chunks + c];
+            v_pool[(int64_t)s * row_chunks + c] = v_new[i * row_chunks + c];
+        }
+    }
+}
+
+int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
+                    const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                    int32_t Hkv, int32_t D, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                    const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
+                    int32_t batch, int32_t max_extend_len, hipStream_t st) {
+    const int64_t row_bytes = (int64_t)Hkv * D * elt;
+    const int32_t row_chunks = (int32_t)(row_bytes / 16);
+    if (n_tokens == 0) return SGL_OK;
+    const uint4 *kn = (const uint4 *)k_new;
+    const uint4 *vn = (const uint4 *)v_new;
+    uint4 *kp = (uint4 *)k_pool;
+    uint4 *vp = (uint4 *)v_pool;
+    if (mode == 1) {
+        int64_t per_req = (int64_t)max_extend_len * row_chunks;
+        int gx = (int)std::min<int64_t>(ceil_div64(per_req, 256), 1024);
+        if (gx < 1) gx = 1;
+        hipLaunchKernelGGL(store_kv_kernel<1>, dim3(gx, batch), dim3(256), 0, st, kn, vn, kp, vp,
+                           num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
+                           req_rows, lens, q_off);
+    } else {
+        int gx = (int)std::min<int64_t>(ceil_div64(n_tokens * row_chunks, 256), 8192);
+        if (mode == 0)
+            hipLaunchKernelGGL(store_kv_kernel<0>, dim3(gx), dim3(256), 0, st, kn, vn, kp, vp,
+                               num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
+                               req_rows, lens, q_off);
+        else
+            hipLaunchKernelGGL(store_kv_kernel<2>, dim3(gx), dim3(256), 0, st, kn, vn, kp, vp,
+                               num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
+                               req_rows, lens, q_off);
+    }
+    return hip_status(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
+// Merge of partial softmax states.  The pages give the one-key online-softmax
+// update (rescale what was accumulated by e^(m_old - m_new), chenxutan.com
+// section 3.2 PagedPrefill); applied to whole blocks it is
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s o_s 2^(m_s - M) / L
+// (m in log2 units).  One wave per (request, q head); lanes own dims.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int find_group(const int32_t *group_ptr, int G, int r) {
+    int lo = 0, hi = G - 1;  // last g with group_ptr[g] <= r
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (group_ptr[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <int D, bool OUT_BF16>
+__global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= (int64_t)a.batch * a.Hq) return;
+    const int r = (int)(item / a.Hq), h = (int)(item % a.Hq);
+    const int64_t L = a.seq_lens[r];
+
+    // parts: [prefix splits of r][suffix (or flat) splits of r]
+    int np = 0, ns;
+    if (a.kind == 3) {
+        const int g = find_group(a.group_ptr, a.G, r);
+        int64_t P = a.group_prefix_len[g];
+        P = P < 0 ? 0 : (P > L ? L : P);
+        np = (int)ceil_div64(P, a.chunk_prefix);
+        ns = (int)ceil_div64(L - P, a.chunk_flat);
+    } else {
+        ns = (int)ceil_div64(L, a.chunk_flat);
+    }
+    if (np > a.prefix.S) np = a.prefix.S;
+    if (ns > a.flat_or_suffix.S) ns = a.flat_or_suffix.S;
+    const int total = np + ns;
+
+    auto ml_of = [&](int s) -> float2 {
+        const PartialBuf &pb = s < np ? a.prefix : a.flat_or_suffix;
+        const int ss = s < np ? s : s - np;
+        const float *p = pb.ml + (((int64_t)r * pb.S + ss) * a.Hq + h) * 2;
+        return make_float2(p[0], p[1]);
+    };
+    auto o_of = [&](int s) -> const float * {
+        const PartialBuf &pb = s < np ? a.prefix : a.flat_or_suffix;
+        const int ss = s < np ? s : s - np;
+        return pb.o + (((int64_t)r * pb.S + ss) * a.Hq + h) * D;
+    };
+
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < total; s0 += 64) {
+        const int s = s0 + lane;
+        float m = -INFINITY;
+        if (s < total) {
+            float2 v = ml_of(s);
+            if (v.y > 0.f) m = v.x;
+        }
+        M = fmaxf(M, wave_max(m));
+    }
+    constexpr int PER = D / 64;
+    float acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) acc[i] = 0.f;
+    float Lsum = 0.f;
+    for (int s = 0; s < total; s++) {
+        const float2 v = ml_of(s);
+        if (!(v.y > 0.f)) continue;
+        const float f = exp2f(v.x - M);
+        Lsum += v.y * f;
+        const float *op = o_of(s);
+#pragma unroll
+        for (int i = 0; i < PER; i++) acc[i] += op[lane * PER + i] * f;
+    }
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    const int64_t obase = ((int64_t)r * a.Hq + h) * D + lane * PER;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        if (OUT_BF16)
+            ((__bf16 *)a.o)[obase + i] = (__bf16)(acc[i] * inv);
+        else
+            ((float *)a.o)[obase + i] = acc[i] * inv;
+    }
+    if (a.lse && lane == 0)
+        a.lse[(int64_t)r * a.Hq + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+}
+
+int launch_merge(const MergeArgs &a, hipStream_t st) {
+    const int64_t items = (int64_t)a.batch * a.Hq;
+    if (items == 0) return SGL_OK;
+    dim3 grid((unsigned)ceil_div64(items, 4)), block(256);
+    if (a.D == 128) {
+        if (a.out_bf16) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, st, a);
+    } else {
+        if (a.out_bf16) hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, st, a);
+    }
+    return hip_status(hipGetLastError());
+}

@@ -1,0 +1,226 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (stated by the target of this work): fp32 inputs -> max over
+(row, head) of ||o - r||_inf / ||r||_inf <= 1e-5; bf16 inputs -> max |o - r|
+<= 2e-2 with r computed in fp64 from the same bf16 values.  req_to_token rows
+and match lengths are compared bit-exactly with the brute-force model.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from prefix_shared_paged_amd import decode_attn, extend_attn
+from scenarios import (GroupCase, bf16_err, dev, dev_i, f32_rel_err, oracle_decode, oracle_extend,
+                       run_decode, run_extend)
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+LSE_TOL = 1e-3
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# tiny fp32 workload: setup extend (P = 0), extend step, decode step
+# ---------------------------------------------------------------------------
+def test_tiny_fp32_extend_then_decode():
+    wl = W.tiny(seed=0)
+    s = wl.spec
+    case = GroupCase(wl, creator_extend=True)
+    # the setup extend of the shared prefix with nothing cached = dense causal attention
+    g, q0, o0 = case.creator_out[0]
+    K, V = case.prefix_kv[0]
+    O, _, _, _ = oracle.attention([K], [V], np.zeros(64), np.arange(64), q0, s.Hq, s.Hkv)
+    err = f32_rel_err(o0, O)
+    _print("tiny creator extend rel err", err)
+    assert err <= F32_TOL
+    # step 1: 4 requests match 64 and extend 16 each
+    E = np.full(wl.B, 16, np.int64)
+    res = run_extend(case, E)
+    case.check_r2t()
+    idx, O, LSE = oracle_extend(case, res)
+    err = f32_rel_err(res["o"][idx], O)
+    _print("tiny extend rel err", err)
+    assert err <= F32_TOL
+    assert np.max(np.abs(res["lse"][idx] - LSE)) < 1e-4
+    # step 2: the same requests decode one token each at position 80 (L = 81)
+    rows = case.rows
+    case.cache.append(rows, [1] * wl.B)
+    for st in rows:
+        case.mirror.append(st.row, 1)
+    case.check_r2t()
+    kn = np.stack([case.suffix_kv(r)[0][16] for r in range(wl.B)])
+    vn = np.stack([case.suffix_kv(r)[1][16] for r in range(wl.B)])
+    q = np.stack([wl.queries(r, 1, step=1)[0] for r in range(wl.B)])
+    L = np.full(wl.B, 81, np.int32)
+    o = decode_attn(dev(q, "f32"), case.cache.k_pool, case.cache.v_pool, case.cache.r2t,
+                    case.cache.rows_tensor(rows), dev_i(L), 81, k_new=dev(kn, "f32"), v_new=dev(vn, "f32"))
+    from prefix_shared_paged_amd import cascade_decode_attn
+    oc = cascade_decode_attn(dev(q, "f32"), case.cache.k_pool, case.cache.v_pool, case.cache.r2t,
+                             case.cache.rows_tensor(rows), dev_i(L), dev_i([0, wl.B]), dev_i([64]), 81,
+                             wl.B, 64)
+    torch.cuda.synchronize()
+    for r in range(wl.B):
+        Kr, Vr = case.logical_kv(r, 17)
+        Or, _, _, _ = oracle.attention([Kr], [Vr], [0], [80], q[r][None], s.Hq, s.Hkv)
+        e1 = f32_rel_err(o[r].cpu().numpy()[None], Or)
+        e2 = f32_rel_err(oc[r].cpu().numpy()[None], Or)
+        _print("tiny decode rel err", r, e1, e2)
+        assert e1 <= F32_TOL and e2 <= F32_TOL
+
+
+# ---------------------------------------------------------------------------
+# extend: small ragged cases (several tiles, ragged tails, GQA widths, D 64)
+# ---------------------------------------------------------------------------
+def _small_extend_workload(seed, Hq, Hkv, D, prefixes, members, dtype="bf16"):
+    spec = W.Spec("small", dtype, Hq, Hkv, D, 1, 1 << 14, 0.5 if dtype == "bf16" else 1.0, seed)
+    grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
+    sib = np.concatenate([np.arange(m) for m in members]).astype(np.int64)
+    ctx = np.array([prefixes[g] + 300 for g in grp], np.int64)
+    return W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, sib, ctx)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 64), (16, 2, 128), (64, 8, 128), (8, 4, 64)])
+def test_extend_small_ragged(Hq, Hkv, D):
+    wl = _small_extend_workload(1, Hq, Hkv, D, prefixes=[0, 37, 200], members=[2, 2, 2])
+    case = GroupCase(wl)
+    E = np.array([1, 130, 77, 0, 33, 257], np.int64)
+    res = run_extend(case, E)
+    case.check_r2t()
+    idx, O, LSE = oracle_extend(case, res)
+    err = bf16_err(res["o"][idx], O)
+    lerr = float(np.max(np.abs(res["lse"][idx] - LSE)))
+    _print(f"extend small Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL
+    assert lerr <= LSE_TOL
+
+
+def test_extend_fp32_small_ragged():
+    wl = _small_extend_workload(2, 8, 2, 128, prefixes=[5, 64], members=[2, 1], dtype="f32")
+    case = GroupCase(wl)
+    E = np.array([70, 1, 129], np.int64)
+    res = run_extend(case, E)
+    idx, O, _ = oracle_extend(case, res)
+    err = f32_rel_err(res["o"][idx], O)
+    _print("extend fp32 small rel err", err)
+    assert err <= F32_TOL
+
+
+# ---------------------------------------------------------------------------
+# extend at full size: 64 requests x 256 new over a cached 2048-token prefix
+# ---------------------------------------------------------------------------
+def test_extend_full_size_sampled():
+    wl = W.extend(seed=0)
+    case = GroupCase(wl)
+    E = np.full(wl.B, 256, np.int64)
+    res = run_extend(case, E)
+    case.check_r2t()
+    rng = np.random.default_rng(5)
+    sample = [(r, i) for r in range(wl.B) for i in sorted({0, 1, 31, 32, 127, 255, int(rng.integers(256))})]
+    idx, O, LSE = oracle_extend(case, res, rows_sample=sample)
+    err = bf16_err(res["o"][idx], O)
+    lerr = float(np.max(np.abs(res["lse"][idx] - LSE)))
+    _print(f"extend full-size sampled {len(idx)} rows: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+    # every output is finite
+    assert np.isfinite(res["o"]).all()
+
+
+# ---------------------------------------------------------------------------
+# GPU invariants
+# ---------------------------------------------------------------------------
+def _direct_extend(order, P, E, seed=3, Hq=32, Hkv=8, D=128, slots=4096):
+    """One request, logical K/V of P + E tokens; the first P stored as cached prefix."""
+    spec = W.Spec("inv", "bf16", Hq, Hkv, D, 1, slots, 0.5, seed)
+    K = W.values(spec, (P + E, Hkv, D), 1)
+    V = W.values(spec, (P + E, Hkv, D), 2)
+    Q = W.values(spec, (P + E, Hq, D), 3)
+    from prefix_shared_paged_amd.paged_cache import PagedKVCache
+    c = PagedKVCache(slots, 1, Hkv, D, torch.bfloat16, 2, P + E + 1, order)
+    [st] = c.admit([np.arange(P + E, dtype=np.int32) + 1])
+    c.append([st], [P + E])
+    c.store(dev(K[:P], "bf16"), dev(V[:P], "bf16"), st.slots[:P])
+    o = extend_attn(dev(Q[P:], "bf16"), c.k_pool, c.v_pool, c.r2t, c.rows_tensor([st]), dev_i([P]),
+                    dev_i([0, E], torch.int64), E, k_new=dev(K[P:], "bf16"), v_new=dev(V[P:], "bf16"))
+    torch.cuda.synchronize()
+    return o.cpu()
+
+
+def test_prefix_reuse_equals_recompute_bitwise():
+    # rows P.. of extend(P cached, E new) == the same rows of extend(0 cached, P+E new)
+    order = np.random.default_rng(0).permutation(4096).astype(np.int32)
+    for P, E in [(100, 50), (64, 64), (1, 200), (300, 1)]:
+        a = _direct_extend(order, P, E)
+        b = _direct_extend(order, 0, P + E)
+        assert torch.equal(a, b[P:]), (P, E)
+
+
+def test_slot_permutation_invariance_bitwise():
+    o1 = _direct_extend(np.random.default_rng(1).permutation(4096).astype(np.int32), 150, 90)
+    o2 = _direct_extend(np.random.default_rng(2).permutation(4096).astype(np.int32), 150, 90)
+    assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# decode and cascade decode
+# ---------------------------------------------------------------------------
+def _small_decode_workload(seed, Hq=32, Hkv=8, D=128):
+    spec = W.Spec("small_dec", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed)
+    members = [1, 3, 5, 16]
+    prefixes = [0, 1, 300, 256]
+    grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
+    sib = np.concatenate([np.arange(m) for m in members]).astype(np.int64)
+    rng = np.random.default_rng(seed)
+    L = np.array([rng.integers(prefixes[g] + 1, 1300) for g in grp], np.int64)
+    L[1] = 2      # prefix 1 + current token
+    L[4] = 301    # suffix is only the current token
+    L[9] = 257
+    return W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, sib, L)
+
+
+@pytest.mark.parametrize("cascade", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64)])
+def test_decode_small(cascade, Hq, Hkv, D):
+    wl = _small_decode_workload(7, Hq, Hkv, D)
+    if cascade and (Hq // Hkv) * 16 > 64:
+        wl = W.GroupWorkload(wl.spec, wl.prefix_len[:3], wl.grp[:9], wl.sib[:9], wl.ctx_len[:9])
+    case = GroupCase(wl)
+    res = run_decode(case, wl.ctx_len.copy(), cascade)
+    case.check_r2t()
+    reqs, O, LSE = oracle_decode(case, res)
+    err = bf16_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"decode small cascade={cascade} Hq={Hq}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+def test_decode_full_size_flat_and_cascade():
+    wl = W.decode(seed=0)
+    case = GroupCase(wl)
+    res = run_decode(case, wl.ctx_len.copy(), cascade=False, both=True)
+    case.check_r2t()
+    reqs, O, LSE = oracle_decode(case, res)
+    for tag, o, l in (("flat", res["o"], res["lse"]), ("cascade", res["o_c"], res["lse_c"])):
+        err = bf16_err(o[reqs], O)
+        lerr = float(np.max(np.abs(l[reqs] - LSE)))
+        _print(f"decode full {tag}: {len(reqs)} requests, max abs err {err:.3e}, lse err {lerr:.2e}")
+        assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("s", [1, 2, 64, 255, 256, 512])
+def test_fork_cascade(s):
+    wl = W.fork(seed=0)
+    case = GroupCase(wl)
+    L = np.full(wl.B, 4096 + s, np.int64)
+    res = run_decode(case, L, cascade=False, both=True)
+    reqs, O, LSE = oracle_decode(case, res)
+    err = bf16_err(res["o"][reqs], O)
+    err_c = bf16_err(res["o_c"][reqs], O)
+    _print(f"fork s={s}: flat max abs err {err:.3e}, cascade {err_c:.3e}")
+    assert err <= BF16_TOL and err_c <= BF16_TOL

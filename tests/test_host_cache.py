@@ -1,0 +1,158 @@
+"""Host bookkeeping of the library (compressed radix tree + slot pool, C++)
+against the brute-force model in oracle/radix_model.py (an uncompressed trie),
+bit-exact: match lengths and slots, cached-prefix lengths on insert, freed
+counts on evict, tree statistics and the pool's free-list order.
+"""
+import numpy as np
+import pytest
+
+import prefix_shared_paged_amd as sp
+from oracle.radix_model import OutOfSlots, PrefixCache, SlotPool
+
+
+def _drain(pool_lib, pool_model):
+    """Compare the two free lists by allocating everything that is left."""
+    n = pool_model.available()
+    assert pool_lib.available() == n
+    if n == 0:
+        return
+    got = pool_lib.alloc(n)
+    want = pool_model.alloc(0, -1, n)
+    np.testing.assert_array_equal(got, np.asarray(want, np.int32))
+
+
+@pytest.mark.parametrize("p,seed", [(1, 0), (1, 1), (2, 2), (4, 3), (16, 4)])
+def test_random_operations_match_model(p, seed):
+    rng = np.random.default_rng(seed)
+    n_slots = 4096 if p < 16 else 16384
+    order = rng.permutation(n_slots // p).astype(np.int32)
+    pool_l, pool_m = sp.KVPool(n_slots, p, order), SlotPool(n_slots, p, order)
+    tree_l, tree_m = sp.RadixTree(p), PrefixCache(p)
+    vocab = 3 if p == 1 else 2
+    live = []            # (lib handle, model node, tokens, slots, matched)
+    for step in range(2500):
+        op = rng.random()
+        if op < 0.45:
+            # a request: match, maybe lock, allocate, maybe insert, maybe release now
+            L = int(rng.integers(0, 6 * p + 3))
+            toks = rng.integers(0, vocab, size=L).astype(np.int32)
+            n_l, s_l, node_l = tree_l.match(toks)
+            n_m, s_m, node_m = tree_m.match(toks)
+            assert n_l == n_m
+            np.testing.assert_array_equal(s_l, np.asarray(s_m, np.int32))
+            cur_last = int(s_l[-1]) if n_l else -1
+            try:
+                new_m = pool_m.alloc(n_m, cur_last, L - n_m)
+                oom = False
+            except OutOfSlots:
+                oom = True
+            if oom:
+                with pytest.raises(sp.OutOfSlots):
+                    pool_l.alloc(L - n_l, n_l, cur_last)
+                continue
+            new_l = pool_l.alloc(L - n_l, n_l, cur_last)
+            np.testing.assert_array_equal(new_l, np.asarray(new_m, np.int32))
+            slots = np.concatenate([s_l, new_l]).astype(np.int32)
+            if rng.random() < 0.7:
+                c_l = tree_l.insert(toks, slots, pool_l)
+                c_m = tree_m.insert(toks, slots, pool_m)
+                assert c_l == c_m
+                ins = L // p * p
+                # the unshared tail (partial page) goes back to the pool now
+                pool_l.free(slots[ins:])
+                pool_m.free(slots[ins:])
+            else:
+                pool_l.free(slots[n_l:])
+                pool_m.free(slots[n_m:])
+            if rng.random() < 0.3 and n_l > 0:
+                tree_l.lock(node_l, +1)
+                tree_m.lock(node_m, +1)
+                live.append((node_l, node_m))
+        elif op < 0.55 and live:
+            i = int(rng.integers(0, len(live)))
+            node_l, node_m = live.pop(i)
+            tree_l.lock(node_l, -1)
+            tree_m.lock(node_m, -1)
+        elif op < 0.75:
+            want = int(rng.integers(0, 8 * p))
+            f_l = tree_l.evict(want, pool_l)
+            f_m = tree_m.evict(want, pool_m)
+            assert f_l == f_m
+        else:
+            # a request with a duplicate computation of an already cached sequence
+            L = int(rng.integers(1, 4 * p + 1))
+            toks = rng.integers(0, vocab, size=L).astype(np.int32)
+            try:
+                slots_m = pool_m.alloc(0, -1, L)
+            except OutOfSlots:
+                with pytest.raises(sp.OutOfSlots):
+                    pool_l.alloc(L)
+                continue
+            slots_l = pool_l.alloc(L)
+            np.testing.assert_array_equal(slots_l, np.asarray(slots_m, np.int32))
+            assert tree_l.insert(toks, slots_l, pool_l) == tree_m.insert(toks, slots_l, pool_m)
+            ins = L // p * p
+            pool_l.free(slots_l[ins:])
+            pool_m.free(slots_l[ins:])
+        if step % 50 == 0:
+            assert tree_l.stats() == (tree_m.cached_tokens(), tree_m.evictable_tokens())
+            assert pool_l.available() == pool_m.available()
+    for node_l, node_m in live:
+        tree_l.lock(node_l, -1)
+        tree_m.lock(node_m, -1)
+    assert tree_l.evict(10 ** 9, pool_l) == tree_m.evict(10 ** 9, pool_m)
+    assert tree_l.stats() == (0, 0)
+    _drain(pool_l, pool_m)
+
+
+def test_pool_errors_leave_pool_unchanged():
+    pool = sp.KVPool(8, 2, [3, 1, 0, 2])
+    a = pool.alloc(3)                       # pages 3, 1 -> 6, 7, 2
+    np.testing.assert_array_equal(a, [6, 7, 2])
+    with pytest.raises(sp.OutOfSlots):
+        pool.alloc(5)
+    assert pool.available() == 4
+    with pytest.raises(sp.SglError):
+        pool.free([6, 6])                   # same page twice
+    with pytest.raises(sp.SglError):
+        pool.free([0])                      # page 0 is free already
+    with pytest.raises(sp.SglError):
+        pool.free([99])                     # out of range
+    assert pool.available() == 4
+    pool.free(a)
+    assert pool.available() == 8
+    with pytest.raises(sp.SglError):
+        sp.KVPool(8, 2, [0, 0, 1, 2])       # not a permutation
+    with pytest.raises(sp.SglError):
+        sp.KVPool(9, 2)                     # not a whole number of pages
+
+
+def test_tree_errors_leave_tree_unchanged():
+    pool = sp.KVPool(64, 4)
+    tree = sp.RadixTree(4)
+    s = pool.alloc(8)
+    tree.insert([1, 2, 3, 4, 5, 6, 7, 8], s, pool)
+    with pytest.raises(sp.SglError):
+        tree.insert([9, 9, 9, 9], [1, 2, 3, 4], pool)      # page not aligned
+    with pytest.raises(sp.SglError):
+        tree.lock(12345, 1)                                 # unknown node
+    n, _, node = tree.match([1, 2, 3, 4, 5, 6, 7, 8])
+    with pytest.raises(sp.SglError):
+        tree.lock(node, -1)                                 # would go negative
+    assert tree.stats() == (8, 8)
+    assert n == 8
+
+
+def test_figure_example_through_library():
+    # 'SGLang 深度拆解' section 2.3 figure: after the three requests the tree holds
+    # System, Q1+R1, Q2+R2, Q3+R3, Q3b+R3b, Q4+R4 once each.
+    seg = {"S": [1, 2, 3], "Q1": [4, 5], "Q2": [6], "Q3": [7, 8], "Q3b": [9], "Q4": [10, 11]}
+    pool = sp.KVPool(64)
+    tree = sp.RadixTree(1)
+    for path in (["S", "Q1", "Q3", "Q4"], ["S", "Q1", "Q3b"], ["S", "Q2"]):
+        toks = [t for x in path for t in seg[x]]
+        n, slots, _ = tree.match(toks)
+        new = pool.alloc(len(toks) - n)
+        tree.insert(toks, np.concatenate([slots, new]), pool)
+    assert tree.stats() == (sum(len(v) for v in seg.values()),) * 2
+    assert tree.match(seg["S"] + seg["Q1"] + seg["Q2"])[0] == 5

@@ -129,7 +129,7 @@ def test_allocator_fifo_and_pages():
         pool.alloc(0, -1, 5)
     assert pool.available() == 4             # unchanged by the failed request
     pool.free(a + b)                         # pages 2, 0, 3 back in slot order
-    assert pool.free_pages == [1, 2, 0, 3]
+    assert list(pool.free_pages) == [1, 2, 0, 3]
     c = pool.alloc(0, -1, 1)
     assert c == [4]
 
@@ -170,5 +170,5 @@ def test_duplicate_pages_are_freed_on_insert():
     before = pool.available()
     assert tree.insert(toks, s2, pool) == 5  # all already cached
     assert pool.available() == before + 5    # the second copy went back to the pool
-    assert pool.free_pages[-5:] == s2
+    assert list(pool.free_pages)[-5:] == s2
     assert tree.match(toks)[1] == s1

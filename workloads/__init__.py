@@ -42,10 +42,12 @@ def rng(seed, *ids):
 
 def round_to_bf16(x):
     """float32 -> nearest bf16 value (ties to even), returned as float32."""
-    x = np.ascontiguousarray(x, np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    u = np.array(x, np.float32, copy=True).view(np.uint32)   # finite inputs only
+    lsb = (u >> 16) & 1
+    u += 0x7FFF
+    u += lsb
+    u &= 0xFFFF0000
+    return u.view(np.float32)
 
 
 def bf16_bits(x):
