@@ -161,6 +161,39 @@ int sgl_radix_evict(sgl_radix *tree, int64_t n_tokens, sgl_kv_pool *pool, int64_
 int sgl_radix_stats(const sgl_radix *tree, int64_t *out_cached, int64_t *out_evictable);
 
 /* ------------------------------------------------------------------------
+ * Batched host bookkeeping: one call per scheduling batch (the scheduler
+ * admits, allocates, inserts and releases whole batches -- "SGLang 深度解读"
+ * module 2 scheduler loop).  Each is exactly the single-request call applied
+ * to requests 0, 1, ..., batch-1 in order; variable-length per-request data
+ * is passed as CSR: request r's tokens are tokens[off[r] .. off[r+1]).
+ * ---------------------------------------------------------------------- */
+
+/* sgl_radix_match for every request.  Request r's matched slots go to
+ * out_slots[off[r] ..] (capacity off[batch]), its length to out_len[r], its
+ * node to out_node[r] (may be NULL).  lock != 0 also adds 1 to the reference
+ * counts along each matched path (sgl_radix_lock(+1) right after its match). */
+int sgl_radix_match_batch(sgl_radix *tree, const int32_t *tokens, const int64_t *off, int32_t batch,
+                          int32_t lock, int32_t *out_slots, int64_t *out_len, uint64_t *out_node);
+
+/* sgl_radix_insert for every request: tokens / slots in CSR (same off).
+ * out_cached_len: [batch] or NULL.  Stops at the first failing request and
+ * returns its status (earlier requests stay inserted). */
+int sgl_radix_insert_batch(sgl_radix *tree, const int32_t *tokens, const int32_t *slots,
+                           const int64_t *off, int32_t batch, sgl_kv_pool *pool,
+                           int64_t *out_cached_len);
+
+/* sgl_radix_lock(node[r], delta) for every request.  All handles are checked
+ * first; on error nothing changes. */
+int sgl_radix_lock_batch(sgl_radix *tree, const uint64_t *nodes, int32_t batch, int32_t delta);
+
+/* sgl_kv_pool_alloc for every request (cur_len[r], last_slot[r], n[r]);
+ * request r's slots go to out_slots[o_r ..] where o_r = n[0] + ... + n[r-1].
+ * All or nothing: if the pool cannot serve the whole batch it returns
+ * SGL_ERR_OOM and is unchanged. */
+int sgl_kv_pool_alloc_batch(sgl_kv_pool *pool, const int64_t *cur_len, const int32_t *last_slot,
+                            const int64_t *n, int32_t batch, int32_t *out_slots);
+
+/* ------------------------------------------------------------------------
  * Device operations.
  * ---------------------------------------------------------------------- */
 
@@ -244,7 +277,9 @@ size_t sgl_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq,
  * columns [0, group_prefix_len[g]) (the prefix slots are read from the row
  * of the group's first request) and group_prefix_len[g] <= seq_lens[r] for
  * its requests.  max_group_size, max_prefix_len: host bounds (grid sizing);
- * max_group_size * (Hq / Hkv) <= 128.
+ * max_group_size * (Hq / Hkv) <= 4096.  Up to 64 query rows of a group
+ * (request x query head) share one read of the prefix; larger groups read it
+ * once per 64 rows.
  * workspace: sgl_cascade_workspace_size(...) bytes. */
 int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new,
                             void *k_pool, void *v_pool, int64_t num_slots,

@@ -59,6 +59,10 @@ def load():
         "sgl_radix_lock": (ctypes.c_int, [P, ctypes.c_uint64, I32]),
         "sgl_radix_evict": (ctypes.c_int, [P, I64, P, P]),
         "sgl_radix_stats": (ctypes.c_int, [P, P, P]),
+        "sgl_radix_match_batch": (ctypes.c_int, [P, P, P, I32, I32, P, P, P]),
+        "sgl_radix_insert_batch": (ctypes.c_int, [P, P, P, P, I32, P, P]),
+        "sgl_radix_lock_batch": (ctypes.c_int, [P, P, I32, I32]),
+        "sgl_kv_pool_alloc_batch": (ctypes.c_int, [P, P, P, P, I32, P]),
         "sgl_build_req_to_token": (ctypes.c_int, [P, I64, I64, P, I32, P, P, P, P, P, P]),
         "sgl_store_kv": (ctypes.c_int, [ctypes.c_int, P, P, I64, P, P, P, I64, I32, I32, P]),
         "sgl_extend_attn": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P, P, P,
@@ -83,7 +87,8 @@ def load():
 EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_kv_pool_create", "sgl_kv_pool_destroy",
            "sgl_kv_pool_alloc", "sgl_kv_pool_free", "sgl_kv_pool_available", "sgl_radix_create",
            "sgl_radix_destroy", "sgl_radix_match", "sgl_radix_insert", "sgl_radix_lock",
-           "sgl_radix_evict", "sgl_radix_stats", "sgl_build_req_to_token", "sgl_store_kv",
+           "sgl_radix_evict", "sgl_radix_stats", "sgl_radix_match_batch", "sgl_radix_insert_batch",
+           "sgl_radix_lock_batch", "sgl_kv_pool_alloc_batch", "sgl_build_req_to_token", "sgl_store_kv",
            "sgl_extend_attn", "sgl_extend_workspace_size", "sgl_decode_attn",
            "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size"]
 
@@ -130,6 +135,18 @@ class KVPool:
         out = np.empty(int(n), np.int32)
         _check("sgl_kv_pool_alloc", load().sgl_kv_pool_alloc(self._h, cur_len, last_slot, n, _np_ptr(out)))
         return out
+
+    def alloc_batch(self, n, cur_len, last_slot):
+        """Batched alloc (all or nothing); returns (flat slots, offsets)."""
+        n = np.ascontiguousarray(n, np.int64)
+        cur = np.ascontiguousarray(cur_len, np.int64)
+        last = _i32(last_slot)
+        off = np.zeros(n.size + 1, np.int64)
+        np.cumsum(n, out=off[1:])
+        out = np.empty(max(int(off[-1]), 1), np.int32)
+        _check("sgl_kv_pool_alloc_batch", load().sgl_kv_pool_alloc_batch(
+            self._h, _np_ptr(cur), _np_ptr(last), _np_ptr(n), n.size, _np_ptr(out)))
+        return out[:off[-1]], off
 
     def free(self, slots):
         s = _i32(slots)
@@ -180,6 +197,33 @@ class RadixTree:
 
     def lock(self, node, delta):
         _check("sgl_radix_lock", load().sgl_radix_lock(self._h, node, delta))
+
+    def match_batch(self, tokens, off, lock=False):
+        """Batched match over CSR tokens; returns (slots CSR on the same off, lens, nodes)."""
+        t = _i32(tokens)
+        off = np.ascontiguousarray(off, np.int64)
+        B = off.size - 1
+        slots = np.empty(max(t.size, 1), np.int32)
+        lens = np.empty(B, np.int64)
+        nodes = np.empty(B, np.uint64)
+        _check("sgl_radix_match_batch", load().sgl_radix_match_batch(
+            self._h, _np_ptr(t), _np_ptr(off), B, int(bool(lock)), _np_ptr(slots), _np_ptr(lens),
+            _np_ptr(nodes)))
+        return slots, lens, nodes
+
+    def insert_batch(self, tokens, slots, off, pool=None):
+        t, s = _i32(tokens), _i32(slots)
+        off = np.ascontiguousarray(off, np.int64)
+        B = off.size - 1
+        cached = np.empty(B, np.int64)
+        _check("sgl_radix_insert_batch", load().sgl_radix_insert_batch(
+            self._h, _np_ptr(t), _np_ptr(s), _np_ptr(off), B, pool.handle if pool is not None else None,
+            _np_ptr(cached)))
+        return cached
+
+    def lock_batch(self, nodes, delta):
+        nd = np.ascontiguousarray(nodes, np.uint64)
+        _check("sgl_radix_lock_batch", load().sgl_radix_lock_batch(self._h, _np_ptr(nd), nd.size, delta))
 
     def evict(self, n_tokens, pool):
         freed = ctypes.c_int64()

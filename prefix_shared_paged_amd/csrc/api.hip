@@ -211,7 +211,7 @@ int decode_common(bool cascade, int dtype, const void *q, const void *k_new, con
     if (cascade) {
         if (G < 1 || G > batch || !group_ptr || !group_prefix_len) return SGL_ERR_INVALID;
         if (max_group_size < 1 || max_prefix_len < 0 || max_prefix_len > max_seq_len) return SGL_ERR_INVALID;
-        if ((int64_t)max_group_size * g > 64) return SGL_ERR_UNSUPPORTED;
+        if ((int64_t)max_group_size * g > 4096) return SGL_ERR_UNSUPPORTED;
     }
     const size_t need = cascade ? sgl_cascade_workspace_size(batch, G, max_seq_len, max_group_size,
                                                              max_prefix_len, Hq, Hkv, D)

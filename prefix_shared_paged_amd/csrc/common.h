@@ -105,6 +105,7 @@ struct SplitArgs {
     int32_t max_splits;    // grid extent over splits
     int32_t chunk;         // keys per split
     int32_t max_members;   // kind 1: rows of a group = members * (Hq/Hkv)
+    int32_t row_blocks;    // kind 1: waves per group (64 rows each) -- set by the launcher
     int32_t Hq, Hkv, D;
     float scale;
     PartialBuf part;

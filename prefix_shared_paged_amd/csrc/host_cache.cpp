@@ -409,4 +409,73 @@ int sgl_radix_stats(const sgl_radix *t, int64_t *out_cached, int64_t *out_evicta
     return SGL_OK;
 }
 
+int sgl_radix_match_batch(sgl_radix *t, const int32_t *tokens, const int64_t *off, int32_t batch,
+                          int32_t lock, int32_t *out_slots, int64_t *out_len, uint64_t *out_node) {
+    if (!t || batch < 0 || (batch > 0 && (!off || !out_len))) return SGL_ERR_INVALID;
+    for (int32_t r = 0; r < batch; r++)
+        if (off[r] < 0 || off[r + 1] < off[r]) return SGL_ERR_INVALID;
+    for (int32_t r = 0; r < batch; r++) {
+        uint64_t node = 0;
+        int rc = sgl_radix_match(t, tokens + off[r], off[r + 1] - off[r], out_slots ? out_slots + off[r] : nullptr,
+                                 &out_len[r], &node);
+        if (rc != SGL_OK) return rc;
+        if (lock && (rc = sgl_radix_lock(t, node, +1)) != SGL_OK) return rc;
+        if (out_node) out_node[r] = node;
+    }
+    return SGL_OK;
+}
+
+int sgl_radix_insert_batch(sgl_radix *t, const int32_t *tokens, const int32_t *slots, const int64_t *off,
+                           int32_t batch, sgl_kv_pool *pool, int64_t *out_cached_len) {
+    if (!t || batch < 0 || (batch > 0 && !off)) return SGL_ERR_INVALID;
+    for (int32_t r = 0; r < batch; r++) {
+        if (off[r] < 0 || off[r + 1] < off[r]) return SGL_ERR_INVALID;
+        int rc = sgl_radix_insert(t, tokens + off[r], slots + off[r], off[r + 1] - off[r], pool,
+                                  out_cached_len ? &out_cached_len[r] : nullptr);
+        if (rc != SGL_OK) return rc;
+    }
+    return SGL_OK;
+}
+
+int sgl_radix_lock_batch(sgl_radix *t, const uint64_t *nodes, int32_t batch, int32_t delta) {
+    if (!t || batch < 0 || (batch > 0 && !nodes) || (delta != 1 && delta != -1)) return SGL_ERR_INVALID;
+    return guarded([&] {
+        // check everything first (a node may appear several times)
+        std::unordered_map<Node *, int64_t> change;
+        for (int32_t r = 0; r < batch; r++) {
+            if (nodes[r] == 0) continue;
+            auto it = t->by_id.find(nodes[r]);
+            if (it == t->by_id.end()) return (int)SGL_ERR_INVALID;
+            for (Node *x = it->second; x && x != &t->root; x = x->parent) change[x] += delta;
+        }
+        for (auto &kv : change)
+            if (kv.first->ref + kv.second < 0) return (int)SGL_ERR_INVALID;
+        for (auto &kv : change) kv.first->ref += kv.second;
+        return (int)SGL_OK;
+    });
+}
+
+int sgl_kv_pool_alloc_batch(sgl_kv_pool *pool, const int64_t *cur_len, const int32_t *last_slot,
+                            const int64_t *n, int32_t batch, int32_t *out_slots) {
+    if (!pool || batch < 0 || (batch > 0 && (!cur_len || !last_slot || !n))) return SGL_ERR_INVALID;
+    const int32_t p = pool->page;
+    int64_t need_pages = 0, total = 0;
+    for (int32_t r = 0; r < batch; r++) {
+        if (n[r] < 0 || cur_len[r] < 0) return SGL_ERR_INVALID;
+        int64_t fill = 0;
+        if (p > 1 && cur_len[r] % p != 0) fill = std::min<int64_t>(n[r], p - cur_len[r] % p);
+        need_pages += (n[r] - fill + p - 1) / p;
+        total += n[r];
+    }
+    if (total > 0 && !out_slots) return SGL_ERR_INVALID;
+    if (need_pages > (int64_t)pool->free_pages.size()) return SGL_ERR_OOM;
+    int64_t o = 0;
+    for (int32_t r = 0; r < batch; r++) {
+        int rc = sgl_kv_pool_alloc(pool, cur_len[r], last_slot[r], n[r], out_slots + o);
+        if (rc != SGL_OK) return rc;   // only argument errors can remain here
+        o += n[r];
+    }
+    return SGL_OK;
+}
+
 }  // extern "C"

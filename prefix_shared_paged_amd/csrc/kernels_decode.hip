@@ -56,7 +56,9 @@ __global__ void __launch_bounds__(64) split_bf16_kernel(SplitArgs a) {
     const int lane = threadIdx.x;
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
-    const int set = blockIdx.z;
+    const int n_rb = a.kind == 1 ? a.row_blocks : 1;   // 16*NB-row blocks of a big group
+    const int set = blockIdx.z / n_rb;
+    const int rb = blockIdx.z % n_rb;
     const int g = a.Hq / a.Hkv;
 
     // ---- which rows, which keys ----------------------------------------------
@@ -85,8 +87,9 @@ __global__ void __launch_bounds__(64) split_bf16_kernel(SplitArgs a) {
         }
         hi = L;
     }
-    const int rows = n_members * g;
-    if (rows > 16 * NB) return;  // host guarantees this never happens
+    const int row_base = rb * 16 * NB;              // first group row of this wave
+    const int rows = n_members * g - row_base;      // rows left from row_base on
+    if (rows <= 0) return;
     if (ref_row < 0 || ref_row >= a.num_rows) return;
     if (hi > a.row_stride) hi = a.row_stride;
     const int64_t n_split = ceil_div64(hi - lo, a.chunk);
@@ -109,8 +112,8 @@ __global__ void __launch_bounds__(64) split_bf16_kernel(SplitArgs a) {
     for (int nb = 0; nb < NB; nb++) {
         const int rho = nb * 16 + n16;
         if (rho < rows) {
-            const int req = first_req + rho / g;
-            const int h = kvh * g + rho % g;
+            const int req = first_req + (row_base + rho) / g;
+            const int h = kvh * g + (row_base + rho) % g;
             const uint4 *src = (const uint4 *)(q + ((int64_t)req * a.Hq + h) * D + (D / 4) * kq);
 #pragma unroll
             for (int t = 0; t < QT; t++) qf[nb][t] = as_bf16x8(src[t]);
@@ -249,8 +252,8 @@ __global__ void __launch_bounds__(64) split_bf16_kernel(SplitArgs a) {
         l += __shfl_xor(l, 32, 64);
         const int rho = nb * 16 + n16;
         if (rho >= rows) continue;
-        const int req = first_req + rho / g;
-        const int h = kvh * g + rho % g;
+        const int req = first_req + (row_base + rho) / g;
+        const int h = kvh * g + (row_base + rho) % g;
         const int64_t idx = ((int64_t)req * a.part.S + s) * a.Hq + h;
         float *op = a.part.o + idx * D;
 #pragma unroll
@@ -267,21 +270,25 @@ __global__ void __launch_bounds__(64) split_bf16_kernel(SplitArgs a) {
 int launch_split_bf16(const SplitArgs &a, hipStream_t st) {
     if (a.n_sets == 0 || a.max_splits == 0) return SGL_OK;
     const int g = a.Hq / a.Hkv;
-    const int rows = (a.kind == 1 ? a.max_members : 1) * g;
-    dim3 grid(a.Hkv, a.max_splits, a.n_sets), block(64);
+    int rows = (a.kind == 1 ? a.max_members : 1) * g;
+    SplitArgs b = a;
+    b.row_blocks = 1;
+    if (rows > 64) {                 // big groups: several 64-row waves per group
+        b.row_blocks = (rows + 63) / 64;
+        rows = 64;
+    }
+    dim3 grid(a.Hkv, a.max_splits, a.n_sets * b.row_blocks), block(64);
     const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
 #define SGL_LAUNCH(DD, NBB) \
-    hipLaunchKernelGGL((split_bf16_kernel<DD, NBB>), grid, block, dyn, st, a)
+    hipLaunchKernelGGL((split_bf16_kernel<DD, NBB>), grid, block, dyn, st, b)
     if (a.D == 128) {
         if (rows <= 16) SGL_LAUNCH(128, 1);
         else if (rows <= 32) SGL_LAUNCH(128, 2);
-        else if (rows <= 64) SGL_LAUNCH(128, 4);
-        else return SGL_ERR_UNSUPPORTED;
+        else SGL_LAUNCH(128, 4);
     } else {
         if (rows <= 16) SGL_LAUNCH(64, 1);
         else if (rows <= 32) SGL_LAUNCH(64, 2);
-        else if (rows <= 64) SGL_LAUNCH(64, 4);
-        else return SGL_ERR_UNSUPPORTED;
+        else SGL_LAUNCH(64, 4);
     }
 #undef SGL_LAUNCH
     return hip_status(hipGetLastError());

@@ -156,3 +156,55 @@ def test_figure_example_through_library():
         tree.insert(toks, np.concatenate([slots, new]), pool)
     assert tree.stats() == (sum(len(v) for v in seg.values()),) * 2
     assert tree.match(seg["S"] + seg["Q1"] + seg["Q2"])[0] == 5
+
+
+def test_batched_calls_equal_sequential_calls():
+    rng = np.random.default_rng(11)
+    for p in (1, 4):
+        order = rng.permutation(2048 // p).astype(np.int32)
+        pa, pb = sp.KVPool(2048, p, order), sp.KVPool(2048, p, order)
+        ta, tb = sp.RadixTree(p), sp.RadixTree(p)
+        for it in range(30):
+            B = int(rng.integers(1, 6))
+            toks = [rng.integers(0, 3, size=int(rng.integers(0, 5 * p + 2))).astype(np.int32) for _ in range(B)]
+            off = np.zeros(B + 1, np.int64)
+            off[1:] = np.cumsum([len(t) for t in toks])
+            flat = np.concatenate(toks) if off[-1] else np.zeros(0, np.int32)
+            sl, lens, nodes = ta.match_batch(flat, off, lock=True)
+            singles = []
+            for r, t in enumerate(toks):
+                n, s1, node = tb.match(t)
+                tb.lock(node, +1)
+                singles.append((n, s1, node))
+                assert lens[r] == n
+                np.testing.assert_array_equal(sl[off[r]:off[r] + n], s1)
+            need = np.array([len(t) - n for t, (n, _, _) in zip(toks, singles)], np.int64)
+            cur = np.array([n for n, _, _ in singles], np.int64)
+            last = np.array([int(s1[-1]) if n else -1 for n, s1, _ in singles], np.int32)
+            new_a, noff = pa.alloc_batch(need, cur, last)
+            new_b = [pb.alloc(int(k), int(c), int(l)) for k, c, l in zip(need, cur, last)]
+            np.testing.assert_array_equal(new_a, np.concatenate(new_b) if new_b else new_a)
+            full = [np.concatenate([s1, new_a[noff[r]:noff[r + 1]]]) for r, (n, s1, _) in enumerate(singles)]
+            ca = ta.insert_batch(flat, np.concatenate(full) if off[-1] else np.zeros(0, np.int32), off, pa)
+            cb = [tb.insert(t, f, pb) for t, f in zip(toks, full)]
+            np.testing.assert_array_equal(ca, cb)
+            for r, t in enumerate(toks):
+                ins = len(t) // p * p
+                pa.free(full[r][ins:])
+                pb.free(full[r][ins:])
+            ta.lock_batch(nodes, -1)
+            for _, _, node in singles:
+                tb.lock(node, -1)
+            assert ta.stats() == tb.stats()
+            assert pa.available() == pb.available()
+            want = int(rng.integers(0, 6))
+            assert ta.evict(want, pa) == tb.evict(want, pb)
+
+
+def test_batched_alloc_is_all_or_nothing():
+    pool = sp.KVPool(64, 4)
+    with pytest.raises(sp.OutOfSlots):
+        pool.alloc_batch([32, 40], [0, 0], [-1, -1])
+    assert pool.available() == 64
+    a, off = pool.alloc_batch([3, 5], [0, 0], [-1, -1])
+    assert off.tolist() == [0, 3, 8] and pool.available() == 64 - 12

@@ -83,9 +83,9 @@ def test_device_calls_reject_bad_arguments_before_gpu_work():
     assert need > 0
     assert lib.sgl_decode_attn(sp.SGL_BF16, p, None, None, p, p, 16, p, 4, 1000, p, p, 4, 1000, 32,
                                8, 128, 0.1, p, None, p, need - 1, None) == sp.SGL_ERR_WORKSPACE
-    # cascade: group too large for one wave's rows (16 requests x 8 heads = 128 > 64)
+    # cascade: group larger than supported (1024 requests x 8 heads > 4096 rows)
     assert lib.sgl_cascade_decode_attn(sp.SGL_BF16, p, None, None, p, p, 16, p, 16, 100, p, p, p, p,
-                                       16, 1, 100, 16, 50, 64, 8, 128, 0.1, p, None, p, 1 << 24,
+                                       1024, 1, 100, 1024, 50, 64, 8, 128, 0.1, p, None, p, 1 << 24,
                                        None) == sp.SGL_ERR_UNSUPPORTED
     # cascade: prefix bound larger than the context bound
     assert lib.sgl_cascade_decode_attn(sp.SGL_BF16, p, None, None, p, p, 16, p, 4, 100, p, p, p, p, 4,
