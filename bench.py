@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--config", default="extend", choices=["extend", "decode", "fork", "multiturn"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (scales HBM counters)")
     return ap.parse_args()
 
 
@@ -310,8 +312,415 @@ def cpu_baseline_extend(wl, P, E, target_s):
                       f"{P}+i keys), fp64 oracle, {t:.1f} s"}
 
 
+
+# ---------------------------------------------------------------------------
+# shared helpers for the other workloads
+# ---------------------------------------------------------------------------
+def fill_random(t, scale=0.5, seed=0, chunk=1 << 26):
+    """Fill a bf16 device tensor with N(0,1)*scale values (device RNG, in chunks)."""
+    import torch
+    g = torch.Generator(device=t.device)
+    g.manual_seed(seed)
+    flat = t.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        flat[i:i + n] = (torch.randn(n, generator=g, device=t.device) * scale).to(t.dtype)
+
+
+def cpu_baseline_rows(K_list, V_list, rows, Hq, Hkv, target_s, what):
+    """Time the oracle on query rows (req, pos, q) of given logical sequences; the
+    sample grows from a calibration run to take about target_s seconds."""
+    import oracle
+    rows = list(rows)
+
+    def run(k):
+        sub = rows[:k]
+        t0 = time.perf_counter()
+        oracle.attention(K_list, V_list, [r for r, _, _ in sub], [p for _, p, _ in sub],
+                         np.stack([q for _, _, q in sub]), Hq, Hkv)
+        return time.perf_counter() - t0
+
+    k = max(1, min(len(rows), 8))
+    t = run(k)
+    k2 = int(min(len(rows), max(k, k * target_s / max(t, 1e-3))))
+    if k2 > k:
+        k, t = k2, run(k2)
+    return {"value": k / t, "unit": "tokens/s", "cores": __import__("oracle").default_threads(),
+            "kind": "oracle", "sample": f"{k} {what} query tokens (all {Hq} heads), fp64 oracle, {t:.1f} s"}
+
+
+def setup_groups(cache, wl, store_prefix=False):
+    """Insert each group's prefix into the tree (its K/V are whatever the pool holds)."""
+    for g in range(wl.G):
+        toks = wl.prefix_tokens(g)
+        [st] = cache.admit([toks])
+        cache.append([st], [len(toks)])
+        cache.insert(st)
+        cache.release(st)
+
+
+def time_events(fn, n, warm=3):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def base_line(metric_value, ms, args, config, roofline, extra):
+    line = {"metric": "decode attn tokens/s + HBM GB/s; extend attn TFLOP/s (frac of roofline)",
+            "value": metric_value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
+            "roofline": roofline}
+    line.update(extra)
+    return line
+
+
+# ---------------------------------------------------------------------------
+# decode batch: 256 requests in 16 prefix groups, one token each (flat and cascade)
+# ---------------------------------------------------------------------------
+def bench_decode(args):
+    import torch
+    import workloads as W
+    import prefix_shared_paged_amd as sp
+    from prefix_shared_paged_amd import accounting as acc
+    from prefix_shared_paged_amd.paged_cache import PagedKVCache
+
+    wl = W.decode(seed=0)
+    s = wl.spec
+    B, G, Hq, Hkv, D = wl.B, wl.G, s.Hq, s.Hkv, s.D
+    dev = "cuda"
+    L = wl.ctx_len.astype(np.int64)
+    P = wl.prefix_len[wl.grp].astype(np.int64)
+    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, int(L.max()) + 1, W.pool_order(s), dev)
+    fill_random(cache.k_pool, seed=1)
+    fill_random(cache.v_pool, seed=2)
+    setup_groups(cache, wl)
+    toks = [np.concatenate([wl.prefix_tokens(wl.grp[r]), wl.suffix_tokens(r)]) for r in range(B)]
+    rows = cache.admit(toks)
+    assert all(st.matched == P[r] for r, st in enumerate(rows))
+    cache.append(rows, (L - P - 1).tolist())          # cached history of each suffix
+    q = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    kn = torch.empty((B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vn = torch.empty((B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    for t, sd in ((q, 3), (kn, 4), (vn, 5)):
+        fill_random(t, seed=sd)
+    o = torch.empty_like(q)
+    req_rows = cache.rows_tensor(rows)
+    seq = torch.from_numpy(L.astype(np.int32)).to(dev)
+    col0 = torch.from_numpy((L - 1).astype(np.int32)).to(dev)
+    gptr = torch.from_numpy(np.concatenate([[0], np.cumsum(np.bincount(wl.grp, minlength=G))]).astype(np.int32)).to(dev)
+    gpl = torch.from_numpy(wl.prefix_len.astype(np.int32)).to(dev)
+    ws_f = torch.empty(sp.decode_workspace_size(B, int(L.max()), Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(sp.cascade_workspace_size(B, G, int(L.max()), 16, int(wl.prefix_len.max()), Hq, Hkv, D),
+                       dtype=torch.uint8, device=dev)
+    d_new = torch.empty(B, dtype=torch.int32, device=dev)
+    d_noff = torch.arange(B + 1, dtype=torch.int64, device=dev)
+    pin = Pinned(torch, 3, {"new": (B, torch.int32)})
+    pool = cache.pool
+    last = np.array([int(st.slots[-1]) for st in rows], np.int32)
+    ev = []
+
+    def step(cascade, timed):
+        # a1: one slot per request for the current token;  a3: append it to req_to_token
+        new, _ = pool.alloc_batch(np.ones(B, np.int64), L - 1, last)
+        k, buf = pin.next()
+        buf["new"].numpy()[:] = new
+        d_new.copy_(buf["new"], non_blocking=True)
+        pin.done(k)
+        sp.build_req_to_token(cache.r2t, req_rows, d_new, d_noff, new_col0=col0)
+        if timed:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+        if cascade:   # a4 + a7
+            sp.cascade_decode_attn(q, cache.k_pool, cache.v_pool, cache.r2t, req_rows, seq, gptr, gpl,
+                                   int(L.max()), 16, int(wl.prefix_len.max()), k_new=kn, v_new=vn, o=o,
+                                   workspace=ws_c)
+        else:         # a4 + a6
+            sp.decode_attn(q, cache.k_pool, cache.v_pool, cache.r2t, req_rows, seq, int(L.max()),
+                           k_new=kn, v_new=vn, o=o, workspace=ws_f)
+        if timed:
+            b.record()
+            ev.append((a, b))
+        pool.free(new)
+
+    res = {}
+    for mode in ("cascade", "flat"):
+        ev.clear()
+        for _ in range(args.warmup):
+            step(mode == "cascade", False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(mode == "cascade", True)
+        torch.cuda.synchronize()
+        res[mode] = ((time.perf_counter() - t0) * 1e3 / args.steps,
+                     float(np.mean([a.elapsed_time(b) for a, b in ev])))
+    flat_bytes = acc.decode_bytes_flat(L, Hq, Hkv, D, 2)
+    casc_bytes = acc.decode_bytes_cascade(L, wl.grp, wl.prefix_len, Hq, Hkv, D, 2)
+    ms_c, call_c = res["cascade"]
+    ms_f, call_f = res["flat"]
+    gbps_c = casc_bytes / (call_c * 1e-3) / 1e9
+    gbps_f = flat_bytes / (call_f * 1e-3) / 1e9
+    config = {"workload": "decode: 256 requests in 16 prefix groups (prefix ~U[512,4096], context "
+                          "~U[max(1024,P+1),8192]), one token each, cascade decode; 32/8 heads, head_dim 128, "
+                          "2^21-slot pool, page 1", "batch": B, "groups": G}
+    roof = {"bound": "hbm", "achieved": gbps_c, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": gbps_c / PEAK_HBM_GBPS, "traffic": traffic_record("split_bf16_kernel"),
+            "kernel": "cascade decode call (prefix + suffix split kernels + merge)",
+            "bytes_per_launch": casc_bytes, "avg_launch_ms": call_c}
+    line = base_line(B / (ms_c * 1e-3), ms_c, args, config, roof, {
+        "flat": {"ms_per_step": ms_f, "call_ms": call_f, "hbm_gbps": gbps_f, "frac": gbps_f / PEAK_HBM_GBPS,
+                 "tokens_per_s": B / (ms_f * 1e-3), "algorithmic_bytes": flat_bytes},
+        "cascade": {"call_ms": call_c, "hbm_gbps": gbps_c, "algorithmic_bytes": casc_bytes,
+                    "tokens_per_s_call_only": B / (call_c * 1e-3)}})
+    if not args.no_cpu_baseline:
+        # oracle sample: decode rows of the first requests, drawn by the seeded generator
+        Ks, Vs, rws = [], [], []
+        for r in range(min(B, 24)):
+            K, V = wl.logical_kv(r)
+            Ks.append(K)
+            Vs.append(V)
+            rws.append((r, int(L[r]) - 1, wl.queries(r, 1)[0]))
+        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "decode")
+    return line
+
+
+# ---------------------------------------------------------------------------
+# fork: 16 prompts x 4096 tokens, 8 branches each; suffixes grow 1..512 (cascade)
+# ---------------------------------------------------------------------------
+def bench_fork(args):
+    import torch
+    import workloads as W
+    import prefix_shared_paged_amd as sp
+    from prefix_shared_paged_amd import accounting as acc
+    from prefix_shared_paged_amd.paged_cache import PagedKVCache
+
+    wl = W.fork(seed=0)
+    s = wl.spec
+    B, G, Hq, Hkv, D = wl.B, wl.G, s.Hq, s.Hkv, s.D
+    Pp, S = 4096, 512
+    dev = "cuda"
+    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, Pp + S + 1, W.pool_order(s), dev)
+    fill_random(cache.k_pool, seed=1)
+    fill_random(cache.v_pool, seed=2)
+    setup_groups(cache, wl)
+    rows = cache.admit([np.concatenate([wl.prefix_tokens(wl.grp[r]), wl.suffix_tokens(r, 1)]) for r in range(B)])
+    assert all(st.matched == Pp for st in rows)
+    q = torch.empty((S, B, Hq, D), dtype=torch.bfloat16, device=dev)     # one query batch per step
+    kn = torch.empty((S, B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vn = torch.empty((S, B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    for t, sd in ((q, 3), (kn, 4), (vn, 5)):
+        fill_random(t, seed=sd)
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    req_rows = cache.rows_tensor(rows)
+    gptr = torch.arange(0, B + 1, 8, dtype=torch.int32, device=dev)
+    gpl = torch.full((G,), Pp, dtype=torch.int32, device=dev)
+    seqs = [torch.full((B,), Pp + k, dtype=torch.int32, device=dev) for k in range(1, S + 1)]
+    col0s = [torch.full((B,), Pp + k - 1, dtype=torch.int32, device=dev) for k in range(1, S + 1)]
+    ws = torch.empty(sp.cascade_workspace_size(B, G, Pp + S, 8, Pp, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    d_new = torch.empty((S, B), dtype=torch.int32, device=dev)
+    d_noff = torch.arange(B + 1, dtype=torch.int64, device=dev)
+    pool = cache.pool
+    pin = torch.empty((S, B), dtype=torch.int32, pin_memory=True)
+    per_s = np.zeros(S)
+
+    def sweep(timed):
+        # a1 for the whole sweep up front (host), one upload; then 512 decode rounds
+        cur = np.full(B, Pp, np.int64)
+        last = np.array([int(st.slots[-1]) for st in rows], np.int32)
+        slots = np.empty((S, B), np.int32)
+        for k in range(S):
+            new, _ = pool.alloc_batch(np.ones(B, np.int64), cur, last)
+            slots[k] = new
+            cur += 1
+            last = new
+        pin.numpy()[:] = slots
+        d_new.copy_(pin, non_blocking=True)
+        evs = []
+        for k in range(S):
+            sp.build_req_to_token(cache.r2t, req_rows, d_new[k], d_noff, new_col0=col0s[k])
+            if timed:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+            sp.cascade_decode_attn(q[k], cache.k_pool, cache.v_pool, cache.r2t, req_rows, seqs[k], gptr, gpl,
+                                   Pp + k + 1, 8, Pp, k_new=kn[k], v_new=vn[k], o=o, workspace=ws)
+            if timed:
+                b.record()
+                evs.append((a, b))
+        torch.cuda.synchronize()
+        pool.free(slots.reshape(-1))
+        return evs
+
+    for _ in range(max(1, args.warmup // 5)):
+        sweep(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_sweeps = max(1, args.steps // 10)
+    for _ in range(n_sweeps):
+        evs = sweep(True)
+        per_s += np.array([a.elapsed_time(b) for a, b in evs])
+    t1 = time.perf_counter()
+    per_s /= n_sweeps
+    ms = (t1 - t0) * 1e3 / n_sweeps
+    bytes_s = np.array([acc.decode_bytes_cascade([Pp + k] * B, np.repeat(np.arange(G), 8), [Pp] * G, Hq, Hkv, D, 2)
+                        for k in range(1, S + 1)], np.float64)
+    gbps = bytes_s.sum() / (per_s.sum() * 1e-3) / 1e9
+    config = {"workload": "fork: 16 prompts x 4096 tokens, 8 branches each (128 requests), suffix grows "
+                          "1..512 in lockstep, cascade decode per step; 32/8 heads, head_dim 128, 2^18-slot pool",
+              "prompts": G, "branches": 8, "prompt_len": Pp, "steps_per_sweep": S}
+    roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+            "traffic": None, "kernel": "cascade decode call, summed over the sweep",
+            "bytes_per_sweep": float(bytes_s.sum()), "avg_launch_ms": float(per_s.mean())}
+    line = base_line(B * S / (ms * 1e-3), ms, args, config, roof, {
+        "per_s_gbps": {str(k): float(bytes_s[k - 1] / (per_s[k - 1] * 1e-3) / 1e9) for k in (1, 2, 64, 256, 512)},
+        "per_s_ms": {str(k): float(per_s[k - 1]) for k in (1, 2, 64, 256, 512)},
+        "sweeps": n_sweeps})
+    line["steps"] = n_sweeps
+    if not args.no_cpu_baseline:
+        Ks, Vs, rws = [], [], []
+        for r in range(0, B, 4):
+            K, V = wl.logical_kv(r, S)
+            Ks.append(K)
+            Vs.append(V)
+            rws.append((len(Ks) - 1, Pp + S - 1, wl.queries(r, 1)[0]))
+        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "fork (s=512)")
+    return line
+
+
+# ---------------------------------------------------------------------------
+# multi-turn: 128 sessions, ~70% cached history, chunked prefill (512) + decode, page 16
+# ---------------------------------------------------------------------------
+def bench_multiturn(args):
+    import torch
+    import workloads as W
+    from prefix_shared_paged_amd import accounting as acc
+    from prefix_shared_paged_amd.chunked import ChunkedRunner, plan_rounds
+    from prefix_shared_paged_amd.paged_cache import PagedKVCache
+
+    wl = W.multiturn(seed=0)
+    s = wl.spec
+    n, Hq, Hkv, D = wl.n, s.Hq, s.Hkv, s.D
+    dev = "cuda"
+    rounds = plan_rounds(wl.hist, wl.cached, wl.chunk)
+    max_dec = len(rounds)
+    toks = [W.tokens(s, W.T_TOK_PREFIX, int(wl.hist[i]) + max_dec, i + 1, i) for i in range(n)]
+    stride = int(wl.hist.max()) + max_dec + 16
+    # round inputs, resident in HBM before timing
+    inp = []
+    for ext, dec in rounds:
+        ne = sum(hi - lo for _, lo, hi in ext)
+        tq = torch.empty((ne, Hq, D), dtype=torch.bfloat16, device=dev)
+        tk = torch.empty((ne, Hkv, D), dtype=torch.bfloat16, device=dev)
+        tv = torch.empty((ne, Hkv, D), dtype=torch.bfloat16, device=dev)
+        dq = torch.empty((len(dec), Hq, D), dtype=torch.bfloat16, device=dev)
+        dk = torch.empty((len(dec), Hkv, D), dtype=torch.bfloat16, device=dev)
+        dv = torch.empty((len(dec), Hkv, D), dtype=torch.bfloat16, device=dev)
+        for j, t in enumerate((tq, tk, tv, dq, dk, dv)):
+            if t.numel():
+                fill_random(t, seed=100 + j)
+        inp.append((tq, tk, tv, dq, dk, dv))
+    ext_flops = [sum(acc.extend_flops([lo], [hi - lo], Hq, D) for _, lo, hi in e) for e, _ in rounds]
+    dec_bytes = [acc.decode_bytes_flat([p + 1 for _, p in d], Hq, Hkv, D, 2) if d else 0 for _, d in rounds]
+
+    def run_once(timed):
+        cache = PagedKVCache(s.num_slots, s.page_size, Hkv, D, torch.bfloat16, 2 * n, stride, W.pool_order(s), dev)
+        if run_once.pools is None:
+            fill_random(cache.k_pool, seed=1)
+            fill_random(cache.v_pool, seed=2)
+            run_once.pools = (cache.k_pool, cache.v_pool)
+        else:
+            cache.k_pool, cache.v_pool = run_once.pools
+        setup = cache.admit([t[:int(c)] for t, c in zip(toks, wl.cached)])
+        cache.append(setup, [int(c) for c in wl.cached])
+        for st in setup:
+            cache.insert(st)
+            cache.release(st)
+        runner = ChunkedRunner(cache, wl.chunk)
+        runner.admit(list(range(n)), toks, wl.hist)
+        torch.cuda.synchronize()
+        evs = []
+        it = iter(inp)
+
+        def inputs(ext, dec):
+            return next(it)
+
+        orig_extend = None
+        t0 = time.perf_counter()
+        r = 0
+        while True:
+            last = not runner.pending()
+            if timed:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record()
+            runner.run_round(inputs)
+            if timed:
+                b = torch.cuda.Event(enable_timing=True)
+                b.record()
+                evs.append((a, b))
+            r += 1
+            if last:
+                break
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3, evs
+
+    run_once.pools = None
+    run_once(False)
+    tot_ms, round_ms = [], []
+    for _ in range(max(1, args.steps // 10)):
+        ms, evs = run_once(True)
+        tot_ms.append(ms)
+        round_ms.append([a.elapsed_time(b) for a, b in evs])
+    ms = float(np.mean(tot_ms))
+    rms = np.mean(np.array(round_ms), axis=0)
+    n_tokens = sum(hi - lo for e, _ in rounds for _, lo, hi in e) + sum(len(d) for _, d in rounds)
+    flops, dbytes = float(sum(ext_flops)), float(sum(dec_bytes))
+    config = {"workload": "multiturn: 128 sessions, history lognormal(median 3000, sigma 1) clamped to "
+                          "[32, 32768], ~70% cached, chunked prefill 512 interleaved with decode, page 16; "
+                          "64/8 heads, head_dim 128, 2^20-slot pool", "sessions": n, "rounds": len(rounds)}
+    line = base_line(n_tokens / (ms * 1e-3), ms, args, config,
+                     {"bound": "mfma", "achieved": flops / (rms.sum() * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                      "unit": "TFLOP/s", "traffic": None,
+                      "kernel": "whole rounds (extend + decode calls), extend FLOPs only",
+                      "flops_per_run": flops},
+                     {"extend_flops": flops, "decode_bytes": dbytes, "round_ms": rms.tolist(),
+                      "tokens_per_run": n_tokens})
+    line["roofline"]["frac"] = line["roofline"]["achieved"] / PEAK_BF16_TFLOPS
+    line["steps"] = len(tot_ms)
+    if not args.no_cpu_baseline:
+        # oracle sample: last-chunk rows of a few sessions
+        Ks, Vs, rws = [], [], []
+        for i in np.argsort(wl.hist)[len(wl.hist) // 2: len(wl.hist) // 2 + 6]:
+            K, V = wl.kv(int(i), 0, int(wl.hist[i]))
+            Ks.append(K)
+            Vs.append(V)
+            for p in range(int(wl.hist[i]) - 64, int(wl.hist[i])):
+                rws.append((len(Ks) - 1, p, wl.queries(int(i), p, p + 1)[0]))
+        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "multiturn prefill")
+    return line
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part "
               "of this build", file=sys.stderr)
@@ -327,9 +736,8 @@ def main():
         else:
             line["cpu_baseline"] = None
     else:
-        from prefix_shared_paged_amd import benchmarks
-        line = benchmarks.run(args)
-    print(json.dumps(line), flush=True)
+        line = {"decode": bench_decode, "fork": bench_fork, "multiturn": bench_multiturn}[args.config](args)
+    print(json.dumps(line, default=lambda x: x.item() if hasattr(x, "item") else str(x)), flush=True)
 
 
 if __name__ == "__main__":
