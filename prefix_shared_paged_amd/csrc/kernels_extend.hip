@@ -13,37 +13,49 @@
 // id % 8 (the XCD a workgroup lands on) follows the KV head: all tiles of one
 // KV head share an XCD and its L2 holds that head's prefix.
 //
-// Per 64-key tile:
-//   - the 4 waves gather the next tile's 64 K rows and 64 V rows of this KV
-//     head by slot id straight from HBM into the other half of a
-//     double-buffered LDS tile with global_load_lds_dwordx4 (no register
-//     staging; the slot ids are fetched one tile ahead).  Such a load writes
-//     LDS contiguously by lane, so each lane picks WHICH 16-byte chunk of its
-//     row it fetches: chunk c of row r sits at position c ^ swz(r), an XOR
-//     swizzle under which both the MFMA operand reads of K and the transposed
-//     reads of V are bank-conflict free, with no padding;
-//   - each wave computes S^T = K Q^T for its 32 rows with
-//     v_mfma_f32_32x32x16_bf16 (keys on M, rows on N), so a lane owns one
-//     query row's scores;
-//   - online softmax in fp32 on raw scores: the scale is folded into the
-//     exponent (one FMA per score), exponentials are v_exp_f32, the causal
-//     mask is applied only on tiles that cross the diagonal, and the
-//     accumulator is rescaled lazily -- only when a row's running maximum
-//     grows by more than 2^8 (the exact result is unchanged: the stored
-//     maximum is simply a slightly stale reference point);
-//   - P is rounded to bf16 and O^T += V^T P^T runs on MFMA with V^T read by
-//     ds_read_b64_tr_b16; the key order inside each MFMA matches the
-//     accumulator layout of S^T, so P needs no lane exchange.
+// Keys are gathered by slot id straight from HBM into LDS with
+// global_load_lds_dwordx4 (no register staging), 32 keys at a time, into rings
+// of four K tiles and four V tiles.  Such a load writes LDS contiguously by
+// lane, so each lane picks WHICH 16-byte chunk of its row it fetches: chunk c
+// of row r sits at position c ^ swz(r), an XOR swizzle under which both the
+// MFMA operand reads of K and the transposed reads of V are bank-conflict
+// free.  The slot ids themselves are copied once into a table in LDS (4096
+// keys, refilled half by half for longer contexts), so the loop issues no
+// global loads other than the tile loads.
+//
+// Each wave owns 32 query rows and walks the keys one 32-key tile at a time
+// with a two-stage software pipeline, so that the matrix pipe always has
+// independent work while the vector ALU runs the softmax:
+//   stage n, part 1: S^T(n+1) = K Q^T on MFMA (keys on M, rows on N, so a lane
+//                    owns one row's scores)  ||  p = 2^s of tile n, its bf16
+//                    rounding and row sum;
+//   stage n, part 2: O^T += V^T P^T of tile n on MFMA (V^T via
+//                    ds_read_b64_tr_b16; the key order inside each MFMA matches
+//                    the S^T accumulator layout, so P needs no lane exchange)
+//                    ||  tile n+1's causal mask and row maximum;
+//   then the loads of K tile n+4 and V tile n+3 into the ring slots that K
+//   tile n and V tile n-1 have left, and one barrier.
+// Every tile load thus has two stages to land.  Softmax details: Q is
+// pre-multiplied by scale*log2(e), so scores come out in log2 units; the
+// running reference maximum enters as the accumulator input of the first
+// S^T MFMA, so p = 2^s needs no further arithmetic; the reference is moved
+// lazily, only when a row's tile maximum exceeds it by more than 2^8 (the
+// exact result is unchanged: the reference is only a scaling point), and the
+// mask is applied only to tiles that may cross the diagonal.
 #include <type_traits>
 
 #include "common.h"
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 namespace {
 
-constexpr int BN = 64;        // keys per tile
+constexpr int BN = 32;        // keys per LDS tile
+constexpr int RING = 4;       // LDS tiles per ring (K and V each)
+constexpr int TABH = 2048;    // keys per half of the LDS slot-id table
 constexpr int BM = 128;       // query rows per workgroup
 constexpr int NT = 256;       // threads
-constexpr float kLazy = 8.f;  // rescale only when the max grows by more than 2^8
+constexpr float kLazy = 8.f;  // move the reference only when the max grows by more than 2^8
 
 // Position of 16-byte chunk c of LDS row r is c ^ swz<D>(r).
 template <int D>
@@ -52,15 +64,37 @@ __device__ __forceinline__ int swz(int r) {
     return (((r >> 1) & 1) << 2) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
 }
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 __device__ __forceinline__ bf16x8 ld_bf16x8(const void *p) {
     union { uint4 u; bf16x8 b; } x;
     x.u = *(const uint4 *)p;
     return x.b;
 }
 
-template <int D>
+// Combine lanes l and l^32, which hold the two halves of a row's 32-key block.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// s_waitcnt vmcnt(N) (lgkmcnt and expcnt left alone), as the builtin so that
+// the compiler's own wait insertion knows which loads have completed
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// OFF32: every K/V byte offset fits in 32 bits (num_slots * Hkv * D * 2 <=
+// 2^32), so the slot table holds ready byte offsets and a load address is the
+// uniform pool base plus a 32-bit per-lane offset.
+template <int D, bool OFF32>
 __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_pool,
     const __bf16 *__restrict__ v_pool, int64_t num_slots, const int32_t *__restrict__ r2t,
@@ -72,16 +106,30 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     constexpr int ROWB = 2 * D;           // bytes per K or V row of one KV head
     constexpr int CHK = D / 8;            // 16-byte chunks per row
     constexpr int RPB = 64 / CHK;         // rows per 1 KiB direct-load block
-    constexpr int NB = BN / RPB / 4;      // blocks per wave per tile (K and V each)
-    constexpr int KTILE = BN * ROWB;
-    constexpr int BUFB = 2 * KTILE;       // K tile then V tile
-    // two separate LDS objects, one per buffer, so the compiler can tell that
-    // reads of one buffer do not wait on the direct loads into the other
-    __shared__ __attribute__((aligned(16))) unsigned char lds_buf0[BUFB];   // [K V]
-    __shared__ __attribute__((aligned(16))) unsigned char lds_buf1[BUFB];   // [K V]
+    constexpr int NB = BN / RPB / 4;      // 1 KiB blocks per wave per tile (K and V each)
+    constexpr int TILEB = BN * ROWB;
+    // one LDS object per ring slot, so the compiler can tell that reads of one
+    // slot do not wait on the direct loads into another
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds2[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds3[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds2[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds3[TILEB];
+    auto kbuf = [&](auto i) -> unsigned char * {
+        constexpr int I = decltype(i)::value % RING;
+        return I == 0 ? k_lds0 : I == 1 ? k_lds1 : I == 2 ? k_lds2 : k_lds3;
+    };
+    auto vbuf = [&](auto i) -> unsigned char * {
+        constexpr int I = decltype(i)::value % RING;
+        return I == 0 ? v_lds0 : I == 1 ? v_lds1 : I == 2 ? v_lds2 : v_lds3;
+    };
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int id = blockIdx.x;
     const int kvh = id % Hkv;
     const int rest = id / Hkv;
@@ -113,7 +161,11 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     {
         const __bf16 *src = q + ((t0 + (row_valid ? tok_local : 0)) * Hq + h) * D + 8 * h2;
 #pragma unroll
-        for (int t = 0; t < QT; t++) qf[t] = ld_bf16x8(src + 16 * t);
+        for (int t = 0; t < QT; t++) {
+            const bf16x8 raw = ld_bf16x8(src + 16 * t);
+#pragma unroll
+            for (int e = 0; e < 8; e++) qf[t][e] = (__bf16)((float)raw[e] * qscale);
+        }
     }
 
     f32x16 oacc[DBLK];
@@ -123,52 +175,89 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
         for (int j = 0; j < 16; j++) oacc[b][j] = 0.f;
     float m_run = -INFINITY;     // reference maximum (log2 units of the scaled score)
     float l_run = 0.f;           // this lane's part of the row sum
+    // -reference, broadcast: the accumulator input of the first S^T MFMA, so
+    // scores come out relative to the reference (0 until the first tile,
+    // which always moves it)
+    f32x16 mneg;
+#pragma unroll
+    for (int j = 0; j < 16; j++) mneg[j] = 0.f;
+    float thr = -INFINITY;       // a tile maximum above this moves the reference
 
-    // ---- tile loader: wave w fills 1 KiB blocks w*NB .. w*NB+NB-1 of K and V --
-    // lane -> (row r = block * RPB + lane / CHK, position lane % CHK), fetching
-    // chunk (lane % CHK) ^ swz(r) of key tile0 + r.
-    // Slot ids are loaded unconditionally (index clamped into the row) and
-    // checked only when used; sl[b] holds the ids of the tile that goes into
-    // LDS buffer b, so a load lands directly where its use reads it.
-    int sl[2][NB];
-    auto fetch_slots = [&](int tile0, int (&dst)[NB]) {
+    // ---- slot ids: a table in LDS holds the ids of keys [c*TABH, (c+1)*TABH)
+    // in half c % 2, so the loop reads them from LDS instead of HBM.  The
+    // first two chunks are filled here; a longer context refills a half once
+    // its last key has been looked up (every TABH / BN stages).
+    // Entries past the end hold the last key's slot, so look-ups need no
+    // clamp (a tile past the end is a harmless copy of that key).  With 32-bit
+    // offsets the table stores the byte offset of the slot's row of this KV
+    // head (an id outside the pool is replaced by slot 0).
+    using TabT = typename std::conditional<OFF32, uint32_t, int32_t>::type;
+    __shared__ TabT slot_tab[2 * TABH];
+    const char *row_b = (const char *)row;
+    const uint32_t rowbytes = (uint32_t)rowstride_el * 2u;
+    const uint32_t ns32 = OFF32 ? (uint32_t)num_slots : 0u;
+    auto fill = [&](auto count_tag, int k0) {        // keys k0 .. k0 + count*NT - 1
+        constexpr int CNT = decltype(count_tag)::value;
+        int v[CNT];
 #pragma unroll
-        for (int i = 0; i < NB; i++) {
-            const int j = tile0 + (wave * NB + i) * RPB + lane / CHK;
-            dst[i] = row[j < kv_end ? j : kv_end - 1];
+        for (int u = 0; u < CNT; u++) {
+            const int k = min(k0 + u * NT + tid, kv_end - 1);
+            v[u] = *(const int32_t *)(row_b + (uint32_t)k * 4u);
+        }
+#pragma unroll
+        for (int u = 0; u < CNT; u++) {
+            TabT e;
+            if (OFF32) e = ((uint32_t)v[u] < ns32 ? (uint32_t)v[u] : 0u) * rowbytes + (uint32_t)(kvh * D * 2);
+            else e = v[u];
+            slot_tab[(k0 + u * NT + tid) & (2 * TABH - 1)] = e;
         }
     };
-    auto issue = [&](int buf, const int (&sl)[NB]) {
+
+    // ---- tile loader: wave w fills 1 KiB blocks w*NB .. w*NB+NB-1 of a tile ---
+    // lane -> (row rr = block * RPB + lane / CHK, position lane % CHK),
+    // fetching chunk (lane % CHK) ^ swz(rr) of key tile*BN + rr (clamped to
+    // the last key, so tiles past the end are harmless copies).
+    int jl[NB];                  // this lane's key within a tile, per block
+    uint32_t lp[NB];             // byte offset of this lane's chunk within a K/V row
+#pragma unroll
+    for (int i = 0; i < NB; i++) {
+        const int rr = (wave * NB + i) * RPB + lane / CHK;
+        jl[i] = rr;
+        lp[i] = (uint32_t)(8 * ((lane % CHK) ^ swz<D>(rr))) * 2u;
+    }
+    using Off = typename std::conditional<OFF32, uint32_t, int64_t>::type;
+    // pool byte offsets of this lane's rows of tile `tile` (a K tile and the V
+    // tile of the same keys share them)
+    auto offsets = [&](int tile, Off (&dst)[NB]) {
 #pragma unroll
         for (int i = 0; i < NB; i++) {
-            const int blk = wave * NB + i;
-            const int rr = blk * RPB + lane / CHK;
-            const int c = (lane % CHK) ^ swz<D>(rr);
-            const int64_t off = (int64_t)safe_slot(sl[i], num_slots) * rowstride_el + kvh * D + c * 8;
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)(k_pool + off),
-                                             (SGL_LDS void *)((buf ? lds_buf1 : lds_buf0) + blk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)(v_pool + off),
-                                             (SGL_LDS void *)((buf ? lds_buf1 : lds_buf0) + KTILE + blk * 1024), 16, 0,
-                                             0);
+            const TabT e = slot_tab[(tile * BN + jl[i]) & (2 * TABH - 1)];
+            if (OFF32) dst[i] = e + lp[i];
+            else dst[i] = (int64_t)safe_slot(e, num_slots) * rowstride_el * 2 + (kvh * D * 2 + lp[i]);
         }
     };
-    // V rows past the end of the context must hold zeros (their P is 0, and
-    // whatever slot 0 holds must not turn 0 * v into NaN); runs after the
-    // loads of that tile have landed.
-    auto zero_tail = [&](int buf, int tile0) {
-        const int nvalid = kv_end - tile0;
+    auto issue = [&](const __bf16 *pool, unsigned char *dst, const Off (&off)[NB]) {
+#pragma unroll
+        for (int i = 0; i < NB; i++)
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)((const char *)pool + off[i]),
+                                             (SGL_LDS void *)(dst + (wave * NB + i) * 1024), 16, 0, 0);
+    };
+    // V rows past the end of the context must hold zeros (their p is 0, and
+    // whatever slot they were read from must not turn 0 * v into NaN); runs
+    // after the loads of that tile have landed.
+    auto zero_tail = [&](unsigned char *vt, int tile) {
+        const int nvalid = kv_end - tile * BN;
         if (nvalid >= BN) return;
-        unsigned char *vt = (buf ? lds_buf1 : lds_buf0) + KTILE;
         for (int idx = tid; idx < (BN - nvalid) * CHK; idx += NT)
             *(uint4 *)(vt + (nvalid + idx / CHK) * ROWB + 16 * (idx % CHK)) = make_uint4(0, 0, 0, 0);
     };
 
     // Per-lane LDS byte offsets of the MFMA operand reads.  The swizzle of a
-    // row depends only on bits that stay fixed across the 32-row K blocks and
-    // the 16-row V steps, so the loop indices become immediate offsets.
+    // row depends only on bits that stay fixed across the 16-row V steps, so
+    // the step index becomes an immediate offset.
     const int grp = (lane >> 4) & 1;                 // which 16 dims of a 32-dim block
     const int r4 = (lane & 15) >> 2, qq = lane & 3;
-    int koff[QT];                                    // K operand of step t, key block 0
+    int koff[QT];                                    // K operand of step t
     {
         const int sk = swz<D>(n32);
 #pragma unroll
@@ -186,125 +275,184 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
         }
     }
 
-    // One 64-key tile from LDS buffer BUF.  Both 32-key blocks' S^T MFMAs are
-    // issued first; block 0's softmax (VALU) then runs while block 1's S^T is in
-    // the matrix pipe, and block 0's PV MFMAs while block 1's softmax runs.
-    // MASK: the tile may cross the diagonal of some row.
-    auto tile = [&](const int tile0, auto buf_tag, auto mask_tag) {
-        constexpr int BUF = decltype(buf_tag)::value;
-        constexpr bool MASK = decltype(mask_tag)::value;
-        const unsigned char *Kt = BUF ? lds_buf1 : lds_buf0;
-        const unsigned char *Vt = Kt + KTILE;
-        // K operands of key block 0, read ahead of their MFMAs
-        bf16x8 kf[QT];
+    // S^T of one tile (K operands from LDS, Q from registers)
+    auto s_tile = [&](const unsigned char *kt) {
+        f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(kt + koff[0]), qf[0], mneg, 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < QT; t++) kf[t] = ld_bf16x8(Kt + koff[t]);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 sacc[2];
+        for (int t = 1; t < QT; t++)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(kt + koff[t]), qf[t], s, 0, 0, 0);
+        return s;
+    };
+    // causal mask of tile n (absolute key of accumulator element j:
+    // 32n + 8*(j/4) + 4*h2 + j%4) and the row maximum
+    auto mask_max = [&](f32x16 &s, int n, auto mask_tag) {
+        if (decltype(mask_tag)::value) {
+            const int lim = pos - n * BN - 4 * h2;
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            // S^T = K Q^T (raw, unscaled scores) for keys kb*32 .. kb*32+31
+            for (int j = 0; j < 16; j++)
+                if (8 * (j >> 2) + (j & 3) > lim) s[j] = -INFINITY;
+        }
+        float mx = s[0];
 #pragma unroll
-            for (int j = 0; j < 16; j++) sacc[kb][j] = 0.f;
+        for (int j = 1; j < 16; j++) mx = fmaxf(mx, s[j]);
+        return max_xor32(mx);
+    };
+    // lazy move of the reference (scores and mx are relative to it); rescales
+    // O and l, so it runs after the PV MFMAs issued before it
+    auto move_ref = [&](f32x16 &s, float mx) {
+        const bool need = mx > thr;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+            const float shift = need ? mx : 0.f;
+            const float m_new = m_ref + shift;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
-            for (int t = 0; t < QT; t++)
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[t], sacc[kb], 0, 0, 0);
-            if (kb == 0) {
-                // block 1's K operands are read while block 0's softmax and PV run
-#pragma unroll
-                for (int t = 0; t < QT; t++) kf[t] = ld_bf16x8(Kt + 32 * ROWB + koff[t]);
-            }
-            f32x16 sc = sacc[kb];
-            if (MASK) {
-                // key (tile-local) of accumulator element j: kb*32 + 8*(j/4) + 4*h2 + j%4
-                const int lim = pos - tile0 - kb * 32 - 4 * h2;
-#pragma unroll
-                for (int j = 0; j < 16; j++)
-                    if (8 * (j >> 2) + (j & 3) > lim) sc[j] = -INFINITY;
-            }
-            float mx = sc[0];
-#pragma unroll
-            for (int j = 1; j < 16; j++) mx = fmaxf(mx, sc[j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_blk = mx * qscale;
-            // lazy rescale: only when some row's maximum moved by more than 2^kLazy
-            const bool need = m_blk > m_run + kLazy;
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                const float m_new = need ? m_blk : m_run;
-                const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int b = 0; b < DBLK; b++) oacc[b] *= alpha;
-                m_run = m_new;
-            }
-            // p = 2^(s * scale * log2e - m_run), rounded to bf16 for the PV product
-            bf16x8 pf[2];        // B operands of the 2 PV steps of this block
-            float psum = 0.f;
+            for (int b = 0; b < DBLK; b++) oacc[b] *= alpha;
 #pragma unroll
             for (int j = 0; j < 16; j++) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sc[j], qscale, -m_run));
-                psum += p;
-                pf[j >> 3][j & 7] = (__bf16)p;
+                s[j] -= shift;
+                mneg[j] = -m_new;
             }
-            l_run += psum;
-            // O^T += V^T P^T; step st covers keys 16*st + {4*h2 + 0..3, 8 + 4*h2 + 0..3}
+            m_run = m_new;
+            thr = kLazy;
+        }
+    };
+    // p = 2^s rounded to bf16 (the B operands of the tile's 2 PV steps);
+    // the row sum adds up the same rounded values, two at a time
+    auto exp_tile = [&](const f32x16 &s, bf16x8 (&pf)[2]) {
 #pragma unroll
-            for (int s2 = 0; s2 < 2; s2++) {
-                const int st = kb * 2 + s2;
+        for (int j = 0; j < 16; j++) pf[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(s[j]);
+        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-                for (int b = 0; b < DBLK; b++) {
-                    const unsigned char *p0 = Vt + st * 16 * ROWB + voff0[b];
-                    const unsigned char *p1 = Vt + st * 16 * ROWB + voff1[b];
-                    i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p0);
-                    i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p1);
-                    typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    const i16x8 cat = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pf[s2],
-                                                                     oacc[b], 0, 0, 0);
-                }
+        for (int j = 0; j < 8; j++) {
+            const bf16x2 pp = {pf[j >> 2][2 * (j & 3)], pf[j >> 2][2 * (j & 3) + 1]};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, l_run, false);
+        }
+    };
+    // O^T += V^T P^T; step s2 covers keys 16*s2 + {4*h2 + 0..3, 8 + 4*h2 + 0..3}
+    auto pv_tile = [&](const unsigned char *vt, const bf16x8 (&pf)[2]) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++) {
+#pragma unroll
+            for (int b = 0; b < DBLK; b++) {
+                const unsigned char *p0 = vt + s2 * 16 * ROWB + voff0[b];
+                const unsigned char *p1 = vt + s2 * 16 * ROWB + voff1[b];
+                i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p0);
+                i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p1);
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                const i16x8 cat = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pf[s2],
+                                                                 oacc[b], 0, 0, 0);
             }
         }
     };
 
-    const int n_tiles = (kv_end + BN - 1) / BN;
+    const int N = (kv_end + BN - 1) / BN;            // key tiles
     const int min_pos = P + q0;                      // smallest position in the tile
-    // tiles every row sees whole (no mask), rounded down to an even count so
-    // both loops below start on LDS buffer 0
-    const int n_full = min((min_pos + 1) / BN, n_tiles) & ~1;
-    fetch_slots(0, sl[0]);
-    issue(0, sl[0]);
-    if (n_tiles > 1) fetch_slots(BN, sl[1]);
-    wait_vm_all();
-    zero_tail(0, 0);
-    __syncthreads();
-    // One tile: start loading tile it+1 into the other buffer, compute tile it,
-    // then wait for the load and publish it.
-    auto step = [&](const int it, auto buf_tag, auto mask_tag) {
-        constexpr int BUF = decltype(buf_tag)::value;
-        if (it + 1 < n_tiles) {
-            if (it + 2 < n_tiles) fetch_slots((it + 2) * BN, sl[BUF]);   // before the direct loads
-            issue(BUF ^ 1, sl[BUF ^ 1]);
-        }
-        tile(it * BN, buf_tag, mask_tag);
-        wait_vm_all();
-        if (it + 1 < n_tiles) zero_tail(BUF ^ 1, (it + 1) * BN);
-        __syncthreads();
+    // Workgroup barrier for LDS reuse.  __syncthreads (or any LDS release
+    // fence) would also wait for every direct load still meant to be in
+    // flight, since those write LDS; here the LDS reads are drained and the
+    // direct loads are waited for by count (vm_wait) before each barrier.
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    int it = 0;
-    for (; it < n_full; it += 2) {                   // straight-line pairs, no mask
-        step(it, B0{}, std::false_type{});
-        step(it + 1, B1{}, std::false_type{});
+
+    // ---- prologue: slot table, then K tiles 0..RING-1 and V tiles 0..RING-2
+    // in the order of the stages -4..-1 they stand for
+    fill(IC<2 * TABH / NT>{}, 0);
+    __syncthreads();
+    Off off0[NB], off1[NB];                          // offsets of tile j live in off[j % 2]
+    auto offs = [&](auto i) -> Off (&)[NB] { return decltype(i)::value % 2 ? off1 : off0; };
+    offsets(0, off0);
+    issue(k_pool, k_lds0, off0);
+    offsets(1, off1);
+    issue(k_pool, k_lds1, off1);
+    issue(v_pool, v_lds0, off0);
+    offsets(2, off0);
+    issue(k_pool, k_lds2, off0);
+    issue(v_pool, v_lds1, off1);
+    offsets(3, off1);
+    issue(k_pool, k_lds3, off1);
+    issue(v_pool, v_lds2, off0);
+    vm_wait<6 * NB>();           // K tile 0
+    lds_barrier();
+    f32x16 s_cur = s_tile(k_lds0);
+    move_ref(s_cur, 31 > min_pos ? mask_max(s_cur, 0, std::true_type{}) : mask_max(s_cur, 0, std::false_type{}));
+    vm_wait<4 * NB>();           // V tile 0, K tile 1
+    if (N == 1) zero_tail(v_lds0, 0);
+    lds_barrier();
+
+    // ---- stage n (R = n % RING): S^T(n+1) || p of tile n; PV of tile n ||
+    // mask and max of tile n+1; then the loads of K tile n+RING and V tile
+    // n+RING-1 into the ring slots that K tile n and V tile n-1 have left.
+    // MASK: tile n+1 may cross the diagonal (a tile past the end is wholly
+    // masked).
+    auto stage = [&](const int n, auto r_tag, auto mask_tag) {
+        constexpr int R = decltype(r_tag)::value;
+        const f32x16 s_next = s_tile(kbuf(IC<R + 1>{}));
+        bf16x8 pf[2];
+        exp_tile(s_cur, pf);
+        pv_tile(vbuf(IC<R>{}), pf);
+        s_cur = s_next;
+        const float mx = mask_max(s_cur, n + 1, mask_tag);
+        // issue order: the K operand reads first, then each S^T MFMA with two
+        // V^T reads and four VALU ops of the previous tile's softmax, then each
+        // PV MFMA with the mask / maximum work of the next tile
+        __builtin_amdgcn_sched_group_barrier(0x100, QT, 0);
+#pragma unroll
+        for (int t = 0; t < QT; t++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * DBLK / QT, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 2 * DBLK; t++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+        move_ref(s_cur, mx);
+        offsets(n + RING, offs(IC<R>{}));            // tile n+4; tile n+3's are in the other array
+        issue(k_pool, kbuf(IC<R>{}), offs(IC<R>{}));
+        issue(v_pool, vbuf(IC<R + RING - 1>{}), offs(IC<R + 1>{}));
+        // K tile n+2 and V tile n+1 (issued RING-2 stages ago) have landed
+        vm_wait<(RING - 2) * 2 * NB>();
+        if (n + 2 == N) zero_tail(vbuf(IC<R + 1>{}), n + 1);
+        lds_barrier();
+    };
+    // after stage 64m-1 of a long context, half (m+1) % 2 of the slot table
+    // (chunk m-1, whose last look-up was at stage 64m-5) takes chunk m+1
+    auto refill = [&](int n_done) {
+        constexpr int SPC = TABH / BN;               // stages per chunk
+        if (n_done % SPC == 0 && (n_done / SPC + 1) * TABH < kv_end)
+            fill(IC<TABH / NT>{}, (n_done / SPC + 1) * TABH);
+    };
+    // stages whose look-ahead tile n+1 lies wholly at or below every row's
+    // position need no mask; the loops run in groups of RING so that ring
+    // positions are known at compile time
+    const int n_unmasked = (min_pos >= 63 ? (min_pos - 63) / BN + 1 : 0) / RING * RING;
+    int n = 0;
+    for (; n < n_unmasked; n += RING) {
+        stage(n, IC<0>{}, std::false_type{});
+        stage(n + 1, IC<1>{}, std::false_type{});
+        stage(n + 2, IC<2>{}, std::false_type{});
+        stage(n + 3, IC<3>{}, std::false_type{});
+        refill(n + RING);
     }
-    for (; it + 1 < n_tiles; it += 2) {              // pairs that may cross the diagonal
-        step(it, B0{}, std::true_type{});
-        step(it + 1, B1{}, std::true_type{});
+    for (; n < N; n += RING) {
+        stage(n, IC<0>{}, std::true_type{});
+        if (n + 1 < N) stage(n + 1, IC<1>{}, std::true_type{});
+        if (n + 2 < N) stage(n + 2, IC<2>{}, std::true_type{});
+        if (n + 3 < N) stage(n + 3, IC<3>{}, std::true_type{});
+        refill(n + RING);
     }
-    if (it < n_tiles) step(it, B0{}, std::true_type{});
+    vm_wait<0>();                // the trailing clamped loads
 
     // ---- epilogue: normalise and store ----------------------------------------
-    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float l = add_xor32(l_run);
     if (!row_valid) return;
     const float inv = 1.f / l;
     __bf16 *dst = o + ((t0 + tok_local) * Hq + h) * D;
@@ -335,13 +483,17 @@ int launch_extend_bf16(const __bf16 *q, const __bf16 *k_pool, const __bf16 *v_po
     const int64_t n_wg = (int64_t)n_qtiles * batch * Hkv;
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const float qs = scale * kLog2e;
-    if (D == 128)
-        hipLaunchKernelGGL(extend_bf16_kernel<128>, dim3((unsigned)n_wg), dim3(NT), 0, st, q, k_pool,
-                           v_pool, num_slots, r2t, num_rows, row_stride, req_rows, prefix_lens, q_off,
-                           Hq, Hkv, n_qtiles, qs, o, lse);
-    else
-        hipLaunchKernelGGL(extend_bf16_kernel<64>, dim3((unsigned)n_wg), dim3(NT), 0, st, q, k_pool,
-                           v_pool, num_slots, r2t, num_rows, row_stride, req_rows, prefix_lens, q_off,
-                           Hq, Hkv, n_qtiles, qs, o, lse);
+    const bool off32 = num_slots * Hkv * D * 2 <= (int64_t(1) << 32);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(NT), 0, st, q, k_pool, v_pool, num_slots, r2t,
+                           num_rows, row_stride, req_rows, prefix_lens, q_off, Hq, Hkv, n_qtiles, qs, o, lse);
+    };
+    if (D == 128) {
+        if (off32) go(extend_bf16_kernel<128, true>);
+        else go(extend_bf16_kernel<128, false>);
+    } else {
+        if (off32) go(extend_bf16_kernel<64, true>);
+        else go(extend_bf16_kernel<64, false>);
+    }
     return hip_status(hipGetLastError());
 }
