@@ -27,10 +27,16 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + INCLUDE, "-I" + CSRC]
 
+# Per-source flags.  The decode kernel keeps its MFMA accumulators in ordinary
+# VGPRs: its softmax rescales them with vector ALU ops, and AGPR accumulators
+# would be copied to VGPRs and back around every such rescale, costing both
+# instructions and the registers that decide how many waves fit per CU.
+SOURCE_FLAGS = {"kernels_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
 
 def _compile(src, verbose):
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip"] + cmd[1:]
     if verbose:

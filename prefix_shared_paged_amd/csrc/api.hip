@@ -9,11 +9,29 @@
 
 namespace {
 
-constexpr int kDecodeChunk = 256;   // keys per split (flat decode and cascade suffix)
-constexpr int kPrefixChunk = 256;   // keys per split (cascade prefix)
+constexpr int kDecodeChunk = 1024;   // keys per split (flat decode and cascade suffix)
+constexpr int kPrefixChunkMax = 512;
+constexpr int kPrefixChunkMin = 64;
+constexpr int64_t kPrefixWorkgroups = 2048;  // ~8 per compute unit
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Keys per split of the cascade prefix stage.  The stage runs one workgroup
+// per (group, KV head, split, block of up to 4 x 16 query rows) -- often far
+// fewer than the flat call has work items -- and a workgroup walks its
+// split's tiles one after another, so the splits are halved (down to 64
+// keys) until about kPrefixWorkgroups workgroups run.  The row-block rule
+// matches the launcher in kernels_decode.hip.
+int prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D) {
+    const int64_t rb = ceil_div64((int64_t)max_group_size * (Hq / Hkv), 16);
+    int64_t wpg = rb >= 3 ? 4 : rb;
+    if (D == 64 && wpg > 2) wpg = 2;
+    const int64_t units = (int64_t)G * Hkv * ceil_div64(rb, wpg);
+    int c = kPrefixChunkMax;
+    while (c > kPrefixChunkMin && units * ceil_div64(max_prefix_len, c) < kPrefixWorkgroups) c /= 2;
+    return c;
+}
 
 bool validate_on() {
     static int v = -1;
@@ -268,7 +286,8 @@ int decode_common(bool cascade, int dtype, const void *q, const void *k_new, con
     std::memset(&m, 0, sizeof m);
     m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
     m.batch = batch; m.G = G; m.Hq = Hq; m.D = D; m.out_bf16 = dtype == SGL_BF16; m.o = o; m.lse = lse;
-    m.chunk_flat = kDecodeChunk; m.chunk_prefix = kPrefixChunk;
+    const int pchunk = cascade ? prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D) : kPrefixChunkMax;
+    m.chunk_flat = kDecodeChunk; m.chunk_prefix = pchunk;
 
     if (!cascade) {
         const int64_t S = ceil_div64(max_seq_len, kDecodeChunk);
@@ -278,10 +297,10 @@ int decode_common(bool cascade, int dtype, const void *q, const void *k_new, con
         m.kind = 0; m.flat_or_suffix = a.part;
         return launch_merge(m, st);
     }
-    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, kPrefixChunk) : 1;
+    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pchunk) : 1;
     const int64_t Ss = ceil_div64(max_seq_len, kDecodeChunk);
     SplitArgs pa = a;
-    pa.kind = 1; pa.chunk = kPrefixChunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size;
+    pa.kind = 1; pa.chunk = pchunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size;
     pa.part = carve(wp, batch, Sp, Hq, D);
     // the f32 path walks (request, head, split) for every kind; the bf16 path one wave per group
     pa.n_sets = dtype == SGL_F32 ? batch : G;
@@ -309,11 +328,11 @@ int sgl_decode_attn(int dtype, const void *q, const void *k_new, const void *v_n
 
 size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len, int32_t max_group_size,
                                   int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D) {
-    (void)Hkv;
-    (void)G;
-    (void)max_group_size;
     if (batch <= 0 || max_seq_len <= 0) return 0;
-    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, kPrefixChunk) : 1;
+    if (G < 1 || Hkv < 1 || Hq < Hkv || max_group_size < 1) return 0;
+    const int64_t Sp = max_prefix_len > 0
+                           ? ceil_div64(max_prefix_len, prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D))
+                           : 1;
     const int64_t Ss = ceil_div64(max_seq_len, kDecodeChunk);
     return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, Ss, Hq, D);
 }

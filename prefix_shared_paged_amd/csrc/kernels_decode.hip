@@ -1,34 +1,56 @@
 // kernels_decode.hip -- bf16 split-K decode attention for gfx950.
 //
-// One wave per (KV head, split, request-or-group).  The wave owns up to
-// 16*NB query rows that read the same KV head: the g = Hq/Hkv query heads of
-// one request (flat decode, cascade suffix), or the g heads of every request
-// of a group (cascade prefix: the shared prefix is read once for all of the
-// group's queries).  For each 32-key tile of its split it
-//   1. gathers the K rows of the tile straight into MFMA operand registers
-//      (lane = key x quarter of head_dim, 64 contiguous bytes per lane);
-//   2. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on M, query
-//      rows on N);
-//   3. updates the running max / sum per row (online softmax, the update of
-//      "SGLang 深度拆解" (chenxutan.com) section 3.2 applied to a tile);
-//   4. gathers the V rows into LDS row-major and reads them back transposed
-//      with ds_read_b64_tr_b16, so O^T += V^T P^T runs on MFMA as well, with
-//      P^T taken directly from the S^T accumulator registers (the key order
-//      inside each MFMA is chosen so that no lane exchange is needed).
-// The split's state (m, l, unnormalised o) goes to the workspace; a merge
-// kernel combines the splits of a request (and, for the cascade, its group's
-// prefix splits) with the log-sum-exp rule.
+// Decode reads every K/V row of a request's context once and does little
+// arithmetic per byte ("SGLang 深度拆解" (chenxutan.com) section 4.1: decode is
+// memory-bound), so this kernel is built around keeping HBM busy.  On gfx950
+// the achieved gather bandwidth grows with the number of waves resident per
+// compute unit far more than with the bytes each wave has in flight (a wave
+// resumes only when the slowest of its loads has returned), so every wave is
+// kept small -- about 100 registers and 8-12 KiB of LDS:
+//   - one work item per (KV head, key split, request or group);
+//   - 16-key tiles: the K and V rows of a tile go straight from HBM into LDS
+//     (global_load_lds_dwordx4, no register staging), each load instruction
+//     covering four whole 256-byte rows, with non-temporal hints since every
+//     row is read once.  The next tile's K loads are issued as soon as the
+//     current K operands have been read, its V loads as soon as the current
+//     V tile has been read;
+//   - each row's 16-byte chunks are stored under an XOR swizzle (a bijection
+//     of the row's low bits) so that the MFMA operand reads of K
+//     (ds_read_b128, 16 rows x one chunk) and the transposed reads of V
+//     (ds_read_b64_tr_b16) spread over the LDS banks.
+// Per tile: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (16 keys on M, 16 query
+// rows on N), the online-softmax update of p1 section 3.2 applied to the tile
+// (fp32, base-2 exponentials with scale * log2(e) folded into one multiply),
+// then O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, whose B operand is exactly
+// the S^T accumulator layout (lane: row, four consecutive keys), so P needs no
+// lane exchange.  The split's state (m, l, unnormalised o) goes to the
+// workspace; a merge kernel combines the splits of a request -- and for the
+// cascade its group's prefix splits -- with the log-sum-exp rule.
+//
+// Work items: the flat call and the cascade suffix give the g = Hq/Hkv query
+// heads of one request to a one-wave workgroup (16-row MFMA tiles, g <= 16),
+// which keeps the most waves resident.  The cascade prefix stage gives all
+// members x g query rows of a group to workgroups of up to four waves (16
+// rows each) that share every prefix tile they load, so the shared prefix is
+// read from HBM once per 64 query rows; it uses two tile buffers, since its
+// work items are few and long.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
 
-constexpr int TILE = 32;   // keys per tile
+constexpr int TILE = 16;   // keys per tile
 
+// Position of 16-byte chunk c of K/V row r (within a tile) is c ^ swz<D>(r).
+// A K operand read touches one chunk of all 16 rows; a V^T read touches two
+// adjacent chunks of 8 rows per half wave.  For 16 chunks per row the swizzle
+// puts the row's low three bits on chunk bits 1..3 and bit 3 on chunk bit 0.
 template <int D>
-struct DecodeLds {
-    static constexpr int kRowBytes = D * 2 + 32;               // padded V row (bank spread)
-    static constexpr int kVBytes = TILE * kRowBytes;
-};
+__device__ __forceinline__ int swz(int r) {
+    if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    return (r & 7) ^ ((r >> 3) & 1);                                // 8 chunks per row
+}
 
 __device__ __forceinline__ int find_group_dec(const int32_t *group_ptr, int G, int r) {
     int lo = 0, hi = G - 1;
@@ -39,37 +61,82 @@ __device__ __forceinline__ int find_group_dec(const int32_t *group_ptr, int G, i
     return lo;
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-    union { uint4 u; bf16x8 b; } x;
-    x.u = u;
-    return x.b;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 ld_q(const __bf16 *p) {
+    return __builtin_bit_cast(bf16x8, *(const u32x4 *)p);
 }
 
-template <int D, int NB>
-__global__ void __launch_bounds__(64) split_bf16_kernel(SplitArgs a) {
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void lgkm_wait0() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+
+// WPG waves per workgroup share each K/V tile in LDS: the loads of a tile
+// are split among them (each issues NI/WPG of the K and of the V load
+// instructions) and every wave computes its own 16 query rows against the
+// whole tile.  DEPTH LDS buffers per tile ring: with 1, tile n+1's K loads go
+// out once tile n's K operands are read and its V loads once tile n's V is
+// read; with 2, tile n+1 is in flight while tile n is computed.
+template <int D, int DEPTH, int WPG>
+__global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     constexpr int QT = D / 32;          // MFMA k-steps over head_dim
     constexpr int DB = D / 16;          // 16-dim output blocks
-    constexpr int ROWB = DecodeLds<D>::kRowBytes;
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[DecodeLds<D>::kVBytes];
+    constexpr int ROWB = 2 * D;         // bytes of one K/V row of one head
+    constexpr int CHK = D / 8;          // 16-byte chunks per row
+    constexpr int RPI = 64 / CHK;       // rows per direct-load instruction (1 KiB)
+    constexpr int NI = TILE / RPI;      // direct-load instructions per K or V tile
+    static_assert(NI % WPG == 0, "each wave issues the same number of loads");
+    constexpr int NIW = NI / WPG;       // K (and V) load instructions per wave per tile
+    constexpr int TB = TILE * ROWB;
+    constexpr int TB1 = DEPTH > 1 ? TB : 16;
+    // one LDS object per buffer, so the compiler can tell that reads of one
+    // buffer do not wait on the direct loads into the other
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TB];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TB];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TB1];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TB1];
     extern __shared__ int32_t slot_lds[];  // [chunk]
 
-    const int lane = threadIdx.x;
-    const int kvh = blockIdx.x;
-    const int s = blockIdx.y;
-    const int n_rb = a.kind == 1 ? a.row_blocks : 1;   // 16*NB-row blocks of a big group
-    const int set = blockIdx.z / n_rb;
-    const int rb = blockIdx.z % n_rb;
+    const int lane = threadIdx.x & 63;
+    const int w = WPG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    auto wg_barrier = [&]() {
+        if (WPG > 1) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+    };
+
+    // ---- work item: id = ((item / 8) * n_rbg + rbg) * 8 + item % 8 -------------
+    // item = (set, split, KV head); rbg = which WPG row blocks of the item
+    const int n_rbg = (a.row_blocks + WPG - 1) / WPG;
+    const int id = blockIdx.x;
+    const int rest = id >> 3;
+    const int rbg = rest % n_rbg;
+    const int64_t item = (int64_t)(rest / n_rbg) * 8 + (id & 7);
+    const int kvh = (int)(item % a.Hkv);
+    const int64_t t_ = item / a.Hkv;
+    const int s = (int)(t_ % a.max_splits);
+    const int64_t set64 = t_ / a.max_splits;
+    if (set64 >= a.n_sets) return;
+    const int set = (int)set64;
     const int g = a.Hq / a.Hkv;
 
-    // ---- which rows, which keys ----------------------------------------------
+    // ---- which rows, which keys (uniform over the workgroup) ---------------------
     int first_req, n_members;
     int64_t lo, hi, ref_row;
     if (a.kind == 1) {
-        const int grp = set;
-        first_req = a.group_ptr[grp];
-        n_members = a.group_ptr[grp + 1] - first_req;
+        first_req = a.group_ptr[set];
+        n_members = a.group_ptr[set + 1] - first_req;
         if (n_members <= 0 || first_req < 0 || first_req + n_members > a.batch) return;
-        int64_t P = a.group_prefix_len[grp];
+        const int64_t P = a.group_prefix_len[set];
         lo = 0;
         hi = P < 0 ? 0 : P;
         ref_row = a.req_rows[first_req];
@@ -82,214 +149,230 @@ __global__ void __launch_bounds__(64) split_bf16_kernel(SplitArgs a) {
             lo = 0;
         } else {
             const int grp = find_group_dec(a.group_ptr, a.G, set);
-            int64_t P = a.group_prefix_len[grp];
+            const int64_t P = a.group_prefix_len[grp];
             lo = P < 0 ? 0 : (P > L ? L : P);
         }
         hi = L;
     }
-    const int row_base = rb * 16 * NB;              // first group row of this wave
-    const int rows = n_members * g - row_base;      // rows left from row_base on
-    if (rows <= 0) return;
+    if (n_members * g <= rbg * WPG * 16) return;    // no rows left for this workgroup
     if (ref_row < 0 || ref_row >= a.num_rows) return;
     if (hi > a.row_stride) hi = a.row_stride;
     const int64_t n_split = ceil_div64(hi - lo, a.chunk);
     if (s >= n_split || s >= a.part.S) return;
     const int64_t k0 = lo + (int64_t)s * a.chunk;
-    const int64_t k1 = k0 + a.chunk < hi ? k0 + a.chunk : hi;
-    const int nk = (int)(k1 - k0);
+    const int nk = (int)((k0 + a.chunk < hi ? k0 + a.chunk : hi) - k0);
+    const int N = (nk + TILE - 1) / TILE;           // tiles, >= 1
+    const int row_base = (rbg * WPG + w) * 16;      // first group row of this wave
+    const int rows = n_members * g - row_base;      // may be <= 0: the wave still loads
 
-    const int32_t *row = a.r2t + ref_row * a.row_stride;
-    for (int j = lane; j < nk; j += 64) slot_lds[j] = safe_slot(row[k0 + j], a.num_slots);
+    const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
+    for (int j = threadIdx.x; j < nk; j += 64 * WPG) slot_lds[j] = safe_slot(row[j], a.num_slots);
 
     const __bf16 *q = (const __bf16 *)a.q;
-    const __bf16 *kp = (const __bf16 *)a.k_pool;
-    const __bf16 *vp = (const __bf16 *)a.v_pool;
+    const char *kp = (const char *)a.k_pool + kvh * D * 2;
+    const char *vp = (const char *)a.v_pool + kvh * D * 2;
+    const int64_t rowstride_el = (int64_t)a.Hkv * D;
     const int n16 = lane & 15, kq = lane >> 4;
 
-    // ---- Q^T operand: lane (row n16, quarter kq) holds dims (D/4)kq + 8t + i --
-    bf16x8 qf[NB][QT];
+    // ---- Q^T operand: lane (row n16, kq) holds dims 32t + 8kq + i in step t --
+    bf16x8 qf[QT];
+    {
+        const int rho = n16 < rows ? n16 : 0;
+        const int rr = row_base + rho < n_members * g ? row_base + rho : 0;
+        const int req = first_req + rr / g;
+        const int h = kvh * g + rr % g;
+        const __bf16 *src = q + ((int64_t)req * a.Hq + h) * D + 8 * kq;
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-        const int rho = nb * 16 + n16;
-        if (rho < rows) {
-            const int req = first_req + (row_base + rho) / g;
-            const int h = kvh * g + (row_base + rho) % g;
-            const uint4 *src = (const uint4 *)(q + ((int64_t)req * a.Hq + h) * D + (D / 4) * kq);
+        for (int t = 0; t < QT; t++) qf[t] = ld_q(src + 32 * t);
+        if (n16 >= rows)
 #pragma unroll
-            for (int t = 0; t < QT; t++) qf[nb][t] = as_bf16x8(src[t]);
-        } else {
-#pragma unroll
-            for (int t = 0; t < QT; t++) qf[nb][t] = as_bf16x8(make_uint4(0, 0, 0, 0));
-        }
+            for (int t = 0; t < QT; t++) qf[t] = bf16x8{};
     }
 
-    f32x4 oacc[DB][NB];
+    // ---- per-lane constants of the loads and LDS reads --------------------------
+    // direct load instruction ii: lane -> row ii*RPI + lane/CHK of the tile, LDS
+    // position lane%CHK, which holds chunk (lane%CHK) ^ swz(row).  This wave
+    // issues instructions ii = w + WPG*u of the K tile and of the V tile.
+    const int lrow0 = lane / CHK;
+    int lrow[NIW], lchk[NIW];
 #pragma unroll
-    for (int db = 0; db < DB; db++)
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) oacc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[NB], l_run[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; nb++) { m_run[nb] = -INFINITY; l_run[nb] = 0.f; }
+    for (int u = 0; u < NIW; u++) {
+        const int ii = w + WPG * u;
+        lrow[u] = ii * RPI + lrow0;
+        lchk[u] = 16 * ((lane % CHK) ^ swz<D>(lrow[u]));
+    }
+    // K operand of step t: lane (key n16, kq) reads chunk 4t + kq of row n16
+    const int ksw = swz<D>(n16);
+    const int kbase = n16 * ROWB;
+    // V^T read of dim block db: lane (r4, qq) of group kq reads 4 dims of row
+    // (key) 4kq + r4; the transposed result gives lane (dim, kq) keys 4kq..4kq+3
+    const int r4 = n16 >> 2, qq = n16 & 3;
+    const int vr = kq * 4 + r4;
+    const int vsw = swz<D>(vr);
+    const int vbase = vr * ROWB + 8 * (qq & 1);
 
+    __syncthreads();   // slot table visible
+
+    // This wave's loads of tile n (keys past the split end repeat its last key,
+    // so every address is a real row of the context; their scores are masked)
+    auto issue = [&](int n, const char *pool, unsigned char *dst) {
+#pragma unroll
+        for (int u = 0; u < NIW; u++) {
+            const int kk = min(n * TILE + lrow[u], nk - 1);
+            const char *src = pool + (int64_t)slot_lds[kk] * rowstride_el * 2 + lchk[u];
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                             (SGL_LDS void *)(dst + (w + WPG * u) * 1024), 16, 0, 2 /* nt */);
+        }
+    };
+
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
     const float qscale = a.scale * kLog2e;
-    const int64_t rowstride_el = (int64_t)a.Hkv * D;
-    __syncthreads();
 
-    for (int t0 = 0; t0 < nk; t0 += TILE) {
-        // ---- gather K (registers) and V (registers, then LDS) ---------------
-        uint4 kf[2][QT];
+    // S^T = K Q^T of one tile: lane (row n16, kq) gets keys 4kq + j
+    auto s_tile = [&](const unsigned char *kb) {
+        bf16x8 kf[QT];
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            const int kk = t0 + kb * 16 + n16;
-            if (kk < nk) {
-                const uint4 *src = (const uint4 *)(kp + (int64_t)slot_lds[kk] * rowstride_el +
-                                                   kvh * D + (D / 4) * kq);
+        for (int t = 0; t < QT; t++) kf[t] = *(const bf16x8 *)(kb + kbase + 16 * ((4 * t + kq) ^ ksw));
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int t = 0; t < QT; t++) kf[kb][t] = src[t];
-            } else {
+        for (int t = 0; t < QT; t++) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], qf[t], sacc, 0, 0, 0);
+        return sacc;
+    };
+    // online softmax of the row over tile n, then O^T += V^T P^T
+    auto pv_tile = [&](int n, const f32x4 &sacc, const unsigned char *vb) {
+        float sv[4];
+        float mx = -INFINITY;
 #pragma unroll
-                for (int t = 0; t < QT; t++) kf[kb][t] = make_uint4(0, 0, 0, 0);
-            }
+        for (int j = 0; j < 4; j++) {
+            const float x = n * TILE + kq * 4 + j < nk ? sacc[j] * qscale : -INFINITY;
+            sv[j] = x;
+            mx = fmaxf(mx, x);
         }
-        constexpr int VCH = D / 16;    // uint4 per lane: half a row (lane = key*2 + half)
-        uint4 vf[VCH];
-        {
-            const int kk = t0 + (lane >> 1);
-            if (kk < nk) {
-                const uint4 *src = (const uint4 *)(vp + (int64_t)slot_lds[kk] * rowstride_el +
-                                                   kvh * D + (lane & 1) * (D / 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // The reference m_run moves only when a row's tile maximum exceeds it
+        // by more than 2^8 (always on the first tile), so most tiles skip the
+        // rescale of O and l; p = 2^(s - m_run) <= 2^8 stays exact in fp32 and
+        // in range for bf16, and o / l does not depend on the reference.
+        const bool move = mx > m_run + 8.f;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float m_new = move ? mx : m_run;        // finite: every tile has a valid key
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -inf
+            l_run *= alpha;
 #pragma unroll
-                for (int c = 0; c < VCH; c++) vf[c] = src[c];
-            } else {
-#pragma unroll
-                for (int c = 0; c < VCH; c++) vf[c] = make_uint4(0, 0, 0, 0);
-            }
+            for (int db = 0; db < DB; db++) oacc[db] *= alpha;
+            m_run = m_new;
         }
-
-        // ---- S^T = K Q^T ------------------------------------------------------
-        f32x4 sacc[2][NB];
+        bf16x4 pf;
 #pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < QT; t++)
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kb][t]), qf[nb][t], c, 0, 0, 0);
-                sacc[kb][nb] = c;
-            }
-
-        // ---- V tile -> LDS (row-major, padded rows) ------------------------------
-        {
-            unsigned char *dst = v_lds + (lane >> 1) * ROWB + (lane & 1) * D;
-#pragma unroll
-            for (int c = 0; c < VCH; c++) *(uint4 *)(dst + c * 16) = vf[c];
+        for (int j = 0; j < 4; j++) {
+            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_run);
+            l_run += pj;
+            pf[j] = (__bf16)pj;
         }
-
-        // ---- online softmax per row ------------------------------------------------
-        bf16x8 pf[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) {
-            float sv[2][4];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int kk = t0 + kb * 16 + kq * 4 + j;
-                    float x = sacc[kb][nb][j] * qscale;
-                    x = kk < nk ? x : -INFINITY;
-                    sv[kb][j] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run[nb], mx);
-            const float alpha = exp2f(m_run[nb] - m_new);   // 0 when m_run = -inf
-            float psum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float p = exp2f(sv[kb][j] - m_new);
-                    psum += p;
-                    pf[nb][kb * 4 + j] = (__bf16)p;
-                }
-            l_run[nb] = l_run[nb] * alpha + psum;
-            m_run[nb] = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; db++) oacc[db][nb] *= alpha;
-        }
-
-        __syncthreads();   // V tile visible
-
-        // ---- O^T += V^T P^T ---------------------------------------------------
-        const int r4 = n16 >> 2, qq = n16 & 3;
+        // 16 dims x 16 keys per MFMA
 #pragma unroll
         for (int db = 0; db < DB; db++) {
-            const SGL_LDS i16x4 *p0 =
-                (const SGL_LDS i16x4 *)(v_lds + (kq * 4 + r4) * ROWB + (db * 16 + qq * 4) * 2);
-            const SGL_LDS i16x4 *p1 =
-                (const SGL_LDS i16x4 *)(v_lds + (16 + kq * 4 + r4) * ROWB + (db * 16 + qq * 4) * 2);
-            i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p0);
-            i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p1);
-            union { i16x4 h[2]; bf16x8 b; } va;
-            va.h[0] = lo4;
-            va.h[1] = hi4;
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++)
-                oacc[db][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.b, pf[nb], oacc[db][nb], 0, 0, 0);
+            const int c = 2 * db + (qq >> 1);
+            const i16x4 vt =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)(vb + vbase + 16 * (c ^ vsw)));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, __builtin_bit_cast(i16x4, pf), oacc[db],
+                                                                 0, 0, 0);
         }
-        __syncthreads();   // V tile consumed before the next overwrite
+    };
+
+    issue(0, kp, k_lds0);
+    issue(0, vp, v_lds0);
+    if constexpr (DEPTH == 1) {
+        for (int n = 0; n < N; n++) {
+            vm_wait<0>();                                // this wave's loads of tile n have landed
+            wg_barrier();                                // ... and every wave's
+            const f32x4 sacc = s_tile(k_lds0);
+            if (n + 1 < N) {
+                lgkm_wait0();
+                wg_barrier();                            // every wave has read the K tile
+                issue(n + 1, kp, k_lds0);
+            }
+            pv_tile(n, sacc, v_lds0);
+            if (n + 1 < N) {
+                lgkm_wait0();
+                wg_barrier();                            // every wave has read the V tile
+                issue(n + 1, vp, v_lds0);
+            }
+        }
+    } else {
+        if (N > 1) {
+            issue(1, kp, k_lds1);
+            issue(1, vp, v_lds1);
+        }
+        auto stage = [&](int n, auto par) {
+            constexpr bool P1 = decltype(par)::value;
+            unsigned char *kb = P1 ? k_lds1 : k_lds0;
+            unsigned char *vb = P1 ? v_lds1 : v_lds0;
+            if (n + 1 < N) vm_wait<2 * NIW>(); else vm_wait<0>();   // this wave's tile n has landed
+            wg_barrier();
+            pv_tile(n, s_tile(kb), vb);
+            if (n + 2 < N) {
+                lgkm_wait0();
+                wg_barrier();                            // every wave is done with this buffer
+                issue(n + 2, kp, kb);
+                issue(n + 2, vp, vb);
+            }
+        };
+        for (int n = 0; n < N; n += 2) {
+            stage(n, std::false_type{});
+            if (n + 1 < N) stage(n + 1, std::true_type{});
+        }
     }
 
     // ---- write the split's state ---------------------------------------------
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (n16 >= rows) return;
+    const int req = first_req + (row_base + n16) / g;
+    const int h = kvh * g + (row_base + n16) % g;
+    const int64_t idx = ((int64_t)req * a.part.S + s) * a.Hq + h;
+    float *op = a.part.o + idx * D;
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) {
-        float l = l_run[nb];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
-        const int rho = nb * 16 + n16;
-        if (rho >= rows) continue;
-        const int req = first_req + (row_base + rho) / g;
-        const int h = kvh * g + (row_base + rho) % g;
-        const int64_t idx = ((int64_t)req * a.part.S + s) * a.Hq + h;
-        float *op = a.part.o + idx * D;
-#pragma unroll
-        for (int db = 0; db < DB; db++) *(f32x4 *)(op + db * 16 + kq * 4) = oacc[db][nb];
-        if (kq == 0) {
-            a.part.ml[idx * 2] = m_run[nb];
-            a.part.ml[idx * 2 + 1] = l;
-        }
-    }
+    for (int db = 0; db < DB; db++) *(f32x4 *)(op + db * 16 + kq * 4) = oacc[db];
+    if (kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
 }
 
 }  // namespace
 
-int launch_split_bf16(const SplitArgs &a, hipStream_t st) {
-    if (a.n_sets == 0 || a.max_splits == 0) return SGL_OK;
-    const int g = a.Hq / a.Hkv;
-    int rows = (a.kind == 1 ? a.max_members : 1) * g;
-    SplitArgs b = a;
-    b.row_blocks = 1;
-    if (rows > 64) {                 // big groups: several 64-row waves per group
-        b.row_blocks = (rows + 63) / 64;
-        rows = 64;
-    }
-    dim3 grid(a.Hkv, a.max_splits, a.n_sets * b.row_blocks), block(64);
+int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
+    if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
+    if (a0.chunk % TILE != 0) return SGL_ERR_INVALID;
+    SplitArgs a = a0;
+    const int rows = (a.kind == 1 ? a.max_members : 1) * (a.Hq / a.Hkv);
+    a.row_blocks = (rows + 15) / 16;
+    // The flat and suffix calls have many short work items: one wave per
+    // workgroup and one buffer keep the most waves resident.  The prefix
+    // stage has few long items with up to 4 row blocks (64 query rows) per
+    // KV head: the row blocks share each tile, and two buffers double what
+    // each workgroup keeps in flight.
+    int wpg = 1;
+    if (a.kind == 1) wpg = a.row_blocks >= 3 ? 4 : a.row_blocks;
+    if (a.D == 64 && wpg > 2) wpg = 2;               // 2 load instructions per 64-dim tile
+    const int n_rbg = (a.row_blocks + wpg - 1) / wpg;
+    const int64_t items = (int64_t)a.n_sets * a.max_splits * a.Hkv;
+    const int64_t n_wg = ceil_div64(items, 8) * 8 * n_rbg;
+    if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
-#define SGL_LAUNCH(DD, NBB) \
-    hipLaunchKernelGGL((split_bf16_kernel<DD, NBB>), grid, block, dyn, st, b)
+    const dim3 grid((unsigned)n_wg), block(64 * wpg);
+#define SGL_SPLIT(DD, DP, W) hipLaunchKernelGGL((split_bf16_kernel<DD, DP, W>), grid, block, dyn, st, a)
     if (a.D == 128) {
-        if (rows <= 16) SGL_LAUNCH(128, 1);
-        else if (rows <= 32) SGL_LAUNCH(128, 2);
-        else SGL_LAUNCH(128, 4);
+        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT(128, 2, 1); else SGL_SPLIT(128, 1, 1); }
+        else if (wpg == 2) SGL_SPLIT(128, 2, 2);
+        else SGL_SPLIT(128, 2, 4);
     } else {
-        if (rows <= 16) SGL_LAUNCH(64, 1);
-        else if (rows <= 32) SGL_LAUNCH(64, 2);
-        else SGL_LAUNCH(64, 4);
+        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT(64, 2, 1); else SGL_SPLIT(64, 1, 1); }
+        else SGL_SPLIT(64, 2, 2);
     }
-#undef SGL_LAUNCH
+#undef SGL_SPLIT
     return hip_status(hipGetLastError());
 }

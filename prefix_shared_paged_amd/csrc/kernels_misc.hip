@@ -179,6 +179,9 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
         return pb.o + (((int64_t)r * pb.S + ss) * a.Hq + h) * D;
     };
 
+    // lane j holds the state of parts j, j + 64, ...: the maximum first, then
+    // each part's weight 2^(m - M) (0 for an empty part), broadcast by
+    // readlane while the o rows of eight parts are in flight at once
     float M = -INFINITY;
     for (int s0 = 0; s0 < total; s0 += 64) {
         const int s = s0 + lane;
@@ -193,16 +196,35 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) acc[i] = 0.f;
-    float Lsum = 0.f;
-    for (int s = 0; s < total; s++) {
-        const float2 v = ml_of(s);
-        if (!(v.y > 0.f)) continue;
-        const float f = exp2f(v.x - M);
-        Lsum += v.y * f;
-        const float *op = o_of(s);
+    float Lpart = 0.f;
+    for (int s0 = 0; s0 < total; s0 += 64) {
+        const int s = s0 + lane;
+        float f = 0.f;
+        if (s < total) {
+            const float2 v = ml_of(s);
+            if (v.y > 0.f) {
+                f = exp2f(v.x - M);
+                Lpart += v.y * f;
+            }
+        }
+        const int cnt = total - s0 < 64 ? total - s0 : 64;
+        for (int u0 = 0; u0 < cnt; u0 += 8) {
+            float ov[8][PER], fu[8];
 #pragma unroll
-        for (int i = 0; i < PER; i++) acc[i] += op[lane * PER + i] * f;
+            for (int u = 0; u < 8; u++) {
+                const int uu = u0 + u < cnt ? u0 + u : cnt - 1;
+                fu[u] = u0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), uu)) : 0.f;
+                const float *op = o_of(s0 + uu);
+#pragma unroll
+                for (int i = 0; i < PER; i++) ov[u][i] = op[lane * PER + i];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+#pragma unroll
+                for (int i = 0; i < PER; i++) acc[i] += fu[u] == 0.f ? 0.f : ov[u][i] * fu[u];
+        }
     }
+    const float Lsum = wave_sum(Lpart);
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
     const int64_t obase = ((int64_t)r * a.Hq + h) * D + lane * PER;
 #pragma unroll
