@@ -12,7 +12,7 @@ namespace {
 constexpr int kDecodeChunk = 1024;   // keys per split (flat decode and cascade suffix)
 constexpr int kPrefixChunkMax = 512;
 constexpr int kPrefixChunkMin = 64;
-constexpr int64_t kPrefixWorkgroups = 2048;  // ~8 per compute unit
+constexpr int64_t kPrefixWorkgroups = 1024;  // ~4 per compute unit
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

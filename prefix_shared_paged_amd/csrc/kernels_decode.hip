@@ -67,6 +67,43 @@ __device__ __forceinline__ bf16x8 ld_q(const __bf16 *p) {
     return __builtin_bit_cast(bf16x8, *(const u32x4 *)p);
 }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// LDS reads of the tiles written by direct loads, as inline asm: the kernel
+// itself waits for those loads (vmcnt) and, with several waves, meets at a
+// barrier before reading, so the compiler must not add a wait for every
+// direct load still in flight into the other buffer (its alias tracking of
+// direct-to-LDS loads cannot tell the two buffers apart).  Each group of
+// reads ends with lgkmcnt(0) tied to its results.
+template <int N>
+__device__ __forceinline__ void lds_read_b128(bf16x8 (&out)[N], const uint32_t (&addr)[N]) {
+    u32x4 r[N];
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("ds_read_b128 %0, %1" : "=v"(r[i]) : "v"(addr[i]));
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]));
+#pragma unroll
+    for (int i = 0; i < N; i++) out[i] = __builtin_bit_cast(bf16x8, r[i]);
+}
+template <int N>
+__device__ __forceinline__ void lds_read_tr16(i16x4 (&out)[N], const uint32_t (&addr)[N]) {
+    i32x2 r[N];
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r[i]) : "v"(addr[i]));
+    if constexpr (N == 8)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+#pragma unroll
+    for (int i = 0; i < N; i++) out[i] = __builtin_bit_cast(i16x4, r[i]);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const SGL_LDS void *)p;
+}
+
 // s_waitcnt vmcnt(N), other counters untouched
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -115,7 +152,11 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     };
 
     // ---- work item: id = ((item / 8) * n_rbg + rbg) * 8 + item % 8 -------------
-    // item = (set, split, KV head); rbg = which WPG row blocks of the item
+    // item = (split, set, KV head), split slowest: every request's first split
+    // is dispatched before any second one, so the waves that start last are
+    // the later (often partial) splits of long requests and the kernel's tail
+    // is short; and the first splits of a group's requests, which cover the
+    // shared prefix, run together.  rbg = which WPG row blocks of the item.
     const int n_rbg = (a.row_blocks + WPG - 1) / WPG;
     const int id = blockIdx.x;
     const int rest = id >> 3;
@@ -123,8 +164,9 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     const int64_t item = (int64_t)(rest / n_rbg) * 8 + (id & 7);
     const int kvh = (int)(item % a.Hkv);
     const int64_t t_ = item / a.Hkv;
-    const int s = (int)(t_ % a.max_splits);
-    const int64_t set64 = t_ / a.max_splits;
+    const int64_t set64 = t_ % a.n_sets;
+    const int s = (int)(t_ / a.n_sets);
+    if (s >= a.max_splits) return;
     if (set64 >= a.n_sets) return;
     const int set = (int)set64;
     const int g = a.Hq / a.Hkv;
@@ -233,9 +275,12 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
 
     // S^T = K Q^T of one tile: lane (row n16, kq) gets keys 4kq + j
     auto s_tile = [&](const unsigned char *kb) {
-        bf16x8 kf[QT];
+        const uint32_t b = lds_addr(kb) + kbase;
+        uint32_t ad[QT];
 #pragma unroll
-        for (int t = 0; t < QT; t++) kf[t] = *(const bf16x8 *)(kb + kbase + 16 * ((4 * t + kq) ^ ksw));
+        for (int t = 0; t < QT; t++) ad[t] = b + 16 * ((4 * t + kq) ^ ksw);
+        bf16x8 kf[QT];
+        lds_read_b128(kf, ad);
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < QT; t++) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], qf[t], sacc, 0, 0, 0);
@@ -274,14 +319,16 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
             pf[j] = (__bf16)pj;
         }
         // 16 dims x 16 keys per MFMA
+        const uint32_t b = lds_addr(vb) + vbase;
+        uint32_t ad[DB];
 #pragma unroll
-        for (int db = 0; db < DB; db++) {
-            const int c = 2 * db + (qq >> 1);
-            const i16x4 vt =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)(vb + vbase + 16 * (c ^ vsw)));
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, __builtin_bit_cast(i16x4, pf), oacc[db],
+        for (int db = 0; db < DB; db++) ad[db] = b + 16 * ((2 * db + (qq >> 1)) ^ vsw);
+        i16x4 vt[DB];
+        lds_read_tr16(vt, ad);
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[db], __builtin_bit_cast(i16x4, pf), oacc[db],
                                                                  0, 0, 0);
-        }
     };
 
     issue(0, kp, k_lds0);
