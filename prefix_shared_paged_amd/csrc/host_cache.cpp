@@ -25,7 +25,6 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
-#include <deque>
 #include <functional>
 #include <new>
 #include <queue>
@@ -34,11 +33,47 @@
 
 #include "sgl_attn.h"
 
+// One bit per page: is it on the free list.  A bit vector (128 KiB for 2^20
+// pages) stays cache-resident while pages are allocated and freed in random
+// order, where a byte per page would miss on nearly every access.
+struct PageBits {
+    std::vector<uint64_t> w;
+    int64_t n = 0;
+    void assign(int64_t n_pages) {
+        n = n_pages;
+        w.assign((size_t)((n_pages + 63) / 64), 0);
+    }
+    int64_t size() const { return n; }
+    bool operator[](int64_t i) const { return (w[(size_t)(i >> 6)] >> (i & 63)) & 1; }
+    void set(int64_t i) { w[(size_t)(i >> 6)] |= uint64_t(1) << (i & 63); }
+    void clear(int64_t i) { w[(size_t)(i >> 6)] &= ~(uint64_t(1) << (i & 63)); }
+};
+
+// FIFO of free page ids in a ring of capacity = pages of the pool (the list
+// never holds more).
+struct PageRing {
+    std::vector<int32_t> buf;
+    int64_t head = 0, count = 0;
+    void reserve(int64_t n_pages) { buf.assign((size_t)n_pages, 0); }
+    int64_t size() const { return count; }
+    int32_t front() const { return buf[(size_t)head]; }
+    void pop_front() {
+        head = head + 1 == (int64_t)buf.size() ? 0 : head + 1;
+        count--;
+    }
+    void push_back(int32_t pg) {
+        int64_t tail = head + count;
+        if (tail >= (int64_t)buf.size()) tail -= (int64_t)buf.size();
+        buf[(size_t)tail] = pg;
+        count++;
+    }
+};
+
 struct sgl_kv_pool {
     int64_t num_slots = 0;
     int32_t page = 1;
-    std::deque<int32_t> free_pages;  // head = front
-    std::vector<uint8_t> is_free;
+    PageRing free_pages;  // head = front
+    PageBits is_free;
 };
 
 namespace {
@@ -96,13 +131,20 @@ Node *find_child(const Node *n, const int32_t *tok, int32_t p) {
     return nullptr;
 }
 
-// Number of whole pages that `c`'s edge shares with tok[0 .. avail_pages*p).
+// Number of whole pages that `c`'s edge shares with tok[0 .. avail_pages*p):
+// the first differing token, rounded down to a page.  Long equal runs (a
+// cached prefix) are compared with memcmp -- whole range first, then 64-token
+// blocks -- and only the block holding the first difference token by token.
 int64_t edge_common_pages(const Node *c, const int32_t *tok, int64_t avail_pages, int32_t p) {
-    int64_t edge_pages = (int64_t)c->tokens.size() / p;
-    int64_t lim = std::min(edge_pages, avail_pages);
-    int64_t k = 0;
-    while (k < lim && page_equal(c->tokens.data() + k * p, tok + k * p, p)) k++;
-    return k;
+    const int64_t edge_pages = (int64_t)c->tokens.size() / p;
+    const int64_t lim = std::min(edge_pages, avail_pages) * p;
+    const int32_t *e = c->tokens.data();
+    if (std::memcmp(e, tok, sizeof(int32_t) * (size_t)lim) == 0) return lim / p;
+    constexpr int64_t BLK = 64;
+    int64_t i = 0;
+    while (i + BLK <= lim && std::memcmp(e + i, tok + i, sizeof(int32_t) * BLK) == 0) i += BLK;
+    while (i < lim && e[i] == tok[i]) i++;
+    return i / p;
 }
 
 // Split `c` after `k` pages: a new upper node takes the first k pages and
@@ -127,19 +169,20 @@ Node *split(sgl_radix *t, Node *c, int64_t k) {
 }
 
 int pool_free_pages(sgl_kv_pool *pool, const std::vector<int32_t> &pages) {
-    // validate everything first so that a failed call leaves the pool unchanged
-    std::vector<int32_t> seen;
-    for (int32_t pg : pages) {
-        if (pg < 0 || (int64_t)pg >= (int64_t)pool->is_free.size()) return SGL_ERR_INVALID;
-        if (pool->is_free[pg]) return SGL_ERR_INVALID;
+    // Mark pages free one by one; a page that is out of range, already free,
+    // or repeated in `pages` fails the call, and the marks made so far are
+    // undone, so a failed call leaves the pool unchanged.
+    size_t i = 0;
+    for (; i < pages.size(); i++) {
+        const int32_t pg = pages[i];
+        if (pg < 0 || (int64_t)pg >= pool->is_free.size() || pool->is_free[pg]) break;
+        pool->is_free.set(pg);
     }
-    seen = pages;
-    std::sort(seen.begin(), seen.end());
-    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return SGL_ERR_INVALID;
-    for (int32_t pg : pages) {
-        pool->is_free[pg] = 1;
-        pool->free_pages.push_back(pg);
+    if (i < pages.size()) {
+        for (size_t j = 0; j < i; j++) pool->is_free.clear(pages[j]);
+        return SGL_ERR_INVALID;
     }
+    for (int32_t pg : pages) pool->free_pages.push_back(pg);
     return SGL_OK;
 }
 
@@ -157,14 +200,15 @@ int sgl_kv_pool_create(int64_t num_slots, int32_t page_size, const int32_t *init
         auto *pool = new sgl_kv_pool();
         pool->num_slots = num_slots;
         pool->page = page_size;
-        pool->is_free.assign((size_t)n_pages, 0);
+        pool->is_free.assign(n_pages);
+        pool->free_pages.reserve(n_pages);
         for (int64_t i = 0; i < n_pages; i++) {
             int32_t pg = init_order ? init_order[i] : (int32_t)i;
             if (pg < 0 || pg >= n_pages || pool->is_free[pg]) {
                 delete pool;
                 return (int)SGL_ERR_INVALID;
             }
-            pool->is_free[pg] = 1;
+            pool->is_free.set(pg);
             pool->free_pages.push_back(pg);
         }
         *out = pool;
@@ -195,7 +239,7 @@ int sgl_kv_pool_alloc(sgl_kv_pool *pool, int64_t cur_len, int32_t last_slot, int
     for (int64_t i = 0; i < need; i++) {
         int32_t pg = pool->free_pages.front();
         pool->free_pages.pop_front();
-        pool->is_free[pg] = 0;
+        pool->is_free.clear(pg);
         for (int32_t j = 0; j < p && k < n; j++) out_slots[k++] = pg * p + j;
     }
     return SGL_OK;
@@ -205,10 +249,13 @@ int sgl_kv_pool_free(sgl_kv_pool *pool, const int32_t *slots, int64_t n) {
     if (!pool || n < 0 || (n > 0 && !slots)) return SGL_ERR_INVALID;
     return guarded([&] {
         std::vector<int32_t> pages;
+        const int32_t p = pool->page;
+        pages.reserve((size_t)(p == 1 ? n : n / p + 1));
         for (int64_t i = 0; i < n; i++) {
             int32_t s = slots[i];
             if (s < 0 || s >= pool->num_slots) return (int)SGL_ERR_INVALID;
-            if (s % pool->page == 0) pages.push_back(s / pool->page);
+            if (p == 1) pages.push_back(s);
+            else if (s % p == 0) pages.push_back(s / p);
         }
         return pool_free_pages(pool, pages);
     });
@@ -267,10 +314,16 @@ int sgl_radix_insert(sgl_radix *t, const int32_t *tokens, const int32_t *slots, 
     if (!t || n < 0 || (n > 0 && (!tokens || !slots))) return SGL_ERR_INVALID;
     const int32_t p = t->page;
     const int64_t n_ins = n / p * p;
-    for (int64_t i = 0; i < n_ins; i += p) {
-        if (slots[i] < 0 || slots[i] % p != 0) return SGL_ERR_INVALID;
-        for (int32_t j = 1; j < p; j++)
-            if (slots[i + j] != slots[i] + j) return SGL_ERR_INVALID;
+    if (p == 1) {
+        int32_t mn = 0;
+        for (int64_t i = 0; i < n_ins; i++) mn = std::min(mn, slots[i]);
+        if (mn < 0) return SGL_ERR_INVALID;
+    } else {
+        for (int64_t i = 0; i < n_ins; i += p) {
+            if (slots[i] < 0 || slots[i] % p != 0) return SGL_ERR_INVALID;
+            for (int32_t j = 1; j < p; j++)
+                if (slots[i + j] != slots[i] + j) return SGL_ERR_INVALID;
+        }
     }
     return guarded([&] {
         // Pass 1 (read only): how much is cached and which caller pages are duplicates.
@@ -283,8 +336,10 @@ int sgl_radix_insert(sgl_radix *t, const int32_t *tokens, const int32_t *slots, 
                 const Node *c = find_child(node, tokens + pos, p);
                 if (!c) break;
                 int64_t k = edge_common_pages(c, tokens + pos, (n_ins - pos) / p, p);
-                for (int64_t i = 0; i < k; i++)
-                    if (c->slots[i * p] != slots[pos + i * p]) dup_pages.push_back(slots[pos + i * p] / p);
+                // the caller's slots usually are the tree's (they came from a match)
+                if (std::memcmp(c->slots.data(), slots + pos, sizeof(int32_t) * (size_t)(k * p)) != 0)
+                    for (int64_t i = 0; i < k; i++)
+                        if (c->slots[i * p] != slots[pos + i * p]) dup_pages.push_back(slots[pos + i * p] / p);
                 pos += k * p;
                 if (k < (int64_t)c->tokens.size() / p) break;
                 node = c;
@@ -294,7 +349,7 @@ int sgl_radix_insert(sgl_radix *t, const int32_t *tokens, const int32_t *slots, 
         if (!dup_pages.empty()) {
             if (!pool || pool->page != p) return (int)SGL_ERR_INVALID;
             for (int32_t pg : dup_pages)
-                if (pg < 0 || (int64_t)pg >= (int64_t)pool->is_free.size() || pool->is_free[pg])
+                if (pg < 0 || (int64_t)pg >= pool->is_free.size() || pool->is_free[pg])
                     return (int)SGL_ERR_INVALID;
             std::vector<int32_t> sorted = dup_pages;
             std::sort(sorted.begin(), sorted.end());
@@ -365,13 +420,13 @@ int sgl_radix_evict(sgl_radix *t, int64_t n_tokens, sgl_kv_pool *pool, int64_t *
         while (freed < n_tokens && !heap.empty()) {
             Node *x = heap.top().second;
             heap.pop();
-            while (freed < n_tokens && !x->tokens.empty()) {
-                const size_t last = x->tokens.size() - p;
-                pages.push_back(x->slots[last] / p);
-                x->tokens.resize(last);
-                x->slots.resize(last);
-                freed += p;
-            }
+            // its pages go tail-first: all of them if the leaf goes entirely
+            const int64_t take = std::min<int64_t>((int64_t)x->tokens.size() / p, (n_tokens - freed + p - 1) / p);
+            const size_t keep = x->tokens.size() - (size_t)take * p;
+            for (size_t e = x->tokens.size(); e > keep; e -= p) pages.push_back(p == 1 ? x->slots[e - 1] : x->slots[e - p] / p);
+            x->tokens.resize(keep);
+            x->slots.resize(keep);
+            freed += take * p;
             if (x->tokens.empty()) {
                 Node *par = x->parent;
                 par->children.erase(std::find(par->children.begin(), par->children.end(), x));
@@ -384,8 +439,8 @@ int sgl_radix_evict(sgl_radix *t, int64_t n_tokens, sgl_kv_pool *pool, int64_t *
         // Pages cut from the tree go back to the pool.  A page the pool does not
         // know (slots inserted from another pool) or already holds is skipped.
         for (int32_t pg : pages) {
-            if (pg < 0 || (int64_t)pg >= (int64_t)pool->is_free.size() || pool->is_free[pg]) continue;
-            pool->is_free[pg] = 1;
+            if (pg < 0 || (int64_t)pg >= pool->is_free.size() || pool->is_free[pg]) continue;
+            pool->is_free.set(pg);
             pool->free_pages.push_back(pg);
         }
         if (out_freed) *out_freed = freed;

@@ -293,6 +293,39 @@ def test_decode_small(cascade, Hq, Hkv, D):
     assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
+def _split_edge_workload(seed, Hq, Hkv, D):
+    """Groups whose prefix and context lengths sit on and next to the
+    kernels' split (1024 keys) and tile (16 keys) boundaries, with group sizes
+    that leave partial 16-row blocks and idle waves in the prefix stage."""
+    spec = W.Spec("split_edges", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed)
+    members = [1, 2, 5, 9]
+    prefixes = [1024, 16, 1023, 17]
+    grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
+    sib = np.concatenate([np.arange(m) for m in members]).astype(np.int64)
+    L = np.array([1025,                                  # suffix = current token only
+                  17, 2048,                              # one-token suffix; split-aligned context
+                  1024, 1025, 2047, 2049, 3072,          # contexts around 1024-key splits
+                  18, 33, 1040, 1041, 2065, 3000, 3090, 4096, 4097], np.int64)
+    assert len(L) == len(grp)
+    return W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, sib, L)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 4, 64), (16, 2, 64), (8, 1, 128)])
+def test_decode_split_and_group_edges(Hq, Hkv, D):
+    # (16, 4, 64): 36 rows per KV head in the 9-member group -> 3 row blocks
+    # on 2-wave workgroups; (16, 2, 64): 72 rows; (8, 1, 128): one KV head
+    wl = _split_edge_workload(11, Hq, Hkv, D)
+    case = GroupCase(wl)
+    res = run_decode(case, wl.ctx_len.copy(), cascade=False, both=True)
+    case.check_r2t()
+    reqs, O, LSE = oracle_decode(case, res)
+    for tag, o, l in (("flat", res["o"], res["lse"]), ("cascade", res["o_c"], res["lse_c"])):
+        err = bf16_err(o[reqs], O)
+        lerr = float(np.max(np.abs(l[reqs] - LSE)))
+        _print(f"decode split edges {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+        assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
 def test_decode_full_size_flat_and_cascade():
     wl = W.decode(seed=0)
     case = GroupCase(wl)
