@@ -41,6 +41,7 @@
 namespace {
 
 constexpr int TILE = 16;   // keys per tile
+constexpr int PREFIX_DEPTH = 2;   // tile buffers of the cascade prefix stage
 
 // Position of 16-byte chunk c of K/V row r (within a tile) is c ^ swz<D>(r).
 // A K operand read touches one chunk of all 16 rows; a V^T read touches two
@@ -120,7 +121,7 @@ __device__ __forceinline__ void lgkm_wait0() {
 // instructions) and every wave computes its own 16 query rows against the
 // whole tile.  DEPTH LDS buffers per tile ring: with 1, tile n+1's K loads go
 // out once tile n's K operands are read and its V loads once tile n's V is
-// read; with 2, tile n+1 is in flight while tile n is computed.
+// read; with more, DEPTH-1 tiles are in flight while one is computed.
 template <int D, int DEPTH, int WPG>
 __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     constexpr int QT = D / 32;          // MFMA k-steps over head_dim
@@ -130,15 +131,12 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     constexpr int RPI = 64 / CHK;       // rows per direct-load instruction (1 KiB)
     constexpr int NI = TILE / RPI;      // direct-load instructions per K or V tile
     static_assert(NI % WPG == 0, "each wave issues the same number of loads");
+    static_assert(DEPTH >= 1 && DEPTH <= 4, "ring depth");
     constexpr int NIW = NI / WPG;       // K (and V) load instructions per wave per tile
     constexpr int TB = TILE * ROWB;
-    constexpr int TB1 = DEPTH > 1 ? TB : 16;
-    // one LDS object per buffer, so the compiler can tell that reads of one
-    // buffer do not wait on the direct loads into the other
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TB];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TB];
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TB1];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TB1];
+    // tile t of the split lives in ring buffer t % DEPTH
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TB];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TB];
     extern __shared__ int32_t slot_lds[];  // [chunk]
 
     const int lane = threadIdx.x & 63;
@@ -331,47 +329,48 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
                                                                  0, 0, 0);
     };
 
-    issue(0, kp, k_lds0);
-    issue(0, vp, v_lds0);
     if constexpr (DEPTH == 1) {
+        issue(0, kp, k_lds);
+        issue(0, vp, v_lds);
         for (int n = 0; n < N; n++) {
             vm_wait<0>();                                // this wave's loads of tile n have landed
             wg_barrier();                                // ... and every wave's
-            const f32x4 sacc = s_tile(k_lds0);
+            const f32x4 sacc = s_tile(k_lds);
             if (n + 1 < N) {
                 lgkm_wait0();
                 wg_barrier();                            // every wave has read the K tile
-                issue(n + 1, kp, k_lds0);
+                issue(n + 1, kp, k_lds);
             }
-            pv_tile(n, sacc, v_lds0);
+            pv_tile(n, sacc, v_lds);
             if (n + 1 < N) {
                 lgkm_wait0();
                 wg_barrier();                            // every wave has read the V tile
-                issue(n + 1, vp, v_lds0);
+                issue(n + 1, vp, v_lds);
             }
         }
     } else {
-        if (N > 1) {
-            issue(1, kp, k_lds1);
-            issue(1, vp, v_lds1);
+        // DEPTH-1 tiles stay in flight while one is computed
+        for (int t = 0; t < DEPTH && t < N; t++) {
+            issue(t, kp, k_lds + (t % DEPTH) * TB);
+            issue(t, vp, v_lds + (t % DEPTH) * TB);
         }
-        auto stage = [&](int n, auto par) {
-            constexpr bool P1 = decltype(par)::value;
-            unsigned char *kb = P1 ? k_lds1 : k_lds0;
-            unsigned char *vb = P1 ? v_lds1 : v_lds0;
-            if (n + 1 < N) vm_wait<2 * NIW>(); else vm_wait<0>();   // this wave's tile n has landed
+        for (int n = 0; n < N; n++) {
+            const int ahead = min(DEPTH - 1, N - 1 - n);   // tiles issued after tile n
+            // this wave's loads of tile n have landed when at most ahead * 2 * NIW remain
+            if (ahead >= 3) vm_wait<3 * 2 * NIW>();
+            else if (ahead == 2) vm_wait<2 * 2 * NIW>();
+            else if (ahead == 1) vm_wait<2 * NIW>();
+            else vm_wait<0>();
             wg_barrier();
+            unsigned char *kb = k_lds + (n % DEPTH) * TB;
+            unsigned char *vb = v_lds + (n % DEPTH) * TB;
             pv_tile(n, s_tile(kb), vb);
-            if (n + 2 < N) {
+            if (n + DEPTH < N) {
                 lgkm_wait0();
                 wg_barrier();                            // every wave is done with this buffer
-                issue(n + 2, kp, kb);
-                issue(n + 2, vp, vb);
+                issue(n + DEPTH, kp, kb);
+                issue(n + DEPTH, vp, vb);
             }
-        };
-        for (int n = 0; n < N; n += 2) {
-            stage(n, std::false_type{});
-            if (n + 1 < N) stage(n + 1, std::true_type{});
         }
     }
 
@@ -400,8 +399,8 @@ int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
     // The flat and suffix calls have many short work items: one wave per
     // workgroup and one buffer keep the most waves resident.  The prefix
     // stage has few long items with up to 4 row blocks (64 query rows) per
-    // KV head: the row blocks share each tile, and two buffers double what
-    // each workgroup keeps in flight.
+    // KV head: the row blocks share each tile, and a ring of PREFIX_DEPTH
+    // buffers keeps several tiles in flight per workgroup.
     int wpg = 1;
     if (a.kind == 1) wpg = a.row_blocks >= 3 ? 4 : a.row_blocks;
     if (a.D == 64 && wpg > 2) wpg = 2;               // 2 load instructions per 64-dim tile
@@ -413,12 +412,12 @@ int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
     const dim3 grid((unsigned)n_wg), block(64 * wpg);
 #define SGL_SPLIT(DD, DP, W) hipLaunchKernelGGL((split_bf16_kernel<DD, DP, W>), grid, block, dyn, st, a)
     if (a.D == 128) {
-        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT(128, 2, 1); else SGL_SPLIT(128, 1, 1); }
-        else if (wpg == 2) SGL_SPLIT(128, 2, 2);
-        else SGL_SPLIT(128, 2, 4);
+        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT(128, PREFIX_DEPTH, 1); else SGL_SPLIT(128, 1, 1); }
+        else if (wpg == 2) SGL_SPLIT(128, PREFIX_DEPTH, 2);
+        else SGL_SPLIT(128, PREFIX_DEPTH, 4);
     } else {
-        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT(64, 2, 1); else SGL_SPLIT(64, 1, 1); }
-        else SGL_SPLIT(64, 2, 2);
+        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT(64, PREFIX_DEPTH, 1); else SGL_SPLIT(64, 1, 1); }
+        else SGL_SPLIT(64, PREFIX_DEPTH, 2);
     }
 #undef SGL_SPLIT
     return hip_status(hipGetLastError());
