@@ -9,6 +9,8 @@ Contents
                         per-request sequences (C library, attn_oracle.c)
   attention_probs(...)  explicit probability matrix of one request / head
   merge_states(...)     merge of two partial softmax states
+  fp8                   OCP e4m3fn codes: decode, encode, per-head KV
+                        quantisation (pure numpy, see fp8.py)
   radix_model           brute-force prefix cache + slot allocator model
                         (pure Python, see radix_model.py)
 """
@@ -25,7 +27,8 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        if (not os.path.exists(_build.LIB)
+                or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
             _build.build()
         lib = ctypes.CDLL(_build.LIB)
         p = ctypes.c_void_p
@@ -35,6 +38,10 @@ def _load():
         lib.oracle_attention.argtypes = [i64, p, p, p, i64, p, p, p, i32, i32, i32,
                                          ctypes.c_double, p, i32, p, p, p, p, p, p,
                                          i32, i32]
+        lib.oracle_attention_kv_scaled.restype = ctypes.c_int
+        lib.oracle_attention_kv_scaled.argtypes = [i64, p, p, p, p, p, i64, p, p, p, i32, i32,
+                                                   i32, ctypes.c_double, p, i32, p, p, p, p,
+                                                   p, p, i32, i32]
         lib.oracle_attention_probs.restype = ctypes.c_int
         lib.oracle_attention_probs.argtypes = [i64, p, i64, p, p, i32, i32, i32, i32,
                                                ctypes.c_double, p]
@@ -56,7 +63,7 @@ def default_threads() -> int:
 
 
 def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=None,
-              key_lo=None, key_hi=None, method=0, threads=None):
+              key_lo=None, key_hi=None, method=0, threads=None, kv_scale=None):
     """Attention of query rows over their request's logical sequence.
 
     K_list / V_list: per request float32 arrays [L_r, Hkv, D] (logical order,
@@ -66,6 +73,9 @@ def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=No
     Q: float32 [n_rows, Hq, D].
     heads: optional list of q heads to evaluate (default all).
     key_lo / key_hi: optional per-row key range (intersected with j <= t).
+    kv_scale: optional (k_scale, v_scale), each [Hkv]: the keys and values
+      attended are K * k_scale[kv] and V * v_scale[kv] (a dequantised KV
+      cache: K / V hold the decoded codes, see oracle.fp8), formed in fp64.
     Returns (O [n_rows, n_heads, D], M, Lsum, LSE [n_rows, n_heads]) in float64.
     """
     lib = _load()
@@ -102,11 +112,17 @@ def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=No
     M = np.zeros((n_rows, n_heads), np.float64)
     Ls = np.zeros((n_rows, n_heads), np.float64)
     LSE = np.zeros((n_rows, n_heads), np.float64)
-    rc = lib.oracle_attention(len(kv_off) - 1, _ptr(kv_off), _ptr(K), _ptr(V), n_rows,
-                              _ptr(row_req), _ptr(row_pos), _ptr(Q), Hq, Hkv, D,
-                              float(scale), _ptr(heads), n_heads, _ptr(key_lo),
-                              _ptr(key_hi), _ptr(O), _ptr(M), _ptr(Ls), _ptr(LSE),
-                              int(method), int(threads or default_threads()))
+    ks = vs = None
+    if kv_scale is not None:
+        ks = np.ascontiguousarray(kv_scale[0], np.float64).reshape(-1)
+        vs = np.ascontiguousarray(kv_scale[1], np.float64).reshape(-1)
+        assert ks.shape[0] == Hkv and vs.shape[0] == Hkv
+    rc = lib.oracle_attention_kv_scaled(len(kv_off) - 1, _ptr(kv_off), _ptr(K), _ptr(V),
+                                        _ptr(ks), _ptr(vs), n_rows,
+                                        _ptr(row_req), _ptr(row_pos), _ptr(Q), Hq, Hkv, D,
+                                        float(scale), _ptr(heads), n_heads, _ptr(key_lo),
+                                        _ptr(key_hi), _ptr(O), _ptr(M), _ptr(Ls), _ptr(LSE),
+                                        int(method), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_attention: invalid arguments")
     return O, M, Ls, LSE

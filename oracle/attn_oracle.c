@@ -31,6 +31,11 @@
  *             and accumulator whenever the maximum grows (the online-softmax
  *             update of the PagedPrefill kernel, section 3.2).
  *
+ * A quantised KV cache (FP8 codes, "SGLang 深度拆解" section 4.3) is given as
+ * the decoded code values in K / V plus one factor per KV head for K and one
+ * for V: the key used is K * kscale[kv] and the value V * vscale[kv], each
+ * product formed in double (exact for float32 operands) before it is used.
+ *
  * Plus the merge of two partial softmax states (m, l, o) over disjoint key
  * sets.  The pages do not print this merge; it is the online-softmax update
  * of section 3.2 applied to a whole block instead of a single key.
@@ -49,6 +54,7 @@ typedef struct {
     const float *K, *V, *Q;
     int32_t Hq, Hkv, D;
     double scale;
+    const double *kscale, *vscale; /* per KV head dequantisation factors, NULL -> 1 */
     const int32_t *heads;     /* q heads to evaluate */
     int32_t n_heads;
     const int64_t *key_lo, *key_hi; /* per query row key range, NULL -> [0, t] */
@@ -65,6 +71,8 @@ static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
     const int32_t h = jb->heads ? jb->heads[hs] : hs;
     const int32_t group = Hq / Hkv;
     const int32_t kvh = h / group;
+    const double ks = jb->kscale ? jb->kscale[kvh] : 1.0;
+    const double vs = jb->vscale ? jb->vscale[kvh] : 1.0;
     const int64_t r = jb->row_req[row];
     const int64_t t = jb->row_pos[row];
     const int64_t base = jb->kv_off[r];
@@ -88,7 +96,7 @@ static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
         for (int64_t j = lo; j < hi; j++) {
             const float *k = jb->K + ((base + j) * Hkv + kvh) * D;
             double s = 0.0;
-            for (int32_t d = 0; d < D; d++) s += (double)q[d] * (double)k[d];
+            for (int32_t d = 0; d < D; d++) s += (double)q[d] * ((double)k[d] * ks);
             s *= jb->scale;
             sbuf[j - lo] = s;
             if (s > m) m = s;
@@ -98,7 +106,7 @@ static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
             const float *v = jb->V + ((base + j) * Hkv + kvh) * D;
             double w = exp(sbuf[j - lo] - m);
             l += w;
-            for (int32_t d = 0; d < D; d++) o[d] += w * (double)v[d];
+            for (int32_t d = 0; d < D; d++) o[d] += w * ((double)v[d] * vs);
         }
     } else {
         /* one pass, running maximum */
@@ -106,13 +114,13 @@ static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
             const float *k = jb->K + ((base + j) * Hkv + kvh) * D;
             const float *v = jb->V + ((base + j) * Hkv + kvh) * D;
             double s = 0.0;
-            for (int32_t d = 0; d < D; d++) s += (double)q[d] * (double)k[d];
+            for (int32_t d = 0; d < D; d++) s += (double)q[d] * ((double)k[d] * ks);
             s *= jb->scale;
             double m_new = s > m ? s : m;
             double c = exp(m - m_new);      /* rescale of what came before */
             double w = exp(s - m_new);
             l = l * c + w;
-            for (int32_t d = 0; d < D; d++) o[d] = o[d] * c + w * (double)v[d];
+            for (int32_t d = 0; d < D; d++) o[d] = o[d] * c + w * ((double)v[d] * vs);
             m = m_new;
         }
     }
@@ -152,7 +160,8 @@ static void *worker(void *arg) {
 }
 
 /*
- * oracle_attention -- softmax(q k^T * scale, causal) v for a set of query rows.
+ * oracle_attention, oracle_attention_kv_scaled -- softmax(q k^T * scale,
+ * causal) v for a set of query rows.
  *
  *   n_req, kv_off[n_req+1]: logical K/V rows of request r are
  *       K[kv_off[r] .. kv_off[r+1]) (layout [rows, Hkv, D], float32).
@@ -166,15 +175,18 @@ static void *worker(void *arg) {
  *       M is the maximum score, Lsum = sum_j exp(s_j - M), LSE = M + ln Lsum.
  *       An empty key range gives O = 0, Lsum = 0, M = LSE = -inf.
  *   method: 0 two-pass, 1 online.  n_threads >= 1.
+ *   kscale, vscale [Hkv] (oracle_attention_kv_scaled only, NULL -> 1): the
+ *       keys and values used are K * kscale[kv] and V * vscale[kv].
  * Returns 0, or -1 on invalid arguments / allocation failure.
  */
-int oracle_attention(int64_t n_req, const int64_t *kv_off, const float *K, const float *V,
-                     int64_t n_rows, const int64_t *row_req, const int64_t *row_pos,
-                     const float *Q, int32_t Hq, int32_t Hkv, int32_t D, double scale,
-                     const int32_t *heads, int32_t n_heads,
-                     const int64_t *key_lo, const int64_t *key_hi,
-                     double *O, double *M, double *Lsum, double *LSE,
-                     int32_t method, int32_t n_threads) {
+int oracle_attention_kv_scaled(int64_t n_req, const int64_t *kv_off, const float *K, const float *V,
+                               const double *kscale, const double *vscale,
+                               int64_t n_rows, const int64_t *row_req, const int64_t *row_pos,
+                               const float *Q, int32_t Hq, int32_t Hkv, int32_t D, double scale,
+                               const int32_t *heads, int32_t n_heads,
+                               const int64_t *key_lo, const int64_t *key_hi,
+                               double *O, double *M, double *Lsum, double *LSE,
+                               int32_t method, int32_t n_threads) {
     if (Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || n_threads < 1) return -1;
     if (!heads) n_heads = Hq;
     for (int64_t i = 0; i < n_rows; i++) {
@@ -187,7 +199,7 @@ int oracle_attention(int64_t n_req, const int64_t *kv_off, const float *K, const
     job_t jb;
     memset(&jb, 0, sizeof jb);
     jb.n_rows = n_rows; jb.row_req = row_req; jb.row_pos = row_pos; jb.kv_off = kv_off;
-    jb.K = K; jb.V = V; jb.Q = Q; jb.Hq = Hq; jb.Hkv = Hkv; jb.D = D; jb.scale = scale;
+    jb.K = K; jb.V = V; jb.kscale = kscale; jb.vscale = vscale; jb.Q = Q; jb.Hq = Hq; jb.Hkv = Hkv; jb.D = D; jb.scale = scale;
     jb.heads = heads; jb.n_heads = n_heads; jb.key_lo = key_lo; jb.key_hi = key_hi;
     jb.method = method; jb.n_threads = n_threads; jb.O = O; jb.M = M; jb.L = Lsum; jb.LSE = LSE; jb.next = 0;
     pthread_mutex_init(&jb.mu, NULL);
@@ -211,6 +223,18 @@ int oracle_attention(int64_t n_req, const int64_t *kv_off, const float *K, const
     }
     pthread_mutex_destroy(&jb.mu);
     return rc;
+}
+
+int oracle_attention(int64_t n_req, const int64_t *kv_off, const float *K, const float *V,
+                     int64_t n_rows, const int64_t *row_req, const int64_t *row_pos,
+                     const float *Q, int32_t Hq, int32_t Hkv, int32_t D, double scale,
+                     const int32_t *heads, int32_t n_heads,
+                     const int64_t *key_lo, const int64_t *key_hi,
+                     double *O, double *M, double *Lsum, double *LSE,
+                     int32_t method, int32_t n_threads) {
+    return oracle_attention_kv_scaled(n_req, kv_off, K, V, NULL, NULL, n_rows, row_req, row_pos, Q, Hq,
+                                      Hkv, D, scale, heads, n_heads, key_lo, key_hi, O, M, Lsum, LSE,
+                                      method, n_threads);
 }
 
 /*

@@ -33,7 +33,7 @@ VOCAB = 128000
 SIBLING_BASE = 120000   # first token after a shared prefix: SIBLING_BASE + sibling index
 
 # stream tags
-T_TOK_PREFIX, T_TOK_SUFFIX, T_KV_PREFIX, T_KV_SUFFIX, T_Q, T_LEN, T_POOL, T_KV_NEW = range(8)
+T_TOK_PREFIX, T_TOK_SUFFIX, T_KV_PREFIX, T_KV_SUFFIX, T_Q, T_LEN, T_POOL, T_KV_NEW, T_FP8 = range(9)
 
 
 def rng(seed, *ids):
@@ -82,6 +82,17 @@ def values(spec, shape, *ids):
     if spec.dtype == "bf16":
         x = round_to_bf16(x)
     return x
+
+
+def fp8_scales(spec):
+    """Per-KV-head factors (k_scale, v_scale), float32 [Hkv] each, of an FP8
+    KV cache over this workload's values: value_scale * U(4, 6) / 448, i.e.
+    the largest code stands for 4 to 6 standard deviations (values beyond it
+    clamp).  Drawn, not computed from the data."""
+    r = rng(spec.seed, T_FP8)
+    k = (spec.value_scale * r.uniform(4.0, 6.0, spec.Hkv) / 448.0).astype(np.float32)
+    v = (spec.value_scale * r.uniform(4.0, 6.0, spec.Hkv) / 448.0).astype(np.float32)
+    return k, v
 
 
 def pool_order(spec):
