@@ -295,6 +295,59 @@ size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
                                   int32_t max_group_size, int32_t max_prefix_len,
                                   int32_t Hq, int32_t Hkv, int32_t D);
 
+/* ------------------------------------------------------------------------
+ * FP8 KV cache.  SGLang can keep the KV cache in FP8, which halves its bytes
+ * ("SGLang 深度拆解" (chenxutan.com) section 4.3; the SGLang lecture notes
+ * (bhfrc.com) section 4 list an FP8 KV cache among the kernel work).  The
+ * pages fix neither format nor scaling; this library uses:
+ *   - pools of uint8 OCP e4m3fn codes, layout [num_slots, Hkv, D] as for the
+ *     bf16 pools (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ *     infinity; S.1111.111 is NaN; largest finite 448);
+ *   - one fp32 factor per KV head for K (k_scale[Hkv]) and one for V
+ *     (v_scale[Hkv]), device arrays: code c of head kv stands for
+ *     value(c) * scale[kv];
+ *   - quantisation of x (head kv): y = x / scale[kv] in fp32, clamped to
+ *     [-448, 448], rounded to the nearest e4m3fn value, ties to the even
+ *     code; the sign is kept (a negative y that rounds to 0 gives 0x80).
+ *     A NaN input gives a NaN code.
+ * Attention then equals attention over the dequantised K and V.
+ * ---------------------------------------------------------------------- */
+
+/* Quantise and store K/V rows: as sgl_store_kv, with k_new / v_new of
+ * dtype (SGL_F32 or SGL_BF16, [n_tokens, Hkv, D]) written as codes into the
+ * uint8 pools k_pool / v_pool [num_slots, Hkv, D]. */
+int sgl_store_kv_fp8(int dtype, const void *k_new, const void *v_new, int64_t n_tokens,
+                     const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                     int32_t Hkv, int32_t D, const float *k_scale, const float *v_scale, void *stream);
+
+/* sgl_decode_attn over an FP8 KV cache.  dtype must be SGL_BF16 (q, o and,
+ * when given, k_new / v_new [batch, Hkv, D], which are quantised and stored
+ * first); k_pool / v_pool hold codes, k_scale / v_scale their per-head
+ * factors.  The workspace is sgl_decode_workspace_size(...) bytes, as for
+ * the bf16 call. */
+int sgl_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, const void *v_new,
+                          void *k_pool, void *v_pool, const float *k_scale, const float *v_scale,
+                          int64_t num_slots, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                          const int32_t *req_rows, const int32_t *seq_lens,
+                          int32_t batch, int32_t max_seq_len,
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                          void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* sgl_cascade_decode_attn over an FP8 KV cache (arguments as
+ * sgl_decode_attn_fp8kv plus the group arguments of sgl_cascade_decode_attn;
+ * workspace sgl_cascade_workspace_size(...) bytes).  The result equals
+ * sgl_decode_attn_fp8kv. */
+int sgl_cascade_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, const void *v_new,
+                                  void *k_pool, void *v_pool, const float *k_scale, const float *v_scale,
+                                  int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+                                  int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens,
+                                  const int32_t *group_ptr, const int32_t *group_prefix_len,
+                                  int32_t batch, int32_t G, int32_t max_seq_len,
+                                  int32_t max_group_size, int32_t max_prefix_len,
+                                  int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                  void *o, float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

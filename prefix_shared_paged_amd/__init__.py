@@ -75,6 +75,12 @@ def load():
                                                    P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
                                                    F, P, P, P, SZ, P]),
         "sgl_cascade_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, I32]),
+        "sgl_store_kv_fp8": (ctypes.c_int, [ctypes.c_int, P, P, I64, P, P, P, I64, I32, I32, P, P, P]),
+        "sgl_decode_attn_fp8kv": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, P, P, I64, P, I64, I64,
+                                                 P, P, I32, I32, I32, I32, I32, F, P, P, P, SZ, P]),
+        "sgl_cascade_decode_attn_fp8kv": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, P, P, I64, P,
+                                                         I64, I64, P, P, P, P, I32, I32, I32, I32,
+                                                         I32, I32, I32, I32, F, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -90,7 +96,8 @@ EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_kv_pool_create", "sgl_kv
            "sgl_radix_evict", "sgl_radix_stats", "sgl_radix_match_batch", "sgl_radix_insert_batch",
            "sgl_radix_lock_batch", "sgl_kv_pool_alloc_batch", "sgl_build_req_to_token", "sgl_store_kv",
            "sgl_extend_attn", "sgl_extend_workspace_size", "sgl_decode_attn",
-           "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size"]
+           "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size",
+           "sgl_store_kv_fp8", "sgl_decode_attn_fp8kv", "sgl_cascade_decode_attn_fp8kv"]
 
 
 def status_string(status: int) -> str:
@@ -387,6 +394,88 @@ def cascade_decode_attn(q, k_pool, v_pool, r2t, req_rows, seq_lens, group_ptr, g
         _dtype_code(q), _dev_ptr(q, "q", q.dtype), _dev_ptr(k_new, "k_new", q.dtype, True),
         _dev_ptr(v_new, "v_new", q.dtype, True), _dev_ptr(k_pool, "k_pool", q.dtype),
         _dev_ptr(v_pool, "v_pool", q.dtype), k_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(group_ptr, "group_ptr", torch.int32),
+        _dev_ptr(group_prefix_len, "group_prefix_len", torch.int32), B, G, max_seq_len,
+        max_group_size, max_prefix_len, Hq, Hkv, D, scale, _dev_ptr(o, "o", q.dtype),
+        _dev_ptr(lse, "lse", torch.float32, True), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3fn) KV cache: uint8 code pools [S, Hkv, D] with float32 per-head
+# factors k_scale / v_scale [Hkv] (code c of head kv stands for value(c) * scale[kv])
+# ---------------------------------------------------------------------------
+def _check_fp8_pools(k_pool, v_pool, k_scale, v_scale, Hkv, D):
+    if tuple(k_pool.shape[1:]) != (Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_pool / v_pool must both be [num_slots, Hkv, D]")
+    if k_scale.numel() != Hkv or v_scale.numel() != Hkv:
+        raise ValueError("k_scale / v_scale must hold one factor per KV head")
+
+
+def store_kv_fp8(k_new, v_new, slots, k_pool, v_pool, k_scale, v_scale, stream=None):
+    """Quantise K/V rows [n, Hkv, D] (fp32 or bf16) into the code pools at slots."""
+    torch = _torch()
+    n, Hkv, D = k_new.shape
+    _check_fp8_pools(k_pool, v_pool, k_scale, v_scale, Hkv, D)
+    if tuple(v_new.shape) != tuple(k_new.shape) or slots.numel() != n:
+        raise ValueError("v_new must match k_new and slots hold one slot per row")
+    _check("sgl_store_kv_fp8", load().sgl_store_kv_fp8(
+        _dtype_code(k_new), _dev_ptr(k_new, "k_new", k_new.dtype), _dev_ptr(v_new, "v_new", k_new.dtype), n,
+        _dev_ptr(slots, "slots", torch.int32), _dev_ptr(k_pool, "k_pool", torch.uint8),
+        _dev_ptr(v_pool, "v_pool", torch.uint8), k_pool.shape[0], Hkv, D,
+        _dev_ptr(k_scale, "k_scale", torch.float32), _dev_ptr(v_scale, "v_scale", torch.float32),
+        _stream(stream)))
+
+
+def decode_attn_fp8kv(q, k_pool, v_pool, k_scale, v_scale, r2t, req_rows, seq_lens, max_seq_len,
+                      k_new=None, v_new=None, scale=None, o=None, lse=None, workspace=None, stream=None):
+    """decode_attn over an FP8 KV cache; q bf16 [batch, Hq, D]; returns o."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    _check_fp8_pools(k_pool, v_pool, k_scale, v_scale, Hkv, D)
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    ws_n = decode_workspace_size(B, max_seq_len, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _check("sgl_decode_attn_fp8kv", load().sgl_decode_attn_fp8kv(
+        _dtype_code(q), _dev_ptr(q, "q", q.dtype), _dev_ptr(k_new, "k_new", q.dtype, True),
+        _dev_ptr(v_new, "v_new", q.dtype, True), _dev_ptr(k_pool, "k_pool", torch.uint8),
+        _dev_ptr(v_pool, "v_pool", torch.uint8), _dev_ptr(k_scale, "k_scale", torch.float32),
+        _dev_ptr(v_scale, "v_scale", torch.float32), k_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), B, max_seq_len, Hq, Hkv, D, scale,
+        _dev_ptr(o, "o", q.dtype), _dev_ptr(lse, "lse", torch.float32, True),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+def cascade_decode_attn_fp8kv(q, k_pool, v_pool, k_scale, v_scale, r2t, req_rows, seq_lens, group_ptr,
+                              group_prefix_len, max_seq_len, max_group_size, max_prefix_len, k_new=None,
+                              v_new=None, scale=None, o=None, lse=None, workspace=None, stream=None):
+    """cascade_decode_attn over an FP8 KV cache; returns o."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    _check_fp8_pools(k_pool, v_pool, k_scale, v_scale, Hkv, D)
+    G = group_prefix_len.numel()
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    ws_n = cascade_workspace_size(B, G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _check("sgl_cascade_decode_attn_fp8kv", load().sgl_cascade_decode_attn_fp8kv(
+        _dtype_code(q), _dev_ptr(q, "q", q.dtype), _dev_ptr(k_new, "k_new", q.dtype, True),
+        _dev_ptr(v_new, "v_new", q.dtype, True), _dev_ptr(k_pool, "k_pool", torch.uint8),
+        _dev_ptr(v_pool, "v_pool", torch.uint8), _dev_ptr(k_scale, "k_scale", torch.float32),
+        _dev_ptr(v_scale, "v_scale", torch.float32), k_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
         r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
         _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(group_ptr, "group_ptr", torch.int32),
         _dev_ptr(group_prefix_len, "group_prefix_len", torch.int32), B, G, max_seq_len,

@@ -100,7 +100,7 @@ const char *sgl_status_string(int status) {
     }
 }
 
-int sgl_abi_version(void) { return 1; }
+int sgl_abi_version(void) { return 2; }
 
 int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
                            const int32_t *req_rows, int32_t batch, const int32_t *prefix_slots,
@@ -150,6 +150,24 @@ int sgl_store_kv(int dtype, const void *k_new, const void *v_new, int64_t n_toke
     }
     return launch_store_kv(0, elt_size(dtype), k_new, v_new, n_tokens, slots, k_pool, v_pool, num_slots,
                            Hkv, D, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0, st);
+}
+
+int sgl_store_kv_fp8(int dtype, const void *k_new, const void *v_new, int64_t n_tokens,
+                     const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                     int32_t Hkv, int32_t D, const float *k_scale, const float *v_scale, void *stream) {
+    if (!shape_ok(dtype, Hkv, Hkv, D)) return SGL_ERR_UNSUPPORTED;
+    if (n_tokens < 0 || num_slots < 0) return SGL_ERR_INVALID;
+    if (n_tokens == 0) return SGL_OK;
+    if (!k_new || !v_new || !slots || !k_pool || !v_pool || !k_scale || !v_scale) return SGL_ERR_INVALID;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_on()) {
+        std::vector<int32_t> s;
+        if (!fetch(s, slots, (size_t)n_tokens, st)) return SGL_ERR_HIP;
+        for (int32_t x : s)
+            if (x < 0 || x >= num_slots) return SGL_ERR_INVALID;
+    }
+    return launch_store_kv_fp8(0, elt_size(dtype), k_new, v_new, n_tokens, slots, k_pool, v_pool, num_slots,
+                               Hkv, D, k_scale, v_scale, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0, st);
 }
 
 size_t sgl_extend_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
@@ -211,18 +229,20 @@ size_t sgl_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq,
 
 namespace {
 
-int decode_common(bool cascade, int dtype, const void *q, const void *k_new, const void *v_new,
-                  void *k_pool, void *v_pool, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *k_new, const void *v_new,
+                  void *k_pool, void *v_pool, const float *k_scale, const float *v_scale, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
                   int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens,
                   const int32_t *group_ptr, const int32_t *group_prefix_len, int32_t batch, int32_t G,
                   int32_t max_seq_len, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq,
                   int32_t Hkv, int32_t D, float scale, void *o, float *lse, void *workspace,
                   size_t workspace_bytes, void *stream) {
     if (!shape_ok(dtype, Hq, Hkv, D)) return SGL_ERR_UNSUPPORTED;
+    if (fp8 && dtype != SGL_BF16) return SGL_ERR_UNSUPPORTED;   // FP8 KV: bf16 queries only
     if (batch < 0 || max_seq_len < 0 || num_slots < 1 || num_rows < 0 || row_stride < 0)
         return SGL_ERR_INVALID;
     if (batch == 0) return SGL_OK;
     if (!q || !k_pool || !v_pool || !r2t || !req_rows || !seq_lens || !o) return SGL_ERR_INVALID;
+    if (fp8 && (!k_scale || !v_scale)) return SGL_ERR_INVALID;
     if ((k_new == nullptr) != (v_new == nullptr)) return SGL_ERR_INVALID;
     if (max_seq_len < 1) return SGL_ERR_INVALID;
     const int g = Hq / Hkv;
@@ -266,8 +286,11 @@ int decode_common(bool cascade, int dtype, const void *q, const void *k_new, con
 
     int rc = SGL_OK;
     if (k_new) {
-        rc = launch_store_kv(2, elt_size(dtype), k_new, v_new, batch, nullptr, k_pool, v_pool, num_slots,
-                             Hkv, D, r2t, num_rows, row_stride, req_rows, seq_lens, nullptr, batch, 0, st);
+        rc = fp8 ? launch_store_kv_fp8(2, elt_size(dtype), k_new, v_new, batch, nullptr, k_pool, v_pool,
+                                       num_slots, Hkv, D, k_scale, v_scale, r2t, num_rows, row_stride,
+                                       req_rows, seq_lens, nullptr, batch, 0, st)
+                 : launch_store_kv(2, elt_size(dtype), k_new, v_new, batch, nullptr, k_pool, v_pool, num_slots,
+                                   Hkv, D, r2t, num_rows, row_stride, req_rows, seq_lens, nullptr, batch, 0, st);
         if (rc != SGL_OK) return rc;
     }
 
@@ -277,8 +300,9 @@ int decode_common(bool cascade, int dtype, const void *q, const void *k_new, con
     a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots; a.r2t = r2t;
     a.num_rows = num_rows; a.row_stride = row_stride; a.req_rows = req_rows; a.seq_lens = seq_lens;
     a.group_ptr = group_ptr; a.group_prefix_len = group_prefix_len; a.batch = batch; a.G = G;
-    a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.scale = scale;
+    a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
     auto run_split = [&](const SplitArgs &x) {
+        if (fp8) return launch_split_fp8(x, st);
         return dtype == SGL_F32 ? launch_split_f32(x, st) : launch_split_bf16(x, st);
     };
 
@@ -321,9 +345,20 @@ int sgl_decode_attn(int dtype, const void *q, const void *k_new, const void *v_n
                     int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens, int32_t batch,
                     int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D, float scale, void *o,
                     float *lse, void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(false, dtype, q, k_new, v_new, k_pool, v_pool, num_slots, r2t, num_rows,
-                         row_stride, req_rows, seq_lens, nullptr, nullptr, batch, 0, max_seq_len, 0, 0,
-                         Hq, Hkv, D, scale, o, lse, workspace, workspace_bytes, stream);
+    return decode_common(false, false, dtype, q, k_new, v_new, k_pool, v_pool, nullptr, nullptr, num_slots,
+                         r2t, num_rows, row_stride, req_rows, seq_lens, nullptr, nullptr, batch, 0,
+                         max_seq_len, 0, 0, Hq, Hkv, D, scale, o, lse, workspace, workspace_bytes, stream);
+}
+
+int sgl_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,
+                          void *v_pool, const float *k_scale, const float *v_scale, int64_t num_slots,
+                          const int32_t *r2t, int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                          const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, int32_t Hq,
+                          int32_t Hkv, int32_t D, float scale, void *o, float *lse, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return decode_common(false, true, dtype, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, num_slots,
+                         r2t, num_rows, row_stride, req_rows, seq_lens, nullptr, nullptr, batch, 0,
+                         max_seq_len, 0, 0, Hq, Hkv, D, scale, o, lse, workspace, workspace_bytes, stream);
 }
 
 size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len, int32_t max_group_size,
@@ -344,9 +379,24 @@ int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const v
                             int32_t G, int32_t max_seq_len, int32_t max_group_size,
                             int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D, float scale,
                             void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
-    return decode_common(true, dtype, q, k_new, v_new, k_pool, v_pool, num_slots, r2t, num_rows,
-                         row_stride, req_rows, seq_lens, group_ptr, group_prefix_len, batch, G,
-                         max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D, scale, o, lse,
+    return decode_common(true, false, dtype, q, k_new, v_new, k_pool, v_pool, nullptr, nullptr, num_slots,
+                         r2t, num_rows, row_stride, req_rows, seq_lens, group_ptr, group_prefix_len, batch,
+                         G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D, scale, o, lse,
+                         workspace, workspace_bytes, stream);
+}
+
+int sgl_cascade_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, const void *v_new,
+                                  void *k_pool, void *v_pool, const float *k_scale, const float *v_scale,
+                                  int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+                                  int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens,
+                                  const int32_t *group_ptr, const int32_t *group_prefix_len, int32_t batch,
+                                  int32_t G, int32_t max_seq_len, int32_t max_group_size,
+                                  int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                  void *o, float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    return decode_common(true, true, dtype, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, num_slots,
+                         r2t, num_rows, row_stride, req_rows, seq_lens, group_ptr, group_prefix_len, batch,
+                         G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D, scale, o, lse,
                          workspace, workspace_bytes, stream);
 }
 

@@ -69,6 +69,14 @@ int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int
                     const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
                     int32_t batch, int32_t max_extend_len, hipStream_t st);
 
+// The same three modes, quantising to e4m3fn codes with per-KV-head factors.
+int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
+                        const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                        int32_t Hkv, int32_t D, const float *k_scale, const float *v_scale,
+                        const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                        const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
+                        int32_t batch, int32_t max_extend_len, hipStream_t st);
+
 int launch_extend_f32(const float *q, const float *k_pool, const float *v_pool, int64_t num_slots,
                       const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                       const int32_t *req_rows, const int32_t *prefix_lens, const int64_t *q_off,
@@ -108,11 +116,14 @@ struct SplitArgs {
     int32_t row_blocks;    // kind 1: waves per group (64 rows each) -- set by the launcher
     int32_t Hq, Hkv, D;
     float scale;
+    const float *k_scale;  // FP8 KV only: per KV head factors of the K and V codes
+    const float *v_scale;
     PartialBuf part;
 };
 
 int launch_split_f32(const SplitArgs &a, hipStream_t st);
 int launch_split_bf16(const SplitArgs &a, hipStream_t st);
+int launch_split_fp8(const SplitArgs &a, hipStream_t st);
 
 // Merge partial states of (optionally) a prefix buffer and a suffix buffer.
 //   kind 0: parts = flat splits of r;  kind 3: parts = prefix splits of group(r) for r

@@ -62,6 +62,76 @@ __device__ __forceinline__ int find_group_dec(const int32_t *group_ptr, int G, i
     return lo;
 }
 
+// ---- work item of a split kernel ------------------------------------------------
+// Workgroup id = ((item / 8) * n_rbg + rbg) * 8 + item % 8 with item = (split,
+// set, KV head), split slowest: every request's first split is dispatched
+// before any second one, so the waves that start last are the later (often
+// partial) splits of long requests and the kernel's tail is short; and the
+// first splits of a group's requests, which cover the shared prefix, run
+// together.  rbg = which WPG row blocks of the item; consecutive ids differ in
+// the KV head first, so the 8 XCDs see the 8 heads of one (split, set).
+struct SplitItem {
+    int kvh, s, first_req, n_members, row_base, nk;
+    int64_t k0, ref_row;
+};
+
+template <int WPG>
+__device__ __forceinline__ bool split_item(const SplitArgs &a, int w, SplitItem &it) {
+    const int n_rbg = (a.row_blocks + WPG - 1) / WPG;
+    const int id = blockIdx.x;
+    const int rest = id >> 3;
+    const int rbg = rest % n_rbg;
+    const int64_t item = (int64_t)(rest / n_rbg) * 8 + (id & 7);
+    const int kvh = (int)(item % a.Hkv);
+    const int64_t t_ = item / a.Hkv;
+    const int64_t set64 = t_ % a.n_sets;
+    const int s = (int)(t_ / a.n_sets);
+    if (s >= a.max_splits) return false;
+    if (set64 >= a.n_sets) return false;
+    const int set = (int)set64;
+    const int g = a.Hq / a.Hkv;
+
+    // which rows, which keys (uniform over the workgroup)
+    int first_req, n_members;
+    int64_t lo, hi, ref_row;
+    if (a.kind == 1) {
+        first_req = a.group_ptr[set];
+        n_members = a.group_ptr[set + 1] - first_req;
+        if (n_members <= 0 || first_req < 0 || first_req + n_members > a.batch) return false;
+        const int64_t P = a.group_prefix_len[set];
+        lo = 0;
+        hi = P < 0 ? 0 : P;
+        ref_row = a.req_rows[first_req];
+    } else {
+        first_req = set;
+        n_members = 1;
+        const int64_t L = a.seq_lens[set];
+        ref_row = a.req_rows[set];
+        if (a.kind == 0) {
+            lo = 0;
+        } else {
+            const int grp = find_group_dec(a.group_ptr, a.G, set);
+            const int64_t P = a.group_prefix_len[grp];
+            lo = P < 0 ? 0 : (P > L ? L : P);
+        }
+        hi = L;
+    }
+    if (n_members * g <= rbg * WPG * 16) return false;    // no rows left for this workgroup
+    if (ref_row < 0 || ref_row >= a.num_rows) return false;
+    if (hi > a.row_stride) hi = a.row_stride;
+    const int64_t n_split = ceil_div64(hi - lo, a.chunk);
+    if (s >= n_split || s >= a.part.S) return false;
+    it.kvh = kvh;
+    it.s = s;
+    it.first_req = first_req;
+    it.n_members = n_members;
+    it.row_base = (rbg * WPG + w) * 16;
+    it.k0 = lo + (int64_t)s * a.chunk;
+    it.nk = (int)((it.k0 + a.chunk < hi ? it.k0 + a.chunk : hi) - it.k0);
+    it.ref_row = ref_row;
+    return true;
+}
+
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 ld_q(const __bf16 *p) {
@@ -149,60 +219,14 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
         }
     };
 
-    // ---- work item: id = ((item / 8) * n_rbg + rbg) * 8 + item % 8 -------------
-    // item = (split, set, KV head), split slowest: every request's first split
-    // is dispatched before any second one, so the waves that start last are
-    // the later (often partial) splits of long requests and the kernel's tail
-    // is short; and the first splits of a group's requests, which cover the
-    // shared prefix, run together.  rbg = which WPG row blocks of the item.
-    const int n_rbg = (a.row_blocks + WPG - 1) / WPG;
-    const int id = blockIdx.x;
-    const int rest = id >> 3;
-    const int rbg = rest % n_rbg;
-    const int64_t item = (int64_t)(rest / n_rbg) * 8 + (id & 7);
-    const int kvh = (int)(item % a.Hkv);
-    const int64_t t_ = item / a.Hkv;
-    const int64_t set64 = t_ % a.n_sets;
-    const int s = (int)(t_ / a.n_sets);
-    if (s >= a.max_splits) return;
-    if (set64 >= a.n_sets) return;
-    const int set = (int)set64;
-    const int g = a.Hq / a.Hkv;
-
-    // ---- which rows, which keys (uniform over the workgroup) ---------------------
-    int first_req, n_members;
-    int64_t lo, hi, ref_row;
-    if (a.kind == 1) {
-        first_req = a.group_ptr[set];
-        n_members = a.group_ptr[set + 1] - first_req;
-        if (n_members <= 0 || first_req < 0 || first_req + n_members > a.batch) return;
-        const int64_t P = a.group_prefix_len[set];
-        lo = 0;
-        hi = P < 0 ? 0 : P;
-        ref_row = a.req_rows[first_req];
-    } else {
-        first_req = set;
-        n_members = 1;
-        const int64_t L = a.seq_lens[set];
-        ref_row = a.req_rows[set];
-        if (a.kind == 0) {
-            lo = 0;
-        } else {
-            const int grp = find_group_dec(a.group_ptr, a.G, set);
-            const int64_t P = a.group_prefix_len[grp];
-            lo = P < 0 ? 0 : (P > L ? L : P);
-        }
-        hi = L;
-    }
-    if (n_members * g <= rbg * WPG * 16) return;    // no rows left for this workgroup
-    if (ref_row < 0 || ref_row >= a.num_rows) return;
-    if (hi > a.row_stride) hi = a.row_stride;
-    const int64_t n_split = ceil_div64(hi - lo, a.chunk);
-    if (s >= n_split || s >= a.part.S) return;
-    const int64_t k0 = lo + (int64_t)s * a.chunk;
-    const int nk = (int)((k0 + a.chunk < hi ? k0 + a.chunk : hi) - k0);
+    SplitItem it;
+    if (!split_item<WPG>(a, w, it)) return;
+    const int kvh = it.kvh, s = it.s, g = a.Hq / a.Hkv;
+    const int first_req = it.first_req, n_members = it.n_members;
+    const int64_t k0 = it.k0, ref_row = it.ref_row;
+    const int nk = it.nk;
     const int N = (nk + TILE - 1) / TILE;           // tiles, >= 1
-    const int row_base = (rbg * WPG + w) * 16;      // first group row of this wave
+    const int row_base = it.row_base;               // first group row of this wave
     const int rows = n_members * g - row_base;      // may be <= 0: the wave still loads
 
     const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
@@ -388,6 +412,289 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     if (kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
 }
 
+// =============================================================================
+// FP8 (e4m3fn) KV cache.  The pools hold one byte per element and one fp32
+// factor per KV head for K and for V; code c of head kv stands for
+// decode(c) * scale[kv].  Every e4m3fn value is exact in bf16, so the tiles
+// are widened to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, two codes per
+// instruction, factor 1) and the bf16 MFMAs of the kernel above do the rest;
+// the K factor joins the score scale and the V factor multiplies the split's
+// output.  A tile holds 32 keys, the same 4 KiB per pool as a bf16 tile of 16
+// keys at D = 128:
+//   - S^T = K Q^T as two 16-key MFMA blocks.  Block b's row m is tile key
+//     8 (m / 4) + 4 b + m % 4, so that the accumulators give lane (row, kq)
+//     the 8 consecutive keys 8 kq .. 8 kq + 7, which is the B operand layout of
+//     the 32-key PV MFMA: P needs no lane exchange.
+//   - The head dims are split into four contiguous quarters, one per lane
+//     group kq (the order of a dot product's terms is free as long as Q and K
+//     agree), so a lane reads whole 16-byte chunks of K rows.
+//   - O^T += V^T P^T with v_mfma_f32_16x16x32_bf16; its A operand (lane: one
+//     dim, 8 consecutive keys) comes from ds_read_b64_tr_b8, which hands lane
+//     (j, group G) byte k of the 8 rows addressed by its group, column j.
+// =============================================================================
+constexpr int TILE8 = 32;   // keys per fp8 tile
+
+// Position of 16-byte chunk c of fp8 row r (within a tile) is c ^ swz8<D>(r):
+// the 16 rows of a K operand read and the 8 rows of each V^T read fall on
+// distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+    if (D == 128) return ((r >> 1) ^ (r >> 3)) & 7;
+    return ((r >> 2) ^ (r >> 3)) & 3;                                // 4 chunks per row
+}
+
+// 8 e4m3fn codes (little-endian in two words) -> 8 exact bf16 values
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// LDS reads as inline asm (see lds_read_b128), results tied to one wait
+template <class T, int N>
+__device__ __forceinline__ void lgkm_wait_tied(T (&r)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("" : "+v"(r[i]));
+}
+template <int N>
+__device__ __forceinline__ void lds_read_raw128(u32x4 (&r)[N], const uint32_t (&addr)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("ds_read_b128 %0, %1" : "=v"(r[i]) : "v"(addr[i]));
+    lgkm_wait_tied(r);
+}
+template <int N>
+__device__ __forceinline__ void lds_read_tr8(i32x2 (&r)[N], const uint32_t (&addr)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i++) asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r[i]) : "v"(addr[i]));
+    lgkm_wait_tied(r);
+}
+
+template <int D, int DEPTH, int WPG>
+__global__ void __launch_bounds__(64 * WPG) split_fp8_kernel(SplitArgs a) {
+    constexpr int QT = D / 32;          // MFMA k-steps over head_dim
+    constexpr int DB = D / 16;          // 16-dim output blocks
+    constexpr int ROWB = D;             // bytes of one K/V row of one head
+    constexpr int CHK = D / 16;         // 16-byte chunks per row
+    constexpr int RPI = 64 / CHK;       // rows per direct-load instruction (1 KiB)
+    constexpr int NI = TILE8 / RPI;     // direct-load instructions per K or V tile
+    static_assert(NI % WPG == 0, "each wave issues the same number of loads");
+    static_assert(DEPTH >= 1 && DEPTH <= 4, "ring depth");
+    constexpr int NIW = NI / WPG;
+    constexpr int TB = TILE8 * ROWB;
+    constexpr int KCH = D / 64;         // K chunks per lane per 16-key block (a quarter row)
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TB];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TB];
+    extern __shared__ int32_t slot_lds[];  // [chunk]
+
+    const int lane = threadIdx.x & 63;
+    const int w = WPG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+    auto wg_barrier = [&]() {
+        if (WPG > 1) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+    };
+
+    SplitItem it;
+    if (!split_item<WPG>(a, w, it)) return;
+    const int kvh = it.kvh, s = it.s, g = a.Hq / a.Hkv;
+    const int first_req = it.first_req, n_members = it.n_members;
+    const int nk = it.nk;
+    const int N = (nk + TILE8 - 1) / TILE8;         // tiles, >= 1
+    const int row_base = it.row_base;
+    const int rows = n_members * g - row_base;      // may be <= 0: the wave still loads
+
+    const int32_t *row = a.r2t + it.ref_row * a.row_stride + it.k0;
+    for (int j = threadIdx.x; j < nk; j += 64 * WPG) slot_lds[j] = safe_slot(row[j], a.num_slots);
+
+    const __bf16 *q = (const __bf16 *)a.q;
+    const unsigned char *kp = (const unsigned char *)a.k_pool + kvh * D;
+    const unsigned char *vp = (const unsigned char *)a.v_pool + kvh * D;
+    const int64_t rowstride = (int64_t)a.Hkv * D;   // bytes per slot
+    const int n16 = lane & 15, kq = lane >> 4;
+
+    // ---- Q^T operand: lane (row n16, kq) holds dims kq*D/4 + 8t + i in step t --
+    bf16x8 qf[QT];
+    {
+        const int rho = n16 < rows ? n16 : 0;
+        const int rr = row_base + rho < n_members * g ? row_base + rho : 0;
+        const int req = first_req + rr / g;
+        const int h = kvh * g + rr % g;
+        const __bf16 *src = q + ((int64_t)req * a.Hq + h) * D + kq * (D / 4);
+#pragma unroll
+        for (int t = 0; t < QT; t++) qf[t] = ld_q(src + 8 * t);
+        if (n16 >= rows)
+#pragma unroll
+            for (int t = 0; t < QT; t++) qf[t] = bf16x8{};
+    }
+
+    // ---- per-lane constants of the loads and LDS reads --------------------------
+    const int lrow0 = lane / CHK;
+    int lrow[NIW], lchk[NIW];
+#pragma unroll
+    for (int u = 0; u < NIW; u++) {
+        const int ii = w + WPG * u;
+        lrow[u] = ii * RPI + lrow0;
+        lchk[u] = 16 * ((lane % CHK) ^ swz8<D>(lrow[u]));
+    }
+    // K block b: lane (n16, kq) reads the chunks KCH*kq .. of tile row kr[b]
+    int kbase[2], ksw[2];
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+        const int kr = 8 * (n16 >> 2) + 4 * b + (n16 & 3);
+        kbase[b] = kr * ROWB;
+        ksw[b] = swz8<D>(kr);
+    }
+    // V^T of dim block db: lane (n16, kq) addresses row 8kq + n16/2, half n16%2
+    // of chunk db; the result gives lane (dim 16db + n16, kq) keys 8kq .. 8kq+7
+    const int vr = 8 * kq + (n16 >> 1);
+    const int vsw = swz8<D>(vr);
+    const int vbase = vr * ROWB + 8 * (n16 & 1);
+
+    __syncthreads();   // slot table visible
+
+    auto issue = [&](int n, const unsigned char *pool, unsigned char *dst) {
+#pragma unroll
+        for (int u = 0; u < NIW; u++) {
+            const int kk = min(n * TILE8 + lrow[u], nk - 1);
+            const unsigned char *src = pool + (int64_t)slot_lds[kk] * rowstride + lchk[u];
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                             (SGL_LDS void *)(dst + (w + WPG * u) * 1024), 16, 0, 2 /* nt */);
+        }
+    };
+
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float qscale = a.scale * kLog2e * a.k_scale[kvh];
+
+    // S^T = K Q^T of one tile, two 16-key blocks
+    auto s_tile = [&](const unsigned char *kb, f32x4 (&sacc)[2]) {
+        const uint32_t b0 = lds_addr(kb);
+        uint32_t ad[2 * KCH];
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int c = 0; c < KCH; c++) ad[b * KCH + c] = b0 + kbase[b] + 16 * ((KCH * kq + c) ^ ksw[b]);
+        u32x4 raw[2 * KCH];
+        lds_read_raw128(raw, ad);
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            sacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < QT; t++) {
+                const u32x4 &r = raw[b * KCH + (t >> 1)];
+                const bf16x8 kf = (t & 1) ? fp8x8_to_bf16(r[2], r[3]) : fp8x8_to_bf16(r[0], r[1]);
+                sacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t], sacc[b], 0, 0, 0);
+            }
+        }
+    };
+    // online softmax of the row over tile n, then O^T += V^T P^T
+    auto pv_tile = [&](int n, const f32x4 (&sacc)[2], const unsigned char *vb) {
+        float sv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float x = n * TILE8 + 8 * kq + 4 * b + j < nk ? sacc[b][j] * qscale : -INFINITY;
+                sv[4 * b + j] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // lazy reference maximum, as in split_bf16_kernel
+        const bool move = mx > m_run + 8.f;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float m_new = move ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; db++) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        bf16x8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_run);
+            l_run += pj;
+            pf[j] = (__bf16)pj;
+        }
+        const uint32_t b = lds_addr(vb) + vbase;
+        uint32_t ad[DB];
+#pragma unroll
+        for (int db = 0; db < DB; db++) ad[db] = b + 16 * (db ^ vsw);
+        i32x2 vt[DB];
+        lds_read_tr8(vt, ad);
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(vt[db][0], vt[db][1]), pf,
+                                                                oacc[db], 0, 0, 0);
+    };
+
+    if constexpr (DEPTH == 1) {
+        issue(0, kp, k_lds);
+        issue(0, vp, v_lds);
+        for (int n = 0; n < N; n++) {
+            vm_wait<0>();
+            wg_barrier();
+            f32x4 sacc[2];
+            s_tile(k_lds, sacc);
+            if (n + 1 < N) {
+                wg_barrier();                            // every wave has read the K tile
+                issue(n + 1, kp, k_lds);
+            }
+            pv_tile(n, sacc, v_lds);
+            if (n + 1 < N) {
+                wg_barrier();                            // every wave has read the V tile
+                issue(n + 1, vp, v_lds);
+            }
+        }
+    } else {
+        for (int t = 0; t < DEPTH && t < N; t++) {
+            issue(t, kp, k_lds + (t % DEPTH) * TB);
+            issue(t, vp, v_lds + (t % DEPTH) * TB);
+        }
+        for (int n = 0; n < N; n++) {
+            const int ahead = min(DEPTH - 1, N - 1 - n);
+            if (ahead >= 3) vm_wait<3 * 2 * NIW>();
+            else if (ahead == 2) vm_wait<2 * 2 * NIW>();
+            else if (ahead == 1) vm_wait<2 * NIW>();
+            else vm_wait<0>();
+            wg_barrier();
+            unsigned char *kb = k_lds + (n % DEPTH) * TB;
+            unsigned char *vb = v_lds + (n % DEPTH) * TB;
+            f32x4 sacc[2];
+            s_tile(kb, sacc);
+            pv_tile(n, sacc, vb);
+            if (n + DEPTH < N) {
+                wg_barrier();                            // every wave is done with this buffer
+                issue(n + DEPTH, kp, kb);
+                issue(n + DEPTH, vp, vb);
+            }
+        }
+    }
+
+    // ---- write the split's state (o carries the V factor) --------------------
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (n16 >= rows) return;
+    const float vscale = a.v_scale[kvh];
+    const int req = first_req + (row_base + n16) / g;
+    const int h = kvh * g + (row_base + n16) % g;
+    const int64_t idx = ((int64_t)req * a.part.S + s) * a.Hq + h;
+    float *op = a.part.o + idx * D;
+#pragma unroll
+    for (int db = 0; db < DB; db++) *(f32x4 *)(op + db * 16 + kq * 4) = oacc[db] * vscale;
+    if (kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
+}
+
 }  // namespace
 
 int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
@@ -420,5 +727,34 @@ int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
         else SGL_SPLIT(64, PREFIX_DEPTH, 2);
     }
 #undef SGL_SPLIT
+    return hip_status(hipGetLastError());
+}
+
+int launch_split_fp8(const SplitArgs &a0, hipStream_t st) {
+    if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
+    if (a0.chunk % TILE8 != 0 || !a0.k_scale || !a0.v_scale) return SGL_ERR_INVALID;
+    SplitArgs a = a0;
+    const int rows = (a.kind == 1 ? a.max_members : 1) * (a.Hq / a.Hkv);
+    a.row_blocks = (rows + 15) / 16;
+    // same work split as launch_split_bf16
+    int wpg = 1;
+    if (a.kind == 1) wpg = a.row_blocks >= 3 ? 4 : a.row_blocks;
+    if (a.D == 64 && wpg > 2) wpg = 2;               // 2 load instructions per 64-dim tile
+    const int n_rbg = (a.row_blocks + wpg - 1) / wpg;
+    const int64_t items = (int64_t)a.n_sets * a.max_splits * a.Hkv;
+    const int64_t n_wg = ceil_div64(items, 8) * 8 * n_rbg;
+    if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+    const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
+    const dim3 grid((unsigned)n_wg), block(64 * wpg);
+#define SGL_SPLIT8(DD, DP, W) hipLaunchKernelGGL((split_fp8_kernel<DD, DP, W>), grid, block, dyn, st, a)
+    if (a.D == 128) {
+        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT8(128, PREFIX_DEPTH, 1); else SGL_SPLIT8(128, 1, 1); }
+        else if (wpg == 2) SGL_SPLIT8(128, PREFIX_DEPTH, 2);
+        else SGL_SPLIT8(128, PREFIX_DEPTH, 4);
+    } else {
+        if (wpg == 1) { if (a.kind == 1) SGL_SPLIT8(64, PREFIX_DEPTH, 1); else SGL_SPLIT8(64, 1, 1); }
+        else SGL_SPLIT8(64, PREFIX_DEPTH, 2);
+    }
+#undef SGL_SPLIT8
     return hip_status(hipGetLastError());
 }

@@ -129,6 +129,123 @@ int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int
 }
 
 // ---------------------------------------------------------------------------
+// FP8 KV store: the same rows as store_kv_kernel, quantised to e4m3fn codes on
+// the way ("SGLang 深度拆解" section 4.3 keeps the KV cache in FP8 to halve
+// it).  For head kv: y = x / scale[kv] (fp32, IEEE division), clamped to
+// [-448, 448], rounded to the nearest e4m3fn value with ties to even
+// (v_cvt_pk_fp8_f32).  One thread writes one 16-byte chunk of codes.
+// ---------------------------------------------------------------------------
+template <int ELT>
+__device__ __forceinline__ uint4 quant16(const char *src, float sc) {
+    float x[16];
+    if (ELT == 2) {
+        const uint4 a = ((const uint4 *)src)[0], b = ((const uint4 *)src)[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 f = ((const float4 *)src)[i];
+            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+        }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float v = x[4 * i + j] / sc;
+            y[j] = v > 448.f ? 448.f : (v < -448.f ? -448.f : v);   // NaN stays NaN
+        }
+        int t = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        t = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], t, true);
+        w[i] = (uint32_t)t;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int MODE, int ELT>
+__global__ void __launch_bounds__(256) store_kv_fp8_kernel(
+    const char *__restrict__ k_new, const char *__restrict__ v_new, uint4 *__restrict__ k_pool,
+    uint4 *__restrict__ v_pool, int64_t num_slots, int32_t row_chunks, int32_t head_chunks,
+    const float *__restrict__ k_scale, const float *__restrict__ v_scale, int64_t n_tokens,
+    const int32_t *__restrict__ slots, const int32_t *__restrict__ r2t, int64_t num_rows,
+    int64_t stride, const int32_t *__restrict__ req_rows, const int32_t *__restrict__ lens,
+    const int64_t *__restrict__ q_off) {
+    constexpr int IN_CHUNK = 16 * ELT;   // input bytes per 16 codes
+    int64_t t0 = 0, n = n_tokens * row_chunks, row = 0, P = 0;
+    if (MODE == 1) {
+        const int r = blockIdx.y;
+        t0 = q_off[r];
+        const int64_t t1 = q_off[r + 1];
+        row = req_rows[r];
+        P = lens[r];
+        if (row < 0 || row >= num_rows || t0 < 0 || t1 > n_tokens || t0 > t1 || P < 0) return;
+        n = (t1 - t0) * row_chunks;
+    }
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = idx / row_chunks, c = idx % row_chunks;
+        int32_t s;
+        if (MODE == 0) {
+            s = slots[i];
+        } else if (MODE == 1) {
+            const int64_t col = P + i;
+            if (col >= stride) continue;
+            s = r2t[row * stride + col];
+        } else {
+            const int64_t rw = req_rows[i];
+            const int64_t col = (int64_t)lens[i] - 1;
+            if (rw < 0 || rw >= num_rows || col < 0 || col >= stride) continue;
+            s = r2t[rw * stride + col];
+        }
+        if (s < 0 || s >= num_slots) continue;
+        const int h = (int)(c / head_chunks);
+        const int64_t src = ((t0 + i) * row_chunks + c) * IN_CHUNK;
+        k_pool[(int64_t)s * row_chunks + c] = quant16<ELT>(k_new + src, k_scale[h]);
+        v_pool[(int64_t)s * row_chunks + c] = quant16<ELT>(v_new + src, v_scale[h]);
+    }
+}
+
+int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
+                        const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
+                        int32_t Hkv, int32_t D, const float *k_scale, const float *v_scale,
+                        const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                        const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
+                        int32_t batch, int32_t max_extend_len, hipStream_t st) {
+    if (n_tokens == 0) return SGL_OK;
+    const int32_t row_chunks = Hkv * D / 16, head_chunks = D / 16;
+    const char *kn = (const char *)k_new;
+    const char *vn = (const char *)v_new;
+    uint4 *kp = (uint4 *)k_pool;
+    uint4 *vp = (uint4 *)v_pool;
+    dim3 grid;
+    if (mode == 1) {
+        const int64_t per_req = (int64_t)max_extend_len * row_chunks;
+        const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div64(per_req, 256), 1024));
+        grid = dim3(gx, batch);
+    } else {
+        grid = dim3((unsigned)std::min<int64_t>(ceil_div64(n_tokens * row_chunks, 256), 8192));
+    }
+#define SGL_STORE8(M, E)                                                                                    \
+    hipLaunchKernelGGL((store_kv_fp8_kernel<M, E>), grid, dim3(256), 0, st, kn, vn, kp, vp, num_slots,     \
+                       row_chunks, head_chunks, k_scale, v_scale, n_tokens, slots, r2t, num_rows,          \
+                       row_stride, req_rows, lens, q_off)
+    if (elt == 2) {
+        if (mode == 0) SGL_STORE8(0, 2); else if (mode == 1) SGL_STORE8(1, 2); else SGL_STORE8(2, 2);
+    } else {
+        if (mode == 0) SGL_STORE8(0, 4); else if (mode == 1) SGL_STORE8(1, 4); else SGL_STORE8(2, 4);
+    }
+#undef SGL_STORE8
+    return hip_status(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
 // Merge of partial softmax states.  The pages give the one-key online-softmax
 // update (rescale what was accumulated by e^(m_old - m_new), chenxutan.com
 // section 3.2 PagedPrefill); applied to whole blocks it is

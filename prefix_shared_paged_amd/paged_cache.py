@@ -16,7 +16,7 @@ kernels; this class only marshals host arrays.
 """
 import numpy as np
 
-from . import KVPool, RadixTree, build_req_to_token, store_kv
+from . import KVPool, RadixTree, build_req_to_token, store_kv, store_kv_fp8
 
 
 class Row:
@@ -32,15 +32,24 @@ class Row:
 
 
 class PagedKVCache:
+    """dtype: the K/V values handed to store(); the pools hold that dtype, or
+    e4m3fn codes (uint8) when kv_scale = (k_scale, v_scale) gives the per-KV-head
+    factors of an FP8 cache (float32 [Hkv] each)."""
+
     def __init__(self, num_slots, page_size, Hkv, D, dtype, max_rows, row_stride,
-                 init_order=None, device="cuda"):
+                 init_order=None, device="cuda", kv_scale=None):
         import torch
         self.torch = torch
         self.device = device
         self.Hkv, self.D, self.dtype = Hkv, D, dtype
         self.page_size = page_size
-        self.k_pool = torch.zeros((num_slots, Hkv, D), dtype=dtype, device=device)
-        self.v_pool = torch.zeros((num_slots, Hkv, D), dtype=dtype, device=device)
+        self.fp8 = kv_scale is not None
+        pool_dtype = torch.uint8 if self.fp8 else dtype
+        self.k_pool = torch.zeros((num_slots, Hkv, D), dtype=pool_dtype, device=device)
+        self.v_pool = torch.zeros((num_slots, Hkv, D), dtype=pool_dtype, device=device)
+        if self.fp8:
+            self.k_scale = self._dev(np.asarray(kv_scale[0], np.float32).reshape(Hkv), torch.float32)
+            self.v_scale = self._dev(np.asarray(kv_scale[1], np.float32).reshape(Hkv), torch.float32)
         self.r2t = torch.full((max_rows, row_stride), -1, dtype=torch.int32, device=device)
         self.pool = KVPool(num_slots, page_size, init_order)
         self.tree = RadixTree(page_size)
@@ -100,7 +109,11 @@ class PagedKVCache:
         """Store K/V rows (device tensors [n, Hkv, D]) at host slot ids."""
         if len(slots) == 0:
             return
-        store_kv(k, v, self._dev(slots, self.torch.int32), self.k_pool, self.v_pool)
+        if self.fp8:
+            store_kv_fp8(k, v, self._dev(slots, self.torch.int32), self.k_pool, self.v_pool, self.k_scale,
+                         self.v_scale)
+        else:
+            store_kv(k, v, self._dev(slots, self.torch.int32), self.k_pool, self.v_pool)
 
     def insert(self, st, n_tokens=None):
         """Insert the row's first n_tokens (whole pages) into the tree once its

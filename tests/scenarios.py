@@ -10,9 +10,11 @@ import numpy as np
 import torch
 
 import oracle
+import oracle.fp8 as F8
 import workloads as W
 from oracle.radix_model import PrefixCache, SlotPool
-from prefix_shared_paged_amd import cascade_decode_attn, decode_attn, extend_attn
+from prefix_shared_paged_amd import (cascade_decode_attn, cascade_decode_attn_fp8kv, decode_attn,
+                                     decode_attn_fp8kv, extend_attn)
 from prefix_shared_paged_amd.paged_cache import PagedKVCache
 
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -58,14 +60,18 @@ class Mirror:
 class GroupCase:
     """Prefix groups set up in a fresh cache; requests admitted on top."""
 
-    def __init__(self, wl, order=None, max_rows=None, row_stride=None, creator_extend=False):
+    def __init__(self, wl, order=None, max_rows=None, row_stride=None, creator_extend=False, fp8=False):
+        """fp8: the pools hold e4m3fn codes with the workload's per-head factors."""
         self.wl = wl
         s = wl.spec
         self.order = W.pool_order(s) if order is None else order
         n_rows = max_rows or (wl.B + wl.G)
         stride = row_stride or int(max(wl.ctx_len.max(), wl.prefix_len.max())) + 1
+        assert not (fp8 and creator_extend)
+        self.fp8 = fp8
+        self.kv_scale = W.fp8_scales(s) if fp8 else None
         self.cache = PagedKVCache(s.num_slots, s.page_size, s.Hkv, s.D, TORCH_DT[s.dtype], n_rows, stride,
-                                  self.order)
+                                  self.order, kv_scale=self.kv_scale)
         self.mirror = Mirror(s, self.order)
         self.prefix_kv = {}
         self.creator_out = []
@@ -225,11 +231,14 @@ def run_decode(case, L, cascade, both=False):
     qd = dev(q, s.dtype)
     out = dict(q=q, L=L, P=P)
 
+    c = case.cache
+    fp8_args = (c.k_pool, c.v_pool, c.k_scale, c.v_scale) if case.fp8 else (c.k_pool, c.v_pool)
+
     def flat(store):
         lse_t = torch.empty((wl.B, s.Hq), dtype=torch.float32, device="cuda")
         kw = dict(k_new=dev(kn, s.dtype), v_new=dev(vn, s.dtype)) if store else {}
-        o = decode_attn(qd, case.cache.k_pool, case.cache.v_pool, case.cache.r2t, req_rows, dev_i(L),
-                        int(L.max()), lse=lse_t, **kw)
+        fn = decode_attn_fp8kv if case.fp8 else decode_attn
+        o = fn(qd, *fp8_args, c.r2t, req_rows, dev_i(L), int(L.max()), lse=lse_t, **kw)
         return o, lse_t
 
     def casc(store):
@@ -237,9 +246,9 @@ def run_decode(case, L, cascade, both=False):
         kw = dict(k_new=dev(kn, s.dtype), v_new=dev(vn, s.dtype)) if store else {}
         gptr = np.zeros(wl.G + 1, np.int32)
         gptr[1:] = np.cumsum(np.bincount(wl.grp, minlength=wl.G))
-        o = cascade_decode_attn(qd, case.cache.k_pool, case.cache.v_pool, case.cache.r2t, req_rows,
-                                dev_i(L), dev_i(gptr), dev_i(wl.prefix_len), int(L.max()),
-                                int(np.diff(gptr).max()), int(wl.prefix_len.max()), lse=lse_t, **kw)
+        fn = cascade_decode_attn_fp8kv if case.fp8 else cascade_decode_attn
+        o = fn(qd, *fp8_args, c.r2t, req_rows, dev_i(L), dev_i(gptr), dev_i(wl.prefix_len), int(L.max()),
+               int(np.diff(gptr).max()), int(wl.prefix_len.max()), lse=lse_t, **kw)
         return o, lse_t
 
     if both:
@@ -265,10 +274,13 @@ def oracle_decode(case, res, reqs=None, heads=None, batch=16):
         Ks, Vs = [], []
         for r in part:
             K, V = case.logical_kv(r, int(res["L"][r] - res["P"][r]))
+            if case.fp8:   # the oracle's own codes of the same values, decoded exactly
+                K = F8.decode(F8.quantize(K, case.kv_scale[0])).astype(np.float32)
+                V = F8.decode(F8.quantize(V, case.kv_scale[1])).astype(np.float32)
             Ks.append(K)
             Vs.append(V)
         O, M, Ls, LSE = oracle.attention(Ks, Vs, np.arange(len(part)), [int(res["L"][r]) - 1 for r in part],
-                                         res["q"][part], s.Hq, s.Hkv, heads=heads)
+                                         res["q"][part], s.Hq, s.Hkv, heads=heads, kv_scale=case.kv_scale)
         Os.append(O)
         LSEs.append(LSE)
     return np.array(reqs), np.concatenate(Os), np.concatenate(LSEs)

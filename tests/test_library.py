@@ -96,6 +96,22 @@ def test_device_calls_reject_bad_arguments_before_gpu_work():
     # empty batches are a no-op
     assert lib.sgl_decode_attn(sp.SGL_BF16, p, None, None, p, p, 16, p, 1, 8, p, p, 0, 8, 32, 8, 128,
                                0.1, p, None, None, 0, None) == sp.SGL_OK
+    # FP8 KV: fp32 queries are not supported
+    assert lib.sgl_decode_attn_fp8kv(sp.SGL_F32, p, None, None, p, p, p, p, 16, p, 1, 8, p, p, 1, 8, 32,
+                                     8, 128, 0.1, p, None, p, 1 << 20, None) == sp.SGL_ERR_UNSUPPORTED
+    # FP8 KV: missing per-head factors
+    assert lib.sgl_decode_attn_fp8kv(sp.SGL_BF16, p, None, None, p, p, None, p, 16, p, 1, 8, p, p, 1, 8,
+                                     32, 8, 128, 0.1, p, None, p, 1 << 20, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_cascade_decode_attn_fp8kv(sp.SGL_BF16, p, None, None, p, p, p, None, 16, p, 4, 100, p,
+                                             p, p, p, 4, 1, 100, 4, 50, 32, 8, 128, 0.1, p, None, p,
+                                             1 << 24, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_store_kv_fp8(sp.SGL_BF16, p, p, 4, p, p, p, 16, 8, 128, None, p,
+                                None) == sp.SGL_ERR_INVALID
+    # FP8 KV: unsupported head_dim
+    assert lib.sgl_store_kv_fp8(sp.SGL_BF16, p, p, 4, p, p, p, 16, 8, 96, p, p,
+                                None) == sp.SGL_ERR_UNSUPPORTED
+    # FP8 KV: empty store is a no-op
+    assert lib.sgl_store_kv_fp8(sp.SGL_F32, p, p, 0, p, p, p, 16, 8, 128, p, p, None) == sp.SGL_OK
 
 
 def test_workspace_sizes_grow_with_the_problem():
