@@ -13,6 +13,7 @@ constexpr int kDecodeChunk = 1024;   // keys per split (flat decode and cascade 
 constexpr int kPrefixChunkMax = 512;
 constexpr int kPrefixChunkMin = 64;
 constexpr int64_t kPrefixWorkgroups = 1024;  // ~4 per compute unit
+constexpr int kFlatXcdBlock = 16;    // consecutive requests per XCD block (flat fp8 decode)
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -301,9 +302,23 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     a.num_rows = num_rows; a.row_stride = row_stride; a.req_rows = req_rows; a.seq_lens = seq_lens;
     a.group_ptr = group_ptr; a.group_prefix_len = group_prefix_len; a.batch = batch; a.G = G;
     a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
+    // Kernel choice (measured on the 256-request decode workload):
+    //  - cascade suffix: whole-row loads, requests dealt to the XCDs one by
+    //    one (the suffixes share nothing, so balance matters most);
+    //  - flat fp8: whole-row loads with blocks of kFlatXcdBlock consecutive
+    //    requests per XCD, so siblings share prefix rows through one L2;
+    //  - flat bf16: the per-head kernel, whose head-per-XCD order already gets
+    //    that reuse with every XCD holding an equal share of each request;
+    //  - other shapes, and the cascade prefix stage: the per-head kernels.
     auto run_split = [&](const SplitArgs &x) {
-        if (fp8) return launch_split_fp8(x, st);
-        return dtype == SGL_F32 ? launch_split_f32(x, st) : launch_split_bf16(x, st);
+        if (dtype == SGL_F32) return launch_split_f32(x, st);
+        if (x.kind == 2 || (x.kind == 0 && fp8)) {
+            SplitArgs y = x;
+            y.xcd_block = x.kind == 2 ? 1 : kFlatXcdBlock;
+            const int rc_rows = launch_split_rows(y, fp8, st);
+            if (rc_rows != SGL_ERR_UNSUPPORTED) return rc_rows;
+        }
+        return fp8 ? launch_split_fp8(x, st) : launch_split_bf16(x, st);
     };
 
     MergeArgs m;

@@ -118,12 +118,16 @@ struct SplitArgs {
     float scale;
     const float *k_scale;  // FP8 KV only: per KV head factors of the K and V codes
     const float *v_scale;
+    int32_t xcd_block;     // launch_split_rows: consecutive requests per XCD block
     PartialBuf part;
 };
 
 int launch_split_f32(const SplitArgs &a, hipStream_t st);
 int launch_split_bf16(const SplitArgs &a, hipStream_t st);
 int launch_split_fp8(const SplitArgs &a, hipStream_t st);
+// kinds 0 and 2 with one workgroup per (request, split) over all KV heads;
+// SGL_ERR_UNSUPPORTED for shapes left to the per-head kernels
+int launch_split_rows(const SplitArgs &a, bool fp8, hipStream_t st);
 
 // Merge partial states of (optionally) a prefix buffer and a suffix buffer.
 //   kind 0: parts = flat splits of r;  kind 3: parts = prefix splits of group(r) for r
