@@ -9,7 +9,8 @@
 
 namespace {
 
-constexpr int kDecodeChunk = 1024;   // keys per split (flat decode and cascade suffix)
+constexpr int kDecodeChunk = 1024;   // keys per split of the per-head kernels (flat, suffix)
+constexpr int kRowsChunk = 512;      // keys per split of the whole-row kernel (flat, suffix)
 constexpr int kPrefixChunkMax = 512;
 constexpr int kPrefixChunkMin = 64;
 constexpr int64_t kPrefixWorkgroups = 1024;  // ~4 per compute unit
@@ -221,10 +222,12 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
                               max_extend_len, Hq, Hkv, D, scale, (__bf16 *)o, lse, st);
 }
 
+// Splits of the flat call and the cascade suffix are sized for the smaller
+// split of the two kernels that may run them.
 size_t sgl_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq, int32_t Hkv, int32_t D) {
     (void)Hkv;
     if (batch <= 0 || max_seq_len <= 0) return 0;
-    const int64_t S = ceil_div64(max_seq_len, kDecodeChunk);
+    const int64_t S = ceil_div64(max_seq_len, kRowsChunk);
     return part_bytes(batch, S, Hq, D);
 }
 
@@ -303,20 +306,22 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     a.group_ptr = group_ptr; a.group_prefix_len = group_prefix_len; a.batch = batch; a.G = G;
     a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
     // Kernel choice (measured on the 256-request decode workload):
-    //  - cascade suffix: whole-row loads, requests dealt to the XCDs one by
-    //    one (the suffixes share nothing, so balance matters most);
+    //  - cascade suffix: whole-row loads, work dealt to the XCDs set by set
+    //    (the suffixes share nothing, so balance matters most);
     //  - flat fp8: whole-row loads with blocks of kFlatXcdBlock consecutive
     //    requests per XCD, so siblings share prefix rows through one L2;
     //  - flat bf16: the per-head kernel, whose head-per-XCD order already gets
     //    that reuse with every XCD holding an equal share of each request;
     //  - other shapes, and the cascade prefix stage: the per-head kernels.
-    auto run_split = [&](const SplitArgs &x) {
+    const bool rows_ok = dtype != SGL_F32 && (Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16) && g <= 16;
+    const bool rows_flat = rows_ok && fp8;
+    const bool rows_suffix = rows_ok;
+    auto run_split = [&](const SplitArgs &x, bool rows) {
         if (dtype == SGL_F32) return launch_split_f32(x, st);
-        if (x.kind == 2 || (x.kind == 0 && fp8)) {
+        if (rows) {
             SplitArgs y = x;
             y.xcd_block = x.kind == 2 ? 1 : kFlatXcdBlock;
-            const int rc_rows = launch_split_rows(y, fp8, st);
-            if (rc_rows != SGL_ERR_UNSUPPORTED) return rc_rows;
+            return launch_split_rows(y, fp8, st);
         }
         return fp8 ? launch_split_fp8(x, st) : launch_split_bf16(x, st);
     };
@@ -326,28 +331,29 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
     m.batch = batch; m.G = G; m.Hq = Hq; m.D = D; m.out_bf16 = dtype == SGL_BF16; m.o = o; m.lse = lse;
     const int pchunk = cascade ? prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D) : kPrefixChunkMax;
-    m.chunk_flat = kDecodeChunk; m.chunk_prefix = pchunk;
+    const int fchunk = (cascade ? rows_suffix : rows_flat) ? kRowsChunk : kDecodeChunk;
+    m.chunk_flat = fchunk; m.chunk_prefix = pchunk;
 
     if (!cascade) {
-        const int64_t S = ceil_div64(max_seq_len, kDecodeChunk);
-        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)S; a.chunk = kDecodeChunk;
+        const int64_t S = ceil_div64(max_seq_len, fchunk);
+        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)S; a.chunk = fchunk;
         a.part = carve(wp, batch, S, Hq, D);
-        if ((rc = run_split(a)) != SGL_OK) return rc;
+        if ((rc = run_split(a, rows_flat)) != SGL_OK) return rc;
         m.kind = 0; m.flat_or_suffix = a.part;
         return launch_merge(m, st);
     }
     const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pchunk) : 1;
-    const int64_t Ss = ceil_div64(max_seq_len, kDecodeChunk);
+    const int64_t Ss = ceil_div64(max_seq_len, fchunk);
     SplitArgs pa = a;
     pa.kind = 1; pa.chunk = pchunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size;
     pa.part = carve(wp, batch, Sp, Hq, D);
     // the f32 path walks (request, head, split) for every kind; the bf16 path one wave per group
     pa.n_sets = dtype == SGL_F32 ? batch : G;
     SplitArgs sa = a;
-    sa.kind = 2; sa.chunk = kDecodeChunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
+    sa.kind = 2; sa.chunk = fchunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
     sa.part = carve(wp, batch, Ss, Hq, D);
-    if (max_prefix_len > 0 && (rc = run_split(pa)) != SGL_OK) return rc;
-    if ((rc = run_split(sa)) != SGL_OK) return rc;
+    if (max_prefix_len > 0 && (rc = run_split(pa, false)) != SGL_OK) return rc;
+    if ((rc = run_split(sa, rows_suffix)) != SGL_OK) return rc;
     m.kind = 3; m.prefix = pa.part; m.flat_or_suffix = sa.part;
     if (max_prefix_len == 0) m.kind = 0, m.flat_or_suffix = sa.part;
     return launch_merge(m, st);
@@ -383,7 +389,7 @@ size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
     const int64_t Sp = max_prefix_len > 0
                            ? ceil_div64(max_prefix_len, prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D))
                            : 1;
-    const int64_t Ss = ceil_div64(max_seq_len, kDecodeChunk);
+    const int64_t Ss = ceil_div64(max_seq_len, kRowsChunk);
     return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, Ss, Hq, D);
 }
 

@@ -26,23 +26,28 @@ using namespace sgl_decode;
 // apart, so a chunk's LDS bank group (of 16) is its position's low four bits:
 // the four-bit swizzle spreads the 16 rows of a K operand read and the rows
 // of a transposed V read over distinct bank groups.
+constexpr int kRowsHeads = 4;   // KV heads per workgroup (at most)
+
 template <bool FP8, int CR>
 __device__ __forceinline__ int rsw(int r) {
     const int f = FP8 ? ((r & 15) ^ ((r >> 4) << 2)) : (((r & 7) << 1) | ((r >> 3) & 1));
     return f & (CR - 1);
 }
 
-template <int D, bool FP8, int HKV>
-__global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
+// HPW waves per workgroup, one per KV head of the head group hg: the
+// workgroup loads the group's HPW * D * elt bytes of every row (the whole row
+// when HPW = Hkv).
+template <int D, bool FP8, int HPW>
+__global__ void __launch_bounds__(64 * HPW) split_rows_kernel(SplitArgs a) {
     constexpr int ELT = FP8 ? 1 : 2;
     constexpr int T = FP8 ? 32 : 16;        // keys per tile
-    constexpr int R = HKV * D * ELT;        // bytes of one pool row (all heads of a slot)
-    constexpr int CR = R / 16;              // 16-byte chunks per row
+    constexpr int R = HPW * D * ELT;        // bytes of one tile row (the group's heads of a slot)
+    constexpr int CR = R / 16;              // 16-byte chunks per tile row
     constexpr int HC = D * ELT / 16;        // chunks per head
     constexpr int TB = T * R;               // bytes of one K (or V) tile
     constexpr int NI = TB / 1024;           // 1 KiB direct-load instructions per tile
-    static_assert(TB % 1024 == 0 && NI % HKV == 0, "whole load instructions per wave");
-    constexpr int NIW = NI / HKV;
+    static_assert(TB % 1024 == 0 && NI % HPW == 0, "whole load instructions per wave");
+    constexpr int NIW = NI / HPW;
     constexpr int QT = D / 32;              // MFMA k-steps over head_dim
     constexpr int DB = D / 16;              // 16-dim output blocks
     constexpr int KCH = D / 64;             // fp8: K chunks per lane per 16-key block
@@ -51,28 +56,36 @@ __global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
     extern __shared__ int32_t slot_lds[];  // [chunk]
 
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wave
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // head of this wave in its group
     auto barrier = [&]() {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
 
-    // ---- work item (uniform over the workgroup): split s of request `set` --------
-    // Workgroups go to the 8 XCDs round-robin by id, so id % 8 picks the XCD.
-    // The requests form blocks of rb consecutive ones, dealt to the XCDs in
-    // turn: XCD x takes blocks x, x + 8, ...  With rb > 1 sibling requests
-    // (adjacent in the batch) read the prefix rows they share through one
-    // XCD's L2; rb = 1 spreads the work most evenly.  Within an XCD the order
-    // is split-major: every request's first split starts before any second
-    // one (short tail).
+    // ---- work item (uniform over the workgroup): split s of (request, head group)
+    // The work sets are v = hg * n_sets + request; they form blocks of rb
+    // consecutive ones (one head group of rb consecutive requests).
+    // Workgroups go to the 8 XCDs round-robin by id (id % 8 is the XCD), and
+    // each XCD runs its workgroups in id order.  Split round s gives block b
+    // to XCD (b + s) % 8: the rotation spreads every set's splits over the
+    // XCDs (an XCD's total work does not hang on the lengths of a few
+    // requests), and with rb > 1 sibling requests (adjacent in the batch)
+    // still read the prefix rows of one split through one XCD's L2.  Rounds
+    // are in order, so every set's first split starts before any second one.
+    const int ng = a.Hkv / HPW;
+    const int n_v = a.n_sets * ng;
     const int rb = a.xcd_block;
-    const int spx = ((a.n_sets + rb - 1) / rb + 7) / 8 * rb;   // requests per XCD
+    const int bpx = ((n_v + rb - 1) / rb + 7) / 8;        // blocks per XCD and round
+    const int xcd = (int)(blockIdx.x & 7);
     const int local = (int)(blockIdx.x >> 3);
-    const int sl = local % spx;
-    const int set = ((sl / rb) * 8 + (int)(blockIdx.x & 7)) * rb + sl % rb;
-    const int s = local / spx;
-    if (s >= a.max_splits || set >= a.n_sets) return;
+    const int s = local / (bpx * rb);
+    const int sl = local % (bpx * rb);
+    const int b = (sl / rb) * 8 + ((xcd - s) & 7);
+    const int v = b * rb + sl % rb;
+    if (s >= a.max_splits || v >= n_v) return;
+    const int set = v % a.n_sets, hg = v / a.n_sets;
+    const int kvh = hg * HPW + w;                   // KV head of this wave
     const int64_t L = a.seq_lens[set];
     const int64_t ref_row = a.req_rows[set];
     int64_t lo = 0, hi = L;
@@ -88,18 +101,18 @@ __global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
     const int64_t k0 = lo + (int64_t)s * a.chunk;
     const int nk = (int)((k0 + a.chunk < hi ? k0 + a.chunk : hi) - k0);
     const int N = (nk + T - 1) / T;                 // tiles, >= 1
-    const int g = a.Hq / HKV;                       // query rows of this wave (<= 16)
+    const int g = a.Hq / a.Hkv;                     // query rows of this wave (<= 16)
 
     const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
-    for (int j = threadIdx.x; j < nk; j += 64 * HKV) slot_lds[j] = safe_slot(row[j], a.num_slots);
+    for (int j = threadIdx.x; j < nk; j += 64 * HPW) slot_lds[j] = safe_slot(row[j], a.num_slots);
 
     const int n16 = lane & 15, kq = lane >> 4;
 
-    // ---- Q^T operand of query row n16 (head w*g + n16) ---------------------------
+    // ---- Q^T operand of query row n16 (head kvh*g + n16) -------------------------
     // bf16: step t holds dims 32t + 8kq + i;  fp8: dims kq*D/4 + 8t + i
     bf16x8 qf[QT];
     {
-        const int h = w * g + (n16 < g ? n16 : 0);
+        const int h = kvh * g + (n16 < g ? n16 : 0);
         const __bf16 *src = (const __bf16 *)a.q + ((int64_t)set * a.Hq + h) * D;
 #pragma unroll
         for (int t = 0; t < QT; t++) qf[t] = ld_q(src + (FP8 ? kq * (D / 4) + 8 * t : 32 * t + 8 * kq));
@@ -108,18 +121,19 @@ __global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
             for (int t = 0; t < QT; t++) qf[t] = bf16x8{};
     }
 
-    // ---- direct loads: instruction ii = u*HKV + w of a tile covers its bytes
+    // ---- direct loads: instruction ii = u*HPW + w of a tile covers its bytes
     // [1024 ii, 1024 ii + 1024); lane -> tile row, LDS chunk position, and the
-    // chunk of the pool row that belongs there
+    // chunk of the group's part of the pool row that belongs there
     int lrow[NIW], lsrc[NIW];
 #pragma unroll
     for (int u = 0; u < NIW; u++) {
-        const int off = (u * HKV + w) * 1024 + 16 * lane;
+        const int off = (u * HPW + w) * 1024 + 16 * lane;
         lrow[u] = off / R;
         lsrc[u] = 16 * (((off % R) / 16) ^ rsw<FP8, CR>(lrow[u]));
     }
-    const char *kp = (const char *)a.k_pool;
-    const char *vp = (const char *)a.v_pool;
+    const int64_t pool_row = (int64_t)a.Hkv * D * ELT;   // bytes per slot
+    const char *kp = (const char *)a.k_pool + hg * R;
+    const char *vp = (const char *)a.v_pool + hg * R;
 
     __syncthreads();   // slot table visible
 
@@ -127,9 +141,9 @@ __global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
 #pragma unroll
         for (int u = 0; u < NIW; u++) {
             const int kk = min(n * T + lrow[u], nk - 1);   // past the split end: repeat the last key
-            const char *src = pool + (int64_t)slot_lds[kk] * R + lsrc[u];
+            const char *src = pool + (int64_t)slot_lds[kk] * pool_row + lsrc[u];
             __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                             (SGL_LDS void *)(dst + (u * HKV + w) * 1024), 16, 0, 2 /* nt */);
+                                             (SGL_LDS void *)(dst + (u * HPW + w) * 1024), 16, 0, 2 /* nt */);
         }
     };
     // LDS byte address of chunk c of this wave's head in tile row r
@@ -139,7 +153,7 @@ __global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    const float qscale = FP8 ? a.scale * kLog2e * a.k_scale[w] : a.scale * kLog2e;
+    const float qscale = FP8 ? a.scale * kLog2e * a.k_scale[kvh] : a.scale * kLog2e;
 
     constexpr int NB = FP8 ? 2 : 1;   // 16-key S blocks per tile
     // S^T = K Q^T: block b, lane (row n16, kq) gets 4 keys (see key_of)
@@ -268,8 +282,8 @@ __global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (n16 >= g) return;
-    const float vscale = FP8 ? a.v_scale[w] : 1.f;
-    const int h = w * g + n16;
+    const float vscale = FP8 ? a.v_scale[kvh] : 1.f;
+    const int h = kvh * g + n16;
     const int64_t idx = ((int64_t)set * a.part.S + s) * a.Hq + h;
     float *op = a.part.o + idx * D;
 #pragma unroll
@@ -279,24 +293,27 @@ __global__ void __launch_bounds__(64 * HKV) split_rows_kernel(SplitArgs a) {
 
 }  // namespace
 
-// Flat (kind 0) or suffix (kind 2) splits with whole-row loads.  Returns
-// SGL_ERR_UNSUPPORTED for shapes it does not cover (Hkv not 2, 4 or 8), which
-// the per-head kernels handle.
+// Flat (kind 0) or suffix (kind 2) splits with whole-row loads of head
+// groups of kRowsHeads KV heads (all of them when Hkv is smaller).  Returns
+// SGL_ERR_UNSUPPORTED for shapes it does not cover (Hkv not 2, 4, 8 or 16),
+// which the per-head kernels handle.
 int launch_split_rows(const SplitArgs &a, bool fp8, hipStream_t st) {
     if (a.kind != 0 && a.kind != 2) return SGL_ERR_UNSUPPORTED;
-    if (a.Hkv != 2 && a.Hkv != 4 && a.Hkv != 8) return SGL_ERR_UNSUPPORTED;
+    if (a.Hkv != 2 && a.Hkv != 4 && a.Hkv != 8 && a.Hkv != 16) return SGL_ERR_UNSUPPORTED;
     if (a.Hq / a.Hkv > 16) return SGL_ERR_UNSUPPORTED;
     if (a.n_sets == 0 || a.max_splits == 0) return SGL_OK;
     if (a.chunk % (fp8 ? 32 : 16) != 0 || a.xcd_block < 1) return SGL_ERR_INVALID;
     if (fp8 && (!a.k_scale || !a.v_scale)) return SGL_ERR_INVALID;
+    const int hpw = a.Hkv < kRowsHeads ? a.Hkv : kRowsHeads;
     const int rb = a.xcd_block;
-    const int64_t n_wg = 8 * (int64_t)(((a.n_sets + rb - 1) / rb + 7) / 8) * rb * a.max_splits;
+    const int64_t n_v = (int64_t)a.n_sets * (a.Hkv / hpw);
+    const int64_t n_wg = 8 * (((n_v + rb - 1) / rb + 7) / 8) * rb * a.max_splits;
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
-    const dim3 grid((unsigned)n_wg), block(64 * a.Hkv);
+    const dim3 grid((unsigned)n_wg), block(64 * hpw);
 #define SGL_ROWS(DD, F8, H) hipLaunchKernelGGL((split_rows_kernel<DD, F8, H>), grid, block, dyn, st, a)
 #define SGL_ROWS_H(DD, F8) \
-    do { if (a.Hkv == 8) SGL_ROWS(DD, F8, 8); else if (a.Hkv == 4) SGL_ROWS(DD, F8, 4); else SGL_ROWS(DD, F8, 2); } while (0)
+    do { if (hpw == 8) SGL_ROWS(DD, F8, 8); else if (hpw == 4) SGL_ROWS(DD, F8, 4); else SGL_ROWS(DD, F8, 2); } while (0)
     if (a.D == 128) {
         if (fp8) SGL_ROWS_H(128, true); else SGL_ROWS_H(128, false);
     } else {
