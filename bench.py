@@ -2,7 +2,7 @@
 """Benchmark of the paged prefix-shared attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config extend|decode|fork|multiturn]
-                    [--no-cpu-baseline]
+                    [--kv bf16|fp8] [--no-cpu-baseline]
 
 Default workload ("extend"): 64 requests share a cached 2048-token prefix and
 each adds 256 new causal tokens (32 query / 8 KV heads, head_dim 128, bf16,
@@ -21,7 +21,10 @@ staging buffers, asynchronous copies).  Inputs (Q/K/V) are resident in HBM
 before the timed region.  Prints ONE JSON line.
 
 Other --config values time the decode-batch, fork-sweep and multi-turn
-workloads for reporting; their lines have the same shape.
+workloads for reporting; their lines have the same shape.  --kv fp8 runs the
+decode and fork workloads over an FP8 (e4m3fn) KV cache with per-head
+factors (the same bf16 queries, bf16 MFMA arithmetic, one byte per cached
+element).
 """
 import argparse
 import hashlib
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="extend", choices=["extend", "decode", "fork", "multiturn"])
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="KV cache element type of the decode and fork workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -56,7 +61,10 @@ def parse():
 # the record stale)
 KERNEL_SOURCES = {
     "extend_bf16_kernel": ["kernels_extend.hip", "common.h"],
-    "cascade_decode_call": ["kernels_decode.hip", "kernels_misc.hip", "api.hip", "common.h"],
+    "cascade_decode_call": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
+                            "kernels_misc.hip", "api.hip", "common.h"],
+    "cascade_decode_call_fp8": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
+                                "kernels_misc.hip", "api.hip", "common.h"],
 }
 
 
@@ -335,17 +343,45 @@ def fill_random(t, scale=0.5, seed=0, chunk=1 << 26):
         flat[i:i + n] = (torch.randn(n, generator=g, device=t.device) * scale).to(t.dtype)
 
 
-def cpu_baseline_rows(K_list, V_list, rows, Hq, Hkv, target_s, what):
+def fill_fp8(cache, seed, scale=0.5, chunk=1 << 18):
+    """Fill an FP8 cache's code pools by quantising N(0,1)*scale bf16 rows
+    through the library's store (device RNG, in chunks of slots)."""
+    import torch
+    import prefix_shared_paged_amd as sp
+    g = torch.Generator(device=cache.k_pool.device)
+    g.manual_seed(seed)
+    S, Hkv, D = cache.k_pool.shape
+    for i in range(0, S, chunk):
+        n = min(chunk, S - i)
+        k = (torch.randn((n, Hkv, D), generator=g, device=cache.k_pool.device) * scale).to(torch.bfloat16)
+        v = (torch.randn((n, Hkv, D), generator=g, device=cache.k_pool.device) * scale).to(torch.bfloat16)
+        sl = torch.arange(i, i + n, dtype=torch.int32, device=cache.k_pool.device)
+        sp.store_kv_fp8(k, v, sl, cache.k_pool, cache.v_pool, cache.k_scale, cache.v_scale)
+    torch.cuda.synchronize()
+
+
+def kv_args(cache):
+    """Pool arguments of the decode calls (pools, plus the factors of an FP8 cache)."""
+    return (cache.k_pool, cache.v_pool, cache.k_scale, cache.v_scale) if cache.fp8 else (cache.k_pool, cache.v_pool)
+
+
+def cpu_baseline_rows(K_list, V_list, rows, Hq, Hkv, target_s, what, kv_scale=None):
     """Time the oracle on query rows (req, pos, q) of given logical sequences; the
-    sample grows from a calibration run to take about target_s seconds."""
+    sample grows from a calibration run to take about target_s seconds.  With
+    kv_scale (FP8 cache factors) the oracle quantises K/V first (untimed) and
+    attends over the dequantised values."""
     import oracle
+    import oracle.fp8 as F8
     rows = list(rows)
+    if kv_scale is not None:
+        K_list = [F8.decode(F8.quantize(K, kv_scale[0])).astype(np.float32) for K in K_list]
+        V_list = [F8.decode(F8.quantize(V, kv_scale[1])).astype(np.float32) for V in V_list]
 
     def run(k):
         sub = rows[:k]
         t0 = time.perf_counter()
         oracle.attention(K_list, V_list, [r for r, _, _ in sub], [p for _, p, _ in sub],
-                         np.stack([q for _, _, q in sub]), Hq, Hkv)
+                         np.stack([q for _, _, q in sub]), Hq, Hkv, kv_scale=kv_scale)
         return time.perf_counter() - t0
 
     k = max(1, min(len(rows), 8))
@@ -409,9 +445,14 @@ def bench_decode(args):
     dev = "cuda"
     L = wl.ctx_len.astype(np.int64)
     P = wl.prefix_len[wl.grp].astype(np.int64)
-    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, int(L.max()) + 1, W.pool_order(s), dev)
-    fill_random(cache.k_pool, seed=1)
-    fill_random(cache.v_pool, seed=2)
+    fp8 = args.kv == "fp8"
+    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, int(L.max()) + 1, W.pool_order(s), dev,
+                         kv_scale=W.fp8_scales(s) if fp8 else None)
+    if fp8:
+        fill_fp8(cache, seed=1)
+    else:
+        fill_random(cache.k_pool, seed=1)
+        fill_random(cache.v_pool, seed=2)
     setup_groups(cache, wl)
     toks = [np.concatenate([wl.prefix_tokens(wl.grp[r]), wl.suffix_tokens(r)]) for r in range(B)]
     rows = cache.admit(toks)
@@ -450,12 +491,13 @@ def bench_decode(args):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
         if cascade:   # a4 + a7
-            sp.cascade_decode_attn(q, cache.k_pool, cache.v_pool, cache.r2t, req_rows, seq, gptr, gpl,
-                                   int(L.max()), 16, int(wl.prefix_len.max()), k_new=kn, v_new=vn, o=o,
-                                   workspace=ws_c)
+            (sp.cascade_decode_attn_fp8kv if fp8 else sp.cascade_decode_attn)(
+                q, *kv_args(cache), cache.r2t, req_rows, seq, gptr, gpl, int(L.max()), 16,
+                int(wl.prefix_len.max()), k_new=kn, v_new=vn, o=o, workspace=ws_c)
         else:         # a4 + a6
-            sp.decode_attn(q, cache.k_pool, cache.v_pool, cache.r2t, req_rows, seq, int(L.max()),
-                           k_new=kn, v_new=vn, o=o, workspace=ws_f)
+            (sp.decode_attn_fp8kv if fp8 else sp.decode_attn)(
+                q, *kv_args(cache), cache.r2t, req_rows, seq, int(L.max()), k_new=kn, v_new=vn, o=o,
+                workspace=ws_f)
         if timed:
             b.record()
             ev.append((a, b))
@@ -473,17 +515,20 @@ def bench_decode(args):
         torch.cuda.synchronize()
         res[mode] = ((time.perf_counter() - t0) * 1e3 / args.steps,
                      float(np.mean([a.elapsed_time(b) for a, b in ev])))
-    flat_bytes = acc.decode_bytes_flat(L, Hq, Hkv, D, 2)
-    casc_bytes = acc.decode_bytes_cascade(L, wl.grp, wl.prefix_len, Hq, Hkv, D, 2)
+    kelt = 1 if fp8 else 2
+    flat_bytes = acc.decode_bytes_flat(L, Hq, Hkv, D, kelt, 2)
+    casc_bytes = acc.decode_bytes_cascade(L, wl.grp, wl.prefix_len, Hq, Hkv, D, kelt, 2)
     ms_c, call_c = res["cascade"]
     ms_f, call_f = res["flat"]
     gbps_c = casc_bytes / (call_c * 1e-3) / 1e9
     gbps_f = flat_bytes / (call_f * 1e-3) / 1e9
     config = {"workload": "decode: 256 requests in 16 prefix groups (prefix ~U[512,4096], context "
                           "~U[max(1024,P+1),8192]), one token each, cascade decode; 32/8 heads, head_dim 128, "
-                          "2^21-slot pool, page 1", "batch": B, "groups": G}
+                          "2^21-slot pool, page 1" + (", FP8 e4m3fn KV cache with per-head factors" if fp8 else ""),
+              "batch": B, "groups": G, "kv_cache": "fp8_e4m3fn" if fp8 else "bf16"}
     roof = {"bound": "hbm", "achieved": gbps_c, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": gbps_c / PEAK_HBM_GBPS, "traffic": traffic_record("cascade_decode_call"),
+            "frac": gbps_c / PEAK_HBM_GBPS,
+            "traffic": traffic_record("cascade_decode_call_fp8" if fp8 else "cascade_decode_call"),
             "kernel": "cascade decode call (prefix + suffix split kernels + merge)",
             "bytes_per_launch": casc_bytes, "avg_launch_ms": call_c}
     line = base_line(B / (ms_c * 1e-3), ms_c, args, config, roof, {
@@ -499,7 +544,8 @@ def bench_decode(args):
             Ks.append(K)
             Vs.append(V)
             rws.append((r, int(L[r]) - 1, wl.queries(r, 1)[0]))
-        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "decode")
+        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "decode",
+                                                 W.fp8_scales(s) if fp8 else None)
     return line
 
 
@@ -518,9 +564,14 @@ def bench_fork(args):
     B, G, Hq, Hkv, D = wl.B, wl.G, s.Hq, s.Hkv, s.D
     Pp, S = 4096, 512
     dev = "cuda"
-    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, Pp + S + 1, W.pool_order(s), dev)
-    fill_random(cache.k_pool, seed=1)
-    fill_random(cache.v_pool, seed=2)
+    fp8 = args.kv == "fp8"
+    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, Pp + S + 1, W.pool_order(s), dev,
+                         kv_scale=W.fp8_scales(s) if fp8 else None)
+    if fp8:
+        fill_fp8(cache, seed=1)
+    else:
+        fill_random(cache.k_pool, seed=1)
+        fill_random(cache.v_pool, seed=2)
     setup_groups(cache, wl)
     rows = cache.admit([np.concatenate([wl.prefix_tokens(wl.grp[r]), wl.suffix_tokens(r, 1)]) for r in range(B)])
     assert all(st.matched == Pp for st in rows)
@@ -560,8 +611,9 @@ def bench_fork(args):
             if timed:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-            sp.cascade_decode_attn(q[k], cache.k_pool, cache.v_pool, cache.r2t, req_rows, seqs[k], gptr, gpl,
-                                   Pp + k + 1, 8, Pp, k_new=kn[k], v_new=vn[k], o=o, workspace=ws)
+            (sp.cascade_decode_attn_fp8kv if fp8 else sp.cascade_decode_attn)(
+                q[k], *kv_args(cache), cache.r2t, req_rows, seqs[k], gptr, gpl, Pp + k + 1, 8, Pp,
+                k_new=kn[k], v_new=vn[k], o=o, workspace=ws)
             if timed:
                 b.record()
                 evs.append((a, b))
@@ -580,12 +632,15 @@ def bench_fork(args):
     t1 = time.perf_counter()
     per_s /= n_sweeps
     ms = (t1 - t0) * 1e3 / n_sweeps
-    bytes_s = np.array([acc.decode_bytes_cascade([Pp + k] * B, np.repeat(np.arange(G), 8), [Pp] * G, Hq, Hkv, D, 2)
-                        for k in range(1, S + 1)], np.float64)
+    kelt = 1 if fp8 else 2
+    bytes_s = np.array([acc.decode_bytes_cascade([Pp + k] * B, np.repeat(np.arange(G), 8), [Pp] * G, Hq, Hkv, D,
+                                                 kelt, 2) for k in range(1, S + 1)], np.float64)
     gbps = bytes_s.sum() / (per_s.sum() * 1e-3) / 1e9
     config = {"workload": "fork: 16 prompts x 4096 tokens, 8 branches each (128 requests), suffix grows "
-                          "1..512 in lockstep, cascade decode per step; 32/8 heads, head_dim 128, 2^18-slot pool",
-              "prompts": G, "branches": 8, "prompt_len": Pp, "steps_per_sweep": S}
+                          "1..512 in lockstep, cascade decode per step; 32/8 heads, head_dim 128, 2^18-slot pool"
+                          + (", FP8 e4m3fn KV cache with per-head factors" if fp8 else ""),
+              "prompts": G, "branches": 8, "prompt_len": Pp, "steps_per_sweep": S,
+              "kv_cache": "fp8_e4m3fn" if fp8 else "bf16"}
     roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
             "traffic": None, "kernel": "cascade decode call, summed over the sweep",
             "bytes_per_sweep": float(bytes_s.sum()), "avg_launch_ms": float(per_s.mean())}
@@ -601,7 +656,8 @@ def bench_fork(args):
             Ks.append(K)
             Vs.append(V)
             rws.append((len(Ks) - 1, Pp + S - 1, wl.queries(r, 1)[0]))
-        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "fork (s=512)")
+        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "fork (s=512)",
+                                                 W.fp8_scales(s) if fp8 else None)
     return line
 
 
