@@ -20,8 +20,9 @@ Host work of a step overlaps the GPU work of the previous one (pinned
 staging buffers, asynchronous copies).  Inputs (Q/K/V) are resident in HBM
 before the timed region.  Prints ONE JSON line.
 
-Other --config values time the decode-batch, fork-sweep and multi-turn
-workloads for reporting; their lines have the same shape.  --kv fp8 runs the
+Other --config values time the decode-batch, fork-sweep, verify (small-q
+extend: q_len new tokens per request over long cached contexts) and
+multi-turn workloads for reporting; their lines have the same shape.  --kv fp8 runs the
 decode and fork workloads over an FP8 (e4m3fn) KV cache with per-head
 factors (the same bf16 queries, bf16 MFMA arithmetic, one byte per cached
 element).
@@ -47,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="extend", choices=["extend", "decode", "fork", "multiturn"])
+    ap.add_argument("--config", default="extend", choices=["extend", "decode", "fork", "verify", "multiturn"])
+    ap.add_argument("--q-len", type=int, default=4, help="new tokens per request of the verify workload")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="KV cache element type of the decode and fork workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -662,6 +664,99 @@ def bench_fork(args):
 
 
 # ---------------------------------------------------------------------------
+# verify: 64 requests, own cached contexts ~U[2048, 8192], q_len new tokens each
+# ---------------------------------------------------------------------------
+def bench_verify(args):
+    import torch
+    import workloads as W
+    import prefix_shared_paged_amd as sp
+    from prefix_shared_paged_amd import accounting as acc
+    from prefix_shared_paged_amd.paged_cache import PagedKVCache
+
+    E = args.q_len
+    wl = W.verify(seed=0, q_len=E)
+    s = wl.spec
+    B, Hq, Hkv, D = wl.B, s.Hq, s.Hkv, s.D
+    P = wl.prefix_len.astype(np.int64)
+    dev = "cuda"
+    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, 2 * B, int(P.max()) + E + 1, W.pool_order(s), dev)
+    fill_random(cache.k_pool, seed=1)
+    fill_random(cache.v_pool, seed=2)
+    setup_groups(cache, wl)
+    rows = cache.admit([wl.prefix_tokens(r) for r in range(B)])
+    assert all(st.matched == P[r] for r, st in enumerate(rows))
+    n = B * E
+    q = torch.empty((n, Hq, D), dtype=torch.bfloat16, device=dev)
+    kn = torch.empty((n, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vn = torch.empty((n, Hkv, D), dtype=torch.bfloat16, device=dev)
+    for t, sd in ((q, 3), (kn, 4), (vn, 5)):
+        fill_random(t, seed=sd)
+    o = torch.empty_like(q)
+    req_rows = cache.rows_tensor(rows)
+    pl = torch.from_numpy(P.astype(np.int32)).to(dev)
+    q_off = torch.from_numpy(np.arange(B + 1, dtype=np.int64) * E).to(dev)
+    col0 = torch.from_numpy(P.astype(np.int32)).to(dev)
+    d_new = torch.empty(n, dtype=torch.int32, device=dev)
+    ws_n = sp.extend_workspace_size(B, n, E, Hq, Hkv, D)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev) if ws_n else None
+    pin = Pinned(torch, 3, {"new": (n, torch.int32)})
+    pool = cache.pool
+    last = np.array([int(st.slots[-1]) for st in rows], np.int32)
+    ev = []
+
+    def step(timed):
+        # a1: q_len draft slots per request; a3: append them to req_to_token;
+        # a4 + a5: store the drafts' K/V and attend (small-q extend); the
+        # drafts are then rejected (slots freed) so every step sees the same shapes
+        new, _ = pool.alloc_batch(np.full(B, E, np.int64), P, last)
+        k, buf = pin.next()
+        buf["new"].numpy()[:] = new
+        d_new.copy_(buf["new"], non_blocking=True)
+        pin.done(k)
+        sp.build_req_to_token(cache.r2t, req_rows, d_new, q_off, new_col0=col0)
+        if timed:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+        sp.extend_attn(q, cache.k_pool, cache.v_pool, cache.r2t, req_rows, pl, q_off, E, k_new=kn, v_new=vn,
+                       o=o, workspace=ws)
+        if timed:
+            b.record()
+            ev.append((a, b))
+        pool.free(new)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    call = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    byts = acc.decode_bytes_flat(P + E, Hq, Hkv, D, 2) + (E - 1) * 2 * B * Hq * D * 2
+    gbps = byts / (call * 1e-3) / 1e9
+    config = {"workload": f"verify (small-q extend): {B} requests, own cached contexts ~U[2048,8192], {E} new "
+                          "tokens each (stored, then attended causally); 32/8 heads, head_dim 128, 2^20-slot pool, "
+                          "page 1", "batch": B, "q_len": E,
+              "path": "split-K" if ws_n else "prefill kernel"}
+    roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+            "traffic": None, "kernel": "extend call (split kernel + merge, or the prefill kernel)",
+            "bytes_per_launch": byts, "avg_launch_ms": call}
+    line = base_line(n / (ms * 1e-3), ms, args, config, roof, {"call_ms": call,
+                                                                "tokens_per_s_call_only": n / (call * 1e-3)})
+    if not args.no_cpu_baseline:
+        Ks, Vs, rws = [], [], []
+        for r in range(min(B, 8)):
+            K, V = wl.logical_kv(r)
+            Ks.append(K)
+            Vs.append(V)
+            for i in range(E):
+                rws.append((r, int(P[r]) + i, wl.queries(r, E)[i]))
+        line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "verify")
+    return line
+
+
+# ---------------------------------------------------------------------------
 # multi-turn: 128 sessions, ~70% cached history, chunked prefill (512) + decode, page 16
 # ---------------------------------------------------------------------------
 def bench_multiturn(args):
@@ -800,7 +895,8 @@ def main():
         else:
             line["cpu_baseline"] = None
     else:
-        line = {"decode": bench_decode, "fork": bench_fork, "multiturn": bench_multiturn}[args.config](args)
+        line = {"decode": bench_decode, "fork": bench_fork, "verify": bench_verify,
+                "multiturn": bench_multiturn}[args.config](args)
     print(json.dumps(line, default=lambda x: x.item() if hasattr(x, "item") else str(x)), flush=True)
 
 

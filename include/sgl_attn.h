@@ -235,7 +235,11 @@ int sgl_store_kv(int dtype, const void *k_new, const void *v_new, int64_t n_toke
  *   lse: device float32 [n_tokens, Hq] log-sum-exp of the scaled scores
  *     (natural log), or NULL.
  *   workspace: device scratch of sgl_extend_workspace_size(...) bytes (may be
- *     NULL when that size is 0).
+ *     NULL when that size is 0).  The size is non-zero for bf16 calls with
+ *     max_extend_len * (Hq / Hkv) <= 16 -- a few new tokens per request, as in
+ *     the verify step of speculative decoding -- which run as a split-K pass
+ *     over each request's keys plus a log-sum-exp merge (the result is the
+ *     same attention).
  * scale multiplies q.k (normally 1/sqrt(D)). */
 int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_new,
                     void *k_pool, void *v_pool, int64_t num_slots,

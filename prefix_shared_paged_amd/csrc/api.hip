@@ -86,6 +86,27 @@ bool slots_ok(const std::vector<int32_t> &tab, int64_t row_stride, int64_t row, 
     return true;
 }
 
+// Small-q extend (a few new tokens per request over a long cached context,
+// the verify step of speculative decoding): when every request's new tokens
+// times the query heads per KV head fit one 16-row MFMA block, the extend
+// runs as a split-K decode of those rows -- each request's keys cut into
+// n_spl splits, one wave per (request, KV head, split) -- and a log-sum-exp
+// merge, instead of the 128-row tiles of the prefill kernel, which stream
+// each long context through one workgroup per KV head with most rows empty.
+// Measured on 64 requests over contexts of 2-8k keys (32/8 heads): 1, 2, 4
+// new tokens take 287, 293, 310 us this way against 336, 332, 326 us in the
+// prefill kernel; with 32 or 64 rows per KV head (several waves sharing each
+// tile) the split-K form is slower, so those stay in the prefill kernel.
+constexpr int kSmallQRows = 16;
+bool small_q_extend(int32_t max_extend_len, int32_t Hq, int32_t Hkv) {
+    return Hkv > 0 && (int64_t)max_extend_len * (Hq / Hkv) <= kSmallQRows;
+}
+int32_t extend_splits(int32_t batch, int32_t Hkv) {
+    const int64_t items = (int64_t)batch * Hkv;
+    int64_t n = items > 0 ? (2048 + items - 1) / items : 1;
+    return (int32_t)(n < 1 ? 1 : (n > 8 ? 8 : n));
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,7 +193,11 @@ int sgl_store_kv_fp8(int dtype, const void *k_new, const void *v_new, int64_t n_
                                Hkv, D, k_scale, v_scale, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0, st);
 }
 
-size_t sgl_extend_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t sgl_extend_workspace_size(int32_t batch, int64_t n_tokens, int32_t max_extend_len, int32_t Hq,
+                                 int32_t Hkv, int32_t D) {
+    if (batch <= 0 || n_tokens <= 0 || max_extend_len <= 0 || !small_q_extend(max_extend_len, Hq, Hkv)) return 0;
+    return part_bytes(n_tokens, extend_splits(batch, Hkv), Hq, D);
+}
 
 int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,
                     void *v_pool, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
@@ -180,8 +205,6 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
                     const int64_t *q_off, int32_t batch, int64_t n_tokens, int32_t max_extend_len,
                     int32_t Hq, int32_t Hkv, int32_t D, float scale, void *o, float *lse,
                     void *workspace, size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (!shape_ok(dtype, Hq, Hkv, D)) return SGL_ERR_UNSUPPORTED;
     if (batch < 0 || n_tokens < 0 || max_extend_len < 0 || num_slots < 1 || num_rows < 0 || row_stride < 0)
         return SGL_ERR_INVALID;
@@ -212,6 +235,26 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
                              num_slots, Hkv, D, r2t, num_rows, row_stride, req_rows, prefix_lens,
                              q_off, batch, max_extend_len, st);
         if (rc != SGL_OK) return rc;
+    }
+    if (dtype == SGL_BF16 && small_q_extend(max_extend_len, Hq, Hkv)) {
+        const size_t need = sgl_extend_workspace_size(batch, n_tokens, max_extend_len, Hq, Hkv, D);
+        if (workspace_bytes < need || !workspace) return SGL_ERR_WORKSPACE;
+        if (n_tokens > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+        const int32_t n_spl = extend_splits(batch, Hkv);
+        char *wp = (char *)workspace;
+        SplitArgs a;
+        std::memset(&a, 0, sizeof a);
+        a.kind = 4; a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots; a.r2t = r2t;
+        a.num_rows = num_rows; a.row_stride = row_stride; a.req_rows = req_rows; a.q_off = q_off;
+        a.prefix_lens = prefix_lens; a.batch = batch; a.n_sets = batch; a.max_splits = n_spl; a.n_spl = n_spl;
+        a.chunk = 16; a.max_members = max_extend_len; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.scale = scale;
+        a.part = carve(wp, n_tokens, n_spl, Hq, D);
+        if ((rc = launch_split_bf16(a, st)) != SGL_OK) return rc;
+        MergeArgs m;
+        std::memset(&m, 0, sizeof m);
+        m.kind = 4; m.flat_or_suffix = a.part; m.batch = (int32_t)n_tokens; m.Hq = Hq; m.D = D; m.out_bf16 = 1;
+        m.o = o; m.lse = lse; m.q_off = q_off; m.prefix_lens = prefix_lens; m.n_req = batch; m.n_spl = n_spl;
+        return launch_merge(m, st);
     }
     if (dtype == SGL_F32)
         return launch_extend_f32((const float *)q, (const float *)k_pool, (const float *)v_pool,

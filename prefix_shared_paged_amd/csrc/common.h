@@ -94,6 +94,11 @@ int launch_extend_bf16(const __bf16 *q, const __bf16 *k_pool, const __bf16 *v_po
 //   kind 1 (prefix): per group g, keys [0, group_prefix_len[g]) of the group's first row,
 //                    query rows = every member of the group
 //   kind 2 (suffix): per request r, keys [group_prefix_len[group(r)], seq_lens[r])
+//   kind 4 (small-q extend): per request r with P = prefix_lens[r] cached keys and
+//                    E = q_off[r+1] - q_off[r] new tokens, keys [0, P + E) cut into
+//                    n_spl splits of verify_chunk(P + E, n_spl) keys; query rows =
+//                    (new token i, q head), row of token i sees keys <= P + i; split
+//                    states are indexed by token (q_off[r] + i) instead of request
 struct SplitArgs {
     int kind;
     const void *q;
@@ -119,8 +124,18 @@ struct SplitArgs {
     const float *k_scale;  // FP8 KV only: per KV head factors of the K and V codes
     const float *v_scale;
     int32_t xcd_block;     // launch_split_rows: consecutive requests per XCD block
+    const int64_t *q_off;          // kind 4: token offsets [batch + 1]
+    const int32_t *prefix_lens;    // kind 4: cached keys per request
+    int32_t n_spl;                 // kind 4: splits per request
     PartialBuf part;
 };
+
+// Keys per split of a small-q extend request with L keys cut into n_spl
+// splits (whole 16-key tiles); the split kernel and the merge both use it.
+__host__ __device__ __forceinline__ int64_t verify_chunk(int64_t L, int32_t n_spl) {
+    const int64_t c = ceil_div64(ceil_div64(L, n_spl), 16) * 16;
+    return c < 16 ? 16 : c;
+}
 
 int launch_split_f32(const SplitArgs &a, hipStream_t st);
 int launch_split_bf16(const SplitArgs &a, hipStream_t st);
@@ -131,7 +146,8 @@ int launch_split_rows(const SplitArgs &a, bool fp8, hipStream_t st);
 
 // Merge partial states of (optionally) a prefix buffer and a suffix buffer.
 //   kind 0: parts = flat splits of r;  kind 3: parts = prefix splits of group(r) for r
-//   + suffix splits of r.
+//   + suffix splits of r;  kind 4: r is a token of a small-q extend (batch = tokens),
+//   parts = the splits of its request (n_req requests, q_off, prefix_lens, n_spl).
 struct MergeArgs {
     int kind;
     PartialBuf flat_or_suffix;
@@ -144,5 +160,8 @@ struct MergeArgs {
     int out_bf16;
     void *o;
     float *lse;
+    const int64_t *q_off;
+    const int32_t *prefix_lens;
+    int32_t n_req, n_spl;
 };
 int launch_merge(const MergeArgs &a, hipStream_t st);

@@ -45,6 +45,7 @@ using namespace sgl_decode;
 
 constexpr int TILE = 16;   // keys per tile
 constexpr int PREFIX_DEPTH = 2;   // tile buffers of the cascade prefix stage
+constexpr int kSlotTab = 2048;    // slot ids held in LDS at a time (longer splits refill)
 
 // ---- work item of a split kernel ------------------------------------------------
 // Workgroup id = ((item / 8) * n_rbg + rbg) * 8 + item % 8 with item = (split,
@@ -57,6 +58,7 @@ constexpr int PREFIX_DEPTH = 2;   // tile buffers of the cascade prefix stage
 struct SplitItem {
     int kvh, s, first_req, n_members, row_base, nk;
     int64_t k0, ref_row;
+    int64_t causal;   // kind 4: the row of member i sees keys <= causal + i; else -1
 };
 
 template <int WPG>
@@ -77,8 +79,21 @@ __device__ __forceinline__ bool split_item(const SplitArgs &a, int w, SplitItem 
 
     // which rows, which keys (uniform over the workgroup)
     int first_req, n_members;
-    int64_t lo, hi, ref_row;
-    if (a.kind == 1) {
+    int64_t lo, hi, ref_row, chunk = a.chunk;
+    it.causal = -1;
+    if (a.kind == 4) {
+        // small-q extend: the members are the request's new tokens
+        const int64_t t0 = a.q_off[set], E = a.q_off[set + 1] - t0;
+        const int64_t P = a.prefix_lens[set];
+        if (E <= 0 || t0 < 0 || P < 0) return false;
+        first_req = (int)t0;
+        n_members = (int)E;
+        lo = 0;
+        hi = P + E;
+        chunk = verify_chunk(hi, a.n_spl);
+        ref_row = a.req_rows[set];
+        it.causal = P;
+    } else if (a.kind == 1) {
         first_req = a.group_ptr[set];
         n_members = a.group_ptr[set + 1] - first_req;
         if (n_members <= 0 || first_req < 0 || first_req + n_members > a.batch) return false;
@@ -103,15 +118,15 @@ __device__ __forceinline__ bool split_item(const SplitArgs &a, int w, SplitItem 
     if (n_members * g <= rbg * WPG * 16) return false;    // no rows left for this workgroup
     if (ref_row < 0 || ref_row >= a.num_rows) return false;
     if (hi > a.row_stride) hi = a.row_stride;
-    const int64_t n_split = ceil_div64(hi - lo, a.chunk);
+    const int64_t n_split = ceil_div64(hi - lo, chunk);
     if (s >= n_split || s >= a.part.S) return false;
     it.kvh = kvh;
     it.s = s;
     it.first_req = first_req;
     it.n_members = n_members;
     it.row_base = (rbg * WPG + w) * 16;
-    it.k0 = lo + (int64_t)s * a.chunk;
-    it.nk = (int)((it.k0 + a.chunk < hi ? it.k0 + a.chunk : hi) - it.k0);
+    it.k0 = lo + (int64_t)s * chunk;
+    it.nk = (int)((it.k0 + chunk < hi ? it.k0 + chunk : hi) - it.k0);
     it.ref_row = ref_row;
     return true;
 }
@@ -155,12 +170,17 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     const int first_req = it.first_req, n_members = it.n_members;
     const int64_t k0 = it.k0, ref_row = it.ref_row;
     const int nk = it.nk;
-    const int N = (nk + TILE - 1) / TILE;           // tiles, >= 1
     const int row_base = it.row_base;               // first group row of this wave
     const int rows = n_members * g - row_base;      // may be <= 0: the wave still loads
 
+    // slot ids of the split's keys [pb, pb + kSlotTab) in LDS (one part unless
+    // the split is longer than the table)
     const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
-    for (int j = threadIdx.x; j < nk; j += 64 * WPG) slot_lds[j] = safe_slot(row[j], a.num_slots);
+    auto fill_slots = [&](int pb) {
+        const int cnt = min(kSlotTab, nk - pb);
+        for (int j = threadIdx.x; j < cnt; j += 64 * WPG) slot_lds[j] = safe_slot(row[pb + j], a.num_slots);
+    };
+    fill_slots(0);
 
     const __bf16 *q = (const __bf16 *)a.q;
     const char *kp = (const char *)a.k_pool + kvh * D * 2;
@@ -207,12 +227,18 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
 
     __syncthreads();   // slot table visible
 
-    // This wave's loads of tile n (keys past the split end repeat its last key,
-    // so every address is a real row of the context; their scores are masked)
+    // keys of the current slot-table part: [pbase, pbase + nkp) of the split
+    int pbase = 0, nkp = min(kSlotTab, nk);
+    // small-q extend: this lane's row sees split keys <= clim
+    const int clim = it.causal >= 0 ? (int)(it.causal + (row_base + n16) / g - k0) : 0x7fffffff;
+
+    // This wave's loads of tile n of the part (keys past its end repeat its
+    // last key, so every address is a real row of the context; their scores
+    // are masked)
     auto issue = [&](int n, const char *pool, unsigned char *dst) {
 #pragma unroll
         for (int u = 0; u < NIW; u++) {
-            const int kk = min(n * TILE + lrow[u], nk - 1);
+            const int kk = min(n * TILE + lrow[u], nkp - 1);
             const char *src = pool + (int64_t)slot_lds[kk] * rowstride_el * 2 + lchk[u];
             __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
                                              (SGL_LDS void *)(dst + (w + WPG * u) * 1024), 16, 0, 2 /* nt */);
@@ -244,7 +270,8 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const float x = n * TILE + kq * 4 + j < nk ? sacc[j] * qscale : -INFINITY;
+            const int kidx = pbase + n * TILE + kq * 4 + j;
+            const float x = kidx < nk && kidx <= clim ? sacc[j] * qscale : -INFINITY;
             sv[j] = x;
             mx = fmaxf(mx, x);
         }
@@ -263,10 +290,13 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
             for (int db = 0; db < DB; db++) oacc[db] *= alpha;
             m_run = m_new;
         }
+        // a row with no visible key so far keeps m_run = -inf (its scores are
+        // all -inf, and 2^(-inf - 0) = 0)
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         bf16x4 pf;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_run);
+            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_use);
             l_run += pj;
             pf[j] = (__bf16)pj;
         }
@@ -283,49 +313,60 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
                                                                  0, 0, 0);
     };
 
-    if constexpr (DEPTH == 1) {
-        issue(0, kp, k_lds);
-        issue(0, vp, v_lds);
-        for (int n = 0; n < N; n++) {
-            vm_wait<0>();                                // this wave's loads of tile n have landed
-            wg_barrier();                                // ... and every wave's
-            const f32x4 sacc = s_tile(k_lds);
-            if (n + 1 < N) {
-                lgkm_wait0();
-                wg_barrier();                            // every wave has read the K tile
-                issue(n + 1, kp, k_lds);
+    for (;;) {
+        const int N = (nkp + TILE - 1) / TILE;      // tiles of this part, >= 1
+        if constexpr (DEPTH == 1) {
+            issue(0, kp, k_lds);
+            issue(0, vp, v_lds);
+            for (int n = 0; n < N; n++) {
+                vm_wait<0>();                        // this wave's loads of tile n have landed
+                wg_barrier();                        // ... and every wave's
+                const f32x4 sacc = s_tile(k_lds);
+                if (n + 1 < N) {
+                    lgkm_wait0();
+                    wg_barrier();                    // every wave has read the K tile
+                    issue(n + 1, kp, k_lds);
+                }
+                pv_tile(n, sacc, v_lds);
+                if (n + 1 < N) {
+                    lgkm_wait0();
+                    wg_barrier();                    // every wave has read the V tile
+                    issue(n + 1, vp, v_lds);
+                }
             }
-            pv_tile(n, sacc, v_lds);
-            if (n + 1 < N) {
-                lgkm_wait0();
-                wg_barrier();                            // every wave has read the V tile
-                issue(n + 1, vp, v_lds);
+        } else {
+            // DEPTH-1 tiles stay in flight while one is computed
+            for (int t = 0; t < DEPTH && t < N; t++) {
+                issue(t, kp, k_lds + (t % DEPTH) * TB);
+                issue(t, vp, v_lds + (t % DEPTH) * TB);
+            }
+            for (int n = 0; n < N; n++) {
+                const int ahead = min(DEPTH - 1, N - 1 - n);   // tiles issued after tile n
+                // this wave's loads of tile n have landed when at most ahead * 2 * NIW remain
+                if (ahead >= 3) vm_wait<3 * 2 * NIW>();
+                else if (ahead == 2) vm_wait<2 * 2 * NIW>();
+                else if (ahead == 1) vm_wait<2 * NIW>();
+                else vm_wait<0>();
+                wg_barrier();
+                unsigned char *kb = k_lds + (n % DEPTH) * TB;
+                unsigned char *vb = v_lds + (n % DEPTH) * TB;
+                pv_tile(n, s_tile(kb), vb);
+                if (n + DEPTH < N) {
+                    lgkm_wait0();
+                    wg_barrier();                    // every wave is done with this buffer
+                    issue(n + DEPTH, kp, kb);
+                    issue(n + DEPTH, vp, vb);
+                }
             }
         }
-    } else {
-        // DEPTH-1 tiles stay in flight while one is computed
-        for (int t = 0; t < DEPTH && t < N; t++) {
-            issue(t, kp, k_lds + (t % DEPTH) * TB);
-            issue(t, vp, v_lds + (t % DEPTH) * TB);
-        }
-        for (int n = 0; n < N; n++) {
-            const int ahead = min(DEPTH - 1, N - 1 - n);   // tiles issued after tile n
-            // this wave's loads of tile n have landed when at most ahead * 2 * NIW remain
-            if (ahead >= 3) vm_wait<3 * 2 * NIW>();
-            else if (ahead == 2) vm_wait<2 * 2 * NIW>();
-            else if (ahead == 1) vm_wait<2 * NIW>();
-            else vm_wait<0>();
-            wg_barrier();
-            unsigned char *kb = k_lds + (n % DEPTH) * TB;
-            unsigned char *vb = v_lds + (n % DEPTH) * TB;
-            pv_tile(n, s_tile(kb), vb);
-            if (n + DEPTH < N) {
-                lgkm_wait0();
-                wg_barrier();                            // every wave is done with this buffer
-                issue(n + DEPTH, kp, kb);
-                issue(n + DEPTH, vp, vb);
-            }
-        }
+        pbase += kSlotTab;
+        if (pbase >= nk) break;
+        // next part of a long split: every wave is done with the table and
+        // the tile buffers (no load is in flight); refill the table
+        __syncthreads();
+        fill_slots(pbase);
+        nkp = min(kSlotTab, nk - pbase);
+        __syncthreads();
     }
 
     // ---- write the split's state ---------------------------------------------
@@ -593,21 +634,22 @@ int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
     if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
     if (a0.chunk % TILE != 0) return SGL_ERR_INVALID;
     SplitArgs a = a0;
-    const int rows = (a.kind == 1 ? a.max_members : 1) * (a.Hq / a.Hkv);
+    const bool multi = a.kind == 1 || a.kind == 4;   // several query rows per (set, KV head)
+    const int rows = (multi ? a.max_members : 1) * (a.Hq / a.Hkv);
     a.row_blocks = (rows + 15) / 16;
     // The flat and suffix calls have many short work items: one wave per
     // workgroup and one buffer keep the most waves resident.  The prefix
-    // stage has few long items with up to 4 row blocks (64 query rows) per
-    // KV head: the row blocks share each tile, and a ring of PREFIX_DEPTH
+    // stage (and a small-q extend) has up to 4 row blocks (64 query rows)
+    // per KV head: the row blocks share each tile, and a ring of PREFIX_DEPTH
     // buffers keeps several tiles in flight per workgroup.
     int wpg = 1;
-    if (a.kind == 1) wpg = a.row_blocks >= 3 ? 4 : a.row_blocks;
+    if (multi) wpg = a.row_blocks >= 3 ? 4 : a.row_blocks;
     if (a.D == 64 && wpg > 2) wpg = 2;               // 2 load instructions per 64-dim tile
     const int n_rbg = (a.row_blocks + wpg - 1) / wpg;
     const int64_t items = (int64_t)a.n_sets * a.max_splits * a.Hkv;
     const int64_t n_wg = ceil_div64(items, 8) * 8 * n_rbg;
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
-    const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
+    const size_t dyn = (size_t)(a.kind == 4 ? kSlotTab : min(a.chunk, kSlotTab)) * sizeof(int32_t);
     const dim3 grid((unsigned)n_wg), block(64 * wpg);
 #define SGL_SPLIT(DD, DP, W) hipLaunchKernelGGL((split_bf16_kernel<DD, DP, W>), grid, block, dyn, st, a)
     if (a.D == 128) {
@@ -623,6 +665,7 @@ int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
 }
 
 int launch_split_fp8(const SplitArgs &a0, hipStream_t st) {
+    if (a0.kind == 4) return SGL_ERR_UNSUPPORTED;   // small-q extend runs on bf16 caches only
     if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
     if (a0.chunk % TILE8 != 0 || !a0.k_scale || !a0.v_scale) return SGL_ERR_INVALID;
     SplitArgs a = a0;

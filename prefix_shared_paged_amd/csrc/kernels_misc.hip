@@ -267,18 +267,30 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= (int64_t)a.batch * a.Hq) return;
     const int r = (int)(item / a.Hq), h = (int)(item % a.Hq);
-    const int64_t L = a.seq_lens[r];
 
     // parts: [prefix splits of r][suffix (or flat) splits of r]
     int np = 0, ns;
-    if (a.kind == 3) {
-        const int g = find_group(a.group_ptr, a.G, r);
-        int64_t P = a.group_prefix_len[g];
-        P = P < 0 ? 0 : (P > L ? L : P);
-        np = (int)ceil_div64(P, a.chunk_prefix);
-        ns = (int)ceil_div64(L - P, a.chunk_flat);
+    if (a.kind == 4) {
+        // token r of request rq = the last rq with q_off[rq] <= r
+        int lo = 0, hi = a.n_req - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.q_off[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        const int64_t P = a.prefix_lens[lo], E = a.q_off[lo + 1] - a.q_off[lo];
+        const int64_t L = (P < 0 ? 0 : P) + E;
+        ns = L > 0 ? (int)ceil_div64(L, verify_chunk(L, a.n_spl)) : 0;
     } else {
-        ns = (int)ceil_div64(L, a.chunk_flat);
+        const int64_t L = a.seq_lens[r];
+        if (a.kind == 3) {
+            const int g = find_group(a.group_ptr, a.G, r);
+            int64_t P = a.group_prefix_len[g];
+            P = P < 0 ? 0 : (P > L ? L : P);
+            np = (int)ceil_div64(P, a.chunk_prefix);
+            ns = (int)ceil_div64(L - P, a.chunk_flat);
+        } else {
+            ns = (int)ceil_div64(L, a.chunk_flat);
+        }
     }
     if (np > a.prefix.S) np = a.prefix.S;
     if (ns > a.flat_or_suffix.S) ns = a.flat_or_suffix.S;

@@ -350,3 +350,94 @@ def test_fork_cascade(s):
     err_c = bf16_err(res["o_c"][reqs], O)
     _print(f"fork s={s}: flat max abs err {err:.3e}, cascade {err_c:.3e}")
     assert err <= BF16_TOL and err_c <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# small-q extend (a few new tokens per request over a cached context: the
+# verify step of speculative decoding) -- the split-K path of sgl_extend_attn
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64), (16, 2, 128), (8, 4, 64)])
+def test_small_q_extend_ragged(Hq, Hkv, D):
+    # one request per group, so each request has its own cached prefix; the
+    # prefixes sit on and next to the 16-key tiles and the splits, and the new
+    # tokens (up to the 16 query rows per KV head of the split-K path) are ragged
+    g = Hq // Hkv
+    emax = max(1, 16 // g)
+    prefixes = [0, 1, 15, 16, 17, 300, 1023, 2000]
+    spec = W.Spec("small_q", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, 7)
+    grp = np.arange(len(prefixes), dtype=np.int64)
+    wl = W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, np.zeros(len(prefixes), np.int64),
+                         np.array(prefixes, np.int64) + emax)
+    case = GroupCase(wl)
+    E = np.array([emax, 1, min(3, emax), emax, min(2, emax), max(1, emax // 2), 5 % emax + 1, emax], np.int64)
+    res = run_extend(case, E)
+    case.check_r2t()
+    idx, O, LSE = oracle_extend(case, res)
+    err = bf16_err(res["o"][idx], O)
+    lerr = float(np.max(np.abs(res["lse"][idx] - LSE)))
+    _print(f"small-q extend Hq={Hq} Hkv={Hkv} D={D} E={E.tolist()}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+def _direct_verify(B, Hq, Hkv, D, P, E, seed, num_slots, sample_rows):
+    """Pools filled on the device from a seeded generator, request r's context
+    at random distinct slots, its new tokens' K/V already stored; runs the
+    extend call and returns (o, lse) with the oracle on the sampled
+    (request, token) rows (all heads)."""
+    import oracle
+    from prefix_shared_paged_amd import extend_attn
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    kp = (torch.randn((num_slots, Hkv, D), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    vp = (torch.randn((num_slots, Hkv, D), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    L = P + E
+    slots = np.random.default_rng(seed).permutation(num_slots)[:int(L.sum())].astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(L)])
+    stride = int(L.max()) + 1
+    r2t = np.full((B, stride), -1, np.int32)
+    for r in range(B):
+        r2t[r, :L[r]] = slots[off[r]:off[r + 1]]
+    q_off = np.concatenate([[0], np.cumsum(E)]).astype(np.int64)
+    q = (torch.randn((int(E.sum()), Hq, D), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    lse = torch.empty((int(E.sum()), Hq), dtype=torch.float32, device="cuda")
+    o = extend_attn(q, kp, vp, dev_i(r2t), dev_i(np.arange(B)), dev_i(P), dev_i(q_off, torch.int64),
+                    int(E.max()), lse=lse)
+    torch.cuda.synchronize()
+    o_h, lse_h, q_h = o.float().cpu().numpy(), lse.cpu().numpy(), q.float().cpu().numpy()
+    errs, lerrs = [], []
+    for r, i in sample_rows:
+        sl = torch.from_numpy(r2t[r, :L[r]].astype(np.int64)).cuda()
+        K = kp[sl].float().cpu().numpy()
+        V = vp[sl].float().cpu().numpy()
+        t = int(q_off[r]) + i
+        Or, _, _, Lr = oracle.attention([K], [V], [0], [int(P[r]) + i], q_h[t][None], Hq, Hkv)
+        errs.append(bf16_err(o_h[t][None], Or))
+        lerrs.append(float(np.max(np.abs(lse_h[t] - Lr[0]))))
+    return max(errs), max(lerrs)
+
+
+def test_small_q_extend_slot_table_parts():
+    # 128 requests x 16 KV heads: one split per request, longer than the
+    # 2048-entry slot table, so the kernel refills the table within a split
+    B, Hq, Hkv, D = 128, 16, 16, 64
+    rng = np.random.default_rng(3)
+    P = rng.integers(2040, 4300, B).astype(np.int64)
+    P[:4] = [2047, 2048, 4095, 4096]
+    E = rng.integers(1, 17, B).astype(np.int64)     # g = 1: up to 16 rows per KV head
+    sample = [(r, i) for r in (0, 1, 2, 3, 77, 127) for i in sorted({0, int(E[r]) // 2, int(E[r]) - 1})]
+    err, lerr = _direct_verify(B, Hq, Hkv, D, P, E, 11, 1 << 20, sample)
+    _print(f"small-q extend, slot-table parts: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("q_len", [1, 3, 4, 16])
+def test_small_q_extend_verify_shape_sampled(q_len):
+    # q_len <= 4 takes the split-K path (4 q heads per KV head), 16 the prefill kernel
+    # 64 requests over cached contexts ~U[2048, 8192], 32/8 heads, D 128
+    B, Hq, Hkv, D = 64, 32, 8, 128
+    P = np.random.default_rng(4).integers(2048, 8193, B).astype(np.int64)
+    E = np.full(B, q_len, np.int64)
+    sample = [(r, i) for r in (0, 31, 63) for i in sorted({0, q_len // 2, q_len - 1})]
+    err, lerr = _direct_verify(B, Hq, Hkv, D, P, E, 12, 1 << 20, sample)
+    _print(f"small-q extend, verify shape q_len={q_len}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL

@@ -19,6 +19,9 @@ Values: the shapes and distributions are those of the five workloads:
             context ~U[max(1024, P+1), 8192], 32/8/128, 2^21 slots
   fork      bf16, 16 prompts x 4096 tokens, 8 branches each, suffix 1..512,
             32/8/128, 2^18 slots
+  verify    bf16, 64 requests, own cached contexts ~U[2048, 8192], q_len new
+            tokens each (2-16: the verify step of speculative decoding),
+            32/8/128, 2^20 slots
   multiturn bf16, 128 sessions, history ~ lognormal(median 3000, sigma 1)
             clamped to [32, 32768], cached 16*floor(0.7 H / 16), chunks of
             512, page size 16, 64/8/128, 2^20 slots
@@ -198,6 +201,15 @@ def fork(seed=0, G=16, branches=8, prompt=4096, max_suffix=512, Hq=32, Hkv=8, D=
     sib = np.tile(np.arange(branches), G)
     return GroupWorkload(spec, np.full(G, prompt, np.int64), grp, sib,
                          np.full(G * branches, prompt + max_suffix, np.int64))
+
+
+def verify(seed=0, B=64, q_len=4, p_lo=2048, p_hi=8192, Hq=32, Hkv=8, D=128, num_slots=1 << 20):
+    """Small-q extend (the verify step of speculative decoding): B requests,
+    each with its own cached context of P ~ U[p_lo, p_hi] tokens (one request
+    per group) and q_len new tokens."""
+    spec = Spec("verify", "bf16", Hq, Hkv, D, 1, num_slots, 0.5, seed, extra={"q_len": q_len})
+    P = rng(seed, T_LEN).integers(p_lo, p_hi + 1, size=B).astype(np.int64)
+    return GroupWorkload(spec, P, np.arange(B, dtype=np.int64), np.zeros(B, np.int64), P + q_len)
 
 
 # ---------------------------------------------------------------------------
