@@ -42,6 +42,9 @@ def _load():
         lib.oracle_attention_kv_scaled.argtypes = [i64, p, p, p, p, p, i64, p, p, p, i32, i32,
                                                    i32, ctypes.c_double, p, i32, p, p, p, p,
                                                    p, p, i32, i32]
+        lib.oracle_attention_dv.restype = ctypes.c_int
+        lib.oracle_attention_dv.argtypes = [i64, p, p, p, p, p, i64, p, p, p, i32, i32, i32, i32,
+                                            ctypes.c_double, p, i32, p, p, p, p, p, p, i32, i32]
         lib.oracle_attention_probs.restype = ctypes.c_int
         lib.oracle_attention_probs.argtypes = [i64, p, i64, p, p, i32, i32, i32, i32,
                                                ctypes.c_double, p]
@@ -66,9 +69,10 @@ def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=No
               key_lo=None, key_hi=None, method=0, threads=None, kv_scale=None):
     """Attention of query rows over their request's logical sequence.
 
-    K_list / V_list: per request float32 arrays [L_r, Hkv, D] (logical order,
-      position j is row j) -- or a single concatenated array plus offsets via
-      ``kv_off`` in a tuple (K_cat, kv_off).
+    K_list / V_list: per request float32 arrays [L_r, Hkv, D] and [L_r, Hkv, Dv]
+      (logical order, position j is row j; Dv may differ from D: attention in
+      a latent space whose scores use D dims and values Dv) -- or a single
+      concatenated array plus offsets via ``kv_off`` in a tuple (K_cat, kv_off).
     row_req[i], row_pos[i]: request and absolute position of query row i.
     Q: float32 [n_rows, Hq, D].
     heads: optional list of q heads to evaluate (default all).
@@ -76,7 +80,7 @@ def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=No
     kv_scale: optional (k_scale, v_scale), each [Hkv]: the keys and values
       attended are K * k_scale[kv] and V * v_scale[kv] (a dequantised KV
       cache: K / V hold the decoded codes, see oracle.fp8), formed in fp64.
-    Returns (O [n_rows, n_heads, D], M, Lsum, LSE [n_rows, n_heads]) in float64.
+    Returns (O [n_rows, n_heads, Dv], M, Lsum, LSE [n_rows, n_heads]) in float64.
     """
     lib = _load()
     if isinstance(K_list, tuple):
@@ -86,14 +90,16 @@ def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=No
         lens = [k.shape[0] for k in K_list]
         kv_off = np.zeros(len(lens) + 1, np.int64)
         kv_off[1:] = np.cumsum(lens)
-        K = np.concatenate(K_list, axis=0) if K_list else np.zeros((0, Hkv, 1), np.float32)
-        V = np.concatenate(V_list, axis=0) if V_list else np.zeros((0, Hkv, 1), np.float32)
+        K = np.concatenate(K_list, axis=0) if K_list else np.zeros((0, Hkv, Q.shape[2]), np.float32)
+        V = np.concatenate(V_list, axis=0) if V_list else np.zeros((0, Hkv, Q.shape[2]), np.float32)
     K = np.ascontiguousarray(K, np.float32)
     V = np.ascontiguousarray(V, np.float32)
     Q = np.ascontiguousarray(Q, np.float32)
     kv_off = np.ascontiguousarray(kv_off, np.int64)
     D = Q.shape[2]
+    Dv = V.shape[2]
     assert K.shape[1] == Hkv and K.shape[2] == D and Q.shape[1] == Hq
+    assert V.shape[0] == K.shape[0] and V.shape[1] == Hkv
     row_req = np.ascontiguousarray(row_req, np.int64)
     row_pos = np.ascontiguousarray(row_pos, np.int64)
     n_rows = row_req.shape[0]
@@ -108,7 +114,7 @@ def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=No
         key_hi = np.ascontiguousarray(key_hi, np.int64)
     if scale is None:
         scale = 1.0 / np.sqrt(D)
-    O = np.zeros((n_rows, n_heads, D), np.float64)
+    O = np.zeros((n_rows, n_heads, Dv), np.float64)
     M = np.zeros((n_rows, n_heads), np.float64)
     Ls = np.zeros((n_rows, n_heads), np.float64)
     LSE = np.zeros((n_rows, n_heads), np.float64)
@@ -117,12 +123,12 @@ def attention(K_list, V_list, row_req, row_pos, Q, Hq, Hkv, scale=None, heads=No
         ks = np.ascontiguousarray(kv_scale[0], np.float64).reshape(-1)
         vs = np.ascontiguousarray(kv_scale[1], np.float64).reshape(-1)
         assert ks.shape[0] == Hkv and vs.shape[0] == Hkv
-    rc = lib.oracle_attention_kv_scaled(len(kv_off) - 1, _ptr(kv_off), _ptr(K), _ptr(V),
-                                        _ptr(ks), _ptr(vs), n_rows,
-                                        _ptr(row_req), _ptr(row_pos), _ptr(Q), Hq, Hkv, D,
-                                        float(scale), _ptr(heads), n_heads, _ptr(key_lo),
-                                        _ptr(key_hi), _ptr(O), _ptr(M), _ptr(Ls), _ptr(LSE),
-                                        int(method), int(threads or default_threads()))
+    rc = lib.oracle_attention_dv(len(kv_off) - 1, _ptr(kv_off), _ptr(K), _ptr(V),
+                                 _ptr(ks), _ptr(vs), n_rows,
+                                 _ptr(row_req), _ptr(row_pos), _ptr(Q), Hq, Hkv, D, Dv,
+                                 float(scale), _ptr(heads), n_heads, _ptr(key_lo),
+                                 _ptr(key_hi), _ptr(O), _ptr(M), _ptr(Ls), _ptr(LSE),
+                                 int(method), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_attention: invalid arguments")
     return O, M, Ls, LSE

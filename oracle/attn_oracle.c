@@ -53,6 +53,7 @@ typedef struct {
     const int64_t *kv_off;    /* [n_req+1] first logical K/V row of each request */
     const float *K, *V, *Q;
     int32_t Hq, Hkv, D;
+    int32_t Dv;               /* value width (V rows [Hkv, Dv], O rows Dv) */
     double scale;
     const double *kscale, *vscale; /* per KV head dequantisation factors, NULL -> 1 */
     const int32_t *heads;     /* q heads to evaluate */
@@ -67,7 +68,7 @@ typedef struct {
 
 /* Evaluate one (query row, head) pair. */
 static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
-    const int32_t D = jb->D, Hq = jb->Hq, Hkv = jb->Hkv;
+    const int32_t D = jb->D, Dv = jb->Dv, Hq = jb->Hq, Hkv = jb->Hkv;
     const int32_t h = jb->heads ? jb->heads[hs] : hs;
     const int32_t group = Hq / Hkv;
     const int32_t kvh = h / group;
@@ -81,8 +82,8 @@ static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
     if (hi > t + 1) hi = t + 1;              /* causal: keys j <= t only */
     const float *q = jb->Q + (row * (int64_t)Hq + h) * D;
     const int64_t ho = (int64_t)jb->n_heads * row + hs;
-    double *o = jb->O + ho * D;
-    for (int32_t d = 0; d < D; d++) o[d] = 0.0;
+    double *o = jb->O + ho * Dv;
+    for (int32_t d = 0; d < Dv; d++) o[d] = 0.0;
 
     if (hi <= lo) { /* empty key set: l = 0, m = -inf, o = 0 */
         jb->M[ho] = -INFINITY;
@@ -103,16 +104,16 @@ static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
         }
         /* pass 2: exp-sum and weighted sum of values */
         for (int64_t j = lo; j < hi; j++) {
-            const float *v = jb->V + ((base + j) * Hkv + kvh) * D;
+            const float *v = jb->V + ((base + j) * Hkv + kvh) * Dv;
             double w = exp(sbuf[j - lo] - m);
             l += w;
-            for (int32_t d = 0; d < D; d++) o[d] += w * ((double)v[d] * vs);
+            for (int32_t d = 0; d < Dv; d++) o[d] += w * ((double)v[d] * vs);
         }
     } else {
         /* one pass, running maximum */
         for (int64_t j = lo; j < hi; j++) {
             const float *k = jb->K + ((base + j) * Hkv + kvh) * D;
-            const float *v = jb->V + ((base + j) * Hkv + kvh) * D;
+            const float *v = jb->V + ((base + j) * Hkv + kvh) * Dv;
             double s = 0.0;
             for (int32_t d = 0; d < D; d++) s += (double)q[d] * ((double)k[d] * ks);
             s *= jb->scale;
@@ -120,11 +121,11 @@ static void eval_one(job_t *jb, int64_t row, int32_t hs, double *sbuf) {
             double c = exp(m - m_new);      /* rescale of what came before */
             double w = exp(s - m_new);
             l = l * c + w;
-            for (int32_t d = 0; d < D; d++) o[d] = o[d] * c + w * ((double)v[d] * vs);
+            for (int32_t d = 0; d < Dv; d++) o[d] = o[d] * c + w * ((double)v[d] * vs);
             m = m_new;
         }
     }
-    for (int32_t d = 0; d < D; d++) o[d] /= l;
+    for (int32_t d = 0; d < Dv; d++) o[d] /= l;
     jb->M[ho] = m;
     jb->L[ho] = l;
     jb->LSE[ho] = m + log(l);
@@ -160,8 +161,8 @@ static void *worker(void *arg) {
 }
 
 /*
- * oracle_attention, oracle_attention_kv_scaled -- softmax(q k^T * scale,
- * causal) v for a set of query rows.
+ * oracle_attention, oracle_attention_kv_scaled, oracle_attention_dv --
+ * softmax(q k^T * scale, causal) v for a set of query rows.
  *
  *   n_req, kv_off[n_req+1]: logical K/V rows of request r are
  *       K[kv_off[r] .. kv_off[r+1]) (layout [rows, Hkv, D], float32).
@@ -175,19 +176,22 @@ static void *worker(void *arg) {
  *       M is the maximum score, Lsum = sum_j exp(s_j - M), LSE = M + ln Lsum.
  *       An empty key range gives O = 0, Lsum = 0, M = LSE = -inf.
  *   method: 0 two-pass, 1 online.  n_threads >= 1.
- *   kscale, vscale [Hkv] (oracle_attention_kv_scaled only, NULL -> 1): the
+ *   kscale, vscale [Hkv] (oracle_attention_kv_scaled / _dv, NULL -> 1): the
  *       keys and values used are K * kscale[kv] and V * vscale[kv].
+ *   Dv (oracle_attention_dv; the others use Dv = D): the width of a value row,
+ *       V [rows, Hkv, Dv] and O [n_rows, n_heads, Dv] -- for attention in a
+ *       latent space where scores use D dims and values Dv of them.
  * Returns 0, or -1 on invalid arguments / allocation failure.
  */
-int oracle_attention_kv_scaled(int64_t n_req, const int64_t *kv_off, const float *K, const float *V,
-                               const double *kscale, const double *vscale,
-                               int64_t n_rows, const int64_t *row_req, const int64_t *row_pos,
-                               const float *Q, int32_t Hq, int32_t Hkv, int32_t D, double scale,
+int oracle_attention_dv(int64_t n_req, const int64_t *kv_off, const float *K, const float *V,
+                        const double *kscale, const double *vscale,
+                        int64_t n_rows, const int64_t *row_req, const int64_t *row_pos,
+                        const float *Q, int32_t Hq, int32_t Hkv, int32_t D, int32_t Dv, double scale,
                                const int32_t *heads, int32_t n_heads,
                                const int64_t *key_lo, const int64_t *key_hi,
                                double *O, double *M, double *Lsum, double *LSE,
                                int32_t method, int32_t n_threads) {
-    if (Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || n_threads < 1) return -1;
+    if (Hq <= 0 || Hkv <= 0 || D <= 0 || Dv <= 0 || Hq % Hkv != 0 || n_threads < 1) return -1;
     if (!heads) n_heads = Hq;
     for (int64_t i = 0; i < n_rows; i++) {
         int64_t r = row_req[i];
@@ -199,7 +203,7 @@ int oracle_attention_kv_scaled(int64_t n_req, const int64_t *kv_off, const float
     job_t jb;
     memset(&jb, 0, sizeof jb);
     jb.n_rows = n_rows; jb.row_req = row_req; jb.row_pos = row_pos; jb.kv_off = kv_off;
-    jb.K = K; jb.V = V; jb.kscale = kscale; jb.vscale = vscale; jb.Q = Q; jb.Hq = Hq; jb.Hkv = Hkv; jb.D = D; jb.scale = scale;
+    jb.K = K; jb.V = V; jb.kscale = kscale; jb.vscale = vscale; jb.Q = Q; jb.Hq = Hq; jb.Hkv = Hkv; jb.D = D; jb.Dv = Dv; jb.scale = scale;
     jb.heads = heads; jb.n_heads = n_heads; jb.key_lo = key_lo; jb.key_hi = key_hi;
     jb.method = method; jb.n_threads = n_threads; jb.O = O; jb.M = M; jb.L = Lsum; jb.LSE = LSE; jb.next = 0;
     pthread_mutex_init(&jb.mu, NULL);
@@ -232,9 +236,20 @@ int oracle_attention(int64_t n_req, const int64_t *kv_off, const float *K, const
                      const int64_t *key_lo, const int64_t *key_hi,
                      double *O, double *M, double *Lsum, double *LSE,
                      int32_t method, int32_t n_threads) {
-    return oracle_attention_kv_scaled(n_req, kv_off, K, V, NULL, NULL, n_rows, row_req, row_pos, Q, Hq,
-                                      Hkv, D, scale, heads, n_heads, key_lo, key_hi, O, M, Lsum, LSE,
-                                      method, n_threads);
+    return oracle_attention_dv(n_req, kv_off, K, V, NULL, NULL, n_rows, row_req, row_pos, Q, Hq, Hkv, D, D,
+                               scale, heads, n_heads, key_lo, key_hi, O, M, Lsum, LSE, method, n_threads);
+}
+
+int oracle_attention_kv_scaled(int64_t n_req, const int64_t *kv_off, const float *K, const float *V,
+                               const double *kscale, const double *vscale,
+                               int64_t n_rows, const int64_t *row_req, const int64_t *row_pos,
+                               const float *Q, int32_t Hq, int32_t Hkv, int32_t D, double scale,
+                               const int32_t *heads, int32_t n_heads,
+                               const int64_t *key_lo, const int64_t *key_hi,
+                               double *O, double *M, double *Lsum, double *LSE,
+                               int32_t method, int32_t n_threads) {
+    return oracle_attention_dv(n_req, kv_off, K, V, kscale, vscale, n_rows, row_req, row_pos, Q, Hq, Hkv, D,
+                               D, scale, heads, n_heads, key_lo, key_hi, O, M, Lsum, LSE, method, n_threads);
 }
 
 /*
