@@ -21,7 +21,8 @@ staging buffers, asynchronous copies).  Inputs (Q/K/V) are resident in HBM
 before the timed region.  Prints ONE JSON line.
 
 Other --config values time the decode-batch, fork-sweep, verify (small-q
-extend: q_len new tokens per request over long cached contexts) and
+extend: q_len new tokens per request over long cached contexts), mla (latent
+decode: one 576-dim latent row per token shared by every query head) and
 multi-turn workloads for reporting; their lines have the same shape.  --kv fp8 runs the
 decode and fork workloads over an FP8 (e4m3fn) KV cache with per-head
 factors (the same bf16 queries, bf16 MFMA arithmetic, one byte per cached
@@ -48,7 +49,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="extend", choices=["extend", "decode", "fork", "verify", "multiturn"])
+    ap.add_argument("--config", default="extend",
+                    choices=["extend", "decode", "fork", "verify", "mla", "multiturn"])
+    ap.add_argument("--mla-heads", type=int, default=128, help="query heads of the mla workload")
     ap.add_argument("--q-len", type=int, default=4, help="new tokens per request of the verify workload")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="KV cache element type of the decode and fork workloads")
@@ -757,6 +760,107 @@ def bench_verify(args):
 
 
 # ---------------------------------------------------------------------------
+# mla: latent decode, 128 requests in 16 groups of 8, one 576-dim latent per token
+# ---------------------------------------------------------------------------
+def bench_mla(args):
+    import torch
+    import workloads as W
+    import prefix_shared_paged_amd as sp
+
+    wl = W.mla(seed=0, Hq=args.mla_heads)
+    s = wl.spec
+    B, G, Hq, Dqk, Dv = wl.B, wl.G, s.Hq, 576, 512
+    M = B // G
+    dev = "cuda"
+    L = wl.ctx_len.astype(np.int64)
+    Pg = wl.prefix_len.astype(np.int64)
+    # request r: its group's prefix slots, then its own; the pool is random
+    # latents (values do not change the work)
+    pool = torch.empty((s.num_slots, Dqk), dtype=torch.bfloat16, device=dev)
+    fill_random(pool, seed=1)
+    perm = W.pool_order(s)
+    stride = int(L.max()) + 1
+    r2t_h = np.full((B, stride), -1, np.int32)
+    pos = 0
+    for g in range(G):
+        pre = perm[pos:pos + Pg[g]]
+        pos += Pg[g]
+        for r in range(g * M, (g + 1) * M):
+            n = int(L[r] - Pg[g])
+            r2t_h[r, :Pg[g]] = pre
+            r2t_h[r, Pg[g]:L[r]] = perm[pos:pos + n]
+            pos += n
+    r2t = torch.from_numpy(r2t_h).to(dev)
+    q = torch.empty((B, Hq, Dqk), dtype=torch.bfloat16, device=dev)
+    kvn = torch.empty((B, Dqk), dtype=torch.bfloat16, device=dev)
+    fill_random(q, seed=3)
+    fill_random(kvn, seed=4)
+    o = torch.empty((B, Hq, Dv), dtype=torch.bfloat16, device=dev)
+    rows = torch.arange(B, dtype=torch.int32, device=dev)
+    seq = torch.from_numpy(L.astype(np.int32)).to(dev)
+    gptr = torch.from_numpy((np.arange(G + 1) * M).astype(np.int32)).to(dev)
+    gpl = torch.from_numpy(Pg.astype(np.int32)).to(dev)
+    ws_f = torch.empty(sp.mla_decode_workspace_size(B, int(L.max()), Hq), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(sp.mla_cascade_workspace_size(B, G, int(L.max()), M, int(Pg.max()), Hq), dtype=torch.uint8,
+                       device=dev)
+    flat = lambda: sp.mla_decode_attn(q, pool, r2t, rows, seq, int(L.max()), kv_new=kvn, o=o, workspace=ws_f)
+    casc = lambda: sp.mla_cascade_decode_attn(q, pool, r2t, rows, seq, gptr, gpl, int(L.max()), M, int(Pg.max()),
+                                              kv_new=kvn, o=o, workspace=ws_c)
+    res = {}
+    for name, fn in (("cascade", casc), ("flat", flat)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        res[name] = ((time.perf_counter() - t0) * 1e3 / args.steps, float(np.mean([a.elapsed_time(b) for a, b in evs])))
+    row_b = Dqk * 2 + 4                                   # latent + its req_to_token entry
+    qo = B * Hq * (Dqk + Dv) * 2
+    flat_bytes = int(L.sum()) * row_b + qo
+    casc_bytes = (int(Pg.sum()) + int((L - Pg[wl.grp]).sum())) * row_b + qo
+    flops = float(L.sum()) * Hq * (Dqk + Dv) * 2
+    ms_c, call_c = res["cascade"]
+    ms_f, call_f = res["flat"]
+    gbps_c = casc_bytes / (call_c * 1e-3) / 1e9
+    gbps_f = flat_bytes / (call_f * 1e-3) / 1e9
+    config = {"workload": f"mla latent decode: {B} requests in {G} prefix groups of {M} (prefix ~U[512,4096], context "
+                          f"~U[max(1024,P+1),8192]), one token each, cascade decode; {Hq} query heads over one "
+                          "576-dim latent per token (values: its first 512), 2^21-slot pool, page 1",
+              "batch": B, "groups": G, "Hq": Hq, "Dqk": Dqk, "Dv": Dv}
+    roof = {"bound": "hbm", "achieved": gbps_c, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps_c / PEAK_HBM_GBPS,
+            "traffic": None, "kernel": "mla cascade decode call (prefix + suffix split kernels + merge)",
+            "bytes_per_launch": casc_bytes, "avg_launch_ms": call_c}
+    line = base_line(B / (ms_c * 1e-3), ms_c, args, config, roof, {
+        "flat": {"call_ms": call_f, "hbm_gbps": gbps_f, "frac": gbps_f / PEAK_HBM_GBPS,
+                 "tflops": flops / (call_f * 1e-3) / 1e12, "algorithmic_bytes": flat_bytes},
+        "cascade": {"call_ms": call_c, "hbm_gbps": gbps_c, "algorithmic_bytes": casc_bytes,
+                    "tflops": flops / (call_c * 1e-3) / 1e12, "mfma_frac": flops / (call_c * 1e-3) / 1e12 / 2500.0},
+        "flops_per_call": flops})
+    if not args.no_cpu_baseline:
+        import oracle
+        q_h = q[:4].float().cpu().numpy()
+        kvn_h = kvn[:4].float().cpu().numpy()
+        t0 = time.perf_counter()
+        for r in range(4):
+            lat = pool[torch.from_numpy(r2t_h[r, :L[r] - 1].astype(np.int64)).to(dev)].float().cpu().numpy()
+            lat = np.concatenate([lat, kvn_h[r][None]])[:, None, :]
+            oracle.attention([lat], [np.ascontiguousarray(lat[:, :, :Dv])], [0], [int(L[r]) - 1], q_h[r][None], Hq, 1,
+                             scale=1.0 / np.sqrt(192.0))
+        t = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": 4 / t, "unit": "tokens/s", "cores": __import__("oracle").default_threads(),
+                                "kind": "oracle", "sample": f"4 decode tokens (all {Hq} heads), fp64 oracle, "
+                                                            f"{t:.1f} s including the latent gathers"}
+    return line
+
+
+# ---------------------------------------------------------------------------
 # multi-turn: 128 sessions, ~70% cached history, chunked prefill (512) + decode, page 16
 # ---------------------------------------------------------------------------
 def bench_multiturn(args):
@@ -895,7 +999,7 @@ def main():
         else:
             line["cpu_baseline"] = None
     else:
-        line = {"decode": bench_decode, "fork": bench_fork, "verify": bench_verify,
+        line = {"decode": bench_decode, "fork": bench_fork, "verify": bench_verify, "mla": bench_mla,
                 "multiturn": bench_multiturn}[args.config](args)
     print(json.dumps(line, default=lambda x: x.item() if hasattr(x, "item") else str(x)), flush=True)
 

@@ -352,6 +352,44 @@ int sgl_cascade_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, c
                                   void *o, float *lse, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/* ------------------------------------------------------------------------
+ * Latent (MLA-style) decode.  With the decompression matrices absorbed into
+ * the query and output projections, DeepSeek's MLA attention runs directly on
+ * the compressed latent ("Lecture 16 · 案例研究：SGLang" (semidirectx.com)
+ * section 4, "More engineering"): each token has ONE latent row of Dqk = 576
+ * dims (512 compressed K/V dims followed by 64 RoPE dims) shared by every
+ * query head; the score of head h is q_h . latent (all 576 dims) * scale and
+ * the value is the latent's first Dv = 512 dims.  It is grouped-query
+ * attention with one KV head whose value rows are a prefix of its key rows.
+ *   q: device bf16 [batch, Hq, 576], Hq a multiple of 16 up to 128;
+ *   kv_pool: device bf16 [num_slots, 576] (the latent of every slot);
+ *   kv_new: device bf16 [batch, 576] stored first at position seq_lens[r]-1,
+ *     or NULL;
+ *   o: device bf16 [batch, Hq, 512];  lse: device float32 [batch, Hq] or NULL;
+ *   scale multiplies q . latent (1/sqrt(192) for DeepSeek's 128 + 64 dims).
+ * Other arguments as sgl_decode_attn / sgl_cascade_decode_attn (the cascade's
+ * precondition on shared prefix slots applies).  Dqk must be 576 and Dv 512
+ * (else SGL_ERR_UNSUPPORTED).  Workspace: the sizes below.
+ * ---------------------------------------------------------------------- */
+int sgl_mla_decode_attn(const void *q, const void *kv_new, void *kv_pool, int64_t num_slots,
+                        const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                        const int32_t *req_rows, const int32_t *seq_lens, int32_t batch,
+                        int32_t max_seq_len, int32_t Hq, int32_t Dqk, int32_t Dv, float scale,
+                        void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+size_t sgl_mla_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq, int32_t Dv);
+int sgl_mla_cascade_decode_attn(const void *q, const void *kv_new, void *kv_pool, int64_t num_slots,
+                                const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                                const int32_t *req_rows, const int32_t *seq_lens,
+                                const int32_t *group_ptr, const int32_t *group_prefix_len,
+                                int32_t batch, int32_t G, int32_t max_seq_len,
+                                int32_t max_group_size, int32_t max_prefix_len,
+                                int32_t Hq, int32_t Dqk, int32_t Dv, float scale,
+                                void *o, float *lse, void *workspace, size_t workspace_bytes,
+                                void *stream);
+size_t sgl_mla_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
+                                      int32_t max_group_size, int32_t max_prefix_len,
+                                      int32_t Hq, int32_t Dv);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,6 +81,12 @@ def load():
         "sgl_cascade_decode_attn_fp8kv": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, P, P, I64, P,
                                                          I64, I64, P, P, P, P, I32, I32, I32, I32,
                                                          I32, I32, I32, I32, F, P, P, P, SZ, P]),
+        "sgl_mla_decode_attn": (ctypes.c_int, [P, P, P, I64, P, I64, I64, P, P, I32, I32, I32, I32, I32, F,
+                                               P, P, P, SZ, P]),
+        "sgl_mla_decode_workspace_size": (SZ, [I32, I32, I32, I32]),
+        "sgl_mla_cascade_decode_attn": (ctypes.c_int, [P, P, P, I64, P, I64, I64, P, P, P, P, I32, I32, I32,
+                                                       I32, I32, I32, I32, I32, F, P, P, P, SZ, P]),
+        "sgl_mla_cascade_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -97,7 +103,9 @@ EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_kv_pool_create", "sgl_kv
            "sgl_radix_lock_batch", "sgl_kv_pool_alloc_batch", "sgl_build_req_to_token", "sgl_store_kv",
            "sgl_extend_attn", "sgl_extend_workspace_size", "sgl_decode_attn",
            "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size",
-           "sgl_store_kv_fp8", "sgl_decode_attn_fp8kv", "sgl_cascade_decode_attn_fp8kv"]
+           "sgl_store_kv_fp8", "sgl_decode_attn_fp8kv", "sgl_cascade_decode_attn_fp8kv",
+           "sgl_mla_decode_attn", "sgl_mla_decode_workspace_size", "sgl_mla_cascade_decode_attn",
+           "sgl_mla_cascade_workspace_size"]
 
 
 def status_string(status: int) -> str:
@@ -480,6 +488,74 @@ def cascade_decode_attn_fp8kv(q, k_pool, v_pool, k_scale, v_scale, r2t, req_rows
         _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(group_ptr, "group_ptr", torch.int32),
         _dev_ptr(group_prefix_len, "group_prefix_len", torch.int32), B, G, max_seq_len,
         max_group_size, max_prefix_len, Hq, Hkv, D, scale, _dev_ptr(o, "o", q.dtype),
+        _dev_ptr(lse, "lse", torch.float32, True), _dev_ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+# ---------------------------------------------------------------------------
+# latent (MLA-style) decode: one latent row [576] per slot shared by all heads;
+# scores over 576 dims, values = the first 512
+# ---------------------------------------------------------------------------
+MLA_DQK, MLA_DV = 576, 512
+
+
+def mla_decode_workspace_size(batch, max_seq_len, Hq, Dv=MLA_DV):
+    return int(load().sgl_mla_decode_workspace_size(batch, max_seq_len, Hq, Dv))
+
+
+def mla_cascade_workspace_size(batch, G, max_seq_len, max_group_size, max_prefix_len, Hq, Dv=MLA_DV):
+    return int(load().sgl_mla_cascade_workspace_size(batch, G, max_seq_len, max_group_size, max_prefix_len, Hq, Dv))
+
+
+def _mla_out(q, o):
+    torch = _torch()
+    if o is None:
+        o = torch.empty((q.shape[0], q.shape[1], MLA_DV), dtype=q.dtype, device=q.device)
+    return o
+
+
+def mla_decode_attn(q, kv_pool, r2t, req_rows, seq_lens, max_seq_len, kv_new=None, scale=None, o=None, lse=None,
+                    workspace=None, stream=None):
+    """Latent decode; q bf16 [batch, Hq, 576], kv_pool bf16 [S, 576]; returns o [batch, Hq, 512]."""
+    torch = _torch()
+    B, Hq, Dqk = q.shape
+    o = _mla_out(q, o)
+    if scale is None:
+        scale = 1.0 / (192 ** 0.5)
+    ws_n = mla_decode_workspace_size(B, max_seq_len, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _check("sgl_mla_decode_attn", load().sgl_mla_decode_attn(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(kv_new, "kv_new", torch.bfloat16, True),
+        _dev_ptr(kv_pool, "kv_pool", torch.bfloat16), kv_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), B, max_seq_len, Hq, Dqk, MLA_DV, scale,
+        _dev_ptr(o, "o", torch.bfloat16), _dev_ptr(lse, "lse", torch.float32, True),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+def mla_cascade_decode_attn(q, kv_pool, r2t, req_rows, seq_lens, group_ptr, group_prefix_len, max_seq_len,
+                            max_group_size, max_prefix_len, kv_new=None, scale=None, o=None, lse=None,
+                            workspace=None, stream=None):
+    """Latent cascade decode (each group's shared prefix read once per 64 query rows); returns o."""
+    torch = _torch()
+    B, Hq, Dqk = q.shape
+    G = group_prefix_len.numel()
+    o = _mla_out(q, o)
+    if scale is None:
+        scale = 1.0 / (192 ** 0.5)
+    ws_n = mla_cascade_workspace_size(B, G, max_seq_len, max_group_size, max_prefix_len, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=q.device)
+    _check("sgl_mla_cascade_decode_attn", load().sgl_mla_cascade_decode_attn(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(kv_new, "kv_new", torch.bfloat16, True),
+        _dev_ptr(kv_pool, "kv_pool", torch.bfloat16), kv_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(group_ptr, "group_ptr", torch.int32),
+        _dev_ptr(group_prefix_len, "group_prefix_len", torch.int32), B, G, max_seq_len, max_group_size,
+        max_prefix_len, Hq, Dqk, MLA_DV, scale, _dev_ptr(o, "o", torch.bfloat16),
         _dev_ptr(lse, "lse", torch.float32, True), _dev_ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return o

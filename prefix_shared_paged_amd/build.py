@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libsgl_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["host_cache.cpp", "api.hip", "kernels_misc.hip", "kernels_f32.hip",
-           "kernels_decode.hip", "kernels_decode_rows.hip", "kernels_extend.hip"]
+           "kernels_decode.hip", "kernels_decode_rows.hip", "kernels_mla.hip", "kernels_extend.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,7 +32,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
 # would be copied to VGPRs and back around every such rescale, costing both
 # instructions and the registers that decide how many waves fit per CU.
 SOURCE_FLAGS = {"kernels_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-                "kernels_decode_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+                "kernels_decode_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+                "kernels_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src, verbose):

@@ -107,6 +107,20 @@ int32_t extend_splits(int32_t batch, int32_t Hkv) {
     return (int32_t)(n < 1 ? 1 : (n > 8 ? 8 : n));
 }
 
+// MLA latent decode: keys per split of the flat call and the suffix, and
+// the prefix split (halved down to 64 keys until about kPrefixWorkgroups
+// workgroups run; the row-block rule matches launch_split_mla).
+constexpr int kMlaChunk = 512;
+constexpr int kMlaDqk = 576, kMlaDv = 512;
+int mla_prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq) {
+    const int64_t rb = ceil_div64((int64_t)max_group_size * Hq, 16);
+    const int64_t rbw = rb >= 4 ? 4 : (rb >= 2 ? 2 : 1);
+    const int64_t units = (int64_t)G * ceil_div64(rb, rbw);
+    int c = kPrefixChunkMax;
+    while (c > kPrefixChunkMin && units * ceil_div64(max_prefix_len, c) < kPrefixWorkgroups) c /= 2;
+    return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -462,6 +476,144 @@ int sgl_cascade_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, c
                          r2t, num_rows, row_stride, req_rows, seq_lens, group_ptr, group_prefix_len, batch,
                          G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D, scale, o, lse,
                          workspace, workspace_bytes, stream);
+}
+
+// ---- MLA latent decode ---------------------------------------------------------
+size_t sgl_mla_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq, int32_t Dv) {
+    if (batch <= 0 || max_seq_len <= 0 || Hq <= 0 || Dv <= 0) return 0;
+    return part_bytes(batch, ceil_div64(max_seq_len, kMlaChunk), Hq, Dv);
+}
+
+size_t sgl_mla_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len, int32_t max_group_size,
+                                      int32_t max_prefix_len, int32_t Hq, int32_t Dv) {
+    if (batch <= 0 || max_seq_len <= 0 || G < 1 || max_group_size < 1 || Hq <= 0 || Dv <= 0) return 0;
+    const int64_t Sp = max_prefix_len > 0
+                           ? ceil_div64(max_prefix_len, mla_prefix_chunk(G, max_group_size, max_prefix_len, Hq))
+                           : 1;
+    return part_bytes(batch, Sp, Hq, Dv) + part_bytes(batch, ceil_div64(max_seq_len, kMlaChunk), Hq, Dv);
+}
+
+namespace {
+
+int mla_common(bool cascade, const void *q, const void *kv_new, void *kv_pool, int64_t num_slots,
+               const int32_t *r2t, int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+               const int32_t *seq_lens, const int32_t *group_ptr, const int32_t *group_prefix_len, int32_t batch,
+               int32_t G, int32_t max_seq_len, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq,
+               int32_t Dqk, int32_t Dv, float scale, void *o, float *lse, void *workspace, size_t workspace_bytes,
+               void *stream) {
+    if (Dqk != kMlaDqk || Dv != kMlaDv || Hq < 16 || Hq % 16 != 0 || Hq > 128) return SGL_ERR_UNSUPPORTED;
+    if (batch < 0 || max_seq_len < 0 || num_slots < 1 || num_rows < 0 || row_stride < 0) return SGL_ERR_INVALID;
+    if (batch == 0) return SGL_OK;
+    if (!q || !kv_pool || !r2t || !req_rows || !seq_lens || !o || max_seq_len < 1) return SGL_ERR_INVALID;
+    if (cascade) {
+        if (G < 1 || G > batch || !group_ptr || !group_prefix_len) return SGL_ERR_INVALID;
+        if (max_group_size < 1 || max_prefix_len < 0 || max_prefix_len > max_seq_len) return SGL_ERR_INVALID;
+        if ((int64_t)max_group_size * Hq > 4096) return SGL_ERR_UNSUPPORTED;
+    }
+    const size_t need = cascade ? sgl_mla_cascade_workspace_size(batch, G, max_seq_len, max_group_size,
+                                                                 max_prefix_len, Hq, Dv)
+                                : sgl_mla_decode_workspace_size(batch, max_seq_len, Hq, Dv);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return SGL_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_on()) {
+        std::vector<int32_t> rows, lens, tab, gptr, gpl;
+        if (!fetch(rows, req_rows, batch, st) || !fetch(lens, seq_lens, batch, st) ||
+            !fetch(tab, r2t, (size_t)(num_rows * row_stride), st))
+            return SGL_ERR_HIP;
+        for (int r = 0; r < batch; r++) {
+            if (rows[r] < 0 || rows[r] >= num_rows) return SGL_ERR_INVALID;
+            if (lens[r] < 1 || lens[r] > max_seq_len || lens[r] > row_stride) return SGL_ERR_INVALID;
+            if (!slots_ok(tab, row_stride, rows[r], 0, lens[r], num_slots)) return SGL_ERR_INVALID;
+        }
+        if (cascade) {
+            if (!fetch(gptr, group_ptr, G + 1, st) || !fetch(gpl, group_prefix_len, G, st)) return SGL_ERR_HIP;
+            if (gptr[0] != 0 || gptr[G] != batch) return SGL_ERR_INVALID;
+            for (int gg = 0; gg < G; gg++) {
+                const int a = gptr[gg], b = gptr[gg + 1];
+                if (b <= a || b - a > max_group_size || gpl[gg] < 0 || gpl[gg] > max_prefix_len) return SGL_ERR_INVALID;
+                for (int r = a; r < b; r++) {
+                    if (gpl[gg] > lens[r]) return SGL_ERR_INVALID;
+                    if (std::memcmp(&tab[(size_t)rows[r] * row_stride], &tab[(size_t)rows[a] * row_stride],
+                                    sizeof(int32_t) * (size_t)gpl[gg]) != 0)
+                        return SGL_ERR_INVALID;
+                }
+            }
+        }
+    }
+    int rc = SGL_OK;
+    if (kv_new) {   // one latent pool: the same rows serve as K and V
+        rc = launch_store_kv(2, 2, kv_new, kv_new, batch, nullptr, kv_pool, kv_pool, num_slots, 1, Dqk, r2t,
+                             num_rows, row_stride, req_rows, seq_lens, nullptr, batch, 0, st);
+        if (rc != SGL_OK) return rc;
+    }
+    char *wp = (char *)workspace;
+    SplitArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q; a.k_pool = kv_pool; a.v_pool = kv_pool; a.num_slots = num_slots; a.r2t = r2t;
+    a.num_rows = num_rows; a.row_stride = row_stride; a.req_rows = req_rows; a.seq_lens = seq_lens;
+    a.group_ptr = group_ptr; a.group_prefix_len = group_prefix_len; a.batch = batch; a.G = G;
+    a.Hq = Hq; a.Hkv = 1; a.D = Dqk; a.scale = scale;
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
+    m.batch = batch; m.G = G; m.Hq = Hq; m.D = Dv; m.out_bf16 = 1; m.o = o; m.lse = lse;
+    m.chunk_flat = kMlaChunk;
+    const int64_t Ss = ceil_div64(max_seq_len, kMlaChunk);
+    if (!cascade) {
+        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = kMlaChunk;
+        a.part = carve(wp, batch, Ss, Hq, Dv);
+        if ((rc = launch_split_mla(a, st)) != SGL_OK) return rc;
+        m.kind = 0; m.flat_or_suffix = a.part;
+        return launch_merge(m, st);
+    }
+    // A prefix-stage workgroup holds at most 64 query rows and reads the shared
+    // prefix once for them; a group with more rows would read it once per 64
+    // rows from workgroups of 16 waves, which measured slower than reading it
+    // once per request (128 requests in groups of 8 over 2-8k keys: 16 heads
+    // 253 vs 208 us, 128 heads 885 vs 805 us).  Such groups run the flat
+    // splits (same result).
+    if ((int64_t)max_group_size * Hq > 64) {
+        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = kMlaChunk;
+        a.part = carve(wp, batch, Ss, Hq, Dv);
+        if ((rc = launch_split_mla(a, st)) != SGL_OK) return rc;
+        m.kind = 0; m.flat_or_suffix = a.part;
+        return launch_merge(m, st);
+    }
+    const int pchunk = mla_prefix_chunk(G, max_group_size, max_prefix_len, Hq);
+    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pchunk) : 1;
+    SplitArgs pa = a;
+    pa.kind = 1; pa.chunk = pchunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size; pa.n_sets = G;
+    pa.part = carve(wp, batch, Sp, Hq, Dv);
+    SplitArgs sa = a;
+    sa.kind = 2; sa.chunk = kMlaChunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
+    sa.part = carve(wp, batch, Ss, Hq, Dv);
+    if (max_prefix_len > 0 && (rc = launch_split_mla(pa, st)) != SGL_OK) return rc;
+    if ((rc = launch_split_mla(sa, st)) != SGL_OK) return rc;
+    m.chunk_prefix = pchunk;
+    m.kind = max_prefix_len > 0 ? 3 : 0; m.prefix = pa.part; m.flat_or_suffix = sa.part;
+    return launch_merge(m, st);
+}
+
+}  // namespace
+
+int sgl_mla_decode_attn(const void *q, const void *kv_new, void *kv_pool, int64_t num_slots, const int32_t *r2t,
+                        int64_t num_rows, int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens,
+                        int32_t batch, int32_t max_seq_len, int32_t Hq, int32_t Dqk, int32_t Dv, float scale,
+                        void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    return mla_common(false, q, kv_new, kv_pool, num_slots, r2t, num_rows, row_stride, req_rows, seq_lens, nullptr,
+                      nullptr, batch, 0, max_seq_len, 0, 0, Hq, Dqk, Dv, scale, o, lse, workspace, workspace_bytes,
+                      stream);
+}
+
+int sgl_mla_cascade_decode_attn(const void *q, const void *kv_new, void *kv_pool, int64_t num_slots,
+                                const int32_t *r2t, int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                                const int32_t *seq_lens, const int32_t *group_ptr, const int32_t *group_prefix_len,
+                                int32_t batch, int32_t G, int32_t max_seq_len, int32_t max_group_size,
+                                int32_t max_prefix_len, int32_t Hq, int32_t Dqk, int32_t Dv, float scale, void *o,
+                                float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+    return mla_common(true, q, kv_new, kv_pool, num_slots, r2t, num_rows, row_stride, req_rows, seq_lens, group_ptr,
+                      group_prefix_len, batch, G, max_seq_len, max_group_size, max_prefix_len, Hq, Dqk, Dv, scale,
+                      o, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -143,6 +143,8 @@ int launch_split_fp8(const SplitArgs &a, hipStream_t st);
 // kinds 0 and 2 with one workgroup per (request, split) over all KV heads;
 // SGL_ERR_UNSUPPORTED for shapes left to the per-head kernels
 int launch_split_rows(const SplitArgs &a, bool fp8, hipStream_t st);
+// kinds 0-2 over a latent (MLA) cache: Hkv = 1, 576 score dims, 512 value dims
+int launch_split_mla(const SplitArgs &a, hipStream_t st);
 
 // Merge partial states of (optionally) a prefix buffer and a suffix buffer.
 //   kind 0: parts = flat splits of r;  kind 3: parts = prefix splits of group(r) for r

@@ -371,7 +371,10 @@ int launch_merge(const MergeArgs &a, hipStream_t st) {
     const int64_t items = (int64_t)a.batch * a.Hq;
     if (items == 0) return SGL_OK;
     dim3 grid((unsigned)ceil_div64(items, 4)), block(256);
-    if (a.D == 128) {
+    if (a.D == 512) {   // latent (MLA) values, bf16 only
+        if (!a.out_bf16) return SGL_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL((merge_kernel<512, true>), grid, block, 0, st, a);
+    } else if (a.D == 128) {
         if (a.out_bf16) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, st, a);
     } else {

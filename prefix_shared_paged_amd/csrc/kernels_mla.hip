@@ -1,0 +1,289 @@
+// kernels_mla.hip -- split-K decode over a latent KV cache (MLA-style).
+//
+// DeepSeek's MLA attention, with the decompression matrices absorbed into the
+// query and output projections, runs directly on the compressed latent: one
+// KV "head" per token of Dqk = 576 dims (512 compressed K/V dims + 64 RoPE
+// dims), scores over all 576, values over the first 512, shared by every
+// query head ("Lecture 16 · 案例研究：SGLang" (semidirectx.com) section 4).  So
+// it is grouped-query attention with one KV head, g = Hq, and K and V read
+// from the same rows: a token's latent is read once for both contractions.
+//
+// Layout: latent pool [num_slots, 576] bf16 (1152 bytes per token); q [.., Hq,
+// 576]; o [.., Hq, 512].  Work item (as in kernels_decode.hip): a split of
+// keys of a request (flat, suffix) or of a group's shared prefix (cascade),
+// and a block of up to 4 x 16 query rows (request x head).  Every 16-row block
+// gets four waves: wave q computes the partial S^T = K Q^T of the block over
+// its share of the 576 score dims (5, 5, 4, 4 MFMA steps of 32), the four
+// partial tiles are summed through LDS, and each wave then runs the softmax
+// and O^T += V^T P^T for its quarter of the 512 value dims -- so a wave holds
+// a fifth of Q and a quarter of O.  The waves share each 16-key latent tile
+// (18 KiB) in LDS, gathered by slot with non-temporal direct loads, two tiles
+// in flight.
+#include "common.h"
+#include "decode_util.h"
+
+namespace {
+
+using namespace sgl_decode;
+
+constexpr int MT = 16;          // keys per tile
+constexpr int DQK = 576;        // score dims
+constexpr int DV = 512;         // value dims
+constexpr int RB = DQK * 2;     // bytes per latent row
+constexpr int TBM = MT * RB;    // bytes per tile (18 KiB)
+constexpr int NIM = TBM / 1024; // 1 KiB direct-load instructions per tile (18)
+constexpr int MLA_DEPTH = 2;
+
+// Position of 16-byte chunk c of tile row r is c ^ msw(r), an XOR inside the
+// row's aligned groups of 8 chunks (72 chunks per row = 9 groups).  Rows are
+// 1152 bytes apart, so a chunk's LDS bank group (of 16) is 8 * (r % 2) +
+// position % 16: the swizzle spreads the 16 rows of a K operand read over
+// distinct bank groups.
+__device__ __forceinline__ int msw(int r) { return (r >> 1) & 7; }
+
+// RBW 16-row blocks per workgroup, four waves each
+template <int RBW>
+__global__ void __launch_bounds__(256 * RBW) split_mla_kernel(SplitArgs a) {
+    constexpr int NW = 4 * RBW;                    // waves per workgroup
+    constexpr int QS = 5;                          // MFMA k-steps of 32 dims per wave (at most)
+    constexpr int DBW = DV / 4 / 16;               // 8 16-dim output blocks per wave
+    __shared__ __attribute__((aligned(16))) unsigned char t_lds[MLA_DEPTH * TBM];
+    __shared__ __attribute__((aligned(16))) f32x4 s_part[RBW][4][64];   // partial S^T tiles
+    extern __shared__ int32_t slot_lds[];          // [chunk]
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rbw = w >> 2, quarter = w & 3;       // row block in the workgroup, dim quarter
+    const int t_lo = quarter * 5 - (quarter > 2 ? quarter - 2 : 0);   // first S^T step: 0, 5, 10, 14
+    const int n_st = quarter < 2 ? 5 : 4;          // S^T steps of this wave
+    auto wg_barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // ---- work item: set, split, rows (uniform over the workgroup) --------------
+    const int n_rbg = (a.row_blocks + RBW - 1) / RBW;
+    const int id = blockIdx.x;
+    const int rbg = id % n_rbg;
+    const int64_t item = id / n_rbg;               // = split * n_sets + set
+    const int set = (int)(item % a.n_sets);
+    const int s = (int)(item / a.n_sets);
+    if (s >= a.max_splits) return;
+    const int g = a.Hq;
+    int first_req, n_members;
+    int64_t lo, hi, ref_row;
+    if (a.kind == 1) {
+        first_req = a.group_ptr[set];
+        n_members = a.group_ptr[set + 1] - first_req;
+        if (n_members <= 0 || first_req < 0 || first_req + n_members > a.batch) return;
+        const int64_t P = a.group_prefix_len[set];
+        lo = 0;
+        hi = P < 0 ? 0 : P;
+        ref_row = a.req_rows[first_req];
+    } else {
+        first_req = set;
+        n_members = 1;
+        const int64_t L = a.seq_lens[set];
+        ref_row = a.req_rows[set];
+        lo = 0;
+        if (a.kind == 2) {
+            const int grp = find_group_dec(a.group_ptr, a.G, set);
+            const int64_t P = a.group_prefix_len[grp];
+            lo = P < 0 ? 0 : (P > L ? L : P);
+        }
+        hi = L;
+    }
+    if (n_members * g <= rbg * RBW * 16) return;
+    if (ref_row < 0 || ref_row >= a.num_rows) return;
+    if (hi > a.row_stride) hi = a.row_stride;
+    const int64_t n_split = ceil_div64(hi - lo, a.chunk);
+    if (s >= n_split || s >= a.part.S) return;
+    const int64_t k0 = lo + (int64_t)s * a.chunk;
+    const int nk = (int)((k0 + a.chunk < hi ? k0 + a.chunk : hi) - k0);
+    const int N = (nk + MT - 1) / MT;
+    const int row_base = (rbg * RBW + rbw) * 16;   // first query row of this wave's block
+    const int rows = n_members * g - row_base;     // may be <= 0: the wave still loads
+
+    const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
+    for (int j = threadIdx.x; j < nk; j += 64 * NW) slot_lds[j] = safe_slot(row[j], a.num_slots);
+
+    const int n16 = lane & 15, kq = lane >> 4;
+
+    // ---- Q^T operand of this wave's steps: lane (row n16, kq) holds dims
+    // 32(t_lo + t) + 8kq + i in step t
+    bf16x8 qf[QS];
+    {
+        const int rho = n16 < rows ? n16 : 0;
+        const int rr = row_base + rho < n_members * g ? row_base + rho : 0;
+        const __bf16 *src = (const __bf16 *)a.q + ((int64_t)(first_req + rr / g) * a.Hq + rr % g) * DQK +
+                            32 * t_lo + 8 * kq;
+#pragma unroll
+        for (int t = 0; t < QS; t++) qf[t] = t < n_st ? ld_q(src + 32 * t) : bf16x8{};
+        if (n16 >= rows)
+#pragma unroll
+            for (int t = 0; t < QS; t++) qf[t] = bf16x8{};
+    }
+
+    // ---- direct loads: instruction ii covers tile bytes [1024 ii, 1024 ii + 1024);
+    // wave w issues ii = w, w + NW, ... (the first NIM % NW waves one more)
+    constexpr int MAXI = (NIM + NW - 1) / NW;
+    int lrow[MAXI], lsrc[MAXI];
+#pragma unroll
+    for (int u = 0; u < MAXI; u++) {
+        const int ii = w + NW * u;
+        const int off = (ii < NIM ? ii : 0) * 1024 + 16 * lane;
+        lrow[u] = off / RB;
+        const int c = (off % RB) / 16;
+        lsrc[u] = 16 * (c ^ msw(lrow[u]));
+    }
+    const int n_mine = (NIM - w + NW - 1) / NW;    // instructions this wave issues per tile
+    const char *pool = (const char *)a.k_pool;
+
+    __syncthreads();   // slot table visible
+
+    auto issue = [&](int n, unsigned char *dst) {
+#pragma unroll
+        for (int u = 0; u < MAXI; u++) {
+            if (u < n_mine) {
+                const int kk = min(n * MT + lrow[u], nk - 1);
+                const char *src = pool + (int64_t)slot_lds[kk] * RB + lsrc[u];
+                __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                                 (SGL_LDS void *)(dst + (w + NW * u) * 1024), 16, 0, 2 /* nt */);
+            }
+        }
+    };
+    // byte offset of chunk c of tile row r
+    auto at = [&](int r, int c) { return r * RB + 16 * (c ^ msw(r)); };
+
+    f32x4 oacc[DBW];
+#pragma unroll
+    for (int db = 0; db < DBW; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float qscale = a.scale * kLog2e;
+    // K operand of step t: lane (key n16, kq) reads chunk 4t + kq of row n16
+    // V^T of 16-dim block db of this quarter: lane (r4, qq) of group kq reads 4
+    // dims of row 4kq + r4; the result gives lane (dim, kq) keys 4kq .. 4kq+3
+    const int r4 = n16 >> 2, qq = n16 & 3;
+    const int vr = kq * 4 + r4;
+
+    auto tile = [&](int n, const unsigned char *tb) {
+        const uint32_t base = lds_addr(tb);
+        // partial S^T over this wave's dims (the 5th step of a 4-step wave reads
+        // a real chunk and multiplies it by a zero Q operand)
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        {
+            uint32_t ad[QS];
+#pragma unroll
+            for (int t = 0; t < QS; t++) ad[t] = base + at(n16, 4 * min(t_lo + t, DQK / 32 - 1) + kq);
+            u32x4 raw[QS];
+            lds_read_raw128(raw, ad);
+#pragma unroll
+            for (int t = 0; t < QS; t++)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, raw[t]), qf[t], sacc, 0, 0,
+                                                               0);
+        }
+        // sum the row block's four partial tiles
+        s_part[rbw][quarter][lane] = sacc;
+        lgkm_wait0();
+        wg_barrier();
+        sacc = s_part[rbw][0][lane] + s_part[rbw][1][lane] + s_part[rbw][2][lane] + s_part[rbw][3][lane];
+        // online softmax (lazy reference maximum, as in kernels_decode.hip)
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float x = n * MT + kq * 4 + j < nk ? sacc[j] * qscale : -INFINITY;
+            sv[j] = x;
+            mx = fmaxf(mx, x);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const bool move = mx > m_run + 8.f;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float m_new = move ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DBW; db++) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        bf16x4 pf;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_run);
+            l_run += pj;
+            pf[j] = (__bf16)pj;
+        }
+        uint32_t ad[DBW];
+#pragma unroll
+        for (int db = 0; db < DBW; db++)
+            ad[db] = base + at(vr, quarter * 16 + 2 * db + (qq >> 1)) + 8 * (qq & 1);
+        i16x4 vt[DBW];
+        lds_read_tr16(vt, ad);
+#pragma unroll
+        for (int db = 0; db < DBW; db++)
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[db], __builtin_bit_cast(i16x4, pf), oacc[db],
+                                                                 0, 0, 0);
+    };
+
+    // ring of MLA_DEPTH tiles: this wave's loads of tile n have landed when
+    // only the later tile's remain (their count is this wave's n_mine)
+    for (int t = 0; t < MLA_DEPTH && t < N; t++) issue(t, t_lds + (t % MLA_DEPTH) * TBM);
+    for (int n = 0; n < N; n++) {
+        if (n + 1 < N) {
+            if (n_mine == 5) vm_wait<5>();
+            else if (n_mine == 4) vm_wait<4>();
+            else if (n_mine == 3) vm_wait<3>();
+            else if (n_mine == 2) vm_wait<2>();
+            else if (n_mine == 1) vm_wait<1>();
+            else vm_wait<0>();
+        } else {
+            vm_wait<0>();
+        }
+        wg_barrier();
+        unsigned char *tb = t_lds + (n % MLA_DEPTH) * TBM;
+        tile(n, tb);
+        if (n + MLA_DEPTH < N) {
+            lgkm_wait0();
+            wg_barrier();                              // every wave is done with this buffer
+            issue(n + MLA_DEPTH, tb);
+        }
+    }
+
+    // ---- the split's state: (m, l) by quarter 0, o by every quarter ------------
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (n16 >= rows) return;
+    const int rr = row_base + n16;
+    const int req = first_req + rr / g;
+    const int h = rr % g;
+    const int64_t idx = ((int64_t)req * a.part.S + s) * a.Hq + h;
+    float *op = a.part.o + idx * DV + quarter * (DV / 4);
+#pragma unroll
+    for (int db = 0; db < DBW; db++) *(f32x4 *)(op + db * 16 + kq * 4) = oacc[db];
+    if (quarter == 0 && kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
+}
+
+}  // namespace
+
+// Flat (kind 0), prefix (kind 1) and suffix (kind 2) splits over a latent
+// cache: Hkv = 1, D = 576 scores / 512 values, Hq a multiple of 16.
+int launch_split_mla(const SplitArgs &a0, hipStream_t st) {
+    if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
+    if (a0.chunk % MT != 0 || a0.Hq % 16 != 0 || a0.Hkv != 1) return SGL_ERR_INVALID;
+    SplitArgs a = a0;
+    const int rows = (a.kind == 1 ? a.max_members : 1) * a.Hq;
+    a.row_blocks = (rows + 15) / 16;
+    const int rbw = a.row_blocks >= 4 ? 4 : (a.row_blocks >= 2 ? 2 : 1);
+    const int n_rbg = (a.row_blocks + rbw - 1) / rbw;
+    const int64_t n_wg = (int64_t)a.n_sets * a.max_splits * n_rbg;
+    if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+    const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
+    const dim3 grid((unsigned)n_wg), block(256 * rbw);
+    if (rbw == 4) hipLaunchKernelGGL((split_mla_kernel<4>), grid, block, dyn, st, a);
+    else if (rbw == 2) hipLaunchKernelGGL((split_mla_kernel<2>), grid, block, dyn, st, a);
+    else hipLaunchKernelGGL((split_mla_kernel<1>), grid, block, dyn, st, a);
+    return hip_status(hipGetLastError());
+}

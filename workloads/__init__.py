@@ -22,6 +22,9 @@ Values: the shapes and distributions are those of the five workloads:
   verify    bf16, 64 requests, own cached contexts ~U[2048, 8192], q_len new
             tokens each (2-16: the verify step of speculative decoding),
             32/8/128, 2^20 slots
+  mla       bf16, 128 requests in 16 prefix groups of 8, prefix ~U[512,4096],
+            context ~U[max(1024,P+1),8192], one 576-dim latent row per token
+            (values: its first 512 dims), 128 (or 16) query heads, 2^21 slots
   multiturn bf16, 128 sessions, history ~ lognormal(median 3000, sigma 1)
             clamped to [32, 32768], cached 16*floor(0.7 H / 16), chunks of
             512, page size 16, 64/8/128, 2^20 slots
@@ -210,6 +213,19 @@ def verify(seed=0, B=64, q_len=4, p_lo=2048, p_hi=8192, Hq=32, Hkv=8, D=128, num
     spec = Spec("verify", "bf16", Hq, Hkv, D, 1, num_slots, 0.5, seed, extra={"q_len": q_len})
     P = rng(seed, T_LEN).integers(p_lo, p_hi + 1, size=B).astype(np.int64)
     return GroupWorkload(spec, P, np.arange(B, dtype=np.int64), np.zeros(B, np.int64), P + q_len)
+
+
+def mla(seed=0, G=16, per_group=8, p_lo=512, p_hi=4096, l_lo=1024, l_hi=8192, Hq=128, num_slots=1 << 21):
+    """Latent (MLA-style) decode batch: G*per_group requests in G prefix groups,
+    one latent row of 576 dims per token (D holds 576; values are its first 512),
+    Hq query heads over one KV head."""
+    spec = Spec("mla", "bf16", Hq, 1, 576, 1, num_slots, 0.5, seed, extra={"Dv": 512})
+    r = rng(seed, T_LEN)
+    P = r.integers(p_lo, p_hi + 1, size=G)
+    grp = np.repeat(np.arange(G), per_group)
+    sib = np.tile(np.arange(per_group), G)
+    L = np.array([r.integers(max(l_lo, P[g] + 1), l_hi + 1) for g in grp], np.int64)
+    return GroupWorkload(spec, P.astype(np.int64), grp, sib, L)
 
 
 # ---------------------------------------------------------------------------
