@@ -22,7 +22,8 @@ before the timed region.  Prints ONE JSON line.
 
 Other --config values time the decode-batch, fork-sweep, verify (small-q
 extend: q_len new tokens per request over long cached contexts), mla (latent
-decode: one 576-dim latent row per token shared by every query head) and
+decode: one 576-dim latent row per token shared by every query head),
+hicache (KV rows moved between a page-locked host tier and the pool) and
 multi-turn workloads for reporting; their lines have the same shape.  --kv fp8 runs the
 decode and fork workloads over an FP8 (e4m3fn) KV cache with per-head
 factors (the same bf16 queries, bf16 MFMA arithmetic, one byte per cached
@@ -42,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PEAK_HOST_LINK_GBPS = 63.0     # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b
 
 
 def parse():
@@ -50,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="extend",
-                    choices=["extend", "decode", "fork", "verify", "mla", "multiturn"])
+                    choices=["extend", "decode", "fork", "verify", "mla", "hicache", "multiturn"])
     ap.add_argument("--mla-heads", type=int, default=128, help="query heads of the mla workload")
     ap.add_argument("--q-len", type=int, default=4, help="new tokens per request of the verify workload")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
@@ -861,6 +863,82 @@ def bench_mla(args):
 
 
 # ---------------------------------------------------------------------------
+# hicache: one layer's K/V rows of 65,536 tokens between a pinned host tier and the pool
+# ---------------------------------------------------------------------------
+def bench_hicache(args):
+    import torch
+    import prefix_shared_paged_amd as sp
+
+    Hkv, D, num_slots, n_host, n = 8, 128, 1 << 20, 1 << 18, 65536
+    dev = "cuda"
+    rng = np.random.default_rng(0)
+    pools = [torch.empty((num_slots, Hkv, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    for i, p in enumerate(pools):
+        fill_random(p, seed=i + 1)
+    hosts = [torch.full((n_host, Hkv, D), 0.25 * (i + 1), dtype=torch.bfloat16, pin_memory=True) for i in range(2)]
+    # 32 prefixes of 2048 tokens whose rows are scattered over the host tier
+    # and the pool (page size 1)
+    slots = torch.from_numpy(rng.permutation(num_slots)[:n].astype(np.int32)).to(dev)
+    hrows = torch.from_numpy(rng.permutation(n_host)[:n].astype(np.int64)).to(dev)
+    row_bytes = Hkv * D * 2
+    moved = 2 * n * row_bytes + n * (4 + 8)               # K and V rows + the two index arrays
+    pre = lambda: sp.hicache_prefetch(hosts[0], hosts[1], hrows, slots, pools[0], pools[1])
+    wb = lambda: sp.hicache_write_back(pools[0], pools[1], slots, hrows, hosts[0], hosts[1])
+    # the host link's practical ceiling: one DMA copy of the same bytes, contiguous
+    dma_src = torch.empty(2 * n * row_bytes, dtype=torch.uint8, pin_memory=True)
+    dma_dst = torch.empty(2 * n * row_bytes, dtype=torch.uint8, device=dev)
+    dma = lambda: dma_dst.copy_(dma_src, non_blocking=True)
+    res = {}
+    for name, fn in (("prefetch", pre), ("write_back", wb), ("dma_h2d", dma)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        res[name] = ((time.perf_counter() - t0) * 1e3 / args.steps, float(np.mean([a.elapsed_time(b) for a, b in evs])))
+    ms, call = res["prefetch"]
+    gbps = moved / (call * 1e-3) / 1e9
+    wb_gbps = moved / (res["write_back"][1] * 1e-3) / 1e9
+    dma_gbps = 2 * n * row_bytes / (res["dma_h2d"][1] * 1e-3) / 1e9
+    config = {"workload": "hicache prefetch: K and V rows of 65,536 tokens (32 prefixes of 2048) of one layer "
+                          "(8 KV heads x 128, bf16: 4 KiB per token) gathered from a 2^18-row page-locked host tier "
+                          "into a 2^20-slot pool, rows scattered on both sides (page 1)",
+              "tokens": n, "Hkv": Hkv, "D": D}
+    roof = {"bound": "host-link", "achieved": gbps, "peak": PEAK_HOST_LINK_GBPS, "unit": "GB/s",
+            "frac": gbps / PEAK_HOST_LINK_GBPS, "traffic": None, "kernel": "move_rows_kernel<0> (prefetch)",
+            "bytes_per_launch": moved, "avg_launch_ms": call}
+    line = base_line(n / (ms * 1e-3), ms, args, config, roof, {
+        "write_back": {"call_ms": res["write_back"][1], "gbps": wb_gbps, "frac": wb_gbps / PEAK_HOST_LINK_GBPS},
+        "dma_h2d_contiguous": {"call_ms": res["dma_h2d"][1], "gbps": dma_gbps}})
+    if not args.no_cpu_baseline:
+        from oracle import hicache
+        k = 4096
+        host_np = hosts[0][:n_host].view(torch.int16).numpy()
+        pool_np = np.zeros((8192, Hkv, D), np.int16)
+        hr = hrows[:k].cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            hicache.load(pool_np, host_np, hr, np.arange(k))
+            hicache.load(pool_np, host_np, hr, np.arange(k))   # the V tier
+            reps += 1
+            if time.perf_counter() - t0 > min(args.cpu_seconds, 5.0):
+                break
+        t = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": reps * k / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{reps} x {k} tokens (K and V rows) gathered by the oracle's row loop "
+                                          f"from the pinned host tier into an 8192-row array, {t:.1f} s"}
+    return line
+
+
+# ---------------------------------------------------------------------------
 # multi-turn: 128 sessions, ~70% cached history, chunked prefill (512) + decode, page 16
 # ---------------------------------------------------------------------------
 def bench_multiturn(args):
@@ -985,8 +1063,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part "
-              "of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not "
+              "supported", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -1000,6 +1078,7 @@ def main():
             line["cpu_baseline"] = None
     else:
         line = {"decode": bench_decode, "fork": bench_fork, "verify": bench_verify, "mla": bench_mla,
+                "hicache": bench_hicache,
                 "multiturn": bench_multiturn}[args.config](args)
     print(json.dumps(line, default=lambda x: x.item() if hasattr(x, "item") else str(x)), flush=True)
 

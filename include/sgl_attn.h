@@ -390,6 +390,46 @@ size_t sgl_mla_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_
                                       int32_t max_group_size, int32_t max_prefix_len,
                                       int32_t Hq, int32_t Dv);
 
+/* ----------------------------------------------------------------------
+ * Host tier of the KV cache (HiCache).  KV rows that leave the GPU pool are
+ * kept in a larger page-locked host-memory tier and brought back into pool
+ * slots when a later request matches them ("SGLang：从前端 DSL 到 SRT 服务运行时",
+ * section "从 2024 年论文到今天的缓存栈", the HiCache bullet: GPU memory is the
+ * first tier, host memory the second; a prefix matched in a lower tier is
+ * prefetched, and rows are written back).  The pages give no layout; here a
+ * host row has exactly the pool's row layout (Hkv * D elements of the pool's
+ * dtype, or one latent row), so both moves copy bytes unchanged.
+ *
+ *   sgl_hicache_prefetch:   for i < n:  pool[slots[i]] <- host[host_rows[i]]
+ *   sgl_hicache_write_back: for i < n:  host[host_rows[i]] <- pool[slots[i]]
+ *
+ * Each tensor pair (K and V; or only K with host_v = v_pool = NULL for a
+ * single latent pool) moves row_bytes bytes per row; row_bytes must be a
+ * positive multiple of 16 (bf16 Hkv*D*2, fp8 Hkv*D, latent 576*2).
+ *   host_k, host_v: PAGE-LOCKED host memory (hipHostMalloc, or a pinned
+ *     torch tensor) of n_host_rows rows; the call checks that the whole
+ *     range is page-locked and mapped for the device, else SGL_ERR_INVALID.
+ *     The kernel reads or writes it directly over the host link.
+ *   k_pool, v_pool: device [num_slots] rows;
+ *   host_rows: device int64 [n];  slots: device int32 [n];
+ *   all four buffers 16-byte aligned.
+ * Destinations must be distinct (slots for a prefetch, host_rows for a
+ * write-back); sources may repeat.  A move whose host row or slot lies
+ * outside its buffer is skipped (no access is made); with
+ * SGL_ATTN_VALIDATE=1 such indices, and repeated destinations, return
+ * SGL_ERR_INVALID before anything is launched.  Stream-ordered: the caller
+ * synchronises before reading the host tier after a write-back.  n = 0 is a
+ * no-op.
+ * ---------------------------------------------------------------------- */
+int sgl_hicache_prefetch(const void *host_k, const void *host_v, int64_t n_host_rows,
+                         const int64_t *host_rows, const int32_t *slots, int64_t n,
+                         void *k_pool, void *v_pool, int64_t num_slots, int64_t row_bytes,
+                         void *stream);
+int sgl_hicache_write_back(const void *k_pool, const void *v_pool, int64_t num_slots,
+                           const int32_t *slots, const int64_t *host_rows, int64_t n,
+                           void *host_k, void *host_v, int64_t n_host_rows, int64_t row_bytes,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

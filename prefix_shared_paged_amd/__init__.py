@@ -87,6 +87,8 @@ def load():
         "sgl_mla_cascade_decode_attn": (ctypes.c_int, [P, P, P, I64, P, I64, I64, P, P, P, P, I32, I32, I32,
                                                        I32, I32, I32, I32, I32, F, P, P, P, SZ, P]),
         "sgl_mla_cascade_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32]),
+        "sgl_hicache_prefetch": (ctypes.c_int, [P, P, I64, P, P, I64, P, P, I64, I64, P]),
+        "sgl_hicache_write_back": (ctypes.c_int, [P, P, I64, P, P, I64, P, P, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -105,7 +107,7 @@ EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_kv_pool_create", "sgl_kv
            "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size",
            "sgl_store_kv_fp8", "sgl_decode_attn_fp8kv", "sgl_cascade_decode_attn_fp8kv",
            "sgl_mla_decode_attn", "sgl_mla_decode_workspace_size", "sgl_mla_cascade_decode_attn",
-           "sgl_mla_cascade_workspace_size"]
+           "sgl_mla_cascade_workspace_size", "sgl_hicache_prefetch", "sgl_hicache_write_back"]
 
 
 def status_string(status: int) -> str:
@@ -559,3 +561,46 @@ def mla_cascade_decode_attn(q, kv_pool, r2t, req_rows, seq_lens, group_ptr, grou
         _dev_ptr(lse, "lse", torch.float32, True), _dev_ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return o
+
+
+def _tier_args(host_k, host_v, k_pool, v_pool):
+    """Check a host tier against its pool; returns (host_k, host_v, k_pool, v_pool) pointers and row bytes."""
+    if (host_v is None) != (v_pool is None):
+        raise ValueError("host_v and v_pool go together (both or neither)")
+    for h, p, name in ((host_k, k_pool, "k"), (host_v, v_pool, "v")):
+        if h is None:
+            continue
+        if h.is_cuda or not h.is_pinned():
+            raise ValueError(f"host_{name} must be a page-locked (pinned) CPU tensor")
+        if not h.is_contiguous() or not p.is_contiguous():
+            raise ValueError(f"host_{name} and the pool must be contiguous")
+        if h.dtype != p.dtype or tuple(h.shape[1:]) != tuple(p.shape[1:]):
+            raise ValueError(f"host_{name} rows must have the pool's row shape and dtype")
+    if host_v is not None and (host_v.shape[0] != host_k.shape[0] or v_pool.shape[0] != k_pool.shape[0]):
+        raise ValueError("K and V tiers (and pools) must have the same number of rows")
+    row_bytes = k_pool[0].numel() * k_pool.element_size()
+    hv = None if host_v is None else ctypes.c_void_p(host_v.data_ptr())
+    return (ctypes.c_void_p(host_k.data_ptr()), hv, _dev_ptr(k_pool, "k_pool"),
+            _dev_ptr(v_pool, "v_pool", None, True), row_bytes)
+
+
+def hicache_prefetch(host_k, host_v, host_rows, slots, k_pool, v_pool=None, stream=None):
+    """pool[slots[i]] <- host[host_rows[i]] (host tier -> GPU pool), for K and V (or one latent tier)."""
+    torch = _torch()
+    hk, hv, kp, vp, row_bytes = _tier_args(host_k, host_v, k_pool, v_pool)
+    if host_rows.numel() != slots.numel():
+        raise ValueError("host_rows and slots must have the same length")
+    _check("sgl_hicache_prefetch", load().sgl_hicache_prefetch(
+        hk, hv, host_k.shape[0], _dev_ptr(host_rows, "host_rows", torch.int64),
+        _dev_ptr(slots, "slots", torch.int32), slots.numel(), kp, vp, k_pool.shape[0], row_bytes, _stream(stream)))
+
+
+def hicache_write_back(k_pool, v_pool, slots, host_rows, host_k, host_v=None, stream=None):
+    """host[host_rows[i]] <- pool[slots[i]] (GPU pool -> host tier); synchronise before reading the host tier."""
+    torch = _torch()
+    hk, hv, kp, vp, row_bytes = _tier_args(host_k, host_v, k_pool, v_pool)
+    if host_rows.numel() != slots.numel():
+        raise ValueError("host_rows and slots must have the same length")
+    _check("sgl_hicache_write_back", load().sgl_hicache_write_back(
+        kp, vp, k_pool.shape[0], _dev_ptr(slots, "slots", torch.int32), _dev_ptr(host_rows, "host_rows", torch.int64),
+        slots.numel(), hk, hv, host_k.shape[0], row_bytes, _stream(stream)))

@@ -1,6 +1,8 @@
 // api.hip -- C-ABI device entry points of libsgl_attn: argument checks,
 // optional host-side validation of index metadata, workspace layout, and the
 // kernel launches.  See include/sgl_attn.h for the contract.
+#include <algorithm>
+#include <climits>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -137,7 +139,7 @@ const char *sgl_status_string(int status) {
     }
 }
 
-int sgl_abi_version(void) { return 2; }
+int sgl_abi_version(void) { return 3; }
 
 int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
                            const int32_t *req_rows, int32_t batch, const int32_t *prefix_slots,
@@ -614,6 +616,88 @@ int sgl_mla_cascade_decode_attn(const void *q, const void *kv_new, void *kv_pool
     return mla_common(true, q, kv_new, kv_pool, num_slots, r2t, num_rows, row_stride, req_rows, seq_lens, group_ptr,
                       group_prefix_len, batch, G, max_seq_len, max_group_size, max_prefix_len, Hq, Dqk, Dv, scale,
                       o, lse, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// The device-visible address of a caller's host-tier buffer, after checking
+// that every one of its `bytes` bytes is page-locked host memory mapped for
+// the device (a kernel touching pageable memory would fault).
+int host_tier_addr(const void *p, size_t bytes, char **dev) {
+    hipPointerAttribute_t a, b;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return SGL_ERR_INVALID;
+    }
+    if (a.type != hipMemoryTypeHost || a.devicePointer == nullptr) return SGL_ERR_INVALID;
+    if (hipPointerGetAttributes(&b, (const char *)p + (bytes - 1)) != hipSuccess) {
+        (void)hipGetLastError();
+        return SGL_ERR_INVALID;
+    }
+    if (b.type != hipMemoryTypeHost || (char *)b.devicePointer != (char *)a.devicePointer + (bytes - 1))
+        return SGL_ERR_INVALID;
+    *dev = (char *)a.devicePointer;
+    return SGL_OK;
+}
+
+// dir 0: host rows -> pool slots; dir 1: pool slots -> host rows.
+int hicache_move(int dir, const void *host_k, const void *host_v, int64_t n_host_rows, const int64_t *host_rows,
+                 const int32_t *slots, int64_t n, const void *k_pool, const void *v_pool, int64_t num_slots,
+                 int64_t row_bytes, hipStream_t st) {
+    if (n < 0 || n_host_rows < 0 || num_slots < 0 || row_bytes <= 0 || row_bytes % 16 != 0) return SGL_ERR_INVALID;
+    if (n == 0) return SGL_OK;
+    if (!host_k || !k_pool || !host_rows || !slots || n_host_rows == 0 || num_slots == 0) return SGL_ERR_INVALID;
+    if ((host_v == nullptr) != (v_pool == nullptr)) return SGL_ERR_INVALID;
+    if (((uintptr_t)host_k | (uintptr_t)host_v | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15) return SGL_ERR_INVALID;
+    if (n_host_rows > INT64_MAX / row_bytes || num_slots > INT64_MAX / row_bytes) return SGL_ERR_INVALID;
+    const size_t bytes = (size_t)(n_host_rows * row_bytes);
+    char *hk = nullptr, *hv = nullptr;
+    int rc;
+    if ((rc = host_tier_addr(host_k, bytes, &hk)) != SGL_OK) return rc;
+    if (host_v && (rc = host_tier_addr(host_v, bytes, &hv)) != SGL_OK) return rc;
+    if (validate_on()) {
+        std::vector<int64_t> h;
+        std::vector<int32_t> s;
+        if (!fetch(h, host_rows, (size_t)n, st) || !fetch(s, slots, (size_t)n, st)) return SGL_ERR_HIP;
+        std::vector<int64_t> dst(n);
+        for (int64_t i = 0; i < n; ++i) {
+            if (h[i] < 0 || h[i] >= n_host_rows || s[i] < 0 || s[i] >= num_slots) return SGL_ERR_INVALID;
+            dst[i] = dir == 0 ? s[i] : h[i];
+        }
+        std::sort(dst.begin(), dst.end());
+        if (std::adjacent_find(dst.begin(), dst.end()) != dst.end()) return SGL_ERR_INVALID;
+    }
+    MoveArgs a;
+    const char *pk = (const char *)k_pool, *pv = (const char *)v_pool;
+    a.src[0] = dir == 0 ? hk : pk;
+    a.src[1] = dir == 0 ? hv : pv;
+    a.dst[0] = dir == 0 ? (char *)pk : hk;
+    a.dst[1] = dir == 0 ? (char *)pv : hv;
+    a.host_rows = host_rows;
+    a.slots = slots;
+    a.n = n;
+    a.n_host_rows = n_host_rows;
+    a.num_slots = num_slots;
+    a.row_bytes = row_bytes;
+    a.cpr = row_bytes / 16;
+    a.n_t = host_v ? 2 : 1;
+    return launch_move_rows(dir, a, st);
+}
+
+}  // namespace
+
+int sgl_hicache_prefetch(const void *host_k, const void *host_v, int64_t n_host_rows, const int64_t *host_rows,
+                         const int32_t *slots, int64_t n, void *k_pool, void *v_pool, int64_t num_slots,
+                         int64_t row_bytes, void *stream) {
+    return hicache_move(0, host_k, host_v, n_host_rows, host_rows, slots, n, k_pool, v_pool, num_slots, row_bytes,
+                        (hipStream_t)stream);
+}
+
+int sgl_hicache_write_back(const void *k_pool, const void *v_pool, int64_t num_slots, const int32_t *slots,
+                           const int64_t *host_rows, int64_t n, void *host_k, void *host_v, int64_t n_host_rows,
+                           int64_t row_bytes, void *stream) {
+    return hicache_move(1, host_k, host_v, n_host_rows, host_rows, slots, n, k_pool, v_pool, num_slots, row_bytes,
+                        (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -167,3 +167,18 @@ struct MergeArgs {
     int32_t n_req, n_spl;
 };
 int launch_merge(const MergeArgs &a, hipStream_t st);
+
+// Row moves between a page-locked host tier and the pool (kernels_hicache.hip).
+// Row move i pairs host row host_rows[i] with pool slot slots[i]; tensor t
+// (0 = K, 1 = V; n_t = 1 for a single latent pool) moves row_bytes bytes
+// (cpr = row_bytes / 16 chunks of 16 bytes).  dir 0: host -> pool, dir 1:
+// pool -> host.  src/dst hold the host tier's device-visible addresses.
+struct MoveArgs {
+    const char *src[2];
+    char *dst[2];
+    const int64_t *host_rows;
+    const int32_t *slots;
+    int64_t n, n_host_rows, num_slots, row_bytes, cpr;
+    int n_t;
+};
+int launch_move_rows(int dir, const MoveArgs &a, hipStream_t st);

@@ -20,7 +20,7 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(sgl_[a-z0-9_]+)\s*\(", src)))
 
 
-def test_header_declares_the_north_star_calls():
+def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for n in ["sgl_kv_pool_alloc", "sgl_build_req_to_token", "sgl_extend_attn", "sgl_decode_attn",
               "sgl_cascade_decode_attn"]:
@@ -112,6 +112,20 @@ def test_device_calls_reject_bad_arguments_before_gpu_work():
                                 None) == sp.SGL_ERR_UNSUPPORTED
     # FP8 KV: empty store is a no-op
     assert lib.sgl_store_kv_fp8(sp.SGL_F32, p, p, 0, p, p, p, 16, 8, 128, p, p, None) == sp.SGL_OK
+    # host tier: row bytes not a positive multiple of 16, negative count, K/V pairing, alignment, nulls
+    pf, wb = lib.sgl_hicache_prefetch, lib.sgl_hicache_write_back
+    q = _fake(4)
+    mis = ctypes.c_void_p(q.value + 8)
+    assert pf(q, q, 8, q, q, 4, q, q, 8, 15, None) == sp.SGL_ERR_INVALID
+    assert pf(q, q, 8, q, q, 4, q, q, 8, 0, None) == sp.SGL_ERR_INVALID
+    assert pf(q, q, 8, q, q, -1, q, q, 8, 16, None) == sp.SGL_ERR_INVALID
+    assert pf(q, q, 8, q, q, 4, q, None, 8, 16, None) == sp.SGL_ERR_INVALID
+    assert pf(mis, None, 8, q, q, 4, q, None, 8, 16, None) == sp.SGL_ERR_INVALID
+    assert pf(q, None, 8, None, q, 4, q, None, 8, 16, None) == sp.SGL_ERR_INVALID
+    assert wb(q, q, 8, q, q, 4, q, q, 0, 16, None) == sp.SGL_ERR_INVALID
+    assert wb(q, None, 8, q, q, 4, q, q, 8, 16, None) == sp.SGL_ERR_INVALID
+    assert wb(q, q, 8, q, q, 0, q, q, 8, 16, None) == sp.SGL_OK
+    assert pf(None, None, 8, None, None, 0, None, None, 8, 16, None) == sp.SGL_OK
 
 
 def test_workspace_sizes_grow_with_the_problem():
