@@ -238,7 +238,7 @@ def bench_extend(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    ext_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_ext]))
+    ext_ms, ext_stalls = event_mean_ms(ev_ext)
 
     # decode-only timings (flat vs cascade) on the same state, outside the step
     def time_call(fn, n=20):
@@ -293,7 +293,8 @@ def bench_extend(args):
                    "batch": B, "prefix": P, "new_tokens": E, "Hq": Hq, "Hkv": Hkv, "head_dim": D},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "extend_bf16_kernel", "flops_per_launch": flops, "avg_launch_ms": ext_ms},
+                     "kernel": "extend_bf16_kernel", "flops_per_launch": flops, "avg_launch_ms": ext_ms,
+                     "host_stalled_launches_excluded": ext_stalls},
         "extend_tflops": tflops,
         "decode": {"flat_ms": flat_ms, "cascade_ms": casc_ms,
                    "flat_hbm_gbps": flat_bytes / (flat_ms * 1e-3) / 1e9,
@@ -410,6 +411,17 @@ def setup_groups(cache, wl, store_prefix=False):
         cache.release(st)
 
 
+def event_mean_ms(ev):
+    """Mean HIP-event time of the timed calls (pairs recorded around each call
+    on its stream).  When the host stalls between recording the first event
+    and launching the call, the GPU idles and the pair measures the stall; a
+    call timed at more than 4x the median is such a case: it is left out of
+    the mean and counted (second result)."""
+    t = np.array([a.elapsed_time(b) for a, b in ev], np.float64)
+    keep = t <= 4.0 * float(np.median(t))
+    return float(t[keep].mean()), int((~keep).sum())
+
+
 def time_events(fn, n, warm=3):
     import torch
     for _ in range(warm):
@@ -520,8 +532,7 @@ def bench_decode(args):
         for _ in range(args.steps):
             step(mode == "cascade", True)
         torch.cuda.synchronize()
-        res[mode] = ((time.perf_counter() - t0) * 1e3 / args.steps,
-                     float(np.mean([a.elapsed_time(b) for a, b in ev])))
+        res[mode] = ((time.perf_counter() - t0) * 1e3 / args.steps, event_mean_ms(ev)[0])
     kelt = 1 if fp8 else 2
     flat_bytes = acc.decode_bytes_flat(L, Hq, Hkv, D, kelt, 2)
     casc_bytes = acc.decode_bytes_cascade(L, wl.grp, wl.prefix_len, Hq, Hkv, D, kelt, 2)
@@ -737,7 +748,7 @@ def bench_verify(args):
         step(True)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    call = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    call, stalls = event_mean_ms(ev)
     byts = acc.decode_bytes_flat(P + E, Hq, Hkv, D, 2) + (E - 1) * 2 * B * Hq * D * 2
     gbps = byts / (call * 1e-3) / 1e9
     config = {"workload": f"verify (small-q extend): {B} requests, own cached contexts ~U[2048,8192], {E} new "
@@ -747,7 +758,7 @@ def bench_verify(args):
     roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
             "traffic": None, "kernel": "extend call (split kernel + merge, or the prefill kernel)",
             "bytes_per_launch": byts, "avg_launch_ms": call}
-    line = base_line(n / (ms * 1e-3), ms, args, config, roof, {"call_ms": call,
+    line = base_line(n / (ms * 1e-3), ms, args, config, roof, {"call_ms": call, "host_stalled_calls_excluded": stalls,
                                                                 "tokens_per_s_call_only": n / (call * 1e-3)})
     if not args.no_cpu_baseline:
         Ks, Vs, rws = [], [], []
@@ -822,7 +833,7 @@ def bench_mla(args):
             b.record()
             evs.append((a, b))
         torch.cuda.synchronize()
-        res[name] = ((time.perf_counter() - t0) * 1e3 / args.steps, float(np.mean([a.elapsed_time(b) for a, b in evs])))
+        res[name] = ((time.perf_counter() - t0) * 1e3 / args.steps, event_mean_ms(evs)[0])
     row_b = Dqk * 2 + 4                                   # latent + its req_to_token entry
     qo = B * Hq * (Dqk + Dv) * 2
     flat_bytes = int(L.sum()) * row_b + qo
@@ -902,7 +913,7 @@ def bench_hicache(args):
             b.record()
             evs.append((a, b))
         torch.cuda.synchronize()
-        res[name] = ((time.perf_counter() - t0) * 1e3 / args.steps, float(np.mean([a.elapsed_time(b) for a, b in evs])))
+        res[name] = ((time.perf_counter() - t0) * 1e3 / args.steps, event_mean_ms(evs)[0])
     ms, call = res["prefetch"]
     gbps = moved / (call * 1e-3) / 1e9
     wb_gbps = moved / (res["write_back"][1] * 1e-3) / 1e9

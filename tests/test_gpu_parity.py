@@ -157,12 +157,20 @@ def _direct_extend(order, P, E, seed=3, Hq=32, Hkv=8, D=128, slots=4096):
 
 
 def test_prefix_reuse_equals_recompute_bitwise():
-    # rows P.. of extend(P cached, E new) == the same rows of extend(0 cached, P+E new)
+    # prefill kernel: rows P.. of extend(P cached, E new) == the same rows of
+    # extend(0 cached, P+E new), bit for bit (a row's result depends only on
+    # its keys, not on where the cached part ends)
     order = np.random.default_rng(0).permutation(4096).astype(np.int32)
-    for P, E in [(100, 50), (64, 64), (1, 200), (300, 1)]:
+    for P, E in [(100, 50), (64, 64), (1, 200), (290, 10)]:
         a = _direct_extend(order, P, E)
         b = _direct_extend(order, 0, P + E)
         assert torch.equal(a, b[P:]), (P, E)
+    # one new token (4 query rows per KV head) takes the split-K small-q path,
+    # whose splits follow the context length and whose merge rounds
+    # differently: equal to the recomputation within the bf16 tolerance
+    a = _direct_extend(order, 300, 1)
+    b = _direct_extend(order, 0, 301)
+    assert float((a.float() - b[300:].float()).abs().max()) <= BF16_TOL
 
 
 def test_slot_permutation_invariance_bitwise():
