@@ -112,7 +112,11 @@ int32_t extend_splits(int32_t batch, int32_t Hkv) {
 // MLA latent decode: keys per split of the flat call and the suffix, and
 // the prefix split (halved down to 64 keys until about kPrefixWorkgroups
 // workgroups run; the row-block rule matches launch_split_mla).
-constexpr int kMlaChunk = 512;
+// Keys per flat / suffix split of the latent decode: 1024 when each split
+// has 64 or more query rows (one wave per 16-row block), where the split
+// states (512 fp32 per row and split) would otherwise cost as much traffic
+// as the latents; 512 otherwise.
+int mla_chunk(int32_t Hq) { return Hq >= 64 ? 1024 : 512; }
 constexpr int kMlaDqk = 576, kMlaDv = 512;
 int mla_prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq) {
     const int64_t rb = ceil_div64((int64_t)max_group_size * Hq, 16);
@@ -483,7 +487,7 @@ int sgl_cascade_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, c
 // ---- MLA latent decode ---------------------------------------------------------
 size_t sgl_mla_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq, int32_t Dv) {
     if (batch <= 0 || max_seq_len <= 0 || Hq <= 0 || Dv <= 0) return 0;
-    return part_bytes(batch, ceil_div64(max_seq_len, kMlaChunk), Hq, Dv);
+    return part_bytes(batch, ceil_div64(max_seq_len, mla_chunk(Hq)), Hq, Dv);
 }
 
 size_t sgl_mla_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len, int32_t max_group_size,
@@ -492,7 +496,7 @@ size_t sgl_mla_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_
     const int64_t Sp = max_prefix_len > 0
                            ? ceil_div64(max_prefix_len, mla_prefix_chunk(G, max_group_size, max_prefix_len, Hq))
                            : 1;
-    return part_bytes(batch, Sp, Hq, Dv) + part_bytes(batch, ceil_div64(max_seq_len, kMlaChunk), Hq, Dv);
+    return part_bytes(batch, Sp, Hq, Dv) + part_bytes(batch, ceil_div64(max_seq_len, mla_chunk(Hq)), Hq, Dv);
 }
 
 namespace {
@@ -559,10 +563,11 @@ int mla_common(bool cascade, const void *q, const void *kv_new, void *kv_pool, i
     std::memset(&m, 0, sizeof m);
     m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
     m.batch = batch; m.G = G; m.Hq = Hq; m.D = Dv; m.out_bf16 = 1; m.o = o; m.lse = lse;
-    m.chunk_flat = kMlaChunk;
-    const int64_t Ss = ceil_div64(max_seq_len, kMlaChunk);
+    const int chunk = mla_chunk(Hq);
+    m.chunk_flat = chunk;
+    const int64_t Ss = ceil_div64(max_seq_len, chunk);
     if (!cascade) {
-        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = kMlaChunk;
+        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = chunk;
         a.part = carve(wp, batch, Ss, Hq, Dv);
         if ((rc = launch_split_mla(a, st)) != SGL_OK) return rc;
         m.kind = 0; m.flat_or_suffix = a.part;
@@ -575,7 +580,7 @@ int mla_common(bool cascade, const void *q, const void *kv_new, void *kv_pool, i
     // 253 vs 208 us, 128 heads 885 vs 805 us).  Such groups run the flat
     // splits (same result).
     if ((int64_t)max_group_size * Hq > 64) {
-        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = kMlaChunk;
+        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = chunk;
         a.part = carve(wp, batch, Ss, Hq, Dv);
         if ((rc = launch_split_mla(a, st)) != SGL_OK) return rc;
         m.kind = 0; m.flat_or_suffix = a.part;
@@ -587,7 +592,7 @@ int mla_common(bool cascade, const void *q, const void *kv_new, void *kv_pool, i
     pa.kind = 1; pa.chunk = pchunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size; pa.n_sets = G;
     pa.part = carve(wp, batch, Sp, Hq, Dv);
     SplitArgs sa = a;
-    sa.kind = 2; sa.chunk = kMlaChunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
+    sa.kind = 2; sa.chunk = chunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
     sa.part = carve(wp, batch, Ss, Hq, Dv);
     if (max_prefix_len > 0 && (rc = launch_split_mla(pa, st)) != SGL_OK) return rc;
     if ((rc = launch_split_mla(sa, st)) != SGL_OK) return rc;

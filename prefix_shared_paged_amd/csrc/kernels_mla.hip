@@ -19,6 +19,8 @@
 // a fifth of Q and a quarter of O.  The waves share each 16-key latent tile
 // (18 KiB) in LDS, gathered by slot with non-temporal direct loads, two tiles
 // in flight.
+#include <utility>
+
 #include "common.h"
 #include "decode_util.h"
 
@@ -36,10 +38,13 @@ constexpr int MLA_DEPTH = 2;
 
 // Position of 16-byte chunk c of tile row r is c ^ msw(r), an XOR inside the
 // row's aligned groups of 8 chunks (72 chunks per row = 9 groups).  Rows are
-// 1152 bytes apart, so a chunk's LDS bank group (of 16) is 8 * (r % 2) +
-// position % 16: the swizzle spreads the 16 rows of a K operand read over
-// distinct bank groups.
-__device__ __forceinline__ int msw(int r) { return (r >> 1) & 7; }
+// 1152 bytes apart, so row r starts in the (r % 2) half of a 256-byte bank
+// line.  msw maps the eight rows of each parity to distinct chunk positions
+// (K operand reads: 16 rows, one chunk each, fall on 16 distinct 16-byte
+// bank groups), and rows 2j and 2j + 2 land on different chunk pairs (V^T
+// reads: a half wave reads two adjacent chunks of each of 8 consecutive rows,
+// 256 bytes on distinct banks).
+__device__ __forceinline__ int msw(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 
 // RBW 16-row blocks per workgroup, four waves each
 template <int RBW>
@@ -266,6 +271,262 @@ __global__ void __launch_bounds__(256 * RBW) split_mla_kernel(SplitArgs a) {
     if (quarter == 0 && kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
 }
 
+// Immediate-offset LDS reads (inline asm for the reason given in
+// decode_util.h); OFF is a byte offset added to the address.
+template <int OFF>
+__device__ __forceinline__ void ds_b128(u32x4 &r, uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_tr16(i32x2 &r, uint32_t addr) {
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+}
+// s_waitcnt vmcnt(n) for a wave-uniform n <= M
+template <int M>
+__device__ __forceinline__ void vm_wait_upto(int n) {
+    if constexpr (M == 0) {
+        vm_wait<0>();
+    } else {
+        if (n >= M) vm_wait<M>();
+        else vm_wait_upto<M - 1>(n);
+    }
+}
+// maximum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float max_across_kq(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+template <class F, int... I>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &&f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// One wave per 16-row block over all 576 score dims and all 512 value dims:
+// no reduction across waves.  The RBW waves of a workgroup (RBW row blocks)
+// share each latent tile; a ring of four tiles (three in flight) lets one
+// barrier per tile both publish the tile's direct loads and retire the
+// buffer they refill.
+// A wave keeps its block's Q operand (72 VGPRs) and O^T accumulators (128).
+template <int RBW>
+__global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
+    constexpr int QS = DQK / 32;                   // 18 S^T steps
+    constexpr int DB = DV / 16;                    // 32 output blocks of 16 dims
+    constexpr int DEPTH = 4;
+    constexpr int KB = 3;                          // K operand reads per batch
+    constexpr int VB = 8;                          // V^T reads per batch
+    __shared__ __attribute__((aligned(16))) unsigned char t_lds[DEPTH * TBM];
+    extern __shared__ int32_t slot_lds[];          // [chunk]
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // ---- work item (as split_mla_kernel) -----------------------------------------
+    const int n_rbg = (a.row_blocks + RBW - 1) / RBW;
+    const int id = blockIdx.x;
+    const int rbg = id % n_rbg;
+    const int64_t item = id / n_rbg;
+    const int set = (int)(item % a.n_sets);
+    const int s = (int)(item / a.n_sets);
+    if (s >= a.max_splits) return;
+    const int g = a.Hq;
+    int first_req, n_members;
+    int64_t lo, hi, ref_row;
+    if (a.kind == 1) {
+        first_req = a.group_ptr[set];
+        n_members = a.group_ptr[set + 1] - first_req;
+        if (n_members <= 0 || first_req < 0 || first_req + n_members > a.batch) return;
+        const int64_t P = a.group_prefix_len[set];
+        lo = 0;
+        hi = P < 0 ? 0 : P;
+        ref_row = a.req_rows[first_req];
+    } else {
+        first_req = set;
+        n_members = 1;
+        const int64_t L = a.seq_lens[set];
+        ref_row = a.req_rows[set];
+        lo = 0;
+        if (a.kind == 2) {
+            const int grp = find_group_dec(a.group_ptr, a.G, set);
+            const int64_t P = a.group_prefix_len[grp];
+            lo = P < 0 ? 0 : (P > L ? L : P);
+        }
+        hi = L;
+    }
+    if (n_members * g <= rbg * RBW * 16) return;
+    if (ref_row < 0 || ref_row >= a.num_rows) return;
+    if (hi > a.row_stride) hi = a.row_stride;
+    const int64_t n_split = ceil_div64(hi - lo, a.chunk);
+    if (s >= n_split || s >= a.part.S) return;
+    const int64_t k0 = lo + (int64_t)s * a.chunk;
+    const int nk = (int)((k0 + a.chunk < hi ? k0 + a.chunk : hi) - k0);
+    const int N = (nk + MT - 1) / MT;
+    const int row_base = (rbg * RBW + w) * 16;
+    const int rows = n_members * g - row_base;     // may be <= 0: the wave still loads
+
+    const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
+    for (int j = threadIdx.x; j < nk; j += 64 * RBW) slot_lds[j] = safe_slot(row[j], a.num_slots);
+
+    const int n16 = lane & 15, kq = lane >> 4;
+
+    // ---- Q^T operand: lane (row n16, kq) holds dims 32t + 8kq + i in step t --------
+    bf16x8 qf[QS];
+    {
+        const int rho = n16 < rows ? n16 : 0;
+        const int rr = row_base + rho < n_members * g ? row_base + rho : 0;
+        const __bf16 *src = (const __bf16 *)a.q + ((int64_t)(first_req + rr / g) * a.Hq + rr % g) * DQK + 8 * kq;
+#pragma unroll
+        for (int t = 0; t < QS; t++) qf[t] = n16 < rows ? ld_q(src + 32 * t) : bf16x8{};
+    }
+
+    // ---- direct loads: instruction ii covers tile bytes [1024 ii, 1024 ii + 1024);
+    // wave w issues ii = w, w + RBW, ...
+    constexpr int MAXI = (NIM + RBW - 1) / RBW;
+    int lrow[MAXI], lsrc[MAXI];
+#pragma unroll
+    for (int u = 0; u < MAXI; u++) {
+        const int ii = w + RBW * u;
+        const int off = (ii < NIM ? ii : 0) * 1024 + 16 * lane;
+        lrow[u] = off / RB;
+        const int c = (off % RB) / 16;
+        lsrc[u] = 16 * (c ^ msw(lrow[u]));
+    }
+    const int n_mine = (NIM - w + RBW - 1) / RBW;
+    const char *pool = (const char *)a.k_pool;
+
+    __syncthreads();   // slot table visible
+
+    auto issue = [&](int n, unsigned char *dst) {
+        int32_t sl[MAXI];                          // all look-ups first: one LDS wait
+#pragma unroll
+        for (int u = 0; u < MAXI; u++) sl[u] = slot_lds[min(n * MT + lrow[u], nk - 1)];
+#pragma unroll
+        for (int u = 0; u < MAXI; u++) {
+            if (u < n_mine) {
+                const char *src = pool + (int64_t)sl[u] * RB + lsrc[u];
+                __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                                 (SGL_LDS void *)(dst + (w + RBW * u) * 1024), 16, 0, 2 /* nt */);
+            }
+        }
+    };
+
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float qscale = a.scale * kLog2e;
+    // K operand of step t: chunk 4t + kq of row n16, at position (4t + kq) ^ msw
+    // inside its group of 8: base (t even / odd) + 128 (t / 2)
+    const int mk = msw(n16);
+    const uint32_t koff0 = n16 * RB + 16 * ((0 + kq) ^ mk);
+    const uint32_t koff1 = n16 * RB + 16 * ((4 + kq) ^ mk);
+    // V^T of output block db: lane (r4, qq) of group kq reads dims 16 db + 4 qq ..
+    // of row 4kq + r4: chunk 2db + (qq >> 1), byte 8 (qq & 1); for db = 4j + d
+    // the position is 8j + ((2d + (qq >> 1)) ^ msw(row)): base (d) + 128 j
+    const int r4 = n16 >> 2, qq = n16 & 3;
+    const int vr = kq * 4 + r4;
+    const int mv = msw(vr);
+    uint32_t voff[4];
+#pragma unroll
+    for (int d = 0; d < 4; d++) voff[d] = vr * RB + 16 * ((2 * d + (qq >> 1)) ^ mv) + 8 * (qq & 1);
+
+    auto tile = [&](int n, const unsigned char *tb) {
+        const uint32_t base = lds_addr(tb);
+        const uint32_t kb0 = base + koff0, kb1 = base + koff1;
+        // KB independent accumulators (step t feeds t % KB), so consecutive
+        // MFMAs do not wait on each other
+        f32x4 sp[KB];
+#pragma unroll
+        for (int i = 0; i < KB; i++) sp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        static_for(std::make_integer_sequence<int, QS / KB>{}, [&](auto bi) {
+            constexpr int B0 = decltype(bi)::value * KB;
+            u32x4 raw[KB];
+            static_for(std::make_integer_sequence<int, KB>{}, [&](auto ti) {
+                constexpr int T = B0 + decltype(ti)::value;
+                ds_b128<128 * (T >> 1)>(raw[decltype(ti)::value], (T & 1) ? kb1 : kb0);
+            });
+            lgkm_wait_tied(raw);
+#pragma unroll
+            for (int i = 0; i < KB; i++)
+                sp[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, raw[i]), qf[B0 + i], sp[i],
+                                                                0, 0, 0);
+        });
+        f32x4 sacc = sp[0];
+#pragma unroll
+        for (int i = 1; i < KB; i++) sacc += sp[i];
+        // online softmax over the tile's 16 keys (lazy reference maximum)
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float x = n * MT + kq * 4 + j < nk ? sacc[j] * qscale : -INFINITY;
+            sv[j] = x;
+            mx = fmaxf(mx, x);
+        }
+        mx = max_across_kq(mx);
+        const bool move = mx > m_run + 8.f;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float m_new = move ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; db++) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        bf16x4 pf;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_run);
+            l_run += pj;
+            pf[j] = (__bf16)pj;
+        }
+        const i16x4 pb = __builtin_bit_cast(i16x4, pf);
+        static_for(std::make_integer_sequence<int, DB / VB>{}, [&](auto bi) {
+            constexpr int D0 = decltype(bi)::value * VB;
+            i32x2 vt[VB];
+            static_for(std::make_integer_sequence<int, VB>{}, [&](auto di) {
+                constexpr int DBI = D0 + decltype(di)::value;
+                ds_tr16<128 * (DBI >> 2)>(vt[decltype(di)::value], base + voff[DBI & 3]);
+            });
+            lgkm_wait_tied(vt);
+#pragma unroll
+            for (int i = 0; i < VB; i++)
+                oacc[D0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt[i]), pb,
+                                                                         oacc[D0 + i], 0, 0, 0);
+        });
+    };
+
+    // ring of DEPTH tiles, DEPTH - 1 in flight: at the top of step n this
+    // wave's loads of tile n have landed when only those of tiles n+1 ..
+    // n+DEPTH-2 remain; after the barrier every wave has also finished tile
+    // n-1, whose buffer takes tile n+DEPTH-1
+    for (int t = 0; t < DEPTH - 1 && t < N; t++) issue(t, t_lds + t * TBM);
+    for (int n = 0; n < N; n++) {
+        const int later = min(DEPTH - 2, N - 1 - n);
+        vm_wait_upto<MAXI * (DEPTH - 2)>(n_mine * later);
+        lgkm_wait0();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (n + DEPTH - 1 < N) issue(n + DEPTH - 1, t_lds + ((n + DEPTH - 1) % DEPTH) * TBM);
+        tile(n, t_lds + (n % DEPTH) * TBM);
+    }
+
+    // ---- the split's state -----------------------------------------------------
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (n16 >= rows) return;
+    const int rr = row_base + n16;
+    const int req = first_req + rr / g;
+    const int h = rr % g;
+    const int64_t idx = ((int64_t)req * a.part.S + s) * a.Hq + h;
+    float *op = a.part.o + idx * DV;
+#pragma unroll
+    for (int db = 0; db < DB; db++) *(f32x4 *)(op + db * 16 + kq * 4) = oacc[db];
+    if (kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
+}
+
 }  // namespace
 
 // Flat (kind 0), prefix (kind 1) and suffix (kind 2) splits over a latent
@@ -281,6 +542,14 @@ int launch_split_mla(const SplitArgs &a0, hipStream_t st) {
     const int64_t n_wg = (int64_t)a.n_sets * a.max_splits * n_rbg;
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
+    if (a.row_blocks >= 4 && a.kind != 1) {
+        // 64 or more query rows per split: one wave per 16-row block
+        constexpr int FR = 4;
+        const int64_t n_wf = (int64_t)a.n_sets * a.max_splits * ((a.row_blocks + FR - 1) / FR);
+        if (n_wf > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL((split_mla_full_kernel<FR>), dim3((unsigned)n_wf), dim3(64 * FR), dyn, st, a);
+        return hip_status(hipGetLastError());
+    }
     const dim3 grid((unsigned)n_wg), block(256 * rbw);
     if (rbw == 4) hipLaunchKernelGGL((split_mla_kernel<4>), grid, block, dyn, st, a);
     else if (rbw == 2) hipLaunchKernelGGL((split_mla_kernel<2>), grid, block, dyn, st, a);
