@@ -184,3 +184,34 @@ def test_prefetch_at_full_size():
         assert np.array_equal(_np(h), hicache.store(b, _np(p[sl_d.long()]), np.arange(n), hrows2))
     for p, b in zip(pools, before):
         assert np.array_equal(_np(p[untouched]), b)
+
+
+def test_prefetched_prefix_attends_like_resident():
+    # a request's cached prefix is written back to the host tier, its slots are
+    # reused, and the prefix is prefetched into other slots before the next
+    # extend: the extend over the prefetched rows equals the one over the
+    # resident rows bit for bit (the prefill kernel's result depends on the
+    # values only, not on the slots)
+    from prefix_shared_paged_amd import extend_attn
+    Hq, Hkv, D, P, E, S, n_host = 32, 8, 128, 300, 40, 8192, 1000
+    rng = np.random.default_rng(21)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    rnd = lambda *shape: (torch.randn(shape, generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    kp, vp = rnd(S, Hkv, D), rnd(S, Hkv, D)
+    q, k_new, v_new = rnd(E, Hq, D), rnd(E, Hkv, D), rnd(E, Hkv, D)
+    perm = rng.permutation(S)
+    s1, s_new, s2 = perm[:P], perm[P:P + E], perm[P + E:2 * P + E]
+    args = lambda slots: (_dev(np.concatenate([slots, s_new])[None], torch.int32), _dev([0], torch.int32),
+                          _dev([P], torch.int32), _dev([0, E], torch.int64))
+    o_ref = extend_attn(q, kp, vp, *args(s1), E, k_new=k_new, v_new=v_new)
+    host_k = torch.zeros((n_host, Hkv, D), dtype=torch.bfloat16, pin_memory=True)
+    host_v = torch.zeros((n_host, Hkv, D), dtype=torch.bfloat16, pin_memory=True)
+    hrows = _dev(rng.permutation(n_host)[:P], torch.int64)
+    sp.hicache_write_back(kp, vp, _dev(s1, torch.int32), hrows, host_k, host_v)
+    kp[_dev(s1, torch.int64)] = 0
+    vp[_dev(s1, torch.int64)] = 0
+    sp.hicache_prefetch(host_k, host_v, hrows, _dev(s2, torch.int32), kp, vp)
+    o2 = extend_attn(q, kp, vp, *args(s2), E, k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    assert torch.equal(o_ref, o2)
