@@ -713,7 +713,7 @@ def bench_verify(args):
     q_off = torch.from_numpy(np.arange(B + 1, dtype=np.int64) * E).to(dev)
     col0 = torch.from_numpy(P.astype(np.int32)).to(dev)
     d_new = torch.empty(n, dtype=torch.int32, device=dev)
-    ws_n = sp.extend_workspace_size(B, n, E, Hq, Hkv, D)
+    ws_n = sp.extend_workspace_size(B, n, E, cache.r2t.shape[1], Hq, Hkv, D)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev) if ws_n else None
     pin = Pinned(torch, 3, {"new": (n, torch.int32)})
     pool = cache.pool
@@ -754,7 +754,8 @@ def bench_verify(args):
     config = {"workload": f"verify (small-q extend): {B} requests, own cached contexts ~U[2048,8192], {E} new "
                           "tokens each (stored, then attended causally); 32/8 heads, head_dim 128, 2^20-slot pool, "
                           "page 1", "batch": B, "q_len": E,
-              "path": "split-K" if ws_n else "prefill kernel"}
+              "path": ("split-K" if E * (Hq // Hkv) <= 16 else "prefill kernel, key splits") if ws_n
+              else "prefill kernel"}
     roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
             "traffic": None, "kernel": "extend call (split kernel + merge, or the prefill kernel)",
             "bytes_per_launch": byts, "avg_launch_ms": call}

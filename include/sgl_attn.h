@@ -235,11 +235,16 @@ int sgl_store_kv(int dtype, const void *k_new, const void *v_new, int64_t n_toke
  *   lse: device float32 [n_tokens, Hq] log-sum-exp of the scaled scores
  *     (natural log), or NULL.
  *   workspace: device scratch of sgl_extend_workspace_size(...) bytes (may be
- *     NULL when that size is 0).  The size is non-zero for bf16 calls with
- *     max_extend_len * (Hq / Hkv) <= 16 -- a few new tokens per request, as in
- *     the verify step of speculative decoding -- which run as a split-K pass
- *     over each request's keys plus a log-sum-exp merge (the result is the
- *     same attention).
+ *     NULL when that size is 0), given the same batch, n_tokens,
+ *     max_extend_len, row_stride and heads as the call.  The size is non-zero
+ *     (a) for max_extend_len * (Hq / Hkv) <= 16 -- a few new tokens per
+ *     request, as in the verify step of speculative decoding -- which runs as
+ *     a split-K pass over each request's keys plus a log-sum-exp merge, and
+ *     (b) when the prefill grid (one workgroup per request, 128 query rows and
+ *     KV head) is small and row_stride allows long contexts, where each
+ *     workgroup's keys are split in 4096-key multiples and merged the same way.
+ *     Either way the result is the same attention (bf16 calls; fp32 calls
+ *     ignore the workspace).
  * scale multiplies q.k (normally 1/sqrt(D)). */
 int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_new,
                     void *k_pool, void *v_pool, int64_t num_slots,
@@ -249,7 +254,7 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
                     int32_t Hq, int32_t Hkv, int32_t D, float scale,
                     void *o, float *lse, void *workspace, size_t workspace_bytes, void *stream);
 size_t sgl_extend_workspace_size(int32_t batch, int64_t n_tokens, int32_t max_extend_len,
-                                 int32_t Hq, int32_t Hkv, int32_t D);
+                                 int64_t row_stride, int32_t Hq, int32_t Hkv, int32_t D);
 
 /* Decode attention: one query token per request over its whole context,
  * chenxutan.com section 3.2 PagedDecode.  seq_lens[r] (device int32)

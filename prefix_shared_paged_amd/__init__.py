@@ -67,7 +67,7 @@ def load():
         "sgl_store_kv": (ctypes.c_int, [ctypes.c_int, P, P, I64, P, P, P, I64, I32, I32, P]),
         "sgl_extend_attn": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P, P, P,
                                            I32, I64, I32, I32, I32, I32, F, P, P, P, SZ, P]),
-        "sgl_extend_workspace_size": (SZ, [I32, I64, I32, I32, I32, I32]),
+        "sgl_extend_workspace_size": (SZ, [I32, I64, I32, I64, I32, I32, I32]),
         "sgl_decode_attn": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P, P,
                                            I32, I32, I32, I32, I32, F, P, P, P, SZ, P]),
         "sgl_decode_workspace_size": (SZ, [I32, I32, I32, I32, I32]),
@@ -323,8 +323,8 @@ def store_kv(k_new, v_new, slots, k_pool, v_pool, stream=None):
         _dev_ptr(v_pool, "v_pool", k_new.dtype), k_pool.shape[0], Hkv, D, _stream(stream)))
 
 
-def extend_workspace_size(batch, n_tokens, max_extend_len, Hq, Hkv, D):
-    return int(load().sgl_extend_workspace_size(batch, n_tokens, max_extend_len, Hq, Hkv, D))
+def extend_workspace_size(batch, n_tokens, max_extend_len, row_stride, Hq, Hkv, D):
+    return int(load().sgl_extend_workspace_size(batch, n_tokens, max_extend_len, row_stride, Hq, Hkv, D))
 
 
 def extend_attn(q, k_pool, v_pool, r2t, req_rows, prefix_lens, q_off, max_extend_len, k_new=None,
@@ -337,7 +337,7 @@ def extend_attn(q, k_pool, v_pool, r2t, req_rows, prefix_lens, q_off, max_extend
         o = torch.empty_like(q)
     if scale is None:
         scale = 1.0 / (D ** 0.5)
-    ws_n = extend_workspace_size(req_rows.numel(), n_tokens, max_extend_len, Hq, Hkv, D)
+    ws_n = extend_workspace_size(req_rows.numel(), n_tokens, max_extend_len, r2t.shape[1], Hq, Hkv, D)
     if ws_n and workspace is None:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
     _check("sgl_extend_attn", load().sgl_extend_attn(

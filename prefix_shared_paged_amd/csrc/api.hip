@@ -103,6 +103,31 @@ constexpr int kSmallQRows = 16;
 bool small_q_extend(int32_t max_extend_len, int32_t Hq, int32_t Hkv) {
     return Hkv > 0 && (int64_t)max_extend_len * (Hq / Hkv) <= kSmallQRows;
 }
+// Key splits of the prefill kernel.  Its grid has one workgroup per
+// (request, tile of 128 query rows, KV head), each walking all of its keys;
+// when that grid has at most one workgroup per compute unit (one or two long
+// requests, as in the last rounds of chunked prefill) and rows may be long,
+// each workgroup's keys are cut into splits of ksplit keys (a multiple of
+// 4096, two halves of the kernel's slot table) so that about
+// kExtendWgTarget workgroups run; row_stride bounds every context.  Measured
+// on 64/8 heads: one request over 30k keys (128 workgroups) 554 -> 328 us,
+// over 20k keys (256) 451 -> 425 us; with 512 or more workgroups the splits'
+// merge costs more than it gains, so they run unsplit.
+constexpr int64_t kExtendSplitKeys = 4096;
+constexpr int64_t kExtendWgTarget = 1024;
+constexpr int64_t kExtendSplitMaxWg = 256;
+int32_t extend_key_splits(int32_t batch, int32_t max_extend_len, int64_t row_stride, int32_t Hq, int32_t Hkv,
+                          int32_t *ksplit) {
+    const int64_t g = Hq / Hkv;
+    const int64_t n_wg = ceil_div64(max_extend_len, kExtendTileRows / g) * batch * Hkv;
+    const int64_t chunks = ceil_div64(row_stride, kExtendSplitKeys);
+    int64_t S = 1;
+    if (n_wg <= kExtendSplitMaxWg && chunks >= 2) S = std::min(chunks, ceil_div64(kExtendWgTarget, n_wg));
+    const int64_t per = ceil_div64(chunks, S);
+    *ksplit = (int32_t)(per * kExtendSplitKeys);
+    return (int32_t)ceil_div64(row_stride, per * kExtendSplitKeys);
+}
+
 int32_t extend_splits(int32_t batch, int32_t Hkv) {
     const int64_t items = (int64_t)batch * Hkv;
     int64_t n = items > 0 ? (2048 + items - 1) / items : 1;
@@ -143,7 +168,7 @@ const char *sgl_status_string(int status) {
     }
 }
 
-int sgl_abi_version(void) { return 3; }
+int sgl_abi_version(void) { return 4; }
 
 int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
                            const int32_t *req_rows, int32_t batch, const int32_t *prefix_slots,
@@ -213,10 +238,13 @@ int sgl_store_kv_fp8(int dtype, const void *k_new, const void *v_new, int64_t n_
                                Hkv, D, k_scale, v_scale, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0, st);
 }
 
-size_t sgl_extend_workspace_size(int32_t batch, int64_t n_tokens, int32_t max_extend_len, int32_t Hq,
-                                 int32_t Hkv, int32_t D) {
-    if (batch <= 0 || n_tokens <= 0 || max_extend_len <= 0 || !small_q_extend(max_extend_len, Hq, Hkv)) return 0;
-    return part_bytes(n_tokens, extend_splits(batch, Hkv), Hq, D);
+size_t sgl_extend_workspace_size(int32_t batch, int64_t n_tokens, int32_t max_extend_len, int64_t row_stride,
+                                 int32_t Hq, int32_t Hkv, int32_t D) {
+    if (batch <= 0 || n_tokens <= 0 || max_extend_len <= 0 || Hkv <= 0 || Hq < Hkv) return 0;
+    if (small_q_extend(max_extend_len, Hq, Hkv)) return part_bytes(n_tokens, extend_splits(batch, Hkv), Hq, D);
+    int32_t ksplit;
+    const int32_t S = extend_key_splits(batch, max_extend_len, row_stride, Hq, Hkv, &ksplit);
+    return S > 1 ? part_bytes(n_tokens, S, Hq, D) : 0;
 }
 
 int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,
@@ -257,7 +285,7 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
         if (rc != SGL_OK) return rc;
     }
     if (dtype == SGL_BF16 && small_q_extend(max_extend_len, Hq, Hkv)) {
-        const size_t need = sgl_extend_workspace_size(batch, n_tokens, max_extend_len, Hq, Hkv, D);
+        const size_t need = sgl_extend_workspace_size(batch, n_tokens, max_extend_len, row_stride, Hq, Hkv, D);
         if (workspace_bytes < need || !workspace) return SGL_ERR_WORKSPACE;
         if (n_tokens > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
         const int32_t n_spl = extend_splits(batch, Hkv);
@@ -280,9 +308,30 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
         return launch_extend_f32((const float *)q, (const float *)k_pool, (const float *)v_pool,
                                  num_slots, r2t, num_rows, row_stride, req_rows, prefix_lens, q_off,
                                  batch, max_extend_len, Hq, Hkv, D, scale, (float *)o, lse, st);
-    return launch_extend_bf16((const __bf16 *)q, (const __bf16 *)k_pool, (const __bf16 *)v_pool,
-                              num_slots, r2t, num_rows, row_stride, req_rows, prefix_lens, q_off, batch,
-                              max_extend_len, Hq, Hkv, D, scale, (__bf16 *)o, lse, st);
+    int32_t ksplit;
+    const int32_t n_split = extend_key_splits(batch, max_extend_len, row_stride, Hq, Hkv, &ksplit);
+    if (n_split <= 1) {
+        PartialBuf none;
+        std::memset(&none, 0, sizeof none);
+        return launch_extend_bf16((const __bf16 *)q, (const __bf16 *)k_pool, (const __bf16 *)v_pool, num_slots, r2t,
+                                  num_rows, row_stride, req_rows, prefix_lens, q_off, batch, max_extend_len, Hq, Hkv,
+                                  D, scale, (__bf16 *)o, lse, 1, 0, none, st);
+    }
+    const size_t need = part_bytes(n_tokens, n_split, Hq, D);
+    if (workspace_bytes < need || !workspace) return SGL_ERR_WORKSPACE;
+    if (n_tokens > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+    char *wp = (char *)workspace;
+    const PartialBuf part = carve(wp, n_tokens, n_split, Hq, D);
+    if ((rc = launch_extend_bf16((const __bf16 *)q, (const __bf16 *)k_pool, (const __bf16 *)v_pool, num_slots, r2t,
+                                 num_rows, row_stride, req_rows, prefix_lens, q_off, batch, max_extend_len, Hq, Hkv, D,
+                                 scale, nullptr, nullptr, n_split, ksplit, part, st)) != SGL_OK)
+        return rc;
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    m.kind = 5; m.flat_or_suffix = part; m.batch = (int32_t)n_tokens; m.Hq = Hq; m.Hkv = Hkv; m.D = D;
+    m.out_bf16 = 1; m.o = o; m.lse = lse; m.q_off = q_off; m.prefix_lens = prefix_lens; m.n_req = batch;
+    m.chunk_flat = ksplit; m.row_stride = row_stride;
+    return launch_merge(m, st);
 }
 
 // Splits of the flat call and the cascade suffix are sized for the smaller

@@ -50,6 +50,10 @@ static inline int hip_status(hipError_t e) { return e == hipSuccess ? SGL_OK : S
 //   ml part [B][S][Hq][2] fp32: (m, l) with m in log2 units of the scaled
 //            score (m = max_j s_j * scale * log2 e), l = sum_j 2^(s_j*scale*log2e - m).
 // An empty key set is stored as (m = -inf, l = 0, o = 0).
+// Query rows (new token x query head of one KV head) per workgroup of the
+// bf16 prefill kernel; the merge of its key splits bounds tiles the same way.
+constexpr int kExtendTileRows = 128;
+
 struct PartialBuf {
     float *o;
     float *ml;
@@ -87,7 +91,8 @@ int launch_extend_bf16(const __bf16 *q, const __bf16 *k_pool, const __bf16 *v_po
                        int64_t num_slots, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                        const int32_t *req_rows, const int32_t *prefix_lens, const int64_t *q_off,
                        int32_t batch, int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D,
-                       float scale, __bf16 *o, float *lse, hipStream_t st);
+                       float scale, __bf16 *o, float *lse, int32_t n_split, int32_t ksplit, PartialBuf part,
+                       hipStream_t st);
 
 // Which key range a split kernel covers:
 //   kind 0 (flat):   per request r, keys [0, seq_lens[r])
@@ -149,7 +154,10 @@ int launch_split_mla(const SplitArgs &a, hipStream_t st);
 // Merge partial states of (optionally) a prefix buffer and a suffix buffer.
 //   kind 0: parts = flat splits of r;  kind 3: parts = prefix splits of group(r) for r
 //   + suffix splits of r;  kind 4: r is a token of a small-q extend (batch = tokens),
-//   parts = the splits of its request (n_req requests, q_off, prefix_lens, n_spl).
+//   parts = the splits of its request (n_req requests, q_off, prefix_lens, n_spl);
+//   kind 5: r is a token of a key-split prefill extend (batch = tokens), parts =
+//   the chunk_flat-key splits of its query tile's keys (n_req, q_off,
+//   prefix_lens, Hkv, row_stride).
 struct MergeArgs {
     int kind;
     PartialBuf flat_or_suffix;
@@ -165,6 +173,8 @@ struct MergeArgs {
     const int64_t *q_off;
     const int32_t *prefix_lens;
     int32_t n_req, n_spl;
+    int32_t Hkv;           // kind 5: query rows of a tile follow from Hq / Hkv
+    int64_t row_stride;    // kind 5: bound on a context (keys past it are not read)
 };
 int launch_merge(const MergeArgs &a, hipStream_t st);
 

@@ -53,7 +53,7 @@ namespace {
 constexpr int BN = 32;        // keys per LDS tile
 constexpr int RING = 4;       // LDS tiles per ring (K and V each)
 constexpr int TABH = 2048;    // keys per half of the LDS slot-id table
-constexpr int BM = 128;       // query rows per workgroup
+constexpr int BM = kExtendTileRows;   // query rows per workgroup
 constexpr int NT = 256;       // threads
 constexpr float kLazy = 8.f;  // move the reference only when the max grows by more than 2^8
 
@@ -94,13 +94,19 @@ __device__ __forceinline__ void vm_wait() {
 // OFF32: every K/V byte offset fits in 32 bits (num_slots * Hkv * D * 2 <=
 // 2^32), so the slot table holds ready byte offsets and a load address is the
 // uniform pool base plus a 32-bit per-lane offset.
-template <int D, bool OFF32>
+// SPLIT: the key range of a (request, query tile, KV head) is cut into splits
+// of ksplit keys (a multiple of 2 * TABH), one workgroup each, which write
+// their partial softmax states (m, l in log2 units, unnormalised o in fp32)
+// for the log-sum-exp merge instead of o -- for grids too small to fill the
+// chip over long contexts.
+template <int D, bool OFF32, bool SPLIT>
 __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_pool,
     const __bf16 *__restrict__ v_pool, int64_t num_slots, const int32_t *__restrict__ r2t,
     int64_t num_rows, int64_t stride, const int32_t *__restrict__ req_rows,
     const int32_t *__restrict__ prefix_lens, const int64_t *__restrict__ q_off, int Hq, int Hkv,
-    int n_qtiles, float qscale, __bf16 *__restrict__ o, float *__restrict__ lse) {
+    int n_qtiles, float qscale, __bf16 *__restrict__ o, float *__restrict__ lse, int batch, int ksplit,
+    float *__restrict__ part_o, float *__restrict__ part_ml, int part_S) {
     constexpr int QT = D / 16;            // k-steps of 16 dims for S^T
     constexpr int DBLK = D / 32;          // 32-dim output blocks
     constexpr int ROWB = 2 * D;           // bytes per K or V row of one KV head
@@ -134,7 +140,8 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     const int kvh = id % Hkv;
     const int rest = id / Hkv;
     const int qt = rest % n_qtiles;
-    const int r = rest / n_qtiles;
+    const int r = SPLIT ? (rest / n_qtiles) % batch : rest / n_qtiles;
+    const int sp = SPLIT ? rest / n_qtiles / batch : 0;   // split of the key range
     const int g = Hq / Hkv;
     const int tok_per_tile = BM / g;
 
@@ -147,6 +154,11 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     if (rowi < 0 || rowi >= num_rows || P < 0) return;
     int kv_end = P + (q0 + tok_per_tile < E ? q0 + tok_per_tile : E);   // keys [0, kv_end)
     if (kv_end > stride) kv_end = (int)stride;
+    // this workgroup's keys [k_lo, k_hi): all of them, or split sp
+    const int k_lo = SPLIT ? sp * ksplit : 0;
+    if (k_lo >= kv_end) return;
+    const int k_hi = SPLIT && k_lo + ksplit < kv_end ? k_lo + ksplit : kv_end;
+    const int n0 = k_lo / BN;                        // first key tile (a multiple of 2 TABH / BN)
     const int32_t *row = r2t + rowi * stride;
     const int64_t rowstride_el = (int64_t)Hkv * D;
 
@@ -201,7 +213,7 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
         int v[CNT];
 #pragma unroll
         for (int u = 0; u < CNT; u++) {
-            const int k = min(k0 + u * NT + tid, kv_end - 1);
+            const int k = min(k0 + u * NT + tid, k_hi - 1);
             v[u] = *(const int32_t *)(row_b + (uint32_t)k * 4u);
         }
 #pragma unroll
@@ -246,7 +258,7 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     // whatever slot they were read from must not turn 0 * v into NaN); runs
     // after the loads of that tile have landed.
     auto zero_tail = [&](unsigned char *vt, int tile) {
-        const int nvalid = kv_end - tile * BN;
+        const int nvalid = k_hi - tile * BN;
         if (nvalid >= BN) return;
         for (int idx = tid; idx < (BN - nvalid) * CHK; idx += NT)
             *(uint4 *)(vt + (nvalid + idx / CHK) * ROWB + 16 * (idx % CHK)) = make_uint4(0, 0, 0, 0);
@@ -348,7 +360,7 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
         }
     };
 
-    const int N = (kv_end + BN - 1) / BN;            // key tiles
+    const int N = (k_hi + BN - 1) / BN;              // key tiles end (tiles n0 .. N-1)
     const int min_pos = P + q0;                      // smallest position in the tile
     // Workgroup barrier for LDS reuse.  __syncthreads (or any LDS release
     // fence) would also wait for every direct load still meant to be in
@@ -363,27 +375,28 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
 
     // ---- prologue: slot table, then K tiles 0..RING-1 and V tiles 0..RING-2
     // in the order of the stages -4..-1 they stand for
-    fill(IC<2 * TABH / NT>{}, 0);
+    fill(IC<2 * TABH / NT>{}, k_lo);
     __syncthreads();
     Off off0[NB], off1[NB];                          // offsets of tile j live in off[j % 2]
     auto offs = [&](auto i) -> Off (&)[NB] { return decltype(i)::value % 2 ? off1 : off0; };
-    offsets(0, off0);
+    offsets(n0, off0);
     issue(k_pool, k_lds0, off0);
-    offsets(1, off1);
+    offsets(n0 + 1, off1);
     issue(k_pool, k_lds1, off1);
     issue(v_pool, v_lds0, off0);
-    offsets(2, off0);
+    offsets(n0 + 2, off0);
     issue(k_pool, k_lds2, off0);
     issue(v_pool, v_lds1, off1);
-    offsets(3, off1);
+    offsets(n0 + 3, off1);
     issue(k_pool, k_lds3, off1);
     issue(v_pool, v_lds2, off0);
-    vm_wait<6 * NB>();           // K tile 0
+    vm_wait<6 * NB>();           // K tile n0
     lds_barrier();
     f32x16 s_cur = s_tile(k_lds0);
-    move_ref(s_cur, 31 > min_pos ? mask_max(s_cur, 0, std::true_type{}) : mask_max(s_cur, 0, std::false_type{}));
-    vm_wait<4 * NB>();           // V tile 0, K tile 1
-    if (N == 1) zero_tail(v_lds0, 0);
+    move_ref(s_cur, n0 * BN + 31 > min_pos ? mask_max(s_cur, n0, std::true_type{})
+                                           : mask_max(s_cur, n0, std::false_type{}));
+    vm_wait<4 * NB>();           // V tile n0, K tile n0 + 1
+    if (N == n0 + 1) zero_tail(v_lds0, n0);
     lds_barrier();
 
     // ---- stage n (R = n % RING): S^T(n+1) || p of tile n; PV of tile n ||
@@ -427,14 +440,16 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     // (chunk m-1, whose last look-up was at stage 64m-5) takes chunk m+1
     auto refill = [&](int n_done) {
         constexpr int SPC = TABH / BN;               // stages per chunk
-        if (n_done % SPC == 0 && (n_done / SPC + 1) * TABH < kv_end)
+        if (n_done % SPC == 0 && (n_done / SPC + 1) * TABH < k_hi)
             fill(IC<TABH / NT>{}, (n_done / SPC + 1) * TABH);
     };
     // stages whose look-ahead tile n+1 lies wholly at or below every row's
     // position need no mask; the loops run in groups of RING so that ring
     // positions are known at compile time
-    const int n_unmasked = (min_pos >= 63 ? (min_pos - 63) / BN + 1 : 0) / RING * RING;
-    int n = 0;
+    // (a split's stages also stop before its last tile: the masked loop below
+    // bounds every look-ahead by N)
+    const int n_unmasked = min((min_pos >= 63 ? (min_pos - 63) / BN + 1 : 0) / RING * RING, (N - 1) / RING * RING);
+    int n = n0;
     for (; n < n_unmasked; n += RING) {
         stage(n, IC<0>{}, std::false_type{});
         stage(n + 1, IC<1>{}, std::false_type{});
@@ -454,6 +469,18 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     // ---- epilogue: normalise and store ----------------------------------------
     const float l = add_xor32(l_run);
     if (!row_valid) return;
+    if constexpr (SPLIT) {
+        const int64_t idx = ((t0 + tok_local) * part_S + sp) * Hq + h;
+        float *op = part_o + idx * D;
+#pragma unroll
+        for (int b = 0; b < DBLK; b++)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; a4++)
+                *(f32x4 *)(op + b * 32 + 8 * a4 + 4 * h2) =
+                    f32x4{oacc[b][a4 * 4], oacc[b][a4 * 4 + 1], oacc[b][a4 * 4 + 2], oacc[b][a4 * 4 + 3]};
+        if (h2 == 0) *(float2 *)(part_ml + idx * 2) = make_float2(m_run, l);
+        return;
+    }
     const float inv = 1.f / l;
     __bf16 *dst = o + ((t0 + tok_local) * Hq + h) * D;
 #pragma unroll
@@ -474,26 +501,31 @@ int launch_extend_bf16(const __bf16 *q, const __bf16 *k_pool, const __bf16 *v_po
                        int64_t num_slots, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                        const int32_t *req_rows, const int32_t *prefix_lens, const int64_t *q_off,
                        int32_t batch, int32_t max_extend_len, int32_t Hq, int32_t Hkv, int32_t D,
-                       float scale, __bf16 *o, float *lse, hipStream_t st) {
+                       float scale, __bf16 *o, float *lse, int32_t n_split, int32_t ksplit, PartialBuf part,
+                       hipStream_t st) {
     if (batch == 0 || max_extend_len == 0) return SGL_OK;
     if (row_stride > 0x7fffffff) return SGL_ERR_UNSUPPORTED;   // positions are 32-bit in the kernel
+    if (n_split > 1 && (ksplit <= 0 || ksplit % (2 * TABH) != 0 || !part.o || !part.ml || part.S < n_split))
+        return SGL_ERR_INVALID;
     const int g = Hq / Hkv;
     const int tok_per_tile = BM / g;
     const int n_qtiles = (int)ceil_div64(max_extend_len, tok_per_tile);
-    const int64_t n_wg = (int64_t)n_qtiles * batch * Hkv;
+    const int64_t n_wg = (int64_t)n_qtiles * batch * Hkv * (n_split > 1 ? n_split : 1);
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const float qs = scale * kLog2e;
     const bool off32 = num_slots * Hkv * D * 2 <= (int64_t(1) << 32);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(NT), 0, st, q, k_pool, v_pool, num_slots, r2t,
-                           num_rows, row_stride, req_rows, prefix_lens, q_off, Hq, Hkv, n_qtiles, qs, o, lse);
+                           num_rows, row_stride, req_rows, prefix_lens, q_off, Hq, Hkv, n_qtiles, qs, o, lse, batch,
+                           ksplit, part.o, part.ml, (int)part.S);
     };
+    const bool split = n_split > 1;
     if (D == 128) {
-        if (off32) go(extend_bf16_kernel<128, true>);
-        else go(extend_bf16_kernel<128, false>);
+        if (off32) split ? go(extend_bf16_kernel<128, true, true>) : go(extend_bf16_kernel<128, true, false>);
+        else split ? go(extend_bf16_kernel<128, false, true>) : go(extend_bf16_kernel<128, false, false>);
     } else {
-        if (off32) go(extend_bf16_kernel<64, true>);
-        else go(extend_bf16_kernel<64, false>);
+        if (off32) split ? go(extend_bf16_kernel<64, true, true>) : go(extend_bf16_kernel<64, true, false>);
+        else split ? go(extend_bf16_kernel<64, false, true>) : go(extend_bf16_kernel<64, false, false>);
     }
     return hip_status(hipGetLastError());
 }

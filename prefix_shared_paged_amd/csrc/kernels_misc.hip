@@ -270,7 +270,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
 
     // parts: [prefix splits of r][suffix (or flat) splits of r]
     int np = 0, ns;
-    if (a.kind == 4) {
+    if (a.kind == 4 || a.kind == 5) {
         // token r of request rq = the last rq with q_off[rq] <= r
         int lo = 0, hi = a.n_req - 1;
         while (lo < hi) {
@@ -278,8 +278,19 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
             if (a.q_off[mid] <= r) lo = mid; else hi = mid - 1;
         }
         const int64_t P = a.prefix_lens[lo], E = a.q_off[lo + 1] - a.q_off[lo];
-        const int64_t L = (P < 0 ? 0 : P) + E;
-        ns = L > 0 ? (int)ceil_div64(L, verify_chunk(L, a.n_spl)) : 0;
+        if (a.kind == 4) {
+            const int64_t L = (P < 0 ? 0 : P) + E;
+            ns = L > 0 ? (int)ceil_div64(L, verify_chunk(L, a.n_spl)) : 0;
+        } else {
+            // the keys of the query tile holding token i of the request: as the
+            // prefill kernel bounds them (128 query rows per tile)
+            const int64_t tpt = kExtendTileRows / (a.Hq / a.Hkv);
+            const int64_t i = r - a.q_off[lo];
+            const int64_t q0 = i / tpt * tpt;
+            int64_t kv_end = (P < 0 ? 0 : P) + (q0 + tpt < E ? q0 + tpt : E);
+            if (kv_end > a.row_stride) kv_end = a.row_stride;
+            ns = kv_end > 0 ? (int)ceil_div64(kv_end, a.chunk_flat) : 0;
+        }
     } else {
         const int64_t L = a.seq_lens[r];
         if (a.kind == 3) {

@@ -236,6 +236,39 @@ def test_extend_long_context(Hq, Hkv, D):
     assert err <= BF16_TOL
 
 
+@pytest.mark.parametrize("P_list,E_list", [([20000], [512]), ([12000, 3, 8191], [100, 17, 2])])
+def test_extend_key_splits(P_list, E_list):
+    # grids of a few requests over long contexts (the last rounds of chunked
+    # prefill): each workgroup's keys are cut into 4096-key splits and merged;
+    # contexts end inside, on and just past split boundaries
+    spec = W.Spec("keysplit", "bf16", 64, 8, 128, 1, 1 << 16, 0.5, 9)
+    perm = np.random.default_rng(9).permutation(1 << 16).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(np.array(P_list) + np.array(E_list))])
+    kp, vp, r2t, Ks, Vs, Qs = _pool_extend_case(spec, P_list, E_list, lambda r, n: perm[offs[r]:offs[r] + n],
+                                                1 << 16, 9)
+    from prefix_shared_paged_amd import extend_workspace_size
+    assert extend_workspace_size(len(P_list), sum(E_list), max(E_list), r2t.shape[1], 64, 8, 128) > 0
+    q = dev(np.concatenate(Qs), "bf16")
+    lse = torch.empty((sum(E_list), 64), dtype=torch.float32, device="cuda")
+    o = extend_attn(q, kp, vp, r2t, dev_i(range(len(P_list))), dev_i(P_list),
+                    dev_i(np.concatenate([[0], np.cumsum(E_list)]), torch.int64), max(E_list), lse=lse)
+    torch.cuda.synchronize()
+    err = _check_extend_rows(o, Ks, Vs, Qs, P_list, E_list, spec, np.random.default_rng(1))
+    _print(f"key-split extend P={P_list} E={E_list}: max abs err {err:.3e}")
+    assert err <= BF16_TOL
+    # the log-sum-exp of the last token of each request, within the bound of
+    # the bf16 kernel's arithmetic (bf16-rounded scaled q moves a score by at
+    # most 2^-9 scale sum|q k|; the row sum adds bf16-rounded p: 2^-9 in ln l)
+    q_off = np.concatenate([[0], np.cumsum(E_list)])
+    for r, (P, E) in enumerate(zip(P_list, E_list)):
+        _, _, _, LSE = oracle.attention([Ks[r]], [Vs[r]], [0], [P + E - 1], Qs[r][E - 1:E], 64, 8)
+        qa = np.abs(Qs[r][E - 1].astype(np.float64))
+        ka = np.abs(Ks[r].astype(np.float64))
+        bound = np.array([2.0 ** -9 / np.sqrt(128) * np.max(ka[:, h // 8] @ qa[h]) for h in range(64)])
+        bound += 2.0 ** -9 + 1e-5
+        assert np.all(np.abs(lse[q_off[r] + E - 1].cpu().numpy() - LSE[0]) <= bound)
+
+
 def test_pool_over_4gib_extend_and_decode():
     # a pool whose byte size exceeds 2^32 per K/V view, with rows above the
     # 4 GiB mark: the kernels must take 64-bit row offsets

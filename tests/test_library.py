@@ -135,7 +135,13 @@ def test_workspace_sizes_grow_with_the_problem():
     assert a > b > 0
     c = lib.sgl_cascade_workspace_size(256, 16, 8192, 16, 4096, 32, 8, 128)
     assert c > a
-    assert lib.sgl_extend_workspace_size(64, 16384, 256, 32, 8, 128) == 0
+    # the extend workload's grid (4096 workgroups) needs no key splits
+    assert lib.sgl_extend_workspace_size(64, 16384, 256, 2304, 32, 8, 128) == 0
+    # a few new tokens per request (split-K path), and one long chunked-prefill
+    # request whose 256-workgroup grid gets key splits
+    assert lib.sgl_extend_workspace_size(64, 256, 4, 8300, 32, 8, 128) > 0
+    assert lib.sgl_extend_workspace_size(1, 512, 512, 33000, 64, 8, 128) > 0
+    assert lib.sgl_extend_workspace_size(1, 512, 512, 4096, 64, 8, 128) == 0
 
 
 def test_bytes_per_token_accounting():
