@@ -217,6 +217,22 @@ def _check_extend_rows(o, Ks, Vs, Qs, P_list, E_list, spec, rng, n_rows=6):
     return worst
 
 
+def _check_last_row_lse(lse, Ks, Vs, Qs, P_list, E_list, spec):
+    """The log-sum-exp of the last new token of each request, within the bound
+    of the bf16 kernel's arithmetic: bf16-rounded scaled q moves a score by at
+    most 2^-9 scale sum|q k|, and the row sum adds bf16-rounded p (2^-9 in ln l)."""
+    Hq, Hkv, D = spec.Hq, spec.Hkv, spec.D
+    g = Hq // Hkv
+    q_off = np.concatenate([[0], np.cumsum(E_list)])
+    for r, (P, E) in enumerate(zip(P_list, E_list)):
+        _, _, _, LSE = oracle.attention([Ks[r]], [Vs[r]], [0], [P + E - 1], Qs[r][E - 1:E], Hq, Hkv)
+        qa = np.abs(Qs[r][E - 1].astype(np.float64))
+        ka = np.abs(Ks[r].astype(np.float64))
+        bound = np.array([2.0 ** -9 / np.sqrt(D) * np.max(ka[:, h // g] @ qa[h]) for h in range(Hq)])
+        bound += 2.0 ** -9 + 1e-5
+        assert np.all(np.abs(lse[q_off[r] + E - 1].cpu().numpy() - LSE[0]) <= bound), r
+
+
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 64)])
 def test_extend_long_context(Hq, Hkv, D):
     # contexts of 9000+ keys: the kernel's LDS slot table (4096 keys) is
@@ -228,12 +244,14 @@ def test_extend_long_context(Hq, Hkv, D):
     kp, vp, r2t, Ks, Vs, Qs = _pool_extend_case(spec, P_list, E_list, lambda r, n: perm[offs[r]:offs[r] + n],
                                                 1 << 15, 5)
     q = dev(np.concatenate(Qs), "bf16")
+    lse = torch.empty((sum(E_list), Hq), dtype=torch.float32, device="cuda")
     o = extend_attn(q, kp, vp, r2t, dev_i(range(len(P_list))), dev_i(P_list),
-                    dev_i(np.concatenate([[0], np.cumsum(E_list)]), torch.int64), max(E_list))
+                    dev_i(np.concatenate([[0], np.cumsum(E_list)]), torch.int64), max(E_list), lse=lse)
     torch.cuda.synchronize()
     err = _check_extend_rows(o, Ks, Vs, Qs, P_list, E_list, spec, np.random.default_rng(0))
     _print(f"long-context extend Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}")
     assert err <= BF16_TOL
+    _check_last_row_lse(lse, Ks, Vs, Qs, P_list, E_list, spec)
 
 
 @pytest.mark.parametrize("P_list,E_list", [([20000], [512]), ([12000, 3, 8191], [100, 17, 2])])
@@ -256,17 +274,7 @@ def test_extend_key_splits(P_list, E_list):
     err = _check_extend_rows(o, Ks, Vs, Qs, P_list, E_list, spec, np.random.default_rng(1))
     _print(f"key-split extend P={P_list} E={E_list}: max abs err {err:.3e}")
     assert err <= BF16_TOL
-    # the log-sum-exp of the last token of each request, within the bound of
-    # the bf16 kernel's arithmetic (bf16-rounded scaled q moves a score by at
-    # most 2^-9 scale sum|q k|; the row sum adds bf16-rounded p: 2^-9 in ln l)
-    q_off = np.concatenate([[0], np.cumsum(E_list)])
-    for r, (P, E) in enumerate(zip(P_list, E_list)):
-        _, _, _, LSE = oracle.attention([Ks[r]], [Vs[r]], [0], [P + E - 1], Qs[r][E - 1:E], 64, 8)
-        qa = np.abs(Qs[r][E - 1].astype(np.float64))
-        ka = np.abs(Ks[r].astype(np.float64))
-        bound = np.array([2.0 ** -9 / np.sqrt(128) * np.max(ka[:, h // 8] @ qa[h]) for h in range(64)])
-        bound += 2.0 ** -9 + 1e-5
-        assert np.all(np.abs(lse[q_off[r] + E - 1].cpu().numpy() - LSE[0]) <= bound)
+    _check_last_row_lse(lse, Ks, Vs, Qs, P_list, E_list, spec)
 
 
 def test_pool_over_4gib_extend_and_decode():
