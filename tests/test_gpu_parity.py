@@ -78,8 +78,9 @@ def test_tiny_fp32_extend_then_decode():
 # ---------------------------------------------------------------------------
 # extend: small ragged cases (several tiles, ragged tails, GQA widths, D 64)
 # ---------------------------------------------------------------------------
-def _small_extend_workload(seed, Hq, Hkv, D, prefixes, members, dtype="bf16"):
-    spec = W.Spec("small", dtype, Hq, Hkv, D, 1, 1 << 14, 0.5 if dtype == "bf16" else 1.0, seed)
+def _small_extend_workload(seed, Hq, Hkv, D, prefixes, members, dtype="bf16", q_scale=1.0):
+    spec = W.Spec("small", dtype, Hq, Hkv, D, 1, 1 << 14, 0.5 if dtype == "bf16" else 1.0, seed,
+                  extra={"q_scale": q_scale})
     grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
     sib = np.concatenate([np.arange(m) for m in members]).astype(np.int64)
     ctx = np.array([prefixes[g] + 300 for g in grp], np.int64)
@@ -99,6 +100,24 @@ def test_extend_small_ragged(Hq, Hkv, D):
     bound = extend_lse_bound(case, res)
     _print(f"extend small Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {ldev.max():.2e} "
            f"(worst fraction of its bound {np.max(ldev / bound):.2f})")
+    assert err <= BF16_TOL
+    assert np.all(ldev <= bound)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 64)])
+def test_extend_small_ragged_peaky(Hq, Hkv, D):
+    # queries 8x wider (N(0,1) x 4): scores spread over a few units, so the
+    # softmax concentrates on few keys and a key missed or counted twice
+    # shows in o
+    wl = _small_extend_workload(11, Hq, Hkv, D, prefixes=[0, 37, 200], members=[2, 2, 2], q_scale=8.0)
+    case = GroupCase(wl)
+    E = np.array([1, 130, 77, 0, 33, 257], np.int64)
+    res = run_extend(case, E)
+    idx, O, LSE = oracle_extend(case, res)
+    err = bf16_err(res["o"][idx], O)
+    ldev = np.abs(res["lse"][idx] - LSE)
+    bound = extend_lse_bound(case, res)
+    _print(f"extend peaky Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, worst lse fraction {np.max(ldev / bound):.2f}")
     assert err <= BF16_TOL
     assert np.all(ldev <= bound)
 
@@ -194,7 +213,7 @@ def _pool_extend_case(spec, P_list, E_list, slots_of, num_slots, seed):
     for r, (P, E) in enumerate(zip(P_list, E_list)):
         K = W.values(spec, (P + E, Hkv, D), 10 + r)
         V = W.values(spec, (P + E, Hkv, D), 20 + r)
-        Q = W.values(spec, (E, Hq, D), 30 + r)
+        Q = W.values(spec, (E, Hq, D), 30 + r) * np.float32(spec.extra.get("q_scale", 1.0))
         sl = slots_of(r, P + E)
         assert len(set(sl.tolist())) == P + E and sl.min() >= 0 and sl.max() < num_slots
         idx = torch.as_tensor(sl, dtype=torch.int64, device="cuda")
@@ -254,12 +273,13 @@ def test_extend_long_context(Hq, Hkv, D):
     _check_last_row_lse(lse, Ks, Vs, Qs, P_list, E_list, spec)
 
 
-@pytest.mark.parametrize("P_list,E_list", [([20000], [512]), ([12000, 3, 8191], [100, 17, 2])])
-def test_extend_key_splits(P_list, E_list):
+@pytest.mark.parametrize("P_list,E_list,qs", [([20000], [512], 1.0), ([12000, 3, 8191], [100, 17, 2], 1.0),
+                                              ([12000, 3, 8191], [100, 17, 2], 8.0)])
+def test_extend_key_splits(P_list, E_list, qs):
     # grids of a few requests over long contexts (the last rounds of chunked
     # prefill): each workgroup's keys are cut into 4096-key splits and merged;
     # contexts end inside, on and just past split boundaries
-    spec = W.Spec("keysplit", "bf16", 64, 8, 128, 1, 1 << 16, 0.5, 9)
+    spec = W.Spec("keysplit", "bf16", 64, 8, 128, 1, 1 << 16, 0.5, 9, extra={"q_scale": qs})
     perm = np.random.default_rng(9).permutation(1 << 16).astype(np.int32)
     offs = np.concatenate([[0], np.cumsum(np.array(P_list) + np.array(E_list))])
     kp, vp, r2t, Ks, Vs, Qs = _pool_extend_case(spec, P_list, E_list, lambda r, n: perm[offs[r]:offs[r] + n],
@@ -312,8 +332,8 @@ def test_pool_over_4gib_extend_and_decode():
 # ---------------------------------------------------------------------------
 # decode and cascade decode
 # ---------------------------------------------------------------------------
-def _small_decode_workload(seed, Hq=32, Hkv=8, D=128):
-    spec = W.Spec("small_dec", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed)
+def _small_decode_workload(seed, Hq=32, Hkv=8, D=128, q_scale=1.0):
+    spec = W.Spec("small_dec", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed, extra={"q_scale": q_scale})
     members = [1, 3, 5, 16]
     prefixes = [0, 1, 300, 256]
     grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
@@ -339,6 +359,19 @@ def test_decode_small(cascade, Hq, Hkv, D):
     err = bf16_err(res["o"][reqs], O)
     lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
     _print(f"decode small cascade={cascade} Hq={Hq}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("cascade", [False, True])
+def test_decode_small_peaky(cascade):
+    # queries 8x wider (see test_extend_small_ragged_peaky)
+    wl = _small_decode_workload(17, 32, 8, 128, q_scale=8.0)
+    case = GroupCase(wl)
+    res = run_decode(case, wl.ctx_len.copy(), cascade)
+    reqs, O, LSE = oracle_decode(case, res)
+    err = bf16_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"decode peaky cascade={cascade}: max abs err {err:.3e}, lse err {lerr:.2e}")
     assert err <= BF16_TOL and lerr <= LSE_TOL
 
 

@@ -164,8 +164,12 @@ class GroupWorkload:
         return np.concatenate([kp, ks]), np.concatenate([vp, vs])
 
     def queries(self, r, n, step=0):
+        # spec.extra["q_scale"] (a power of two, so bf16 values stay exact)
+        # widens the queries alone: sharper softmax over the same keys
         s = self.spec
-        return values(s, (n, s.Hq, s.D), T_Q, r, step)
+        q = values(s, (n, s.Hq, s.D), T_Q, r, step)
+        qs = s.extra.get("q_scale", 1.0)
+        return q * np.float32(qs) if qs != 1.0 else q
 
 
 def tiny(seed=0):
