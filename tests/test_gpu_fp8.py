@@ -84,8 +84,8 @@ def _check_pools(case, res, reqs):
         np.testing.assert_array_equal(vp[sl], F8.quantize(V, vs))
 
 
-def _small_decode_workload(seed, Hq, Hkv, D):
-    spec = W.Spec("small_dec_fp8", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed)
+def _small_decode_workload(seed, Hq, Hkv, D, q_scale=1.0):
+    spec = W.Spec("small_dec_fp8", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed, extra={"q_scale": q_scale})
     members = [1, 3, 5, 16]
     prefixes = [0, 1, 300, 256]
     grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
@@ -99,8 +99,8 @@ def _small_decode_workload(seed, Hq, Hkv, D):
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64), (16, 4, 64)])
-def test_decode_fp8_small_flat_and_cascade(Hq, Hkv, D):
-    wl = _small_decode_workload(21, Hq, Hkv, D)
+def test_decode_fp8_small_flat_and_cascade(Hq, Hkv, D, q_scale=1.0):
+    wl = _small_decode_workload(21, Hq, Hkv, D, q_scale)
     case = GroupCase(wl, fp8=True)
     res = run_decode(case, wl.ctx_len.copy(), cascade=False, both=True)
     case.check_r2t()
@@ -111,6 +111,11 @@ def test_decode_fp8_small_flat_and_cascade(Hq, Hkv, D):
         lerr = float(np.max(np.abs(l[reqs] - LSE)))
         _print(f"decode fp8 small {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+def test_decode_fp8_peaky():
+    # queries 8x wider: sharper softmax over the dequantised keys
+    test_decode_fp8_small_flat_and_cascade(32, 8, 128, q_scale=8.0)
 
 
 def _tile_edge_workload(seed, Hq, Hkv, D):

@@ -32,14 +32,14 @@ def _dev_i(x, dtype=torch.int32):
     return torch.as_tensor(np.ascontiguousarray(x)).to(dtype).to("cuda")
 
 
-def _case(seed, Hq, members, prefixes, L, num_slots=1 << 17):
+def _case(seed, Hq, members, prefixes, L, num_slots=1 << 17, q_scale=0.5):
     """Groups of requests sharing prefix slots; returns the device tensors and
     the host bookkeeping needed by the oracle."""
     B = sum(members)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
     pool = (torch.randn((num_slots, DQK), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
-    q = (torch.randn((B, Hq, DQK), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    q = (torch.randn((B, Hq, DQK), generator=gen, device="cuda") * q_scale).to(torch.bfloat16)
     kv_new = (torch.randn((B, DQK), generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
     perm = np.random.default_rng(seed).permutation(num_slots).astype(np.int32)
     stride = int(max(L)) + 1
@@ -150,3 +150,17 @@ def test_mla_cascade_prefix_stage(Hq, members):
     L[0] = 1
     c = _case(31 + Hq, Hq, members, prefixes, L)
     _check(c, list(range(c["B"])), f"prefix stage Hq={Hq} members={members}")
+
+
+@pytest.mark.parametrize("Hq", [16, 128])
+def test_mla_peaky(Hq):
+    # queries 4x wider than the latents (N(0,1) x 2): the softmax concentrates
+    # on few keys, so a key missed or counted twice shows in the output
+    members = [1, 3, 5, 16]
+    prefixes = [0, 1, 300, 1024]
+    rng = np.random.default_rng(40 + Hq)
+    L = []
+    for m, P in zip(members, prefixes):
+        L += [int(x) for x in rng.integers(P + 1, 2600, m)]
+    c = _case(41 + Hq, Hq, members, prefixes, L, q_scale=2.0)
+    _check(c, list(range(c["B"])), f"peaky Hq={Hq}")

@@ -439,14 +439,14 @@ def test_fork_cascade(s):
 # verify step of speculative decoding) -- the split-K path of sgl_extend_attn
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64), (16, 2, 128), (8, 4, 64)])
-def test_small_q_extend_ragged(Hq, Hkv, D):
+def test_small_q_extend_ragged(Hq, Hkv, D, q_scale=1.0):
     # one request per group, so each request has its own cached prefix; the
     # prefixes sit on and next to the 16-key tiles and the splits, and the new
     # tokens (up to the 16 query rows per KV head of the split-K path) are ragged
     g = Hq // Hkv
     emax = max(1, 16 // g)
     prefixes = [0, 1, 15, 16, 17, 300, 1023, 2000]
-    spec = W.Spec("small_q", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, 7)
+    spec = W.Spec("small_q", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, 7, extra={"q_scale": q_scale})
     grp = np.arange(len(prefixes), dtype=np.int64)
     wl = W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, np.zeros(len(prefixes), np.int64),
                          np.array(prefixes, np.int64) + emax)
@@ -459,6 +459,12 @@ def test_small_q_extend_ragged(Hq, Hkv, D):
     lerr = float(np.max(np.abs(res["lse"][idx] - LSE)))
     _print(f"small-q extend Hq={Hq} Hkv={Hkv} D={D} E={E.tolist()}: max abs err {err:.3e}, lse err {lerr:.2e}")
     assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 4, 64)])
+def test_small_q_extend_peaky(Hq, Hkv, D):
+    # queries 8x wider (see test_extend_small_ragged_peaky)
+    test_small_q_extend_ragged(Hq, Hkv, D, q_scale=8.0)
 
 
 def _direct_verify(B, Hq, Hkv, D, P, E, seed, num_slots, sample_rows):
