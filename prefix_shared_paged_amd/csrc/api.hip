@@ -37,6 +37,20 @@ int prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int3
     return c;
 }
 
+// Keys per split of the cascade suffix stage (the whole-row kernel, one
+// workgroup per (request, 4 KV heads, split)).  512 normally; halved (down to
+// 64) while the suffixes -- estimated as max_seq_len - max_prefix_len, which
+// only sizes the splits -- would give fewer than kPrefixWorkgroups
+// workgroups: a batch of a few dozen requests with short suffixes otherwise
+// leaves most compute units idle while each workgroup walks its suffix alone.
+int suffix_chunk(int32_t batch, int32_t max_seq_len, int32_t max_prefix_len, int32_t Hkv) {
+    const int64_t units = (int64_t)batch * (Hkv > 4 ? Hkv / 4 : 1);
+    const int64_t est = std::max<int64_t>(1, (int64_t)max_seq_len - std::max<int32_t>(max_prefix_len, 0));
+    int c = kRowsChunk;
+    while (c > kPrefixChunkMin && units * ceil_div64(est, c) < kPrefixWorkgroups) c /= 2;
+    return c;
+}
+
 bool validate_on() {
     static int v = -1;
     if (v < 0) {
@@ -443,7 +457,8 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
     m.batch = batch; m.G = G; m.Hq = Hq; m.D = D; m.out_bf16 = dtype == SGL_BF16; m.o = o; m.lse = lse;
     const int pchunk = cascade ? prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D) : kPrefixChunkMax;
-    const int fchunk = (cascade ? rows_suffix : rows_flat) ? kRowsChunk : kDecodeChunk;
+    const int fchunk = cascade ? (rows_suffix ? suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv) : kDecodeChunk)
+                               : (rows_flat ? kRowsChunk : kDecodeChunk);
     m.chunk_flat = fchunk; m.chunk_prefix = pchunk;
 
     if (!cascade) {
@@ -501,7 +516,7 @@ size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
     const int64_t Sp = max_prefix_len > 0
                            ? ceil_div64(max_prefix_len, prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D))
                            : 1;
-    const int64_t Ss = ceil_div64(max_seq_len, kRowsChunk);
+    const int64_t Ss = ceil_div64(max_seq_len, suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv));
     return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, Ss, Hq, D);
 }
 
