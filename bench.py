@@ -100,26 +100,40 @@ def traffic_record(kernel):
 
 
 class Pinned:
-    """Ring of pinned host staging buffers, reused only after their copies finished."""
+    """Ring of page-locked staging blocks for the slot lists a step sends to
+    the device.  Each ring slot is one block holding every array (int32), so a
+    step's lists go in a single copy on the compute stream; a host block is
+    refilled only after its copy has finished.  (A copy stream of its own was
+    tried: the cross-stream event waits cost more per step than they hid.)"""
 
-    def __init__(self, torch, n_slots, sizes):
+    def __init__(self, torch, n_slots, sizes, dev):
         self.torch = torch
-        self.bufs = [{k: torch.empty(n, dtype=dt, pin_memory=True) for k, (n, dt) in sizes.items()}
-                     for _ in range(n_slots)]
-        self.events = [None] * n_slots
+        self.offs, total = {}, 0
+        for k, (n, dt) in sizes.items():
+            assert dt == torch.int32
+            self.offs[k] = (total, n)
+            total += n
+        self.blocks = [torch.empty(total, dtype=torch.int32, pin_memory=True) for _ in range(n_slots)]
+        self.bufs = [{k: b[o:o + n] for k, (o, n) in self.offs.items()} for b in self.blocks]
+        self.dblocks = [torch.empty(total, dtype=torch.int32, device=dev) for _ in range(n_slots)]
+        self.copied = [None] * n_slots
         self.i = 0
 
     def next(self):
         i = self.i
         self.i = (self.i + 1) % len(self.bufs)
-        if self.events[i] is not None:
-            self.events[i].synchronize()
+        if self.copied[i] is not None:
+            self.copied[i].synchronize()
         return i, self.bufs[i]
 
-    def done(self, i):
+    def send(self, i):
+        """Copy slot i to its device block; returns the device views of its arrays."""
+        d = self.dblocks[i]
+        d.copy_(self.blocks[i], non_blocking=True)
         ev = self.torch.cuda.Event()
         ev.record()
-        self.events[i] = ev
+        self.copied[i] = ev
+        return {k: d[o:o + n] for k, (o, n) in self.offs.items()}
 
 
 # ---------------------------------------------------------------------------
@@ -168,13 +182,10 @@ def bench_extend(args):
     gpl = torch.tensor([P], dtype=torch.int32, device=dev)
     ws = torch.empty(sp.cascade_workspace_size(B, 1, P + E + 1, B, P, Hq, Hkv, D), dtype=torch.uint8,
                      device=dev)
-    d_prefix = torch.empty(B * P, dtype=torch.int32, device=dev)
     d_poff = torch.arange(0, (B + 1) * P, P, dtype=torch.int64, device=dev)
-    d_new = torch.empty(B * (E + 1), dtype=torch.int32, device=dev)
     d_noff = torch.arange(0, (B + 1) * (E + 1), E + 1, dtype=torch.int64, device=dev)
-    d_store = torch.empty(B * E, dtype=torch.int32, device=dev)
     pin = Pinned(torch, 3, {"prefix": (B * P, torch.int32), "new": (B * (E + 1), torch.int32),
-                            "store": (B * E, torch.int32)})
+                            "store": (B * E, torch.int32)}, dev)
     stream = torch.cuda.current_stream()
     ev_ext = []
 
@@ -199,14 +210,11 @@ def bench_extend(args):
         buf["prefix"].numpy().reshape(B, P)[:] = mslots.reshape(B, P + E)[:, :P]
         buf["new"].numpy()[:] = new
         buf["store"].numpy().reshape(B, E)[:] = new2[:, :E]
-        d_prefix.copy_(buf["prefix"], non_blocking=True)
-        d_new.copy_(buf["new"], non_blocking=True)
-        d_store.copy_(buf["store"], non_blocking=True)
-        pin.done(k)
+        dv = pin.send(k)
         # a3: req_to_token rows (prefix || E + 1 new slots)
-        sp.build_req_to_token(cache.r2t, rows, d_new, d_noff, prefix_slots=d_prefix, prefix_off=d_poff)
+        sp.build_req_to_token(cache.r2t, rows, dv["new"], d_noff, prefix_slots=dv["prefix"], prefix_off=d_poff)
         # a4: store the new tokens' K/V
-        sp.store_kv(k_ext, v_ext, d_store, cache.k_pool, cache.v_pool)
+        sp.store_kv(k_ext, v_ext, dv["store"], cache.k_pool, cache.v_pool)
         # a5: extend attention
         if timed:
             e0 = torch.cuda.Event(enable_timing=True)
@@ -256,8 +264,8 @@ def bench_extend(args):
     flat, off = tokens_of(10 ** 6)
     mslots, lens, nodes = tree.match_batch(flat, off, lock=True)
     new, _ = pool.alloc_batch(np.full(B, E + 1, np.int64), lens, mslots[off[:-1] + P - 1])
-    d_prefix.copy_(torch.from_numpy(mslots.reshape(B, P + E)[:, :P].reshape(-1).copy()))
-    d_new.copy_(torch.from_numpy(new))
+    d_prefix = torch.from_numpy(mslots.reshape(B, P + E)[:, :P].reshape(-1).copy()).to(dev)
+    d_new = torch.from_numpy(new).to(dev)
     sp.build_req_to_token(cache.r2t, rows, d_new, d_noff, prefix_slots=d_prefix, prefix_off=d_poff)
     dws = torch.empty(sp.decode_workspace_size(B, P + E + 1, Hq, Hkv, D), dtype=torch.uint8, device=dev)
     flat_ms = time_call(lambda: sp.decode_attn(q_dec, cache.k_pool, cache.v_pool, cache.r2t, rows, seq_lens,
@@ -491,9 +499,8 @@ def bench_decode(args):
     ws_f = torch.empty(sp.decode_workspace_size(B, int(L.max()), Hq, Hkv, D), dtype=torch.uint8, device=dev)
     ws_c = torch.empty(sp.cascade_workspace_size(B, G, int(L.max()), 16, int(wl.prefix_len.max()), Hq, Hkv, D),
                        dtype=torch.uint8, device=dev)
-    d_new = torch.empty(B, dtype=torch.int32, device=dev)
     d_noff = torch.arange(B + 1, dtype=torch.int64, device=dev)
-    pin = Pinned(torch, 3, {"new": (B, torch.int32)})
+    pin = Pinned(torch, 3, {"new": (B, torch.int32)}, dev)
     pool = cache.pool
     last = np.array([int(st.slots[-1]) for st in rows], np.int32)
     ev = []
@@ -503,8 +510,7 @@ def bench_decode(args):
         new, _ = pool.alloc_batch(np.ones(B, np.int64), L - 1, last)
         k, buf = pin.next()
         buf["new"].numpy()[:] = new
-        d_new.copy_(buf["new"], non_blocking=True)
-        pin.done(k)
+        d_new = pin.send(k)["new"]
         sp.build_req_to_token(cache.r2t, req_rows, d_new, d_noff, new_col0=col0)
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -712,10 +718,9 @@ def bench_verify(args):
     pl = torch.from_numpy(P.astype(np.int32)).to(dev)
     q_off = torch.from_numpy(np.arange(B + 1, dtype=np.int64) * E).to(dev)
     col0 = torch.from_numpy(P.astype(np.int32)).to(dev)
-    d_new = torch.empty(n, dtype=torch.int32, device=dev)
     ws_n = sp.extend_workspace_size(B, n, E, cache.r2t.shape[1], Hq, Hkv, D)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev) if ws_n else None
-    pin = Pinned(torch, 3, {"new": (n, torch.int32)})
+    pin = Pinned(torch, 3, {"new": (n, torch.int32)}, dev)
     pool = cache.pool
     last = np.array([int(st.slots[-1]) for st in rows], np.int32)
     ev = []
@@ -727,8 +732,7 @@ def bench_verify(args):
         new, _ = pool.alloc_batch(np.full(B, E, np.int64), P, last)
         k, buf = pin.next()
         buf["new"].numpy()[:] = new
-        d_new.copy_(buf["new"], non_blocking=True)
-        pin.done(k)
+        d_new = pin.send(k)["new"]
         sp.build_req_to_token(cache.r2t, req_rows, d_new, q_off, new_col0=col0)
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
