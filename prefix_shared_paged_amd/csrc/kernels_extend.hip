@@ -15,33 +15,35 @@
 //
 // Keys are gathered by slot id straight from HBM into LDS with
 // global_load_lds_dwordx4 (no register staging), 32 keys at a time, into rings
-// of four K tiles and four V tiles.  Such a load writes LDS contiguously by
+// of three K tiles and three V tiles.  Such a load writes LDS contiguously by
 // lane, so each lane picks WHICH 16-byte chunk of its row it fetches: chunk c
 // of row r sits at position c ^ swz(r), an XOR swizzle under which both the
 // MFMA operand reads of K and the transposed reads of V are bank-conflict
-// free.  The slot ids themselves are copied once into a table in LDS (4096
-// keys, refilled half by half for longer contexts), so the loop issues no
-// global loads other than the tile loads.
+// free.  The slot ids themselves are copied into a table in LDS (1024 keys,
+// refilled half by half for longer contexts), so the loop issues no global
+// loads other than the tile loads.
 //
-// Each wave owns 32 query rows and walks the keys one 32-key tile at a time
-// with a two-stage software pipeline, so that the matrix pipe always has
-// independent work while the vector ALU runs the softmax:
-//   stage n, part 1: S^T(n+1) = K Q^T on MFMA (keys on M, rows on N, so a lane
-//                    owns one row's scores)  ||  p = 2^s of tile n, its bf16
-//                    rounding and row sum;
-//   stage n, part 2: O^T += V^T P^T of tile n on MFMA (V^T via
-//                    ds_read_b64_tr_b16; the key order inside each MFMA matches
-//                    the S^T accumulator layout, so P needs no lane exchange)
-//                    ||  tile n+1's causal mask and row maximum;
-//   then the loads of K tile n+4 and V tile n+3 into the ring slots that K
-//   tile n and V tile n-1 have left, and one barrier.
-// Every tile load thus has two stages to land.  Softmax details: Q is
+// Occupancy is the lever: every wave's per-tile chain (operand reads, eight
+// chained MFMAs, the row maximum, the exponentials, eight more MFMAs) is
+// latency-bound, and the matrix pipe is kept busy by the other waves of the
+// SIMD.  The kernel is sized for three waves per SIMD (three workgroups per
+// CU: at most 168 VGPRs and 52 KiB of LDS each), which measured faster than
+// two waves per SIMD with a two-stage software pipeline inside each wave.
+// Each wave owns 32 query rows; stage n:
+//   the first K operand reads of tile n, then the slot-table look-ups and the
+//   loads of tile n+2 into the ring slots tile n-1 has left (the two latencies
+//   overlap); S^T(n) = K Q^T on MFMA (keys on M, rows on N, so a lane owns one
+//   row's scores) with each K read four steps ahead of its MFMA; the causal
+//   mask and row maximum; the reference move; p = 2^(s - reference) in bf16
+//   and its row sum; O^T += V^T P^T on MFMA (V^T via ds_read_b64_tr_b16, two
+//   MFMAs ahead; the key order inside each MFMA matches the S^T accumulator
+//   layout, so P needs no lane exchange); the wait for tile n+1; one barrier.
+// Every tile load has two stages to land.  Softmax details: Q is
 // pre-multiplied by scale*log2(e), so scores come out in log2 units; the
-// running reference maximum enters as the accumulator input of the first
-// S^T MFMA, so p = 2^s needs no further arithmetic; the reference is moved
-// lazily, only when a row's tile maximum exceeds it by more than 2^8 (the
-// exact result is unchanged: the reference is only a scaling point), and the
-// mask is applied only to tiles that may cross the diagonal.
+// reference maximum is moved lazily, only when a row's tile maximum exceeds it
+// by more than 2^8 (the exact result is unchanged: the reference is only a
+// scaling point), and the mask is applied only to tiles that may cross the
+// diagonal.
 #include <type_traits>
 
 #include "common.h"
@@ -51,8 +53,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 namespace {
 
 constexpr int BN = 32;        // keys per LDS tile
-constexpr int RING = 4;       // LDS tiles per ring (K and V each)
-constexpr int TABH = 2048;    // keys per half of the LDS slot-id table
+constexpr int RING = 3;       // LDS tiles per ring (K and V each)
+constexpr int TABH = 512;     // keys per half of the LDS slot-id table
 constexpr int BM = kExtendTileRows;   // query rows per workgroup
 constexpr int NT = 256;       // threads
 constexpr float kLazy = 8.f;  // move the reference only when the max grows by more than 2^8
@@ -100,7 +102,7 @@ __device__ __forceinline__ void vm_wait() {
 // for the log-sum-exp merge instead of o -- for grids too small to fill the
 // chip over long contexts.
 template <int D, bool OFF32, bool SPLIT>
-__global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
+__global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_pool,
     const __bf16 *__restrict__ v_pool, int64_t num_slots, const int32_t *__restrict__ r2t,
     int64_t num_rows, int64_t stride, const int32_t *__restrict__ req_rows,
@@ -119,18 +121,16 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char k_lds1[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char k_lds2[TILEB];
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds3[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds1[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds2[TILEB];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds3[TILEB];
     auto kbuf = [&](auto i) -> unsigned char * {
         constexpr int I = decltype(i)::value % RING;
-        return I == 0 ? k_lds0 : I == 1 ? k_lds1 : I == 2 ? k_lds2 : k_lds3;
+        return I == 0 ? k_lds0 : I == 1 ? k_lds1 : k_lds2;
     };
     auto vbuf = [&](auto i) -> unsigned char * {
         constexpr int I = decltype(i)::value % RING;
-        return I == 0 ? v_lds0 : I == 1 ? v_lds1 : I == 2 ? v_lds2 : v_lds3;
+        return I == 0 ? v_lds0 : I == 1 ? v_lds1 : v_lds2;
     };
 
     const int tid = threadIdx.x;
@@ -186,13 +186,8 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 16; j++) oacc[b][j] = 0.f;
     float m_run = -INFINITY;     // reference maximum (log2 units of the scaled score)
+    float m_sub = 0.f;           // the reference as subtracted before 2^x (0 while none)
     float l_run = 0.f;           // this lane's part of the row sum
-    // -reference, broadcast: the accumulator input of the first S^T MFMA, so
-    // scores come out relative to the reference (0 until the first tile,
-    // which always moves it)
-    f32x16 mneg;
-#pragma unroll
-    for (int j = 0; j < 16; j++) mneg[j] = 0.f;
     float thr = -INFINITY;       // a tile maximum above this moves the reference
 
     // ---- slot ids: a table in LDS holds the ids of keys [c*TABH, (c+1)*TABH)
@@ -288,11 +283,23 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
     }
 
     // S^T of one tile (K operands from LDS, Q from registers)
-    auto s_tile = [&](const unsigned char *kt) {
-        f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(kt + koff[0]), qf[0], mneg, 0, 0, 0);
+    // (the operand reads run KA steps ahead of their MFMAs; the fences keep
+    // that order, which the register budget of three waves per SIMD would
+    // otherwise trade for shorter live ranges)
+    constexpr int KA = 4;
+    auto k_first = [&](const unsigned char *kt, bf16x8 (&ka)[KA]) {
 #pragma unroll
-        for (int t = 1; t < QT; t++)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(kt + koff[t]), qf[t], s, 0, 0, 0);
+        for (int t = 0; t < KA; t++) ka[t] = ld_bf16x8(kt + koff[t]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto s_tile = [&](const unsigned char *kt, bf16x8 (&ka)[KA]) {
+        f32x16 s = {};
+#pragma unroll
+        for (int t = 0; t < QT; t++) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % KA], qf[t], s, 0, 0, 0);
+            if (t + KA < QT) ka[t % KA] = ld_bf16x8(kt + koff[t + KA]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         return s;
     };
     // causal mask of tile n (absolute key of accumulator element j:
@@ -309,32 +316,26 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
         for (int j = 1; j < 16; j++) mx = fmaxf(mx, s[j]);
         return max_xor32(mx);
     };
-    // lazy move of the reference (scores and mx are relative to it); rescales
-    // O and l, so it runs after the PV MFMAs issued before it
-    auto move_ref = [&](f32x16 &s, float mx) {
+    // lazy move of the reference (mx is the tile's row maximum); rescales O
+    // and l, so it runs after the PV MFMAs issued before it
+    auto move_ref = [&](float mx) {
         const bool need = mx > thr;
         if (__builtin_amdgcn_ballot_w64(need)) {
-            const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-            const float shift = need ? mx : 0.f;
-            const float m_new = m_ref + shift;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float m_new = need ? mx : m_run;
+            const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int b = 0; b < DBLK; b++) oacc[b] *= alpha;
-#pragma unroll
-            for (int j = 0; j < 16; j++) {
-                s[j] -= shift;
-                mneg[j] = -m_new;
-            }
             m_run = m_new;
-            thr = kLazy;
+            m_sub = m_new == -INFINITY ? 0.f : m_new;
+            thr = m_new + kLazy;
         }
     };
-    // p = 2^s rounded to bf16 (the B operands of the tile's 2 PV steps);
-    // the row sum adds up the same rounded values, two at a time
+    // p = 2^(s - reference) rounded to bf16 (the B operands of the tile's 2 PV
+    // steps); the row sum adds up the same rounded values, two at a time
     auto exp_tile = [&](const f32x16 &s, bf16x8 (&pf)[2]) {
 #pragma unroll
-        for (int j = 0; j < 16; j++) pf[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(s[j]);
+        for (int j = 0; j < 16; j++) pf[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(s[j] - m_sub);
         const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -343,20 +344,24 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
         }
     };
     // O^T += V^T P^T; step s2 covers keys 16*s2 + {4*h2 + 0..3, 8 + 4*h2 + 0..3}
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    constexpr int VA = 2;
+    auto v_op = [&](const unsigned char *vt, int i) {     // operand of PV MFMA i = s2 * DBLK + b
+        const int s2 = i / DBLK, b = i % DBLK;
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)(vt + s2 * 16 * ROWB + voff0[b]));
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)(vt + s2 * 16 * ROWB + voff1[b]));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     auto pv_tile = [&](const unsigned char *vt, const bf16x8 (&pf)[2]) {
+        bf16x8 va[VA];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; s2++) {
+        for (int i = 0; i < VA; i++) va[i] = v_op(vt, i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int b = 0; b < DBLK; b++) {
-                const unsigned char *p0 = vt + s2 * 16 * ROWB + voff0[b];
-                const unsigned char *p1 = vt + s2 * 16 * ROWB + voff1[b];
-                i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p0);
-                i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)p1);
-                typedef short i16x8 __attribute__((ext_vector_type(8)));
-                const i16x8 cat = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, cat), pf[s2],
-                                                                 oacc[b], 0, 0, 0);
-            }
+        for (int i = 0; i < 2 * DBLK; i++) {
+            oacc[i % DBLK] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % VA], pf[i / DBLK], oacc[i % DBLK], 0, 0, 0);
+            if (i + VA < 2 * DBLK) va[i % VA] = v_op(vt, i + VA);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -373,95 +378,70 @@ __global__ void __launch_bounds__(NT, 2) extend_bf16_kernel(
         asm volatile("" ::: "memory");
     };
 
-    // ---- prologue: slot table, then K tiles 0..RING-1 and V tiles 0..RING-2
-    // in the order of the stages -4..-1 they stand for
+    // ---- prologue: slot table, then tiles n0 and n0 + 1 (K and V)
     fill(IC<2 * TABH / NT>{}, k_lo);
     __syncthreads();
-    Off off0[NB], off1[NB];                          // offsets of tile j live in off[j % 2]
-    auto offs = [&](auto i) -> Off (&)[NB] { return decltype(i)::value % 2 ? off1 : off0; };
-    offsets(n0, off0);
-    issue(k_pool, k_lds0, off0);
-    offsets(n0 + 1, off1);
-    issue(k_pool, k_lds1, off1);
-    issue(v_pool, v_lds0, off0);
-    offsets(n0 + 2, off0);
-    issue(k_pool, k_lds2, off0);
-    issue(v_pool, v_lds1, off1);
-    offsets(n0 + 3, off1);
-    issue(k_pool, k_lds3, off1);
-    issue(v_pool, v_lds2, off0);
-    vm_wait<6 * NB>();           // K tile n0
-    lds_barrier();
-    f32x16 s_cur = s_tile(k_lds0);
-    move_ref(s_cur, n0 * BN + 31 > min_pos ? mask_max(s_cur, n0, std::true_type{})
-                                           : mask_max(s_cur, n0, std::false_type{}));
-    vm_wait<4 * NB>();           // V tile n0, K tile n0 + 1
+    Off off[NB];
+    offsets(n0, off);
+    issue(k_pool, k_lds0, off);
+    issue(v_pool, v_lds0, off);
+    offsets(n0 + 1, off);
+    issue(k_pool, k_lds1, off);
+    issue(v_pool, v_lds1, off);
+    vm_wait<2 * NB>();           // tile n0
     if (N == n0 + 1) zero_tail(v_lds0, n0);
     lds_barrier();
 
-    // ---- stage n (R = n % RING): S^T(n+1) || p of tile n; PV of tile n ||
-    // mask and max of tile n+1; then the loads of K tile n+RING and V tile
-    // n+RING-1 into the ring slots that K tile n and V tile n-1 have left.
-    // MASK: tile n+1 may cross the diagonal (a tile past the end is wholly
-    // masked).
+    // ---- stage n (R = (n - n0) % RING): the loads of tile n+2 into the ring
+    // slots tile n-1 has left; S^T of tile n, its mask and row maximum, the
+    // reference move, p, and PV; then the wait for tile n+1 and one barrier.
+    // One chain per wave: the other waves on the SIMD (three per SIMD) fill
+    // the matrix pipe meanwhile.  MASK: tile n may cross the diagonal.
     auto stage = [&](const int n, auto r_tag, auto mask_tag) {
         constexpr int R = decltype(r_tag)::value;
-        const f32x16 s_next = s_tile(kbuf(IC<R + 1>{}));
+        // the first K operand reads go out before the slot-table look-ups of
+        // the loads, so the two latencies overlap
+        bf16x8 ka[KA];
+        k_first(kbuf(IC<R>{}), ka);
+        offsets(n + 2, off);
+        issue(k_pool, kbuf(IC<R + 2>{}), off);
+        issue(v_pool, vbuf(IC<R + 2>{}), off);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 s = s_tile(kbuf(IC<R>{}), ka);
+        move_ref(mask_max(s, n, mask_tag));
         bf16x8 pf[2];
-        exp_tile(s_cur, pf);
+        exp_tile(s, pf);
         pv_tile(vbuf(IC<R>{}), pf);
-        s_cur = s_next;
-        const float mx = mask_max(s_cur, n + 1, mask_tag);
-        // issue order: the K operand reads first, then each S^T MFMA with two
-        // V^T reads and four VALU ops of the previous tile's softmax, then each
-        // PV MFMA with the mask / maximum work of the next tile
-        __builtin_amdgcn_sched_group_barrier(0x100, QT, 0);
-#pragma unroll
-        for (int t = 0; t < QT; t++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * DBLK / QT, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-#pragma unroll
-        for (int t = 0; t < 2 * DBLK; t++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
-        move_ref(s_cur, mx);
-        offsets(n + RING, offs(IC<R>{}));            // tile n+4; tile n+3's are in the other array
-        issue(k_pool, kbuf(IC<R>{}), offs(IC<R>{}));
-        issue(v_pool, vbuf(IC<R + RING - 1>{}), offs(IC<R + 1>{}));
-        // K tile n+2 and V tile n+1 (issued RING-2 stages ago) have landed
-        vm_wait<(RING - 2) * 2 * NB>();
+        vm_wait<2 * NB>();       // tile n+1 has landed
         if (n + 2 == N) zero_tail(vbuf(IC<R + 1>{}), n + 1);
         lds_barrier();
     };
-    // after stage 64m-1 of a long context, half (m+1) % 2 of the slot table
-    // (chunk m-1, whose last look-up was at stage 64m-5) takes chunk m+1
-    auto refill = [&](int n_done) {
-        constexpr int SPC = TABH / BN;               // stages per chunk
-        if (n_done % SPC == 0 && (n_done / SPC + 1) * TABH < k_hi)
-            fill(IC<TABH / NT>{}, (n_done / SPC + 1) * TABH);
+    // the slot table's half that held chunk c - 2 takes chunk c once the
+    // last look-up of chunk c - 2 (tile SPC c - SPC - 1, at stage SPC c - SPC - 3)
+    // is done; chunk c's first look-up comes SPC - 1 stages later
+    constexpr int SPC = TABH / BN;                   // tiles per chunk
+    int fill_c = k_lo / TABH + 2;
+    auto refill = [&](int n_next) {
+        if (n_next >= SPC * (fill_c - 1) - 2 && fill_c * TABH < k_hi) {
+            fill(IC<TABH / NT>{}, fill_c * TABH);
+            ++fill_c;
+        }
     };
-    // stages whose look-ahead tile n+1 lies wholly at or below every row's
-    // position need no mask; the loops run in groups of RING so that ring
-    // positions are known at compile time
-    // (a split's stages also stop before its last tile: the masked loop below
-    // bounds every look-ahead by N)
-    const int n_unmasked = min((min_pos >= 63 ? (min_pos - 63) / BN + 1 : 0) / RING * RING, (N - 1) / RING * RING);
+    // tiles wholly at or below every row's position need no mask; the loops
+    // run in groups of RING so that ring positions are known at compile time
+    const int n_free = min_pos >= 31 ? (min_pos - 31) / BN + 1 : 0;   // tiles 0 .. n_free-1 need no mask
+    const int n_unmasked = n0 + min(max(n_free - n0, 0) / RING * RING, (N - n0) / RING * RING);
     int n = n0;
     for (; n < n_unmasked; n += RING) {
         stage(n, IC<0>{}, std::false_type{});
         stage(n + 1, IC<1>{}, std::false_type{});
         stage(n + 2, IC<2>{}, std::false_type{});
-        stage(n + 3, IC<3>{}, std::false_type{});
         refill(n + RING);
     }
     for (; n < N; n += RING) {
         stage(n, IC<0>{}, std::true_type{});
         if (n + 1 < N) stage(n + 1, IC<1>{}, std::true_type{});
         if (n + 2 < N) stage(n + 2, IC<2>{}, std::true_type{});
-        if (n + 3 < N) stage(n + 3, IC<3>{}, std::true_type{});
         refill(n + RING);
     }
     vm_wait<0>();                // the trailing clamped loads
