@@ -122,11 +122,12 @@ bool small_q_extend(int32_t max_extend_len, int32_t Hq, int32_t Hkv) {
 // when that grid has at most one workgroup per compute unit (one or two long
 // requests, as in the last rounds of chunked prefill) and rows may be long,
 // each workgroup's keys are cut into splits of ksplit keys (a multiple of
-// 4096, two halves of the kernel's slot table) so that about
-// kExtendWgTarget workgroups run; row_stride bounds every context.  Measured
-// on 64/8 heads: one request over 30k keys (128 workgroups) 554 -> 328 us,
-// over 20k keys (256) 451 -> 425 us; with 512 or more workgroups the splits'
-// merge costs more than it gains, so they run unsplit.
+// 4096, so a split starts where the kernel's slot table starts a fill) so
+// that about kExtendWgTarget workgroups run; row_stride bounds every context.
+// Measured on 64/8 heads with the two-waves-per-SIMD kernel: one request over
+// 30k keys (128 workgroups) 554 -> 328 us, over 20k keys (256) 451 -> 425 us;
+// with 512 or more workgroups the splits' merge costs more than it gains, so
+// they run unsplit.
 constexpr int64_t kExtendSplitKeys = 4096;
 constexpr int64_t kExtendWgTarget = 1024;
 constexpr int64_t kExtendSplitMaxWg = 256;
