@@ -249,15 +249,6 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
             __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)((const char *)pool + off[i]),
                                              (SGL_LDS void *)(dst + (wave * NB + i) * 1024), 16, 0, 0);
     };
-    // V rows past the end of the context must hold zeros (their p is 0, and
-    // whatever slot they were read from must not turn 0 * v into NaN); runs
-    // after the loads of that tile have landed.
-    auto zero_tail = [&](unsigned char *vt, int tile) {
-        const int nvalid = k_hi - tile * BN;
-        if (nvalid >= BN) return;
-        for (int idx = tid; idx < (BN - nvalid) * CHK; idx += NT)
-            *(uint4 *)(vt + (nvalid + idx / CHK) * ROWB + 16 * (idx % CHK)) = make_uint4(0, 0, 0, 0);
-    };
 
     // Per-lane LDS byte offsets of the MFMA operand reads.  The swizzle of a
     // row depends only on bits that stay fixed across the 16-row V steps, so
@@ -346,21 +337,31 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
     // O^T += V^T P^T; step s2 covers keys 16*s2 + {4*h2 + 0..3, 8 + 4*h2 + 0..3}
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     constexpr int VA = 2;
-    auto v_op = [&](const unsigned char *vt, int i) {     // operand of PV MFMA i = s2 * DBLK + b
+    // operand of PV MFMA i = s2 * DBLK + b.  TAIL: a tile that may end before
+    // BN keys (nv valid): the values of the missing keys are replaced by zeros
+    // in registers (their p is 0, and the rows they were loaded from must not
+    // turn 0 * v into NaN)
+    auto v_op = [&](const unsigned char *vt, int i, int nv, auto tail_tag) {
         const int s2 = i / DBLK, b = i % DBLK;
         const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)(vt + s2 * 16 * ROWB + voff0[b]));
         const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SGL_LDS i16x4 *)(vt + s2 * 16 * ROWB + voff1[b]));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        i16x8 cat = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        if (decltype(tail_tag)::value) {
+#pragma unroll
+            for (int e = 0; e < 8; e++)         // element e holds key 16 s2 + 8 (e / 4) + 4 h2 + e % 4
+                if (16 * s2 + 8 * (e >> 2) + 4 * h2 + (e & 3) >= nv) cat[e] = 0;
+        }
+        return __builtin_bit_cast(bf16x8, cat);
     };
-    auto pv_tile = [&](const unsigned char *vt, const bf16x8 (&pf)[2]) {
+    auto pv_tile = [&](const unsigned char *vt, const bf16x8 (&pf)[2], int nv, auto tail_tag) {
         bf16x8 va[VA];
 #pragma unroll
-        for (int i = 0; i < VA; i++) va[i] = v_op(vt, i);
+        for (int i = 0; i < VA; i++) va[i] = v_op(vt, i, nv, tail_tag);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 2 * DBLK; i++) {
             oacc[i % DBLK] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % VA], pf[i / DBLK], oacc[i % DBLK], 0, 0, 0);
-            if (i + VA < 2 * DBLK) va[i % VA] = v_op(vt, i + VA);
+            if (i + VA < 2 * DBLK) va[i % VA] = v_op(vt, i + VA, nv, tail_tag);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -389,7 +390,6 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
     issue(k_pool, k_lds1, off);
     issue(v_pool, v_lds1, off);
     vm_wait<2 * NB>();           // tile n0
-    if (N == n0 + 1) zero_tail(v_lds0, n0);
     lds_barrier();
 
     // ---- stage n (R = (n - n0) % RING): the loads of tile n+2 into the ring
@@ -411,9 +411,8 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
         move_ref(mask_max(s, n, mask_tag));
         bf16x8 pf[2];
         exp_tile(s, pf);
-        pv_tile(vbuf(IC<R>{}), pf);
+        pv_tile(vbuf(IC<R>{}), pf, k_hi - n * BN, mask_tag);
         vm_wait<2 * NB>();       // tile n+1 has landed
-        if (n + 2 == N) zero_tail(vbuf(IC<R + 1>{}), n + 1);
         lds_barrier();
     };
     // the slot table's half that held chunk c - 2 takes chunk c once the
