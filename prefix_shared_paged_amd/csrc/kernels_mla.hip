@@ -11,14 +11,20 @@
 // Layout: latent pool [num_slots, 576] bf16 (1152 bytes per token); q [.., Hq,
 // 576]; o [.., Hq, 512].  Work item (as in kernels_decode.hip): a split of
 // keys of a request (flat, suffix) or of a group's shared prefix (cascade),
-// and a block of up to 4 x 16 query rows (request x head).  Every 16-row block
-// gets four waves: wave q computes the partial S^T = K Q^T of the block over
-// its share of the 576 score dims (5, 5, 4, 4 MFMA steps of 32), the four
-// partial tiles are summed through LDS, and each wave then runs the softmax
-// and O^T += V^T P^T for its quarter of the 512 value dims -- so a wave holds
-// a fifth of Q and a quarter of O.  The waves share each 16-key latent tile
-// (18 KiB) in LDS, gathered by slot with non-temporal direct loads, two tiles
-// in flight.
+// and a block of 16-row query blocks (request x head).  Two kernels:
+//   split_mla_full_kernel (flat and suffix splits, every Hq): one wave per
+//     16-row block over all 576 score dims and all 512 value dims, no
+//     reduction across waves; the waves of a workgroup (1, 2 or 4 row blocks)
+//     share each 16-key latent tile (18 KiB) in LDS, gathered by slot with
+//     non-temporal direct loads into a ring of 2 (one or two blocks: four
+//     workgroups per CU) or 4 tiles (four blocks);
+//   split_mla_kernel (the cascade's prefix stage, up to 4 blocks): every
+//     16-row block gets four waves: wave q computes the partial S^T = K Q^T
+//     of the block over its share of the 576 score dims (5, 5, 4, 4 MFMA
+//     steps of 32), the four partial tiles are summed through LDS, and each
+//     wave then runs the softmax and O^T += V^T P^T for its quarter of the
+//     512 value dims -- so a wave holds a fifth of Q and a quarter of O; two
+//     tiles in flight.
 #include <utility>
 
 #include "common.h"
@@ -305,15 +311,16 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &
 
 // One wave per 16-row block over all 576 score dims and all 512 value dims:
 // no reduction across waves.  The RBW waves of a workgroup (RBW row blocks)
-// share each latent tile; a ring of four tiles (three in flight) lets one
+// share each latent tile; a ring of DEPTH tiles (DEPTH - 1 in flight) lets one
 // barrier per tile both publish the tile's direct loads and retire the
-// buffer they refill.
+// buffer they refill.  Four blocks take a ring of four (72 KiB, two
+// workgroups per CU); one or two blocks a ring of two (36 KiB: four
+// workgroups per CU keep more rows in flight than a deeper ring would).
 // A wave keeps its block's Q operand (72 VGPRs) and O^T accumulators (128).
-template <int RBW>
+template <int RBW, int DEPTH>
 __global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
     constexpr int QS = DQK / 32;                   // 18 S^T steps
     constexpr int DB = DV / 16;                    // 32 output blocks of 16 dims
-    constexpr int DEPTH = 4;
     constexpr int KB = 3;                          // K operand reads per batch
     constexpr int VB = 8;                          // V^T reads per batch
     __shared__ __attribute__((aligned(16))) unsigned char t_lds[DEPTH * TBM];
@@ -547,7 +554,19 @@ int launch_split_mla(const SplitArgs &a0, hipStream_t st) {
         constexpr int FR = 4;
         const int64_t n_wf = (int64_t)a.n_sets * a.max_splits * ((a.row_blocks + FR - 1) / FR);
         if (n_wf > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((split_mla_full_kernel<FR>), dim3((unsigned)n_wf), dim3(64 * FR), dyn, st, a);
+        hipLaunchKernelGGL((split_mla_full_kernel<FR, 4>), dim3((unsigned)n_wf), dim3(64 * FR), dyn, st, a);
+        return hip_status(hipGetLastError());
+    }
+    if (a.kind != 1) {
+        // fewer than 64 query rows per split: one wave per 16-row block, one or
+        // two blocks per workgroup sharing a two-tile ring
+        if (a.row_blocks == 1) {
+            hipLaunchKernelGGL((split_mla_full_kernel<1, 2>), dim3((unsigned)n_wg), dim3(64), dyn, st, a);
+        } else {
+            const int64_t n_w2 = (int64_t)a.n_sets * a.max_splits * ((a.row_blocks + 1) / 2);
+            if (n_w2 > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+            hipLaunchKernelGGL((split_mla_full_kernel<2, 2>), dim3((unsigned)n_w2), dim3(128), dyn, st, a);
+        }
         return hip_status(hipGetLastError());
     }
     const dim3 grid((unsigned)n_wg), block(256 * rbw);
