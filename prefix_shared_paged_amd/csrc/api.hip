@@ -382,9 +382,40 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
         if (max_group_size < 1 || max_prefix_len < 0 || max_prefix_len > max_seq_len) return SGL_ERR_INVALID;
         if ((int64_t)max_group_size * g > 4096) return SGL_ERR_UNSUPPORTED;
     }
-    const size_t need = cascade ? sgl_cascade_workspace_size(batch, G, max_seq_len, max_group_size,
-                                                             max_prefix_len, Hq, Hkv, D)
-                                : sgl_decode_workspace_size(batch, max_seq_len, Hq, Hkv, D);
+    // Kernel choice (measured on the 256-request decode workload):
+    //  - cascade suffix: whole-row loads, work dealt to the XCDs set by set
+    //    (the suffixes share nothing, so balance matters most);
+    //  - flat fp8: whole-row loads with blocks of kFlatXcdBlock consecutive
+    //    requests per XCD, so siblings share prefix rows through one L2;
+    //  - flat bf16: the per-head kernel, whose head-per-XCD order already gets
+    //    that reuse with every XCD holding an equal share of each request;
+    //  - other shapes, and the cascade prefix stage: the per-head kernels.
+    const bool rows_ok = dtype != SGL_F32 && (Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16) && g <= 16;
+    const bool rows_flat = rows_ok && fp8;
+    const bool rows_suffix = rows_ok;
+    // Split sizes.  The cascade's preferred prefix and suffix splits depend on
+    // the call's bounds (smaller bounds can prefer smaller splits, hence more
+    // split states), so they are doubled, up to 512 keys, while their states
+    // would not fit the caller's workspace: a workspace sized by
+    // sgl_cascade_workspace_size for larger bounds always holds 512-key splits.
+    int pchunk = kPrefixChunkMax, fchunk = rows_flat ? kRowsChunk : kDecodeChunk;
+    size_t need;
+    if (cascade) {
+        pchunk = prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D);
+        fchunk = rows_suffix ? suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv) : kDecodeChunk;
+        auto need_for = [&](int pc, int fc) {
+            const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pc) : 1;
+            return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, ceil_div64(max_seq_len, fc), Hq, D);
+        };
+        while (need_for(pchunk, fchunk) > workspace_bytes) {
+            if (fchunk < kRowsChunk && (fchunk <= pchunk || pchunk >= kPrefixChunkMax)) fchunk *= 2;
+            else if (pchunk < kPrefixChunkMax) pchunk *= 2;
+            else break;
+        }
+        need = need_for(pchunk, fchunk);
+    } else {
+        need = sgl_decode_workspace_size(batch, max_seq_len, Hq, Hkv, D);
+    }
     if (workspace_bytes < need || (need > 0 && !workspace)) return SGL_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
 
@@ -432,17 +463,6 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     a.num_rows = num_rows; a.row_stride = row_stride; a.req_rows = req_rows; a.seq_lens = seq_lens;
     a.group_ptr = group_ptr; a.group_prefix_len = group_prefix_len; a.batch = batch; a.G = G;
     a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.scale = scale; a.k_scale = k_scale; a.v_scale = v_scale;
-    // Kernel choice (measured on the 256-request decode workload):
-    //  - cascade suffix: whole-row loads, work dealt to the XCDs set by set
-    //    (the suffixes share nothing, so balance matters most);
-    //  - flat fp8: whole-row loads with blocks of kFlatXcdBlock consecutive
-    //    requests per XCD, so siblings share prefix rows through one L2;
-    //  - flat bf16: the per-head kernel, whose head-per-XCD order already gets
-    //    that reuse with every XCD holding an equal share of each request;
-    //  - other shapes, and the cascade prefix stage: the per-head kernels.
-    const bool rows_ok = dtype != SGL_F32 && (Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16) && g <= 16;
-    const bool rows_flat = rows_ok && fp8;
-    const bool rows_suffix = rows_ok;
     auto run_split = [&](const SplitArgs &x, bool rows) {
         if (dtype == SGL_F32) return launch_split_f32(x, st);
         if (rows) {
@@ -457,9 +477,6 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     std::memset(&m, 0, sizeof m);
     m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
     m.batch = batch; m.G = G; m.Hq = Hq; m.D = D; m.out_bf16 = dtype == SGL_BF16; m.o = o; m.lse = lse;
-    const int pchunk = cascade ? prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D) : kPrefixChunkMax;
-    const int fchunk = cascade ? (rows_suffix ? suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv) : kDecodeChunk)
-                               : (rows_flat ? kRowsChunk : kDecodeChunk);
     m.chunk_flat = fchunk; m.chunk_prefix = pchunk;
 
     if (!cascade) {

@@ -207,10 +207,11 @@ def extend_lse_bound(case, res, idx_rows=None):
     return 2.0 ** -9 * (1.0 + scale * np.stack(out)) + 1e-5
 
 
-def run_decode(case, L, cascade, both=False):
+def run_decode(case, L, cascade, both=False, workspace=None):
     """All requests decode one token at position L[r]-1 (L includes it).
     cascade: use the cascade call; both: run the flat call first (it stores the
-    current token's K/V), then the cascade call on the same rows."""
+    current token's K/V), then the cascade call on the same rows.  workspace:
+    the cascade call's workspace (else one sized for this call)."""
     wl = case.wl
     s = wl.spec
     P = np.array([wl.prefix_len[wl.grp[r]] for r in range(wl.B)], np.int64)
@@ -247,6 +248,8 @@ def run_decode(case, L, cascade, both=False):
         gptr = np.zeros(wl.G + 1, np.int32)
         gptr[1:] = np.cumsum(np.bincount(wl.grp, minlength=wl.G))
         fn = cascade_decode_attn_fp8kv if case.fp8 else cascade_decode_attn
+        if workspace is not None:
+            kw["workspace"] = workspace
         o = fn(qd, *fp8_args, c.r2t, req_rows, dev_i(L), dev_i(gptr), dev_i(wl.prefix_len), int(L.max()),
                int(np.diff(gptr).max()), int(wl.prefix_len.max()), lse=lse_t, **kw)
         return o, lse_t

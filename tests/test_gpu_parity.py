@@ -434,6 +434,29 @@ def test_fork_cascade(s):
     assert err <= BF16_TOL and err_c <= BF16_TOL
 
 
+def test_cascade_workspace_sized_for_larger_bounds():
+    # a workspace sized for the longest suffix of a sweep serves the calls with
+    # shorter suffixes, which would prefer smaller (so more) suffix splits: the
+    # call fits its splits to the workspace it is given
+    import prefix_shared_paged_amd as sp
+    wl = W.fork(seed=0)
+    P0 = int(wl.prefix_len.max())
+    big = sp.cascade_workspace_size(wl.B, wl.G, P0 + 512, int(np.bincount(wl.grp).max()), P0, wl.spec.Hq,
+                                    wl.spec.Hkv, wl.spec.D)
+    for s in (2, 40):
+        small = sp.cascade_workspace_size(wl.B, wl.G, P0 + s, int(np.bincount(wl.grp).max()), P0, wl.spec.Hq,
+                                          wl.spec.Hkv, wl.spec.D)
+        case = GroupCase(wl)
+        L = np.full(wl.B, P0 + s, np.int64)
+        ws = torch.empty(big, dtype=torch.uint8, device="cuda")
+        res = run_decode(case, L, cascade=False, both=True, workspace=ws)
+        reqs, O, LSE = oracle_decode(case, res)
+        err_c = bf16_err(res["o_c"][reqs], O)
+        _print(f"fork s={s} in a workspace for s=512 ({big} B; this call alone asks {small} B): "
+               f"cascade max abs err {err_c:.3e}")
+        assert err_c <= BF16_TOL
+
+
 # ---------------------------------------------------------------------------
 # small-q extend (a few new tokens per request over a cached context: the
 # verify step of speculative decoding) -- the split-K path of sgl_extend_attn
