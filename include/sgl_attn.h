@@ -244,7 +244,10 @@ int sgl_store_kv(int dtype, const void *k_new, const void *v_new, int64_t n_toke
  *     KV head) is small and row_stride allows long contexts, where each
  *     workgroup's keys are split in 4096-key multiples and merged the same way.
  *     Either way the result is the same attention (bf16 calls; fp32 calls
- *     ignore the workspace).
+ *     ignore the workspace).  A smaller workspace, or none, is accepted: the
+ *     call then runs the prefill kernel without splits (the same attention
+ *     within rounding, only slower), so a workspace sized for other bounds
+ *     never makes the call fail.
  * scale multiplies q.k (normally 1/sqrt(D)). */
 int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_new,
                     void *k_pool, void *v_pool, int64_t num_slots,

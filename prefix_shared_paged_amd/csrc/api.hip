@@ -299,10 +299,15 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
                              q_off, batch, max_extend_len, st);
         if (rc != SGL_OK) return rc;
     }
-    if (dtype == SGL_BF16 && small_q_extend(max_extend_len, Hq, Hkv)) {
-        const size_t need = sgl_extend_workspace_size(batch, n_tokens, max_extend_len, row_stride, Hq, Hkv, D);
-        if (workspace_bytes < need || !workspace) return SGL_ERR_WORKSPACE;
-        if (n_tokens > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+    // The split-K path of a few new tokens per request and the key splits of
+    // long prefills need workspace for their split states; with less than
+    // that (or none) the call runs the prefill kernel unsplit instead: the
+    // same result, only slower.  So a workspace sized for other bounds never
+    // makes a call fail.
+    const bool small_q_fits = workspace && workspace_bytes >= sgl_extend_workspace_size(batch, n_tokens,
+                                                                                       max_extend_len, row_stride,
+                                                                                       Hq, Hkv, D);
+    if (dtype == SGL_BF16 && small_q_extend(max_extend_len, Hq, Hkv) && small_q_fits && n_tokens <= 0x7fffffff) {
         const int32_t n_spl = extend_splits(batch, Hkv);
         char *wp = (char *)workspace;
         SplitArgs a;
@@ -324,7 +329,9 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
                                  num_slots, r2t, num_rows, row_stride, req_rows, prefix_lens, q_off,
                                  batch, max_extend_len, Hq, Hkv, D, scale, (float *)o, lse, st);
     int32_t ksplit;
-    const int32_t n_split = extend_key_splits(batch, max_extend_len, row_stride, Hq, Hkv, &ksplit);
+    int32_t n_split = extend_key_splits(batch, max_extend_len, row_stride, Hq, Hkv, &ksplit);
+    if (n_split > 1 && (!workspace || workspace_bytes < part_bytes(n_tokens, n_split, Hq, D) || n_tokens > 0x7fffffff))
+        n_split = 1;
     if (n_split <= 1) {
         PartialBuf none;
         std::memset(&none, 0, sizeof none);
@@ -332,9 +339,6 @@ int sgl_extend_attn(int dtype, const void *q, const void *k_new, const void *v_n
                                   num_rows, row_stride, req_rows, prefix_lens, q_off, batch, max_extend_len, Hq, Hkv,
                                   D, scale, (__bf16 *)o, lse, 1, 0, none, st);
     }
-    const size_t need = part_bytes(n_tokens, n_split, Hq, D);
-    if (workspace_bytes < need || !workspace) return SGL_ERR_WORKSPACE;
-    if (n_tokens > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     char *wp = (char *)workspace;
     const PartialBuf part = carve(wp, n_tokens, n_split, Hq, D);
     if ((rc = launch_extend_bf16((const __bf16 *)q, (const __bf16 *)k_pool, (const __bf16 *)v_pool, num_slots, r2t,

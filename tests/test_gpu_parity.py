@@ -434,6 +434,29 @@ def test_fork_cascade(s):
     assert err <= BF16_TOL and err_c <= BF16_TOL
 
 
+@pytest.mark.parametrize("P,E", [(12000, 100), (3000, 2)])
+def test_extend_without_workspace_runs_unsplit(P, E):
+    # key splits (one long request) and the small-q split-K path (2 new tokens)
+    # need split-state workspace; given none, the call runs the prefill kernel
+    # unsplit: the same attention within rounding
+    Hq, Hkv, D, S = 32, 8, 128, 1 << 16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(P + E)
+    rnd = lambda *shape: (torch.randn(shape, generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    kp, vp, q = rnd(S, Hkv, D), rnd(S, Hkv, D), rnd(E, Hq, D)
+    r2t = torch.randperm(S, generator=gen, device="cuda")[:P + E].to(torch.int32)[None]
+    args = (q, kp, vp, r2t, dev_i([0]), dev_i([P]), dev_i([0, E], torch.int64), E)
+    l1 = torch.empty((E, Hq), dtype=torch.float32, device="cuda")
+    l2 = torch.empty((E, Hq), dtype=torch.float32, device="cuda")
+    o1 = extend_attn(*args, lse=l1)
+    o2 = extend_attn(*args, lse=l2, workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    err = float((o1.float() - o2.float()).abs().max())
+    lerr = float((l1 - l2).abs().max())
+    _print(f"extend P={P} E={E}: split vs unsplit max abs diff {err:.3e}, lse {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= 1e-3
+
+
 def test_cascade_workspace_sized_for_larger_bounds():
     # a workspace sized for the longest suffix of a sweep serves the calls with
     # shorter suffixes, which would prefer smaller (so more) suffix splits: the
