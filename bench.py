@@ -1,33 +1,49 @@
 #!/usr/bin/env python3
 """Benchmark of the paged prefix-shared attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config extend|decode|fork|multiturn]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--config extend|tiny|decode|fork|verify|mla|hicache|multiturn]
                     [--kv bf16|fp8] [--no-cpu-baseline]
 
-Default workload ("extend"): 64 requests share a cached 2048-token prefix and
-each adds 256 new causal tokens (32 query / 8 KV heads, head_dim 128, bf16,
-2^20-slot pool, page size 1), then decodes one token.  One step is one pass
-of the whole path over one batch:
-  a1/a2  host: batched longest-prefix match + lock, slot allocation
-  a3     GPU: req_to_token rows (prefix slots + new slots)
-  a4     GPU: store the new tokens' K/V into the pool
-  a5     GPU: extend attention (bf16 MFMA)
-  a2     host: insert the requests into the radix tree (prefill complete)
-  a7     GPU: cascade decode of one token per request (shared prefix read
-         once for the group), with its K/V store and req_to_token append
-  host:  unlock, free the decode slots, LRU-evict the requests' suffixes.
-Host work of a step overlaps the GPU work of the previous one (pinned
-staging buffers, asynchronous copies).  Inputs (Q/K/V) are resident in HBM
-before the timed region.  Prints ONE JSON line.
+Default ("extend"): one JSON line carrying both halves of the metric from one
+run.
+  * The extend workload, timed step by step: 64 requests share a cached
+    2048-token prefix and each adds 256 new causal tokens (32 query / 8 KV
+    heads, head_dim 128, bf16, 2^20-slot pool, page size 1), then decodes
+    one token.  One step is one pass of the whole path over one batch:
+      a1/a2  host: batched longest-prefix match + lock, slot allocation
+      a3     GPU: req_to_token rows (prefix slots + new slots)
+      a4     GPU: store the new tokens' K/V into the pool
+      a5     GPU: extend attention (bf16 MFMA)
+      a2     host: insert the requests into the radix tree (prefill complete)
+      a7     GPU: cascade decode of one token per request (shared prefix read
+             once for the group), with its K/V store and req_to_token append
+      host:  unlock, free the decode slots, LRU-evict the requests' suffixes.
+    Host work of a step overlaps the GPU work of the previous one (pinned
+    staging buffers, asynchronous copies).  `value` is the step's query
+    tokens per second; `roofline` is the extend kernel (bf16 MFMA).
+  * The decode batch (256 requests in 16 prefix groups, contexts up to 8192,
+    2^21-slot pool): flat and cascade decode calls, each with its own HBM
+    roofline ("decode_batch").
+  * The parallel-sampling fork sweep (16 prompts of 4096 tokens x 8
+    branches, suffixes 1..512, cascade decode per step): its aggregate HBM
+    roofline ("fork_sweep").
+Before every timed call a 512 MiB scratch buffer is read and written (twice
+the 256 MB Infinity Cache, far beyond the L2s), outside the call's events:
+it stands in for the model's other layers between two calls of this layer,
+so no call finds the previous repetition's data in a cache.  Inputs (Q/K/V)
+are resident in HBM before the timed region.
 
-Other --config values time the decode-batch, fork-sweep, verify (small-q
-extend: q_len new tokens per request over long cached contexts), mla (latent
-decode: one 576-dim latent row per token shared by every query head),
-hicache (KV rows moved between a page-locked host tier and the pool) and
-multi-turn workloads for reporting; their lines have the same shape.  --kv fp8 runs the
-decode and fork workloads over an FP8 (e4m3fn) KV cache with per-head
-factors (the same bf16 queries, bf16 MFMA arithmetic, one byte per cached
-element).
+Other --config values print one line each: tiny (the fp32 4-request
+extend + decode, hipEvent medians of >= 50 calls and the full oracle),
+decode, fork, verify (small-q extend: q_len new tokens per request over long
+cached contexts), mla (latent decode: one 576-dim latent row per token shared
+by every query head), hicache (KV rows moved between a page-locked host tier
+and the pool) and multiturn (chunked prefill interleaved with decode, page
+16; extend and decode calls timed separately and summed over the rounds).
+--kv fp8 runs the decode and fork workloads over an FP8 (e4m3fn) KV cache
+with per-head factors (the same bf16 queries, bf16 MFMA arithmetic, one byte
+per cached element).
 """
 import argparse
 import hashlib
@@ -44,6 +60,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 PEAK_HOST_LINK_GBPS = 63.0     # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b
+PEAK_F32_VALU_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (dual) x 2.4 GHz)
 
 
 def parse():
@@ -52,7 +69,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="extend",
-                    choices=["extend", "decode", "fork", "verify", "mla", "hicache", "multiturn"])
+                    choices=["extend", "tiny", "decode", "fork", "verify", "mla", "hicache", "multiturn"])
     ap.add_argument("--mla-heads", type=int, default=128, help="query heads of the mla workload")
     ap.add_argument("--q-len", type=int, default=4, help="new tokens per request of the verify workload")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
@@ -61,6 +78,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (scales HBM counters)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="default config: leave out the decode-batch and fork-sweep parts")
     return ap.parse_args()
 
 
@@ -72,6 +91,10 @@ KERNEL_SOURCES = {
                             "kernels_misc.hip", "api.hip", "common.h"],
     "cascade_decode_call_fp8": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
                                 "kernels_misc.hip", "api.hip", "common.h"],
+    "flat_decode_call": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
+                         "kernels_misc.hip", "api.hip", "common.h"],
+    "flat_decode_call_fp8": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
+                             "kernels_misc.hip", "api.hip", "common.h"],
 }
 
 
@@ -136,10 +159,44 @@ class Pinned:
         return {k: d[o:o + n] for k, (o, n) in self.offs.items()}
 
 
+class MallFlush:
+    """Reads and writes a 512 MiB scratch buffer on the launch stream (twice
+    the 256 MB Infinity Cache, far beyond the 4 MB L2 of each XCD), so the
+    next call finds none of the previous repetition's data in a cache.  Runs
+    before every timed call, outside its events; it stands in for the other
+    layers of a model that run between two calls of one layer."""
+    MIB = 512
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.buf = torch.zeros(self.MIB << 18, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.buf.add_(1)
+
+    def time_ms(self, n=10):
+        t = time_events(self, n)
+        return float(np.median(t))
+
+
+def hbm_roofline(byts, ms, kernel, traffic=None, **extra):
+    """Roofline object of an HBM-bound call: algorithmic bytes / time against
+    8 TB/s; with a counter record (traffic, HBM bytes per launch) also the
+    measured HBM rate."""
+    gbps = byts / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+            "traffic": traffic, "kernel": kernel, "bytes_per_launch": byts, "avg_launch_ms": ms}
+    if traffic:
+        roof["hbm_counter_gbps"] = traffic / (ms * 1e-3) / 1e9
+        roof["hbm_counter_frac"] = roof["hbm_counter_gbps"] / PEAK_HBM_GBPS
+    roof.update(extra)
+    return roof
+
+
 # ---------------------------------------------------------------------------
 # default workload: extend over a shared cached prefix + one cascade decode token
 # ---------------------------------------------------------------------------
-def bench_extend(args):
+def bench_extend(args, flush):
     import torch
     import workloads as W
     import prefix_shared_paged_amd as sp
@@ -186,7 +243,6 @@ def bench_extend(args):
     d_noff = torch.arange(0, (B + 1) * (E + 1), E + 1, dtype=torch.int64, device=dev)
     pin = Pinned(torch, 3, {"prefix": (B * P, torch.int32), "new": (B * (E + 1), torch.int32),
                             "store": (B * E, torch.int32)}, dev)
-    stream = torch.cuda.current_stream()
     ev_ext = []
 
     def tokens_of(step):
@@ -215,7 +271,8 @@ def bench_extend(args):
         sp.build_req_to_token(cache.r2t, rows, dv["new"], d_noff, prefix_slots=dv["prefix"], prefix_off=d_poff)
         # a4: store the new tokens' K/V
         sp.store_kv(k_ext, v_ext, dv["store"], cache.k_pool, cache.v_pool)
-        # a5: extend attention
+        # a5: extend attention (caches flushed first, outside its events)
+        flush()
         if timed:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -247,39 +304,10 @@ def bench_extend(args):
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     ext_ms, ext_stalls = event_mean_ms(ev_ext)
-
-    # decode-only timings (flat vs cascade) on the same state, outside the step
-    def time_call(fn, n=20):
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(n):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
-
-    # leave one admitted batch in place for the decode-only timings
-    flat, off = tokens_of(10 ** 6)
-    mslots, lens, nodes = tree.match_batch(flat, off, lock=True)
-    new, _ = pool.alloc_batch(np.full(B, E + 1, np.int64), lens, mslots[off[:-1] + P - 1])
-    d_prefix = torch.from_numpy(mslots.reshape(B, P + E)[:, :P].reshape(-1).copy()).to(dev)
-    d_new = torch.from_numpy(new).to(dev)
-    sp.build_req_to_token(cache.r2t, rows, d_new, d_noff, prefix_slots=d_prefix, prefix_off=d_poff)
-    dws = torch.empty(sp.decode_workspace_size(B, P + E + 1, Hq, Hkv, D), dtype=torch.uint8, device=dev)
-    flat_ms = time_call(lambda: sp.decode_attn(q_dec, cache.k_pool, cache.v_pool, cache.r2t, rows, seq_lens,
-                                               P + E + 1, o=o_dec, workspace=dws))
-    casc_ms = time_call(lambda: sp.cascade_decode_attn(q_dec, cache.k_pool, cache.v_pool, cache.r2t, rows,
-                                                       seq_lens, gptr, gpl, P + E + 1, B, P, o=o_dec,
-                                                       workspace=ws))
+    ext_med = float(np.median([a.elapsed_time(b) for a, b in ev_ext]))
 
     flops = acc.extend_flops([P] * B, [E] * B, Hq, D)
     tflops = flops / (ext_ms * 1e-3) / 1e12
-    elt = 2
-    L = [P + E + 1] * B
-    flat_bytes = acc.decode_bytes_flat(L, Hq, Hkv, D, elt)
-    casc_bytes = acc.decode_bytes_cascade(L, [0] * B, [P], Hq, Hkv, D, elt)
     tokens_per_step = B * E + B
     traffic = traffic_record("extend_bf16_kernel")
     line = {
@@ -302,13 +330,9 @@ def bench_extend(args):
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "extend_bf16_kernel", "flops_per_launch": flops, "avg_launch_ms": ext_ms,
-                     "host_stalled_launches_excluded": ext_stalls},
+                     "median_launch_ms": ext_med, "host_stalled_launches_excluded": ext_stalls},
         "extend_tflops": tflops,
-        "decode": {"flat_ms": flat_ms, "cascade_ms": casc_ms,
-                   "flat_hbm_gbps": flat_bytes / (flat_ms * 1e-3) / 1e9,
-                   "cascade_hbm_gbps": casc_bytes / (casc_ms * 1e-3) / 1e9,
-                   "cascade_tokens_per_s": B / (casc_ms * 1e-3),
-                   "flat_algorithmic_bytes": flat_bytes, "cascade_algorithmic_bytes": casc_bytes},
+        "mall_flush_ms": flush.time_ms(),
     }
     return line, ("extend", wl, P, E)
 
@@ -459,7 +483,10 @@ def base_line(metric_value, ms, args, config, roofline, extra):
 # ---------------------------------------------------------------------------
 # decode batch: 256 requests in 16 prefix groups, one token each (flat and cascade)
 # ---------------------------------------------------------------------------
-def bench_decode(args):
+def measure_decode(args, flush, fp8=False):
+    """The 256-request decode batch, flat and cascade: per-call HIP events
+    (caches flushed before each call, outside its events) and each call's HBM
+    roofline.  Returns (result dict, workload)."""
     import torch
     import workloads as W
     import prefix_shared_paged_amd as sp
@@ -472,7 +499,6 @@ def bench_decode(args):
     dev = "cuda"
     L = wl.ctx_len.astype(np.int64)
     P = wl.prefix_len[wl.grp].astype(np.int64)
-    fp8 = args.kv == "fp8"
     cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, int(L.max()) + 1, W.pool_order(s), dev,
                          kv_scale=W.fp8_scales(s) if fp8 else None)
     if fp8:
@@ -512,6 +538,7 @@ def bench_decode(args):
         buf["new"].numpy()[:] = new
         d_new = pin.send(k)["new"]
         sp.build_req_to_token(cache.r2t, req_rows, d_new, d_noff, new_col0=col0)
+        flush()
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -538,30 +565,45 @@ def bench_decode(args):
         for _ in range(args.steps):
             step(mode == "cascade", True)
         torch.cuda.synchronize()
-        res[mode] = ((time.perf_counter() - t0) * 1e3 / args.steps, event_mean_ms(ev)[0])
+        mean, stalls = event_mean_ms(ev)
+        res[mode] = dict(wall_ms_per_step=(time.perf_counter() - t0) * 1e3 / args.steps, call_ms=mean,
+                         median_ms=float(np.median([a.elapsed_time(b) for a, b in ev])), stalls=stalls)
     kelt = 1 if fp8 else 2
-    flat_bytes = acc.decode_bytes_flat(L, Hq, Hkv, D, kelt, 2)
-    casc_bytes = acc.decode_bytes_cascade(L, wl.grp, wl.prefix_len, Hq, Hkv, D, kelt, 2)
-    ms_c, call_c = res["cascade"]
-    ms_f, call_f = res["flat"]
-    gbps_c = casc_bytes / (call_c * 1e-3) / 1e9
-    gbps_f = flat_bytes / (call_f * 1e-3) / 1e9
-    config = {"workload": "decode: 256 requests in 16 prefix groups (prefix ~U[512,4096], context "
-                          "~U[max(1024,P+1),8192]), one token each, cascade decode; 32/8 heads, head_dim 128, "
-                          "2^21-slot pool, page 1" + (", FP8 e4m3fn KV cache with per-head factors" if fp8 else ""),
-              "batch": B, "groups": G, "kv_cache": "fp8_e4m3fn" if fp8 else "bf16"}
-    roof = {"bound": "hbm", "achieved": gbps_c, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": gbps_c / PEAK_HBM_GBPS,
-            "traffic": traffic_record("cascade_decode_call_fp8" if fp8 else "cascade_decode_call"),
-            "kernel": "cascade decode call (prefix + suffix split kernels + merge)",
-            "bytes_per_launch": casc_bytes, "avg_launch_ms": call_c}
-    line = base_line(B / (ms_c * 1e-3), ms_c, args, config, roof, {
-        "flat": {"ms_per_step": ms_f, "call_ms": call_f, "hbm_gbps": gbps_f, "frac": gbps_f / PEAK_HBM_GBPS,
-                 "tokens_per_s": B / (ms_f * 1e-3), "algorithmic_bytes": flat_bytes},
-        "cascade": {"call_ms": call_c, "hbm_gbps": gbps_c, "algorithmic_bytes": casc_bytes,
-                    "tokens_per_s_call_only": B / (call_c * 1e-3)}})
+    sfx = "_fp8" if fp8 else ""
+    flat_bytes = acc.decode_bytes_flat(L, Hq, Hkv, D, kelt, 2, stored=B)
+    casc_bytes = acc.decode_bytes_cascade(L, wl.grp, wl.prefix_len, Hq, Hkv, D, kelt, 2, stored=B)
+    out = {}
+    for mode, byts in (("flat", flat_bytes), ("cascade", casc_bytes)):
+        r = res[mode]
+        kern = ("flat decode call (split kernel + merge)" if mode == "flat"
+                else "cascade decode call (prefix + suffix split kernels + merge)")
+        roof = hbm_roofline(byts, r["call_ms"], kern, traffic_record(f"{mode}_decode_call{sfx}"),
+                            median_launch_ms=r["median_ms"], host_stalled_calls_excluded=r["stalls"])
+        out[mode] = {"call_ms": r["call_ms"], "tokens_per_s": B / (r["call_ms"] * 1e-3),
+                     "algorithmic_bytes": byts, "roofline": roof, "wall_ms_per_step": r["wall_ms_per_step"]}
+    out["flat"]["note"] = ("flat decode counts each request's shared prefix once per request (the method's "
+                           "algorithmic bytes); the chip serves repeated prefix rows from L2/MALL, so its HBM "
+                           "traffic is hbm_counter_gbps, not achieved")
+    out["config"] = {"workload": "decode: 256 requests in 16 prefix groups (prefix ~U[512,4096], context "
+                                 "~U[max(1024,P+1),8192]), one token each (stored, then attended); 32/8 heads, "
+                                 "head_dim 128, 2^21-slot pool, page 1"
+                                 + (", FP8 e4m3fn KV cache with per-head factors" if fp8 else ""),
+                     "batch": B, "groups": G, "kv_cache": "fp8_e4m3fn" if fp8 else "bf16"}
+    return out, wl
+
+
+def bench_decode(args, flush):
+    import workloads as W
+    fp8 = args.kv == "fp8"
+    res, wl = measure_decode(args, flush, fp8)
+    s = wl.spec
+    B, Hq, Hkv = wl.B, s.Hq, s.Hkv
+    c = res["cascade"]
+    line = base_line(B / (c["call_ms"] * 1e-3), c["call_ms"], args, res["config"], c["roofline"], {
+        "flat": res["flat"], "cascade": c, "mall_flush_ms": flush.time_ms()})
     if not args.no_cpu_baseline:
         # oracle sample: decode rows of the first requests, drawn by the seeded generator
+        L = wl.ctx_len
         Ks, Vs, rws = [], [], []
         for r in range(min(B, 24)):
             K, V = wl.logical_kv(r)
@@ -576,7 +618,10 @@ def bench_decode(args):
 # ---------------------------------------------------------------------------
 # fork: 16 prompts x 4096 tokens, 8 branches each; suffixes grow 1..512 (cascade)
 # ---------------------------------------------------------------------------
-def bench_fork(args):
+def measure_fork(args, flush, fp8=False, n_sweeps=1):
+    """The fork sweep: per step s = 1..512 one cascade decode call (caches
+    flushed before it, outside its events); aggregate = sum of bytes / sum of
+    call times over the sweep.  Returns (result dict, workload)."""
     import torch
     import workloads as W
     import prefix_shared_paged_amd as sp
@@ -588,7 +633,6 @@ def bench_fork(args):
     B, G, Hq, Hkv, D = wl.B, wl.G, s.Hq, s.Hkv, s.D
     Pp, S = 4096, 512
     dev = "cuda"
-    fp8 = args.kv == "fp8"
     cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.bfloat16, B + G, Pp + S + 1, W.pool_order(s), dev,
                          kv_scale=W.fp8_scales(s) if fp8 else None)
     if fp8:
@@ -632,6 +676,7 @@ def bench_fork(args):
         evs = []
         for k in range(S):
             sp.build_req_to_token(cache.r2t, req_rows, d_new[k], d_noff, new_col0=col0s[k])
+            flush()
             if timed:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
@@ -645,41 +690,51 @@ def bench_fork(args):
         pool.free(slots.reshape(-1))
         return evs
 
-    for _ in range(max(1, args.warmup // 5)):
-        sweep(False)
+    sweep(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    n_sweeps = max(1, args.steps // 10)
     for _ in range(n_sweeps):
         evs = sweep(True)
         per_s += np.array([a.elapsed_time(b) for a, b in evs])
-    t1 = time.perf_counter()
+    wall = (time.perf_counter() - t0) * 1e3 / n_sweeps
     per_s /= n_sweeps
-    ms = (t1 - t0) * 1e3 / n_sweeps
     kelt = 1 if fp8 else 2
     bytes_s = np.array([acc.decode_bytes_cascade([Pp + k] * B, np.repeat(np.arange(G), 8), [Pp] * G, Hq, Hkv, D,
-                                                 kelt, 2) for k in range(1, S + 1)], np.float64)
-    gbps = bytes_s.sum() / (per_s.sum() * 1e-3) / 1e9
-    config = {"workload": "fork: 16 prompts x 4096 tokens, 8 branches each (128 requests), suffix grows "
-                          "1..512 in lockstep, cascade decode per step; 32/8 heads, head_dim 128, 2^18-slot pool"
-                          + (", FP8 e4m3fn KV cache with per-head factors" if fp8 else ""),
-              "prompts": G, "branches": 8, "prompt_len": Pp, "steps_per_sweep": S,
-              "kv_cache": "fp8_e4m3fn" if fp8 else "bf16"}
-    roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
-            "traffic": None, "kernel": "cascade decode call, summed over the sweep",
-            "bytes_per_sweep": float(bytes_s.sum()), "avg_launch_ms": float(per_s.mean())}
-    line = base_line(B * S / (ms * 1e-3), ms, args, config, roof, {
-        "per_s_gbps": {str(k): float(bytes_s[k - 1] / (per_s[k - 1] * 1e-3) / 1e9) for k in (1, 2, 64, 256, 512)},
-        "per_s_ms": {str(k): float(per_s[k - 1]) for k in (1, 2, 64, 256, 512)},
-        "sweeps": n_sweeps})
+                                                 kelt, 2, stored=B) for k in range(1, S + 1)], np.float64)
+    tot_ms = float(per_s.sum())
+    roof = hbm_roofline(float(bytes_s.sum()), tot_ms, "cascade decode call, summed over the sweep s = 1..512",
+                        None, bytes_per_sweep=float(bytes_s.sum()), avg_call_ms=float(per_s.mean()))
+    out = {"sweep_ms": tot_ms, "wall_ms_per_sweep": wall, "tokens_per_s": B * S / (tot_ms * 1e-3),
+           "roofline": roof, "sweeps": n_sweeps,
+           "per_s_gbps": {str(k): float(bytes_s[k - 1] / (per_s[k - 1] * 1e-3) / 1e9) for k in (1, 2, 64, 256, 512)},
+           "per_s_ms": {str(k): float(per_s[k - 1]) for k in (1, 2, 64, 256, 512)},
+           "config": {"workload": "fork: 16 prompts x 4096 tokens, 8 branches each (128 requests), suffix grows "
+                                  "1..512 in lockstep, cascade decode per step (current token stored, then "
+                                  "attended); 32/8 heads, head_dim 128, 2^18-slot pool"
+                                  + (", FP8 e4m3fn KV cache with per-head factors" if fp8 else ""),
+                      "prompts": G, "branches": 8, "prompt_len": Pp, "steps_per_sweep": S,
+                      "kv_cache": "fp8_e4m3fn" if fp8 else "bf16"}}
+    return out, wl
+
+
+def bench_fork(args, flush):
+    import workloads as W
+    fp8 = args.kv == "fp8"
+    n_sweeps = max(1, args.steps // 10)
+    res, wl = measure_fork(args, flush, fp8, n_sweeps)
+    s = wl.spec
+    B, Hq, Hkv = wl.B, s.Hq, s.Hkv
+    line = base_line(res["tokens_per_s"], res["sweep_ms"], args, res["config"], res["roofline"], {
+        k: v for k, v in res.items() if k not in ("roofline", "config")})
     line["steps"] = n_sweeps
+    line["mall_flush_ms"] = flush.time_ms()
     if not args.no_cpu_baseline:
         Ks, Vs, rws = [], [], []
         for r in range(0, B, 4):
-            K, V = wl.logical_kv(r, S)
+            K, V = wl.logical_kv(r, 512)
             Ks.append(K)
             Vs.append(V)
-            rws.append((len(Ks) - 1, Pp + S - 1, wl.queries(r, 1)[0]))
+            rws.append((len(Ks) - 1, 4096 + 512 - 1, wl.queries(r, 1)[0]))
         line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "fork (s=512)",
                                                  W.fp8_scales(s) if fp8 else None)
     return line
@@ -688,7 +743,7 @@ def bench_fork(args):
 # ---------------------------------------------------------------------------
 # verify: 64 requests, own cached contexts ~U[2048, 8192], q_len new tokens each
 # ---------------------------------------------------------------------------
-def bench_verify(args):
+def bench_verify(args, flush):
     import torch
     import workloads as W
     import prefix_shared_paged_amd as sp
@@ -734,6 +789,7 @@ def bench_verify(args):
         buf["new"].numpy()[:] = new
         d_new = pin.send(k)["new"]
         sp.build_req_to_token(cache.r2t, req_rows, d_new, q_off, new_col0=col0)
+        flush()
         if timed:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -763,8 +819,9 @@ def bench_verify(args):
     roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
             "traffic": None, "kernel": "extend call (split kernel + merge, or the prefill kernel)",
             "bytes_per_launch": byts, "avg_launch_ms": call}
-    line = base_line(n / (ms * 1e-3), ms, args, config, roof, {"call_ms": call, "host_stalled_calls_excluded": stalls,
-                                                                "tokens_per_s_call_only": n / (call * 1e-3)})
+    line = base_line(n / (call * 1e-3), call, args, config, roof, {
+        "call_ms": call, "wall_ms_per_step": ms, "host_stalled_calls_excluded": stalls,
+        "tokens_per_s_call_only": n / (call * 1e-3)})
     if not args.no_cpu_baseline:
         Ks, Vs, rws = [], [], []
         for r in range(min(B, 8)):
@@ -780,7 +837,7 @@ def bench_verify(args):
 # ---------------------------------------------------------------------------
 # mla: latent decode, 128 requests in 16 groups of 8, one 576-dim latent per token
 # ---------------------------------------------------------------------------
-def bench_mla(args):
+def bench_mla(args, flush):
     import torch
     import workloads as W
     import prefix_shared_paged_amd as sp
@@ -827,11 +884,13 @@ def bench_mla(args):
     res = {}
     for name, fn in (("cascade", casc), ("flat", flat)):
         for _ in range(args.warmup):
+            flush()
             fn()
         torch.cuda.synchronize()
         evs = []
         t0 = time.perf_counter()
         for _ in range(args.steps):
+            flush()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
@@ -855,7 +914,7 @@ def bench_mla(args):
     roof = {"bound": "hbm", "achieved": gbps_c, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps_c / PEAK_HBM_GBPS,
             "traffic": None, "kernel": "mla cascade decode call (prefix + suffix split kernels + merge)",
             "bytes_per_launch": casc_bytes, "avg_launch_ms": call_c}
-    line = base_line(B / (ms_c * 1e-3), ms_c, args, config, roof, {
+    line = base_line(B / (call_c * 1e-3), call_c, args, config, roof, {"wall_ms_per_step": ms_c,
         "flat": {"call_ms": call_f, "hbm_gbps": gbps_f, "frac": gbps_f / PEAK_HBM_GBPS,
                  "tflops": flops / (call_f * 1e-3) / 1e12, "algorithmic_bytes": flat_bytes},
         "cascade": {"call_ms": call_c, "hbm_gbps": gbps_c, "algorithmic_bytes": casc_bytes,
@@ -881,7 +940,7 @@ def bench_mla(args):
 # ---------------------------------------------------------------------------
 # hicache: one layer's K/V rows of 65,536 tokens between a pinned host tier and the pool
 # ---------------------------------------------------------------------------
-def bench_hicache(args):
+def bench_hicache(args, flush):
     import torch
     import prefix_shared_paged_amd as sp
 
@@ -957,7 +1016,7 @@ def bench_hicache(args):
 # ---------------------------------------------------------------------------
 # multi-turn: 128 sessions, ~70% cached history, chunked prefill (512) + decode, page 16
 # ---------------------------------------------------------------------------
-def bench_multiturn(args):
+def bench_multiturn(args, flush):
     import torch
     import workloads as W
     from prefix_shared_paged_amd import accounting as acc
@@ -987,7 +1046,26 @@ def bench_multiturn(args):
                 fill_random(t, seed=100 + j)
         inp.append((tq, tk, tv, dq, dk, dv))
     ext_flops = [sum(acc.extend_flops([lo], [hi - lo], Hq, D) for _, lo, hi in e) for e, _ in rounds]
-    dec_bytes = [acc.decode_bytes_flat([p + 1 for _, p in d], Hq, Hkv, D, 2) if d else 0 for _, d in rounds]
+    dec_bytes = [acc.decode_bytes_flat([p + 1 for _, p in d], Hq, Hkv, D, 2, stored=len(d)) if d else 0
+                 for _, d in rounds]
+
+    class Timing:
+        """HIP events right around each library call (after a cache flush)."""
+
+        def __init__(self):
+            self.ev = {"extend": [], "decode": []}
+            self.open = None
+
+        def before(self, kind):
+            flush()
+            a = torch.cuda.Event(enable_timing=True)
+            a.record()
+            self.open = a
+
+        def after(self, kind):
+            b = torch.cuda.Event(enable_timing=True)
+            b.record()
+            self.ev[kind].append((self.open, b))
 
     def run_once(timed):
         cache = PagedKVCache(s.num_slots, s.page_size, Hkv, D, torch.bfloat16, 2 * n, stride, W.pool_order(s), dev)
@@ -1005,53 +1083,48 @@ def bench_multiturn(args):
         runner = ChunkedRunner(cache, wl.chunk)
         runner.admit(list(range(n)), toks, wl.hist)
         torch.cuda.synchronize()
-        evs = []
         it = iter(inp)
-
-        def inputs(ext, dec):
-            return next(it)
-
-        orig_extend = None
+        timing = Timing()
         t0 = time.perf_counter()
-        r = 0
         while True:
             last = not runner.pending()
-            if timed:
-                a = torch.cuda.Event(enable_timing=True)
-                a.record()
-            runner.run_round(inputs)
-            if timed:
-                b = torch.cuda.Event(enable_timing=True)
-                b.record()
-                evs.append((a, b))
-            r += 1
+            runner.run_round(lambda ext, dec: next(it), timing=timing)
             if last:
                 break
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3, evs
+        return (time.perf_counter() - t0) * 1e3, timing
 
     run_once.pools = None
     run_once(False)
-    tot_ms, round_ms = [], []
+    tot_ms, ext_ms, dec_ms = [], [], []
     for _ in range(max(1, args.steps // 10)):
-        ms, evs = run_once(True)
+        ms, tm = run_once(True)
         tot_ms.append(ms)
-        round_ms.append([a.elapsed_time(b) for a, b in evs])
+        ext_ms.append([a.elapsed_time(b) for a, b in tm.ev["extend"]])
+        dec_ms.append([a.elapsed_time(b) for a, b in tm.ev["decode"]])
     ms = float(np.mean(tot_ms))
-    rms = np.mean(np.array(round_ms), axis=0)
+    e_ms = np.mean(np.array(ext_ms), axis=0)          # per extend call, averaged over runs
+    d_ms = np.mean(np.array(dec_ms), axis=0)
     n_tokens = sum(hi - lo for e, _ in rounds for _, lo, hi in e) + sum(len(d) for _, d in rounds)
-    flops, dbytes = float(sum(ext_flops)), float(sum(dec_bytes))
+    flops = float(sum(f for f, (e, _) in zip(ext_flops, rounds) if e))
+    dbytes = float(sum(b for b, (_, d) in zip(dec_bytes, rounds) if d))
+    ext_tflops = flops / (e_ms.sum() * 1e-3) / 1e12
     config = {"workload": "multiturn: 128 sessions, history lognormal(median 3000, sigma 1) clamped to "
                           "[32, 32768], ~70% cached, chunked prefill 512 interleaved with decode, page 16; "
                           "64/8 heads, head_dim 128, 2^20-slot pool", "sessions": n, "rounds": len(rounds)}
-    line = base_line(n_tokens / (ms * 1e-3), ms, args, config,
-                     {"bound": "mfma", "achieved": flops / (rms.sum() * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                      "unit": "TFLOP/s", "traffic": None,
-                      "kernel": "whole rounds (extend + decode calls), extend FLOPs only",
-                      "flops_per_run": flops},
-                     {"extend_flops": flops, "decode_bytes": dbytes, "round_ms": rms.tolist(),
-                      "tokens_per_run": n_tokens})
-    line["roofline"]["frac"] = line["roofline"]["achieved"] / PEAK_BF16_TFLOPS
+    roof = {"bound": "mfma", "achieved": ext_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ext_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+            "kernel": "extend calls (chunked prefill), summed over the rounds",
+            "flops_per_run": flops, "extend_ms_per_run": float(e_ms.sum()), "extend_calls": int(len(e_ms))}
+    line = base_line(n_tokens / (ms * 1e-3), ms, args, config, roof, {
+        "decode": {"roofline": hbm_roofline(dbytes, float(d_ms.sum()),
+                                            "decode calls (split kernel + merge), summed over the rounds",
+                                            None, decode_calls=int(len(d_ms))),
+                   "tokens_per_s": sum(len(d) for _, d in rounds) / (d_ms.sum() * 1e-3)},
+        "extend_ms_per_call": e_ms.tolist(), "decode_ms_per_call": d_ms.tolist(),
+        "tokens_per_run": n_tokens, "mall_flush_ms": flush.time_ms(),
+        "note": "ms_per_step is one whole run (all rounds: host bookkeeping, copies, cache flushes and both "
+                "calls); the rooflines sum only the calls' own events"})
     line["steps"] = len(tot_ms)
     if not args.no_cpu_baseline:
         # oracle sample: last-chunk rows of a few sessions
@@ -1064,6 +1137,114 @@ def bench_multiturn(args):
                 rws.append((len(Ks) - 1, p, wl.queries(int(i), p, p + 1)[0]))
         line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "multiturn prefill")
     return line
+
+
+# ---------------------------------------------------------------------------
+# tiny: 4 fp32 requests over a shared 64-token prefix, 16 new tokens + 1 decode
+# ---------------------------------------------------------------------------
+def bench_tiny(args, flush):
+    """hipEvent medians of >= 50 extend calls and >= 50 decode calls (caches
+    flushed before each), and the full oracle on the host."""
+    import torch
+    import oracle
+    import workloads as W
+    import prefix_shared_paged_amd as sp
+    from prefix_shared_paged_amd import accounting as acc
+    from prefix_shared_paged_amd.paged_cache import PagedKVCache
+
+    wl = W.tiny(seed=0)
+    s = wl.spec
+    B, P, E = wl.B, 64, 16
+    Hq, Hkv, D = s.Hq, s.Hkv, s.D
+    dev = "cuda"
+    f32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    cache = PagedKVCache(s.num_slots, 1, Hkv, D, torch.float32, B + 1, P + E + 2, W.pool_order(s), dev)
+    [st] = cache.admit([wl.prefix_tokens(0)])
+    cache.append([st], [P])
+    Kp, Vp = wl.prefix_kv(0)
+    cache.store(f32(Kp), f32(Vp), st.slots)
+    cache.insert(st)
+    cache.release(st)
+    rows = cache.admit([np.concatenate([wl.prefix_tokens(0), wl.suffix_tokens(r, E)]) for r in range(B)])
+    assert all(r.matched == P for r in rows)
+    cache.append(rows, [E + 1] * B)
+    kv = [wl.suffix_kv(r, E + 1) for r in range(B)]
+    for r, st in enumerate(rows):
+        cache.store(f32(kv[r][0]), f32(kv[r][1]), st.slots[P:])
+    q_ext = f32(np.concatenate([wl.queries(r, E) for r in range(B)]))
+    q_dec = f32(np.stack([wl.queries(r, 1, step=1)[0] for r in range(B)]))
+    req_rows = cache.rows_tensor(rows)
+    plen = torch.full((B,), P, dtype=torch.int32, device=dev)
+    q_off = torch.arange(0, (B + 1) * E, E, dtype=torch.int64, device=dev)
+    seq = torch.full((B,), P + E + 1, dtype=torch.int32, device=dev)
+    o_ext, o_dec = torch.empty_like(q_ext), torch.empty_like(q_dec)
+    ws = torch.empty(sp.decode_workspace_size(B, P + E + 1, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    n = max(50, args.steps)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(n):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    t0 = time.perf_counter()
+    ext = timed(lambda: sp.extend_attn(q_ext, cache.k_pool, cache.v_pool, cache.r2t, req_rows, plen, q_off, E,
+                                       o=o_ext))
+    dec = timed(lambda: sp.decode_attn(q_dec, cache.k_pool, cache.v_pool, cache.r2t, req_rows, seq, P + E + 1,
+                                       o=o_dec, workspace=ws))
+    wall = (time.perf_counter() - t0) * 1e3
+    flops_e = acc.extend_flops([P] * B, [E] * B, Hq, D)
+    flops_d = acc.decode_flops([P + E + 1] * B, Hq, D)
+    byts_d = acc.decode_bytes_flat([P + E + 1] * B, Hq, Hkv, D, 4)
+    step_ms = ext + dec
+    tflops = (flops_e + flops_d) / (step_ms * 1e-3) / 1e12
+    config = {"workload": "tiny fp32: 4 requests sharing a 64-token prefix, 16 new tokens each (one extend "
+                          "call), then one decode token each (one decode call, L = 81); 8/8 heads, head_dim 64, "
+                          "1024-slot shuffled pool, page 1", "batch": B, "prefix": P, "new_tokens": E}
+    roof = {"bound": "alu", "achieved": tflops, "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_F32_VALU_TFLOPS, "traffic": None,
+            "kernel": "extend_f32 + decode split_f32 + merge (latency-bound: the fraction is not meaningful)",
+            "flops_per_step": flops_e + flops_d, "avg_launch_ms": step_ms}
+    line = base_line((B * E + B) / (step_ms * 1e-3), step_ms, args, config, roof, {
+        "extend": {"median_us": ext * 1e3, "flops": flops_e, "tokens_per_s": B * E / (ext * 1e-3)},
+        "decode": {"median_us": dec * 1e3, "kv_bytes": byts_d, "gbps": byts_d / (dec * 1e-3) / 1e9,
+                   "tokens_per_s": B / (dec * 1e-3)},
+        "reps": n, "timing": "hipEvent median per call, caches flushed before each", "wall_ms_all_reps": wall})
+    line["dtype"] = "f32"
+    line["steps"] = n
+    if not args.no_cpu_baseline:
+        Ks = [np.concatenate([Kp, kv[r][0]]) for r in range(B)]
+        Vs = [np.concatenate([Vp, kv[r][1]]) for r in range(B)]
+        rr = [r for r in range(B) for _ in range(E)] + list(range(B))
+        pos = [P + i for _ in range(B) for i in range(E)] + [P + E] * B
+        Q = np.concatenate([q_ext.cpu().numpy(), q_dec.cpu().numpy()])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.attention(Ks, Vs, rr, pos, Q, Hq, Hkv)
+            reps += 1
+            if time.perf_counter() - t0 > min(args.cpu_seconds, 5.0):
+                break
+        t = (time.perf_counter() - t0) / reps
+        line["cpu_baseline"] = {"value": (B * E + B) / t, "unit": "tokens/s", "cores": oracle.default_threads(),
+                                "kind": "oracle", "sample": f"the full workload (64 extend rows + 4 decode rows, "
+                                                            f"all 8 heads), fp64 oracle, {t * 1e3:.2f} ms per run, "
+                                                            f"{reps} runs"}
+    return line
+
+
+def log(msg):
+    """Progress on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -1086,16 +1267,29 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X); none is visible", file=sys.stderr)
         sys.exit(1)
+    flush = MallFlush(torch, "cuda")
     if args.config == "extend":
-        line, ctx = bench_extend(args)
+        line, ctx = bench_extend(args, flush)
+        log(f"extend steps done: {line['ms_per_step']:.3f} ms/step, extend kernel "
+            f"{line['roofline']['avg_launch_ms']:.3f} ms")
+        if not args.no_decode:
+            torch.cuda.empty_cache()
+            dec, _ = measure_decode(args, flush)
+            line["decode_batch"] = dec
+            log(f"decode batch done: flat {dec['flat']['call_ms']:.3f} ms, cascade {dec['cascade']['call_ms']:.3f} ms")
+            torch.cuda.empty_cache()
+            fork, _ = measure_fork(args, flush)
+            line["fork_sweep"] = fork
+            log(f"fork sweep done: {fork['sweep_ms']:.1f} ms per sweep")
+            torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_extend(ctx[1], ctx[2], ctx[3], args.cpu_seconds)
         else:
             line["cpu_baseline"] = None
     else:
-        line = {"decode": bench_decode, "fork": bench_fork, "verify": bench_verify, "mla": bench_mla,
-                "hicache": bench_hicache,
-                "multiturn": bench_multiturn}[args.config](args)
+        line = {"tiny": bench_tiny, "decode": bench_decode, "fork": bench_fork, "verify": bench_verify,
+                "mla": bench_mla, "hicache": bench_hicache,
+                "multiturn": bench_multiturn}[args.config](args, flush)
     print(json.dumps(line, default=lambda x: x.item() if hasattr(x, "item") else str(x)), flush=True)
 
 

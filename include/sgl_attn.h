@@ -48,7 +48,8 @@
  *     no fault occurs).  With the environment variable SGL_ATTN_VALIDATE=1
  *     the device calls first copy the index metadata to the host (a
  *     synchronising step), check it, and return SGL_ERR_INVALID on any
- *     out-of-range slot, row or length, enqueuing nothing.
+ *     out-of-range slot, row or length, enqueuing nothing; sgl_set_validate
+ *     switches this at run time.
  */
 #ifndef SGL_ATTN_H
 #define SGL_ATTN_H
@@ -79,6 +80,18 @@ const char *sgl_status_string(int status);
 
 /* ABI version of this header (bumped on any signature change). */
 int sgl_abi_version(void);
+
+/* Validation of index metadata by the device calls, switchable at run time
+ * (process-wide, for every thread):  mode 1 = on, 0 = off, -1 = follow the
+ * environment variable SGL_ATTN_VALIDATE (the initial state; "1" = on).
+ * With validation on, every device call first copies its index metadata
+ * (req_to_token, rows, lengths, offsets, group arrays, slot lists) to the
+ * host -- a synchronising step -- and returns SGL_ERR_INVALID, enqueuing
+ * nothing, on an out-of-range slot, row, length or offset, a length beyond
+ * row_stride or the call's max bound, or (cascade calls) a group whose
+ * requests do not share the group's prefix slots.  Returns the previous
+ * mode, or -2 (nothing changed) for a mode outside {-1, 0, 1}. */
+int sgl_set_validate(int mode);
 
 /* ------------------------------------------------------------------------
  * KV slot pool (host).  The pool shares one set of slots between the prefix
@@ -188,8 +201,11 @@ int sgl_radix_lock_batch(sgl_radix *tree, const uint64_t *nodes, int32_t batch, 
 
 /* sgl_kv_pool_alloc for every request (cur_len[r], last_slot[r], n[r]);
  * request r's slots go to out_slots[o_r ..] where o_r = n[0] + ... + n[r-1].
- * All or nothing: if the pool cannot serve the whole batch it returns
- * SGL_ERR_OOM and is unchanged. */
+ * All or nothing: every request's arguments are checked before any page is
+ * popped; if one is invalid (e.g. a last_slot that cannot end a request of
+ * cur_len tokens) the call returns SGL_ERR_INVALID, and if the pool cannot
+ * serve the whole batch it returns SGL_ERR_OOM; either way the pool is
+ * unchanged and out_slots unwritten. */
 int sgl_kv_pool_alloc_batch(sgl_kv_pool *pool, const int64_t *cur_len, const int32_t *last_slot,
                             const int64_t *n, int32_t batch, int32_t *out_slots);
 

@@ -36,17 +36,27 @@ def lib_path() -> str:
 
 
 def load():
-    """Load libsgl_attn.so (building it first if it does not exist)."""
+    """Load libsgl_attn.so (building it first if it does not exist).
+
+    SGL_ATTN_LIBRARY=<path> loads another build of the same sources instead;
+    the sanitizer check of the host bookkeeping uses it for a host-only build
+    (only the symbols that build exports are bound: the device entry points
+    are absent from it and raise AttributeError when called)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        _build.build()
-    lib = ctypes.CDLL(_build.LIB)
+    alt = os.environ.get("SGL_ATTN_LIBRARY")
+    if alt:
+        lib = ctypes.CDLL(alt)
+    else:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     sig = {
         "sgl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "sgl_abi_version": (ctypes.c_int, []),
+        "sgl_set_validate": (ctypes.c_int, [ctypes.c_int]),
         "sgl_kv_pool_create": (ctypes.c_int, [I64, I32, P, P]),
         "sgl_kv_pool_destroy": (ctypes.c_int, [P]),
         "sgl_kv_pool_alloc": (ctypes.c_int, [P, I64, I32, I64, P]),
@@ -91,6 +101,8 @@ def load():
         "sgl_hicache_write_back": (ctypes.c_int, [P, P, I64, P, P, I64, P, P, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
+        if alt and not hasattr(lib, name):
+            continue
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
@@ -98,7 +110,7 @@ def load():
     return lib
 
 
-EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_kv_pool_create", "sgl_kv_pool_destroy",
+EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_set_validate", "sgl_kv_pool_create", "sgl_kv_pool_destroy",
            "sgl_kv_pool_alloc", "sgl_kv_pool_free", "sgl_kv_pool_available", "sgl_radix_create",
            "sgl_radix_destroy", "sgl_radix_match", "sgl_radix_insert", "sgl_radix_lock",
            "sgl_radix_evict", "sgl_radix_stats", "sgl_radix_match_batch", "sgl_radix_insert_batch",
@@ -112,6 +124,15 @@ EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_kv_pool_create", "sgl_kv
 
 def status_string(status: int) -> str:
     return load().sgl_status_string(status).decode()
+
+
+def set_validate(mode: int) -> int:
+    """Index validation of the device calls: 1 on, 0 off, -1 follow
+    SGL_ATTN_VALIDATE.  Returns the previous mode."""
+    prev = load().sgl_set_validate(int(mode))
+    if prev == -2:
+        raise ValueError(f"validation mode must be -1, 0 or 1, not {mode}")
+    return prev
 
 
 def _check(fn, status):

@@ -9,9 +9,11 @@ roofline figure.
       (2 for q.k, 2 for p*v); the masked triangle is not counted.
   decode bytes = every K/V row the method must read (flat: each request
       its whole context; cascade: a group's shared prefix once) + the
-      req_to_token entries it reads + Q + O.  With an FP8 KV cache the K/V
-      rows take 1 byte per element (kv element size) while Q and O keep
-      theirs (q_elt).
+      req_to_token entries it reads + Q + O + the store of the current
+      tokens' K/V when the call makes it (stored = tokens stored: their new
+      K/V read and their pool rows written).  With an FP8 KV cache the K/V
+      rows take 1 byte per element (kv element size) while Q, O and the
+      stored tokens' inputs keep theirs (q_elt).
 """
 import numpy as np
 
@@ -42,21 +44,27 @@ def extend_bytes(prefix_lens, extend_lens, Hq, Hkv, D, elt, shared_prefix_groups
             + 4 * int((P + E).sum()))           # req_to_token entries
 
 
-def decode_bytes_flat(seq_lens, Hq, Hkv, D, elt, q_elt=None):
+def _store_bytes(stored, Hkv, D, elt, q_elt):
+    return int(stored) * (kv_bytes_per_token(Hkv, D, q_elt) + kv_bytes_per_token(Hkv, D, elt))
+
+
+def decode_bytes_flat(seq_lens, Hq, Hkv, D, elt, q_elt=None, stored=0):
     L = np.asarray(seq_lens, np.int64)
     B = len(L)
     q_elt = elt if q_elt is None else q_elt
-    return int(L.sum()) * (kv_bytes_per_token(Hkv, D, elt) + 4) + 2 * B * Hq * D * q_elt
+    return (int(L.sum()) * (kv_bytes_per_token(Hkv, D, elt) + 4) + 2 * B * Hq * D * q_elt
+            + _store_bytes(stored, Hkv, D, elt, q_elt))
 
 
-def decode_bytes_cascade(seq_lens, group_of, group_prefix, Hq, Hkv, D, elt, q_elt=None):
+def decode_bytes_cascade(seq_lens, group_of, group_prefix, Hq, Hkv, D, elt, q_elt=None, stored=0):
     L = np.asarray(seq_lens, np.int64)
     gp = np.asarray(group_prefix, np.int64)
     g = np.asarray(group_of, np.int64)
     B = len(L)
     q_elt = elt if q_elt is None else q_elt
     tokens = int(gp.sum()) + int((L - gp[g]).sum())
-    return tokens * (kv_bytes_per_token(Hkv, D, elt) + 4) + 2 * B * Hq * D * q_elt
+    return (tokens * (kv_bytes_per_token(Hkv, D, elt) + 4) + 2 * B * Hq * D * q_elt
+            + _store_bytes(stored, Hkv, D, elt, q_elt))
 
 
 def decode_flops(seq_lens, Hq, D):

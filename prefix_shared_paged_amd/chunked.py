@@ -19,7 +19,7 @@ processes) come from a caller callback, so the same driver serves the tests
 """
 import numpy as np
 
-from . import decode_attn, decode_workspace_size, extend_attn
+from . import decode_attn, decode_workspace_size, extend_attn, extend_workspace_size
 
 
 class Session:
@@ -71,7 +71,7 @@ class ChunkedRunner:
         self.chunk = chunk
         self.sessions = []
         self.round_no = 0
-        self._ws = None
+        self._ws = {}
 
     def admit(self, sids, token_lists, hists):
         rows = self.cache.admit(token_lists)
@@ -82,16 +82,22 @@ class ChunkedRunner:
     def pending(self):
         return any(s.pos < s.hist for s in self.sessions)
 
-    def _workspace(self, nbytes):
-        if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = self.torch.empty(max(nbytes, 1), dtype=self.torch.uint8, device=self.cache.device)
-        return self._ws
+    def _workspace(self, kind, nbytes):
+        """A reusable workspace per call kind, grown when a round needs more."""
+        ws = self._ws.get(kind)
+        if ws is None or ws.numel() < nbytes:
+            ws = self._ws[kind] = self.torch.empty(max(nbytes, 1), dtype=self.torch.uint8, device=self.cache.device)
+        return ws
 
-    def run_round(self, inputs, lse=False):
+    def run_round(self, inputs, lse=False, timing=None):
         """Run one round.  inputs(ext, dec) gets ext = [(sid, lo, hi)] and
         dec = [(sid, position)] and returns device tensors
         (q_ext [n, Hq, D], k_ext, v_ext [n, Hkv, D], q_dec [m, Hq, D], k_dec, v_dec),
-        rows in list order.  Returns what ran, with the outputs."""
+        rows in list order.  timing (optional) has before(kind) and
+        after(kind), called right around the library's extend and decode
+        calls (kind "extend" / "decode"): every host step of the round and
+        every host-to-device copy of a call's arguments comes before
+        before(kind).  Returns what ran, with the outputs."""
         torch = self.torch
         c = self.cache
         dev = c.device
@@ -110,9 +116,18 @@ class ChunkedRunner:
             offs = np.zeros(len(ext) + 1, np.int64)
             offs[1:] = np.cumsum(n)
             lse_t = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=dev) if lse else None
-            o = extend_attn(q, c.k_pool, c.v_pool, c.r2t, c.rows_tensor(rows),
-                            torch.tensor([lo for _, lo, _ in ext], dtype=torch.int32, device=dev),
-                            torch.from_numpy(offs).to(dev), max(n), k_new=k, v_new=v, lse=lse_t)
+            rows_t = c.rows_tensor(rows)
+            plen_t = torch.tensor([lo for _, lo, _ in ext], dtype=torch.int32, device=dev)
+            off_t = torch.from_numpy(offs).to(dev)
+            o = torch.empty_like(q)
+            ws = self._workspace("extend", extend_workspace_size(len(ext), q.shape[0], max(n), c.r2t.shape[1],
+                                                                 q.shape[1], c.Hkv, q.shape[2]))
+            if timing is not None:
+                timing.before("extend")
+            extend_attn(q, c.k_pool, c.v_pool, c.r2t, rows_t, plen_t, off_t, max(n), k_new=k, v_new=v,
+                        lse=lse_t, o=o, workspace=ws)
+            if timing is not None:
+                timing.after("extend")
             out["extend"] = [(s.sid, lo, hi, int(offs[i])) for i, (s, lo, hi) in enumerate(ext)]
             out["extend_out"] = o
             out["extend_lse"] = lse_t
@@ -125,10 +140,16 @@ class ChunkedRunner:
             rows = [s.row for s in dec]
             c.append(rows, [1] * len(dec))
             B, Hq, D = qd.shape
-            ws = self._workspace(decode_workspace_size(B, max(L), Hq, c.Hkv, D))
-            o = decode_attn(qd, c.k_pool, c.v_pool, c.r2t, c.rows_tensor(rows),
-                            torch.tensor(L, dtype=torch.int32, device=dev), max(L), k_new=kd, v_new=vd,
-                            workspace=ws)
+            ws = self._workspace("decode", decode_workspace_size(B, max(L), Hq, c.Hkv, D))
+            rows_t = c.rows_tensor(rows)
+            len_t = torch.tensor(L, dtype=torch.int32, device=dev)
+            o = torch.empty_like(qd)
+            if timing is not None:
+                timing.before("decode")
+            decode_attn(qd, c.k_pool, c.v_pool, c.r2t, rows_t, len_t, max(L), k_new=kd, v_new=vd, o=o,
+                        workspace=ws)
+            if timing is not None:
+                timing.after("decode")
             out["decode"] = [(s.sid, l) for s, l in zip(dec, L)]
             out["decode_out"] = o
             for s in dec:

@@ -2,6 +2,7 @@
 // optional host-side validation of index metadata, workspace layout, and the
 // kernel launches.  See include/sgl_attn.h for the contract.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -51,13 +52,18 @@ int suffix_chunk(int32_t batch, int32_t max_seq_len, int32_t max_prefix_len, int
     return c;
 }
 
+// Validation mode: -1 follows the SGL_ATTN_VALIDATE environment variable
+// (read once), 0 / 1 are set by sgl_set_validate.
+std::atomic<int> g_validate_mode{-1};
+
 bool validate_on() {
-    static int v = -1;
-    if (v < 0) {
+    const int m = g_validate_mode.load(std::memory_order_relaxed);
+    if (m >= 0) return m == 1;
+    static const bool env = [] {
         const char *e = std::getenv("SGL_ATTN_VALIDATE");
-        v = (e && e[0] && e[0] != '0') ? 1 : 0;
-    }
-    return v == 1;
+        return e && e[0] && e[0] != '0';
+    }();
+    return env;
 }
 
 bool shape_ok(int dtype, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -171,19 +177,12 @@ int mla_prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, 
 
 extern "C" {
 
-const char *sgl_status_string(int status) {
-    switch (status) {
-        case SGL_OK: return "SGL_OK";
-        case SGL_ERR_INVALID: return "SGL_ERR_INVALID";
-        case SGL_ERR_UNSUPPORTED: return "SGL_ERR_UNSUPPORTED";
-        case SGL_ERR_OOM: return "SGL_ERR_OOM";
-        case SGL_ERR_HIP: return "SGL_ERR_HIP";
-        case SGL_ERR_WORKSPACE: return "SGL_ERR_WORKSPACE";
-        default: return "SGL_ERR_UNKNOWN";
-    }
-}
+int sgl_abi_version(void) { return 5; }
 
-int sgl_abi_version(void) { return 4; }
+int sgl_set_validate(int mode) {
+    if (mode < -1 || mode > 1) return -2;
+    return g_validate_mode.exchange(mode);
+}
 
 int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
                            const int32_t *req_rows, int32_t batch, const int32_t *prefix_slots,
@@ -602,9 +601,33 @@ int mla_common(bool cascade, const void *q, const void *kv_new, void *kv_pool, i
         if (max_group_size < 1 || max_prefix_len < 0 || max_prefix_len > max_seq_len) return SGL_ERR_INVALID;
         if ((int64_t)max_group_size * Hq > 4096) return SGL_ERR_UNSUPPORTED;
     }
-    const size_t need = cascade ? sgl_mla_cascade_workspace_size(batch, G, max_seq_len, max_group_size,
-                                                                 max_prefix_len, Hq, Dv)
-                                : sgl_mla_decode_workspace_size(batch, max_seq_len, Hq, Dv);
+    // A prefix-stage workgroup holds at most 64 query rows and reads the shared
+    // prefix once for them; a group with more rows would read it once per 64
+    // rows from workgroups of 16 waves, which measured slower than reading it
+    // once per request (128 requests in groups of 8 over 2-8k keys: 16 heads
+    // 253 vs 208 us, 128 heads 885 vs 805 us).  Such groups run the flat
+    // splits (same result) and need only the flat call's workspace.
+    const bool flat_path = !cascade || (int64_t)max_group_size * Hq > 64;
+    const int chunk = mla_chunk(Hq);
+    const int64_t Ss = ceil_div64(max_seq_len, chunk);
+    // The preferred prefix split depends on the call's bounds (a shorter
+    // prefix can prefer a smaller split, hence more split states), so it is
+    // doubled, up to 512 keys, while the states would not fit the caller's
+    // workspace: a workspace sized by sgl_mla_cascade_workspace_size for
+    // larger bounds always holds 512-key splits.
+    int pchunk = kPrefixChunkMax;
+    size_t need;
+    if (flat_path) {
+        need = sgl_mla_decode_workspace_size(batch, max_seq_len, Hq, Dv);
+    } else {
+        pchunk = mla_prefix_chunk(G, max_group_size, max_prefix_len, Hq);
+        auto need_for = [&](int pc) {
+            const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pc) : 1;
+            return part_bytes(batch, Sp, Hq, Dv) + part_bytes(batch, Ss, Hq, Dv);
+        };
+        while (need_for(pchunk) > workspace_bytes && pchunk < kPrefixChunkMax) pchunk *= 2;
+        need = need_for(pchunk);
+    }
     if (workspace_bytes < need || (need > 0 && !workspace)) return SGL_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     if (validate_on()) {
@@ -649,30 +672,14 @@ int mla_common(bool cascade, const void *q, const void *kv_new, void *kv_pool, i
     std::memset(&m, 0, sizeof m);
     m.seq_lens = seq_lens; m.group_ptr = group_ptr; m.group_prefix_len = group_prefix_len;
     m.batch = batch; m.G = G; m.Hq = Hq; m.D = Dv; m.out_bf16 = 1; m.o = o; m.lse = lse;
-    const int chunk = mla_chunk(Hq);
     m.chunk_flat = chunk;
-    const int64_t Ss = ceil_div64(max_seq_len, chunk);
-    if (!cascade) {
+    if (flat_path) {
         a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = chunk;
         a.part = carve(wp, batch, Ss, Hq, Dv);
         if ((rc = launch_split_mla(a, st)) != SGL_OK) return rc;
         m.kind = 0; m.flat_or_suffix = a.part;
         return launch_merge(m, st);
     }
-    // A prefix-stage workgroup holds at most 64 query rows and reads the shared
-    // prefix once for them; a group with more rows would read it once per 64
-    // rows from workgroups of 16 waves, which measured slower than reading it
-    // once per request (128 requests in groups of 8 over 2-8k keys: 16 heads
-    // 253 vs 208 us, 128 heads 885 vs 805 us).  Such groups run the flat
-    // splits (same result).
-    if ((int64_t)max_group_size * Hq > 64) {
-        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)Ss; a.chunk = chunk;
-        a.part = carve(wp, batch, Ss, Hq, Dv);
-        if ((rc = launch_split_mla(a, st)) != SGL_OK) return rc;
-        m.kind = 0; m.flat_or_suffix = a.part;
-        return launch_merge(m, st);
-    }
-    const int pchunk = mla_prefix_chunk(G, max_group_size, max_prefix_len, Hq);
     const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pchunk) : 1;
     SplitArgs pa = a;
     pa.kind = 1; pa.chunk = pchunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size; pa.n_sets = G;

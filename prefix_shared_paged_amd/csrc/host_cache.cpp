@@ -190,6 +190,18 @@ int pool_free_pages(sgl_kv_pool *pool, const std::vector<int32_t> &pages) {
 
 extern "C" {
 
+const char *sgl_status_string(int status) {
+    switch (status) {
+        case SGL_OK: return "SGL_OK";
+        case SGL_ERR_INVALID: return "SGL_ERR_INVALID";
+        case SGL_ERR_UNSUPPORTED: return "SGL_ERR_UNSUPPORTED";
+        case SGL_ERR_OOM: return "SGL_ERR_OOM";
+        case SGL_ERR_HIP: return "SGL_ERR_HIP";
+        case SGL_ERR_WORKSPACE: return "SGL_ERR_WORKSPACE";
+        default: return "SGL_ERR_UNKNOWN";
+    }
+}
+
 int sgl_kv_pool_create(int64_t num_slots, int32_t page_size, const int32_t *init_order,
                        sgl_kv_pool **out) {
     if (!out || page_size < 1 || page_size > 1024 || num_slots < page_size ||
@@ -221,17 +233,26 @@ int sgl_kv_pool_destroy(sgl_kv_pool *pool) {
     return SGL_OK;
 }
 
+// Slots of the partly filled last page a request of cur_len tokens (last slot
+// last_slot) fills first when it allocates n more, or -1 if last_slot cannot
+// be the slot of position cur_len - 1 (out of range, or at the wrong offset
+// within its page).
+static int64_t partial_fill(const sgl_kv_pool *pool, int64_t cur_len, int32_t last_slot, int64_t n) {
+    const int32_t p = pool->page;
+    if (p == 1 || cur_len % p == 0) return 0;
+    const int64_t fill = std::min<int64_t>(n, p - cur_len % p);
+    if (fill > 0 && (last_slot < 0 || (int64_t)last_slot + fill >= pool->num_slots ||
+                     (last_slot % p) != (cur_len - 1) % p))
+        return -1;
+    return fill;
+}
+
 int sgl_kv_pool_alloc(sgl_kv_pool *pool, int64_t cur_len, int32_t last_slot, int64_t n,
                       int32_t *out_slots) {
     if (!pool || n < 0 || cur_len < 0 || (n > 0 && !out_slots)) return SGL_ERR_INVALID;
     const int32_t p = pool->page;
-    int64_t fill = 0;
-    if (p > 1 && cur_len % p != 0) {
-        fill = std::min<int64_t>(n, p - cur_len % p);
-        if (fill > 0 && (last_slot < 0 || (int64_t)last_slot + fill >= pool->num_slots ||
-                         (last_slot % p) != (cur_len - 1) % p))
-            return SGL_ERR_INVALID;
-    }
+    const int64_t fill = partial_fill(pool, cur_len, last_slot, n);
+    if (fill < 0) return SGL_ERR_INVALID;
     const int64_t need = (n - fill + p - 1) / p;
     if (need > (int64_t)pool->free_pages.size()) return SGL_ERR_OOM;
     int64_t k = 0;
@@ -515,10 +536,12 @@ int sgl_kv_pool_alloc_batch(sgl_kv_pool *pool, const int64_t *cur_len, const int
     if (!pool || batch < 0 || (batch > 0 && (!cur_len || !last_slot || !n))) return SGL_ERR_INVALID;
     const int32_t p = pool->page;
     int64_t need_pages = 0, total = 0;
+    // every request's arguments and the page count are checked before any
+    // page is popped, so a failing call leaves the pool unchanged
     for (int32_t r = 0; r < batch; r++) {
         if (n[r] < 0 || cur_len[r] < 0) return SGL_ERR_INVALID;
-        int64_t fill = 0;
-        if (p > 1 && cur_len[r] % p != 0) fill = std::min<int64_t>(n[r], p - cur_len[r] % p);
+        const int64_t fill = partial_fill(pool, cur_len[r], last_slot[r], n[r]);
+        if (fill < 0) return SGL_ERR_INVALID;
         need_pages += (n[r] - fill + p - 1) / p;
         total += n[r];
     }
@@ -526,8 +549,8 @@ int sgl_kv_pool_alloc_batch(sgl_kv_pool *pool, const int64_t *cur_len, const int
     if (need_pages > (int64_t)pool->free_pages.size()) return SGL_ERR_OOM;
     int64_t o = 0;
     for (int32_t r = 0; r < batch; r++) {
-        int rc = sgl_kv_pool_alloc(pool, cur_len[r], last_slot[r], n[r], out_slots + o);
-        if (rc != SGL_OK) return rc;   // only argument errors can remain here
+        const int rc = sgl_kv_pool_alloc(pool, cur_len[r], last_slot[r], n[r], out_slots + o);
+        if (rc != SGL_OK) return rc;   // cannot happen: every check above passed
         o += n[r];
     }
     return SGL_OK;

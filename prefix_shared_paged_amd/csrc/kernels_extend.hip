@@ -34,21 +34,24 @@
 //   loads of tile n+2 into the ring slots tile n-1 has left (the two latencies
 //   overlap); S^T(n) = K Q^T on MFMA (keys on M, rows on N, so a lane owns one
 //   row's scores) with each K read four steps ahead of its MFMA; the causal
-//   mask and row maximum; the reference move; p = 2^(s - reference) in bf16
-//   and its row sum; O^T += V^T P^T on MFMA (V^T via ds_read_b64_tr_b16, two
+//   mask and row maximum; the reference move; p = 2^(s*c - reference), its
+//   bf16 copy and its fp32 row sum; O^T += V^T P^T on MFMA (V^T via ds_read_b64_tr_b16, two
 //   MFMAs ahead; the key order inside each MFMA matches the S^T accumulator
 //   layout, so P needs no lane exchange); the wait for tile n+1; one barrier.
-// Every tile load has two stages to land.  Softmax details: Q is
-// pre-multiplied by scale*log2(e), so scores come out in log2 units; the
-// reference maximum is moved lazily, only when a row's tile maximum exceeds it
-// by more than 2^8 (the exact result is unchanged: the reference is only a
-// scaling point), and the mask is applied only to tiles that may cross the
-// diagonal.
+// Every tile load has two stages to land.  Softmax details: Q enters the
+// MFMAs exactly as given (a negative scale negates it, which is exact), the
+// scores s = q.k come out of the MFMAs in fp32, and the scale joins them in
+// fp32 inside the exponent: p = 2^(s*c - reference) with c = |scale|*log2(e),
+// one FMA per score; the row maximum is found on s and scaled once.  The
+// reference maximum is moved lazily, only when a row's tile maximum exceeds
+// it by more than 2^8 (the exact result is unchanged: the reference is only
+// a scaling point), and the mask is applied only to tiles that may cross the
+// diagonal.  p is rounded to bf16 for the PV MFMAs (the only reduced-
+// precision step); the row sum l adds the fp32 p, so the log-sum-exp is that
+// of the fp32 scores.
 #include <type_traits>
 
 #include "common.h"
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -169,16 +172,19 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
     const bool row_valid = tok_local < E;
     const int h = kvh * g + rho % g;
     const int pos = P + (row_valid ? tok_local : E - 1);   // absolute position
+    // q as given; negated (exactly) when the scale is negative, so that the
+    // scaled score is |scale| * (q.k) with a positive factor
     bf16x8 qf[QT];
     {
         const __bf16 *src = q + ((t0 + (row_valid ? tok_local : 0)) * Hq + h) * D + 8 * h2;
+        const bool neg = qscale < 0.f;
 #pragma unroll
         for (int t = 0; t < QT; t++) {
-            const bf16x8 raw = ld_bf16x8(src + 16 * t);
-#pragma unroll
-            for (int e = 0; e < 8; e++) qf[t][e] = (__bf16)((float)raw[e] * qscale);
+            qf[t] = ld_bf16x8(src + 16 * t);
+            if (neg) qf[t] = -qf[t];
         }
     }
+    const float cs = fabsf(qscale);   // |scale| * log2(e): scores -> log2 units
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -294,7 +300,8 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
         return s;
     };
     // causal mask of tile n (absolute key of accumulator element j:
-    // 32n + 8*(j/4) + 4*h2 + j%4) and the row maximum
+    // 32n + 8*(j/4) + 4*h2 + j%4) and the row maximum of the scaled scores
+    // (the maximum of s times the positive factor cs)
     auto mask_max = [&](f32x16 &s, int n, auto mask_tag) {
         if (decltype(mask_tag)::value) {
             const int lim = pos - n * BN - 4 * h2;
@@ -305,7 +312,7 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
         float mx = s[0];
 #pragma unroll
         for (int j = 1; j < 16; j++) mx = fmaxf(mx, s[j]);
-        return max_xor32(mx);
+        return max_xor32(mx) * cs;
     };
     // lazy move of the reference (mx is the tile's row maximum); rescales O
     // and l, so it runs after the PV MFMAs issued before it
@@ -322,17 +329,21 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
             thr = m_new + kLazy;
         }
     };
-    // p = 2^(s - reference) rounded to bf16 (the B operands of the tile's 2 PV
-    // steps); the row sum adds up the same rounded values, two at a time
+    // p = 2^(s*cs - reference) in fp32, rounded to bf16 for the B operands of
+    // the tile's 2 PV steps; the row sum adds the fp32 values (a pairwise tree,
+    // so the additions do not form one long dependent chain)
     auto exp_tile = [&](const f32x16 &s, bf16x8 (&pf)[2]) {
+        float p[16];
 #pragma unroll
-        for (int j = 0; j < 16; j++) pf[j >> 3][j & 7] = (__bf16)__builtin_amdgcn_exp2f(s[j] - m_sub);
-        const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const bf16x2 pp = {pf[j >> 2][2 * (j & 3)], pf[j >> 2][2 * (j & 3) + 1]};
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, l_run, false);
+        for (int j = 0; j < 16; j++) {
+            p[j] = __builtin_amdgcn_exp2f(fmaf(s[j], cs, -m_sub));
+            pf[j >> 3][j & 7] = (__bf16)p[j];
         }
+#pragma unroll
+        for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+            for (int j = 0; j < 16; j += 2 * w) p[j] += p[j + w];
+        l_run += p[0];
     };
     // O^T += V^T P^T; step s2 covers keys 16*s2 + {4*h2 + 0..3, 8 + 4*h2 + 0..3}
     typedef short i16x8 __attribute__((ext_vector_type(8)));

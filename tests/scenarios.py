@@ -178,35 +178,6 @@ def oracle_extend(case, res, rows_sample=None, heads=None):
     return np.array(idx), O, LSE
 
 
-def extend_lse_bound(case, res, idx_rows=None):
-    """Per (row, q head) bound on |lse_bf16_kernel - lse_exact| for the rows of
-    oracle_extend (same order), from the arithmetic of the bf16 extend kernel:
-      - q is pre-multiplied by scale*log2(e) and rounded to bf16 (relative
-        error <= 2^-9 per element), so a score moves by at most
-        2^-9 * scale * sum_i |q_i k_i| (natural-log units);
-      - the row sum adds the bf16-rounded p (relative error <= 2^-9 each), so
-        ln l moves by at most 2^-9;
-    plus 1e-5 for the fp32 exponentials and sums."""
-    wl = case.wl
-    s = wl.spec
-    g = s.Hq // s.Hkv
-    scale = 1.0 / np.sqrt(s.D)
-    out = []
-    for r in range(wl.B):
-        E = int(res["E"][r])
-        if E == 0:
-            continue
-        K, _ = case.logical_kv(r, E)
-        P = int(res["P"][r])
-        ii = range(E) if idx_rows is None else [i for rq, i in idx_rows if rq == r]
-        aK = np.ascontiguousarray(np.abs(K.astype(np.float64)).transpose(1, 0, 2))   # [Hkv, L, D]
-        for i in ii:
-            aq = np.abs(res["q"][r][i].astype(np.float64)).reshape(s.Hkv, g, s.D)
-            dots = np.matmul(aK[:, :P + i + 1], aq.transpose(0, 2, 1))              # [Hkv, keys, g]
-            out.append(dots.max(axis=1).reshape(s.Hq))
-    return 2.0 ** -9 * (1.0 + scale * np.stack(out)) + 1e-5
-
-
 def run_decode(case, L, cascade, both=False, workspace=None):
     """All requests decode one token at position L[r]-1 (L includes it).
     cascade: use the cascade call; both: run the flat call first (it stores the

@@ -126,16 +126,45 @@ def test_mla_small(Hq):
     _check(c, list(range(c["B"])), f"small Hq={Hq}")
 
 
-def test_mla_decode_shape_sampled():
-    # 128 requests in 16 groups of 8, prefixes ~U[512, 4096], contexts
-    # ~U[max(1024, P+1), 8192], 16 heads (one tensor-parallel share of 128)
+@pytest.mark.parametrize("Hq", [16, 128])
+def test_mla_decode_shape_sampled(Hq):
+    # the benchmark's shape: 128 requests in 16 groups of 8, prefixes
+    # ~U[512, 4096], contexts ~U[max(1024, P+1), 8192]; 128 heads (all of
+    # them, 1024-key splits, four 16-row blocks per workgroup) and 16 heads
+    # (one tensor-parallel share of 128); sampled requests, all heads
     rng = np.random.default_rng(9)
     members = [8] * 16
     prefixes = [int(x) for x in rng.integers(512, 4097, 16)]
     L = [int(rng.integers(max(1024, P + 1), 8193)) for P in prefixes for _ in range(8)]
-    c = _case(21, 16, members, prefixes, L, num_slots=1 << 20)
-    reqs = sorted(set(rng.choice(c["B"], 24, replace=False).tolist() + [0, c["B"] - 1]))
-    _check(c, reqs, "decode shape Hq=16")
+    c = _case(21 if Hq == 16 else 23, Hq, members, prefixes, L, num_slots=1 << 20)
+    reqs = sorted(set(rng.choice(c["B"], 24, replace=False).tolist() + [0, c["B"] - 1]
+                      + [int(np.argmax(L))]))
+    _check(c, reqs, f"decode shape Hq={Hq}")
+
+
+def test_mla_cascade_workspace_sized_for_larger_bounds():
+    # groups of 4 requests x 16 heads (64 query rows: the prefix stage runs);
+    # the workspace is sized for longer prefixes and contexts than the call
+    # has, and the call fits its prefix splits to it
+    from prefix_shared_paged_amd import mla_cascade_workspace_size
+    rng = np.random.default_rng(77)
+    members = [4] * 8
+    prefixes = [int(x) for x in rng.integers(1024, 2113, 8)]
+    L = [int(rng.integers(P + 1, P + 600)) for P in prefixes for _ in range(4)]
+    c = _case(77, 16, members, prefixes, L, num_slots=1 << 18)
+    B = c["B"]
+    ws = torch.empty(mla_cascade_workspace_size(B, 8, 8192, 4, 4032, 16), dtype=torch.uint8, device="cuda")
+    pool = c["pool"].clone()
+    lse = torch.empty((B, 16), dtype=torch.float32, device="cuda")
+    o = mla_cascade_decode_attn(c["q"], pool, _dev_i(c["r2t"]), _dev_i(np.arange(B)), _dev_i(c["L"]),
+                                _dev_i(c["gptr"]), _dev_i(c["P"]), int(c["L"].max()), 4, int(c["P"].max()),
+                                kv_new=c["kv_new"], scale=SCALE, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    O, LSE = _oracle(c, list(range(B)))
+    err = float(np.max(np.abs(o.float().cpu().numpy().astype(np.float64) - O)))
+    lerr = float(np.max(np.abs(lse.cpu().numpy() - LSE)))
+    _print(f"mla cascade, workspace for larger bounds: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
 @pytest.mark.parametrize("Hq,members", [(16, [1, 2, 4, 3]), (32, [1, 2, 2]), (64, [1, 1])])

@@ -1,8 +1,15 @@
 """GPU parity for the multi-turn mix: sessions with a ~70% cached history,
 chunked prefill (chunks of 512) interleaved with decode, page size 16,
-64 query / 8 KV heads, bf16.  Outputs are checked against the fp64 oracle
-on sampled rows (the first, last and one random row of every chunk, and every
-decode token) of a subset of sessions, on one query head per KV group."""
+64 query / 8 KV heads, bf16.
+
+req_to_token: every allocation the runner makes (the setup of the cached
+histories, every chunk append, every decode append) and every insert at
+prefill completion is replayed on the brute-force slot pool and trie
+(oracle/radix_model.py), and every session's req_to_token row is compared
+bit-exactly with the model's slot list.  Attention: outputs are checked
+against the fp64 oracle on sampled rows (the first, last and one random row
+of every chunk, and every decode token) of every session, on one query head
+per KV group."""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +26,10 @@ BF16_TOL = 2e-2
 
 def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda").to(torch.bfloat16)
+
+
+def st_decoded(runner, sid):
+    return next(x.decoded for x in runner.sessions if x.sid == sid)
 
 
 def run_multiturn(wl, check_sessions, rng_seed=0):
@@ -46,10 +57,16 @@ def run_multiturn(wl, check_sessions, rng_seed=0):
         cache.release(st)
     runner = ChunkedRunner(cache, wl.chunk)
     rows = runner.admit(list(range(n)), toks, hist)
+    model_slots = {}
     for i, st in enumerate(rows):
         m, m_slots, _ = model_tree.match(list(toks[i]))
         assert st.matched == m == cached[i]
         assert list(st.slots) == m_slots
+        model_slots[i] = list(m_slots)
+
+    def model_append(sid, k):
+        cur = model_slots[sid]
+        cur += model_pool.alloc(len(cur), cur[-1] if cur else -1, k)
 
     def inputs(ext, dec):
         q = np.concatenate([wl.queries(i, lo, hi) for i, lo, hi in ext]) if ext else np.zeros((0, s.Hq, s.D))
@@ -73,6 +90,17 @@ def run_multiturn(wl, check_sessions, rng_seed=0):
         ext_plan, dec_plan = rounds[done_rounds]
         assert [(a, b, c) for a, b, c, _ in out["extend"]] == ext_plan
         assert out["decode"] == [(i, p + 1) for i, p in dec_plan]
+        # the same round on the model: chunk appends, inserts at prefill
+        # completion (the runner re-matches the inserted prefix), decode appends
+        for sid, lo, hi, _ in out["extend"]:
+            model_append(sid, hi - lo)
+        for sid, lo, hi, _ in out["extend"]:
+            if hi >= hist[sid]:
+                h = int(hist[sid])
+                model_tree.insert(list(toks[sid][:h]), model_slots[sid][:h], model_pool)
+                model_tree.match(list(toks[sid][:h // s.page_size * s.page_size]))
+        for sid, _ in out["decode"]:
+            model_append(sid, 1)
         torch.cuda.synchronize()
         if out["extend"]:
             o = out["extend_out"]
@@ -91,10 +119,13 @@ def run_multiturn(wl, check_sessions, rng_seed=0):
         if last:
             break
     assert done_rounds == len(rounds)
-    # req_to_token rows of the checked sessions
+    # req_to_token rows of every session, bit-exact against the model's slots
     tab = cache.r2t.cpu().numpy()
-    for st in rows:
-        np.testing.assert_array_equal(tab[st.row, :len(st.slots)], st.slots)
+    for sid, st in enumerate(rows):
+        want = np.array(model_slots[sid], np.int32)
+        assert len(st.slots) == len(want) == int(hist[sid]) + st_decoded(runner, sid)
+        np.testing.assert_array_equal(tab[st.row, :len(want)], want)
+        np.testing.assert_array_equal(st.slots, want)
 
     worst = 0.0
     n_rows = 0
@@ -120,10 +151,8 @@ def test_multiturn_small_all_sessions_checked():
 
 def test_multiturn_full_size_sampled():
     wl = W.multiturn(seed=0)
-    longest = list(np.argsort(-wl.hist)[:3])
-    check = sorted(set(longest) | set(np.random.default_rng(3).choice(wl.n, 5, replace=False).tolist()))
-    worst, n_rows, n_rounds = run_multiturn(wl, check_sessions=check)
+    worst, n_rows, n_rounds = run_multiturn(wl, check_sessions=range(wl.n))
     print(f"multiturn full: {wl.n} sessions, hist median {int(np.median(wl.hist))} max {int(wl.hist.max())}, "
-          f"hit {wl.cached.sum() / wl.hist.sum():.3f}, {n_rounds} rounds; checked {len(check)} sessions, "
-          f"{n_rows} rows x 8 heads, max abs err {worst:.3e}", flush=True)
+          f"hit {wl.cached.sum() / wl.hist.sum():.3f}, {n_rounds} rounds; req_to_token rows of all sessions "
+          f"bit-exact; sampled {n_rows} rows x 8 heads of all sessions, max abs err {worst:.3e}", flush=True)
     assert worst <= BF16_TOL

@@ -12,14 +12,24 @@ import torch
 import oracle
 import workloads as W
 from prefix_shared_paged_amd import decode_attn, extend_attn
-from scenarios import (GroupCase, bf16_err, dev, dev_i, extend_lse_bound, f32_rel_err, oracle_decode,
+from scenarios import (GroupCase, bf16_err, dev, dev_i, f32_rel_err, oracle_decode,
                        oracle_extend, run_decode, run_extend)
 
 pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 F32_TOL = 1e-5
-LSE_TOL = 1e-3       # decode kernels (fp32 softmax state); bf16 extend: extend_lse_bound
+# Log-sum-exp of the scaled scores (natural log), every bf16 kernel, extend
+# and decode alike.  The scores and the row sums are fp32 (only the weights
+# entering the PV product are rounded to bf16), so the kernels' value differs
+# from the exact one by fp32 rounding alone: the score sums over D <= 128
+# products move a scaled score by at most ~1.5e-4 for the 8x-wide "peaky"
+# queries (2e-5 for the others), and the row sum, a 16-term tree per key tile
+# added tile after tile, is off by at most (tiles + 5) * 2^-24 relative
+# (< 5e-5 at 20k keys).  The fixed tolerance sits above that worst case; a
+# key missed or counted twice moves the value by that key's share of the row
+# sum, which the peaky variants make large.
+LSE_TOL = 1e-3
 
 
 def _print(*a):
@@ -96,12 +106,9 @@ def test_extend_small_ragged(Hq, Hkv, D):
     case.check_r2t()
     idx, O, LSE = oracle_extend(case, res)
     err = bf16_err(res["o"][idx], O)
-    ldev = np.abs(res["lse"][idx] - LSE)
-    bound = extend_lse_bound(case, res)
-    _print(f"extend small Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {ldev.max():.2e} "
-           f"(worst fraction of its bound {np.max(ldev / bound):.2f})")
-    assert err <= BF16_TOL
-    assert np.all(ldev <= bound)
+    lerr = float(np.max(np.abs(res["lse"][idx] - LSE)))
+    _print(f"extend small Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 64)])
@@ -115,11 +122,9 @@ def test_extend_small_ragged_peaky(Hq, Hkv, D):
     res = run_extend(case, E)
     idx, O, LSE = oracle_extend(case, res)
     err = bf16_err(res["o"][idx], O)
-    ldev = np.abs(res["lse"][idx] - LSE)
-    bound = extend_lse_bound(case, res)
-    _print(f"extend peaky Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, worst lse fraction {np.max(ldev / bound):.2f}")
-    assert err <= BF16_TOL
-    assert np.all(ldev <= bound)
+    lerr = float(np.max(np.abs(res["lse"][idx] - LSE)))
+    _print(f"extend peaky Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
 def test_extend_fp32_small_ragged():
@@ -146,11 +151,9 @@ def test_extend_full_size_sampled():
     sample = [(r, i) for r in range(wl.B) for i in sorted({0, 1, 31, 32, 127, 255, int(rng.integers(256))})]
     idx, O, LSE = oracle_extend(case, res, rows_sample=sample)
     err = bf16_err(res["o"][idx], O)
-    ldev = np.abs(res["lse"][idx] - LSE)
-    bound = extend_lse_bound(case, res, sample)
-    _print(f"extend full-size sampled {len(idx)} rows: max abs err {err:.3e}, lse err {ldev.max():.2e} "
-           f"(worst fraction of its bound {np.max(ldev / bound):.2f})")
-    assert err <= BF16_TOL and np.all(ldev <= bound)
+    lerr = float(np.max(np.abs(res["lse"][idx] - LSE)))
+    _print(f"extend full-size sampled {len(idx)} rows: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
     # every output is finite
     assert np.isfinite(res["o"]).all()
 
@@ -237,19 +240,15 @@ def _check_extend_rows(o, Ks, Vs, Qs, P_list, E_list, spec, rng, n_rows=6):
 
 
 def _check_last_row_lse(lse, Ks, Vs, Qs, P_list, E_list, spec):
-    """The log-sum-exp of the last new token of each request, within the bound
-    of the bf16 kernel's arithmetic: bf16-rounded scaled q moves a score by at
-    most 2^-9 scale sum|q k|, and the row sum adds bf16-rounded p (2^-9 in ln l)."""
-    Hq, Hkv, D = spec.Hq, spec.Hkv, spec.D
-    g = Hq // Hkv
+    """The log-sum-exp of the last new token of each request, within LSE_TOL."""
+    Hq, Hkv = spec.Hq, spec.Hkv
     q_off = np.concatenate([[0], np.cumsum(E_list)])
+    worst = 0.0
     for r, (P, E) in enumerate(zip(P_list, E_list)):
         _, _, _, LSE = oracle.attention([Ks[r]], [Vs[r]], [0], [P + E - 1], Qs[r][E - 1:E], Hq, Hkv)
-        qa = np.abs(Qs[r][E - 1].astype(np.float64))
-        ka = np.abs(Ks[r].astype(np.float64))
-        bound = np.array([2.0 ** -9 / np.sqrt(D) * np.max(ka[:, h // g] @ qa[h]) for h in range(Hq)])
-        bound += 2.0 ** -9 + 1e-5
-        assert np.all(np.abs(lse[q_off[r] + E - 1].cpu().numpy() - LSE[0]) <= bound), r
+        worst = max(worst, float(np.max(np.abs(lse[q_off[r] + E - 1].cpu().numpy() - LSE[0]))))
+    _print(f"  last-row lse err {worst:.2e}")
+    assert worst <= LSE_TOL
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 64)])

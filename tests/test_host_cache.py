@@ -208,3 +208,22 @@ def test_batched_alloc_is_all_or_nothing():
     assert pool.available() == 64
     a, off = pool.alloc_batch([3, 5], [0, 0], [-1, -1])
     assert off.tolist() == [0, 3, 8] and pool.available() == 64 - 12
+
+
+def test_batched_alloc_rejects_a_bad_request_before_popping():
+    # request 1's last slot cannot end a 3-token request on 4-slot pages: the
+    # batch fails as a whole, request 0's pages stay in the pool, and the free
+    # list keeps its order (the next allocation gets the same slots)
+    pool = sp.KVPool(64, 4)
+    first, _ = pool.alloc_batch([4], [0], [-1])
+    pool.free(first)
+    with pytest.raises(sp.SglError) as e:
+        pool.alloc_batch([5, 2], [0, 3], [-1, 9])
+    assert e.value.status == sp.SGL_ERR_INVALID
+    assert pool.available() == 64
+    again, _ = pool.alloc_batch([5], [0], [-1])
+    ref = sp.KVPool(64, 4)
+    ref.alloc_batch([4], [0], [-1])
+    ref.free(first)
+    want, _ = ref.alloc_batch([5], [0], [-1])
+    np.testing.assert_array_equal(again, want)

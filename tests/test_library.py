@@ -151,3 +151,17 @@ def test_bytes_per_token_accounting():
     from prefix_shared_paged_amd.accounting import kv_bytes_per_token
     assert kv_bytes_per_token(Hkv=8, D=128, elt=2, layers=80) == 327680
     assert abs(4096 * kv_bytes_per_token(8, 128, 2, 80) / 2 ** 30 - 1.25) < 1e-9
+
+
+def test_set_validate_modes():
+    """The validation switch is host state only: it returns the previous mode
+    and rejects modes outside {-1, 0, 1} without changing anything."""
+    import prefix_shared_paged_amd as sp
+    lib = sp.load()
+    prev = lib.sgl_set_validate(1)
+    try:
+        assert lib.sgl_set_validate(0) == 1
+        assert lib.sgl_set_validate(5) == -2
+        assert lib.sgl_set_validate(-1) == 0
+    finally:
+        lib.sgl_set_validate(prev)

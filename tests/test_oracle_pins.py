@@ -14,7 +14,6 @@ import os
 
 import numpy as np
 import pytest
-import torch
 
 import oracle
 
@@ -45,6 +44,7 @@ def test_hand_cases():
 
 def _sdpa_reference(K, V, Q, pos, Hq, Hkv, scale):
     """Dense causal attention with torch SDPA in float64: keys j visible to query at t iff j <= t."""
+    import torch
     L = K.shape[0]
     g = Hq // Hkv
     k = torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2)           # [Hkv, L, D]
