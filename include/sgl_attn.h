@@ -323,6 +323,34 @@ size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
                                   int32_t max_group_size, int32_t max_prefix_len,
                                   int32_t Hq, int32_t Hkv, int32_t D);
 
+/* Allocation-free cascade decode, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops that must not call
+ * hipMalloc, harnesses that forbid allocation.  Same arguments, semantics and
+ * result as sgl_cascade_decode_attn, without the workspace: the split states
+ * live in a static device array of sgl_static_scratch_bytes() = 128 MiB that
+ * every GPU the library runs on holds from its first use until the process
+ * ends.  The call allocates no device memory (and calls no allocating
+ * library routine); with validation on (sgl_set_validate) it still copies
+ * the index metadata into host memory first.  A call whose split states do
+ * not fit 128 MiB -- the sizing rule of sgl_cascade_workspace_size with the
+ * splits doubled up to 512 keys; e.g. 256 requests x 32 query heads x D 128
+ * over contexts up to 8k fit -- returns SGL_ERR_WORKSPACE and enqueues
+ * nothing.  Every call on one GPU shares that GPU's array, and every state a
+ * call reads it has written first, so nothing needs clearing between calls;
+ * calls on one stream are ordered, but calls that can overlap on one GPU
+ * (several streams, or several host threads) race on the array and must not
+ * be issued. */
+int sgl_cascade_decode_attn_static(int dtype, const void *q, const void *k_new, const void *v_new,
+                                   void *k_pool, void *v_pool, int64_t num_slots,
+                                   const int32_t *r2t, int64_t num_rows, int64_t row_stride,
+                                   const int32_t *req_rows, const int32_t *seq_lens,
+                                   const int32_t *group_ptr, const int32_t *group_prefix_len,
+                                   int32_t batch, int32_t G, int32_t max_seq_len,
+                                   int32_t max_group_size, int32_t max_prefix_len,
+                                   int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                   void *o, float *lse, void *stream);
+size_t sgl_static_scratch_bytes(void);
+
 /* ------------------------------------------------------------------------
  * FP8 KV cache.  SGLang can keep the KV cache in FP8, which halves its bytes
  * ("SGLang 深度拆解" (chenxutan.com) section 4.3; the SGLang lecture notes

@@ -85,6 +85,10 @@ def load():
                                                    P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
                                                    F, P, P, P, SZ, P]),
         "sgl_cascade_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, I32]),
+        "sgl_cascade_decode_attn_static": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P,
+                                                          P, P, P, I32, I32, I32, I32, I32, I32, I32, I32,
+                                                          F, P, P, P]),
+        "sgl_static_scratch_bytes": (SZ, []),
         "sgl_store_kv_fp8": (ctypes.c_int, [ctypes.c_int, P, P, I64, P, P, P, I64, I32, I32, P, P, P]),
         "sgl_decode_attn_fp8kv": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, P, P, I64, P, I64, I64,
                                                  P, P, I32, I32, I32, I32, I32, F, P, P, P, SZ, P]),
@@ -117,6 +121,7 @@ EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_set_validate", "sgl_kv_p
            "sgl_radix_lock_batch", "sgl_kv_pool_alloc_batch", "sgl_build_req_to_token", "sgl_store_kv",
            "sgl_extend_attn", "sgl_extend_workspace_size", "sgl_decode_attn",
            "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size",
+           "sgl_cascade_decode_attn_static", "sgl_static_scratch_bytes",
            "sgl_store_kv_fp8", "sgl_decode_attn_fp8kv", "sgl_cascade_decode_attn_fp8kv",
            "sgl_mla_decode_attn", "sgl_mla_decode_workspace_size", "sgl_mla_cascade_decode_attn",
            "sgl_mla_cascade_workspace_size", "sgl_hicache_prefetch", "sgl_hicache_write_back"]
@@ -443,6 +448,35 @@ def _check_fp8_pools(k_pool, v_pool, k_scale, v_scale, Hkv, D):
         raise ValueError("k_pool / v_pool must both be [num_slots, Hkv, D]")
     if k_scale.numel() != Hkv or v_scale.numel() != Hkv:
         raise ValueError("k_scale / v_scale must hold one factor per KV head")
+
+
+def static_scratch_bytes():
+    return int(load().sgl_static_scratch_bytes())
+
+
+def cascade_decode_attn_static(q, k_pool, v_pool, r2t, req_rows, seq_lens, group_ptr, group_prefix_len,
+                               max_seq_len, max_group_size, max_prefix_len, k_new=None, v_new=None,
+                               scale=None, o=None, lse=None, stream=None):
+    """Cascade decode whose split states live in the library's static device
+    scratch (no workspace, no device allocation by the library); returns o."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = group_prefix_len.numel()
+    if o is None:
+        o = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    _check("sgl_cascade_decode_attn_static", load().sgl_cascade_decode_attn_static(
+        _dtype_code(q), _dev_ptr(q, "q", q.dtype), _dev_ptr(k_new, "k_new", q.dtype, True),
+        _dev_ptr(v_new, "v_new", q.dtype, True), _dev_ptr(k_pool, "k_pool", q.dtype),
+        _dev_ptr(v_pool, "v_pool", q.dtype), k_pool.shape[0], _dev_ptr(r2t, "r2t", torch.int32),
+        r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), _dev_ptr(group_ptr, "group_ptr", torch.int32),
+        _dev_ptr(group_prefix_len, "group_prefix_len", torch.int32), B, G, max_seq_len,
+        max_group_size, max_prefix_len, Hq, Hkv, D, scale, _dev_ptr(o, "o", q.dtype),
+        _dev_ptr(lse, "lse", torch.float32, True), _stream(stream)))
+    return o
 
 
 def store_kv_fp8(k_new, v_new, slots, k_pool, v_pool, k_scale, v_scale, stream=None):

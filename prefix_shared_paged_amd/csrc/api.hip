@@ -19,6 +19,8 @@ constexpr int kPrefixChunkMin = 64;
 constexpr int64_t kPrefixWorkgroups = 1024;  // ~4 per compute unit
 constexpr int kFlatXcdBlock = 16;    // consecutive requests per XCD block (flat fp8 decode)
 constexpr size_t kAlign = 256;
+// Split-state scratch of the allocation-free cascade decode (per GPU).
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -552,6 +554,52 @@ int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const v
                          r2t, num_rows, row_stride, req_rows, seq_lens, group_ptr, group_prefix_len, batch,
                          G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D, scale, o, lse,
                          workspace, workspace_bytes, stream);
+}
+
+// ---- allocation-free cascade decode ---------------------------------------------
+// The split states of sgl_cascade_decode_attn_static live in a fixed device
+// array that each GPU the library runs on holds until the process ends.  In
+// host code the array's name is a host-side stand-in, not a device address:
+// its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address reaches the kernels.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::atomic<void *> g_scratch_addr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on its first use).
+static int static_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SGL_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SGL_ERR_UNSUPPORTED;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return SGL_ERR_HIP;
+        }
+        g_scratch_addr[dev].store(p, std::memory_order_release);   // racing threads store the same address
+    }
+    *out = p;
+    return SGL_OK;
+}
+
+size_t sgl_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int sgl_cascade_decode_attn_static(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,
+                                   void *v_pool, int64_t num_slots, const int32_t *r2t, int64_t num_rows,
+                                   int64_t row_stride, const int32_t *req_rows, const int32_t *seq_lens,
+                                   const int32_t *group_ptr, const int32_t *group_prefix_len, int32_t batch,
+                                   int32_t G, int32_t max_seq_len, int32_t max_group_size,
+                                   int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                                   void *o, float *lse, void *stream) {
+    void *ws = nullptr;
+    const int rc = static_scratch(&ws);
+    if (rc != SGL_OK) return rc;
+    return decode_common(true, false, dtype, q, k_new, v_new, k_pool, v_pool, nullptr, nullptr, num_slots,
+                         r2t, num_rows, row_stride, req_rows, seq_lens, group_ptr, group_prefix_len, batch,
+                         G, max_seq_len, max_group_size, max_prefix_len, Hq, Hkv, D, scale, o, lse,
+                         ws, kStaticScratchBytes, stream);
 }
 
 int sgl_cascade_decode_attn_fp8kv(int dtype, const void *q, const void *k_new, const void *v_new,
