@@ -353,8 +353,9 @@ size_t sgl_static_scratch_bytes(void);
 
 /* ------------------------------------------------------------------------
  * FP8 KV cache.  SGLang can keep the KV cache in FP8, which halves its bytes
- * ("SGLang 深度拆解" (chenxutan.com) section 4.3; the SGLang lecture notes
- * (bhfrc.com) section 4 list an FP8 KV cache among the kernel work).  The
+ * ("SGLang 深度拆解" (chenxutan.com) section 4.3; "Lecture 16 · 案例研究：SGLang"
+ * (semidirectx.com) section 4 "More engineering" lists an FP8 KV cache among
+ * the kernel work).  The
  * pages fix neither format nor scaling; this library uses:
  *   - pools of uint8 OCP e4m3fn codes, layout [num_slots, Hkv, D] as for the
  *     bf16 pools (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no

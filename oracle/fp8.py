@@ -5,8 +5,8 @@ __graft_entry__.smoke() and the cpu_baseline leg of bench.py may import this.
 
 The pages say only that SGLang can keep the KV cache in FP8, which halves it
 ("SGLang 深度拆解" (chenxutan.com) section 4.3, on compressing the KV cache
-before it is moved; the SGLang lecture notes (bhfrc.com), section 4 "More
-engineering", list an FP8 KV cache among the v0.3 kernel work).  They fix
+before it is moved; "Lecture 16 · 案例研究：SGLang" (semidirectx.com), section 4
+"More engineering", lists an FP8 KV cache among the v0.3 kernel work).  They fix
 neither the 8-bit format nor the scaling.  Readings taken here:
 
   * Format: OCP 8-bit floating point e4m3fn -- sign bit, 4 exponent bits

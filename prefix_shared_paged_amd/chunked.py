@@ -2,8 +2,8 @@
 
 Long prompts are split into chunks so prefill work mixes with decode work in
 every round ("SGLang：从前端 DSL 到 SRT 服务运行时" (oripoin.cn): chunked
-prefill keeps long prompts from stalling decode; the CS349D lecture notes
-(semidirectx.com) section 3 model a fixed prompt-token budget per round).
+prefill keeps long prompts from stalling decode; "Lecture 16 · 案例研究：SGLang"
+(semidirectx.com) section 3 models a fixed prompt-token budget per round).
 One round:
   1. every session with prompt tokens left runs its next chunk of at most
      `chunk` tokens, all in ONE batched extend call (a chunk attends to the
