@@ -602,10 +602,11 @@ def bench_decode(args, flush):
     line = base_line(B / (c["call_ms"] * 1e-3), c["call_ms"], args, res["config"], c["roofline"], {
         "flat": res["flat"], "cascade": c, "mall_flush_ms": flush.time_ms()})
     if not args.no_cpu_baseline:
-        # oracle sample: decode rows of the first requests, drawn by the seeded generator
+        # oracle sample: decode rows of the requests (as many as the target
+        # time takes), drawn by the seeded generator
         L = wl.ctx_len
         Ks, Vs, rws = [], [], []
-        for r in range(min(B, 24)):
+        for r in range(min(B, 96)):
             K, V = wl.logical_kv(r)
             Ks.append(K)
             Vs.append(V)
@@ -1127,13 +1128,14 @@ def bench_multiturn(args, flush):
                 "calls); the rooflines sum only the calls' own events"})
     line["steps"] = len(tot_ms)
     if not args.no_cpu_baseline:
-        # oracle sample: last-chunk rows of a few sessions
+        # oracle sample: the last 128 prefill rows of the 24 sessions around
+        # the median history
         Ks, Vs, rws = [], [], []
-        for i in np.argsort(wl.hist)[len(wl.hist) // 2: len(wl.hist) // 2 + 6]:
+        for i in np.argsort(wl.hist)[len(wl.hist) // 2 - 12: len(wl.hist) // 2 + 12]:
             K, V = wl.kv(int(i), 0, int(wl.hist[i]))
             Ks.append(K)
             Vs.append(V)
-            for p in range(int(wl.hist[i]) - 64, int(wl.hist[i])):
+            for p in range(int(wl.hist[i]) - 128, int(wl.hist[i])):
                 rws.append((len(Ks) - 1, p, wl.queries(int(i), p, p + 1)[0]))
         line["cpu_baseline"] = cpu_baseline_rows(Ks, Vs, rws, Hq, Hkv, args.cpu_seconds, "multiturn prefill")
     return line
