@@ -502,8 +502,30 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     SplitArgs sa = a;
     sa.kind = 2; sa.chunk = fchunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
     sa.part = carve(wp, batch, Ss, Hq, D);
-    if (max_prefix_len > 0 && (rc = run_split(pa, false)) != SGL_OK) return rc;
-    if ((rc = run_split(sa, rows_suffix)) != SGL_OK) return rc;
+
+    // Both stages in one grid when the shape allows it (D 128, KV heads in
+    // groups of 4) and the suffix items are the longer ones: a suffix item
+    // walks fchunk / 16 tiles one at a time, a prefix item pchunk / 16 tiles
+    // with three in flight, so that is 3 fchunk > pchunk.  The suffix rounds
+    // that suffixes of about max_seq_len - max_prefix_len keys need (twice
+    // that, for groups with shorter prefixes) go first, the prefix items
+    // fill the compute units as they run out, and the rest of the Ss rounds
+    // (mostly empty) go last.  Measured: the 256-request decode workload
+    // takes 651 us this way against 666 us in two launches; on the 8-branch
+    // fork (prefix items longer) one grid with the prefix items first loses
+    // to two launches as the suffixes grow (139 against 129 us at 512 keys),
+    // so such calls keep one launch per stage.
+    const bool one_grid = max_prefix_len > 0 && rows_suffix && D == 128 && Hkv % 4 == 0 && 3 * fchunk > pchunk;
+    if (one_grid) {
+        SplitArgs sx = sa;
+        sx.xcd_block = 1;
+        const int64_t est = std::max<int64_t>(1, (int64_t)max_seq_len - max_prefix_len);
+        const int32_t head = (int32_t)std::min<int64_t>(Ss, 2 * ceil_div64(est, fchunk));
+        if ((rc = launch_cascade_split(pa, sx, head, fp8, st)) != SGL_OK) return rc;
+    } else {
+        if (max_prefix_len > 0 && (rc = run_split(pa, false)) != SGL_OK) return rc;
+        if ((rc = run_split(sa, rows_suffix)) != SGL_OK) return rc;
+    }
     m.kind = 3; m.prefix = pa.part; m.flat_or_suffix = sa.part;
     if (max_prefix_len == 0) m.kind = 0, m.flat_or_suffix = sa.part;
     return launch_merge(m, st);

@@ -148,6 +148,13 @@ int launch_split_fp8(const SplitArgs &a, hipStream_t st);
 // kinds 0 and 2 with one workgroup per (request, split) over all KV heads;
 // SGL_ERR_UNSUPPORTED for shapes left to the per-head kernels
 int launch_split_rows(const SplitArgs &a, bool fp8, hipStream_t st);
+// the cascade's prefix (kind 1) and suffix (kind 2) stages in one launch, for
+// D = 128 and Hkv a multiple of 4 (at most 16, Hq/Hkv <= 16); the suffix
+// uses the whole-row items of launch_split_rows, the prefix four-wave items
+// of up to 64 query rows.  Suffix split rounds [0, head_rounds) are
+// dispatched before the prefix items, the remaining rounds after them.
+// SGL_ERR_UNSUPPORTED for other shapes.
+int launch_cascade_split(const SplitArgs &pa, const SplitArgs &sa, int32_t head_rounds, bool fp8, hipStream_t st);
 // kinds 0-2 over a latent (MLA) cache: Hkv = 1, 576 score dims, 512 value dims
 int launch_split_mla(const SplitArgs &a, hipStream_t st);
 

@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "decode_rows.h"
 #include "decode_util.h"
 
 namespace {
@@ -62,12 +63,11 @@ struct SplitItem {
 };
 
 template <int WPG>
-__device__ __forceinline__ bool split_item(const SplitArgs &a, int w, SplitItem &it) {
+__device__ __forceinline__ bool split_item(const SplitArgs &a, int w, unsigned id, SplitItem &it) {
     const int n_rbg = (a.row_blocks + WPG - 1) / WPG;
-    const int id = blockIdx.x;
-    const int rest = id >> 3;
-    const int rbg = rest % n_rbg;
-    const int64_t item = (int64_t)(rest / n_rbg) * 8 + (id & 7);
+    const unsigned rest = id >> 3;
+    const int rbg = (int)(rest % (unsigned)n_rbg);
+    const int64_t item = (int64_t)(rest / (unsigned)n_rbg) * 8 + (id & 7);
     const int kvh = (int)(item % a.Hkv);
     const int64_t t_ = item / a.Hkv;
     const int64_t set64 = t_ % a.n_sets;
@@ -137,8 +137,13 @@ __device__ __forceinline__ bool split_item(const SplitArgs &a, int w, SplitItem 
 // whole tile.  DEPTH LDS buffers per tile ring: with 1, tile n+1's K loads go
 // out once tile n's K operands are read and its V loads once tile n's V is
 // read; with more, DEPTH-1 tiles are in flight while one is computed.
+//
+// The work item is that of workgroup id (see split_item); k_lds and v_lds
+// hold DEPTH tiles each, slot_lds min(chunk, kSlotTab) slot ids (kSlotTab
+// for kind 4).
 template <int D, int DEPTH, int WPG>
-__global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
+__device__ __forceinline__ void bf16_split(const SplitArgs &a, unsigned id, unsigned char *k_lds,
+                                           unsigned char *v_lds, int32_t *slot_lds) {
     constexpr int QT = D / 32;          // MFMA k-steps over head_dim
     constexpr int DB = D / 16;          // 16-dim output blocks
     constexpr int ROWB = 2 * D;         // bytes of one K/V row of one head
@@ -148,11 +153,7 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     static_assert(NI % WPG == 0, "each wave issues the same number of loads");
     static_assert(DEPTH >= 1 && DEPTH <= 4, "ring depth");
     constexpr int NIW = NI / WPG;       // K (and V) load instructions per wave per tile
-    constexpr int TB = TILE * ROWB;
-    // tile t of the split lives in ring buffer t % DEPTH
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TB];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TB];
-    extern __shared__ int32_t slot_lds[];  // [chunk]
+    constexpr int TB = TILE * ROWB;   // tile t of the split lives in ring buffer t % DEPTH
 
     const int lane = threadIdx.x & 63;
     const int w = WPG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
@@ -165,7 +166,7 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     };
 
     SplitItem it;
-    if (!split_item<WPG>(a, w, it)) return;
+    if (!split_item<WPG>(a, w, id, it)) return;
     const int kvh = it.kvh, s = it.s, g = a.Hq / a.Hkv;
     const int first_req = it.first_req, n_members = it.n_members;
     const int64_t k0 = it.k0, ref_row = it.ref_row;
@@ -405,8 +406,11 @@ __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
 // =============================================================================
 constexpr int TILE8 = 32;   // keys per fp8 tile
 
+// The work item is that of workgroup id (see split_item); k_lds and v_lds
+// hold DEPTH tiles each, slot_lds chunk slot ids.
 template <int D, int DEPTH, int WPG>
-__global__ void __launch_bounds__(64 * WPG) split_fp8_kernel(SplitArgs a) {
+__device__ __forceinline__ void fp8_split(const SplitArgs &a, unsigned id, unsigned char *k_lds,
+                                          unsigned char *v_lds, int32_t *slot_lds) {
     constexpr int QT = D / 32;          // MFMA k-steps over head_dim
     constexpr int DB = D / 16;          // 16-dim output blocks
     constexpr int ROWB = D;             // bytes of one K/V row of one head
@@ -418,9 +422,6 @@ __global__ void __launch_bounds__(64 * WPG) split_fp8_kernel(SplitArgs a) {
     constexpr int NIW = NI / WPG;
     constexpr int TB = TILE8 * ROWB;
     constexpr int KCH = D / 64;         // K chunks per lane per 16-key block (a quarter row)
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TB];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TB];
-    extern __shared__ int32_t slot_lds[];  // [chunk]
 
     const int lane = threadIdx.x & 63;
     const int w = WPG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
@@ -433,7 +434,7 @@ __global__ void __launch_bounds__(64 * WPG) split_fp8_kernel(SplitArgs a) {
     };
 
     SplitItem it;
-    if (!split_item<WPG>(a, w, it)) return;
+    if (!split_item<WPG>(a, w, id, it)) return;
     const int kvh = it.kvh, s = it.s, g = a.Hq / a.Hkv;
     const int first_req = it.first_req, n_members = it.n_members;
     const int nk = it.nk;
@@ -628,7 +629,91 @@ __global__ void __launch_bounds__(64 * WPG) split_fp8_kernel(SplitArgs a) {
     if (kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
 }
 
+template <int D, int DEPTH, int WPG>
+__global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TILE * 2 * D];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TILE * 2 * D];
+    extern __shared__ int32_t slot_lds[];  // [min(chunk, kSlotTab)]
+    bf16_split<D, DEPTH, WPG>(a, blockIdx.x, k_lds, v_lds, slot_lds);
+}
+
+template <int D, int DEPTH, int WPG>
+__global__ void __launch_bounds__(64 * WPG) split_fp8_kernel(SplitArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TILE8 * D];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TILE8 * D];
+    extern __shared__ int32_t slot_lds[];  // [chunk]
+    fp8_split<D, DEPTH, WPG>(a, blockIdx.x, k_lds, v_lds, slot_lds);
+}
+
+// ---- cascade: prefix and suffix stages in one grid ----------------------------
+// The grid holds three ranges of workgroups: suffix-stage items of the first
+// head split rounds (rows_split over four KV heads), then the prefix-stage
+// items (bf16_split / fp8_split, four waves sharing a ring of four tiles: up
+// to 64 query rows of a group per KV head), then the suffix items of the
+// remaining rounds.  Every range holds a multiple of 8 workgroups, so each
+// item lands on the XCD it would have in a launch of its own.  The stages
+// read only the pools and write disjoint state buffers, so nothing orders
+// them.  In one grid the call makes one launch fewer and neither stage waits
+// for the other to drain: on the 256-request decode workload the suffix
+// items (1 MiB each) go first and the prefix items, four times smaller, fill
+// the compute units as the suffix items run out, which shortens the tail.
+// The suffix grid is sized by max_seq_len, so its late rounds are mostly
+// empty workgroups when suffixes are shorter than that; dispatching those
+// after the prefix items keeps them from delaying real work.
+// Both stages fit one LDS budget: 32 KiB of tiles (two 16 KiB suffix tiles
+// or 2 x 4 prefix tiles of 4 KiB) and a slot table.
+template <int D, bool FP8>
+__global__ void __launch_bounds__(256) cascade_split_kernel(SplitArgs pa, SplitArgs sa, unsigned n_head,
+                                                            unsigned n_pre) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+    constexpr int PTB = FP8 ? TILE8 * D : TILE * 2 * D;             // prefix tile bytes
+    constexpr int STB = (FP8 ? 32 : 16) * kRowsHeads * D * (FP8 ? 1 : 2);   // suffix tile bytes
+    static_assert(8 * PTB == 2 * STB, "one LDS budget");
+    const unsigned id = blockIdx.x;
+    if (id < n_head || id - n_head >= n_pre) {
+        const unsigned sid = id < n_head ? id : id - n_pre;
+        rows_split<D, FP8, kRowsHeads>(sa, (int)sid, dyn_lds, dyn_lds + STB, (int32_t *)(dyn_lds + 2 * STB));
+    } else {
+        int32_t *slots = (int32_t *)(dyn_lds + 8 * PTB);
+        if constexpr (FP8) fp8_split<D, 4, 4>(pa, id - n_head, dyn_lds, dyn_lds + 4 * PTB, slots);
+        else bf16_split<D, 4, 4>(pa, id - n_head, dyn_lds, dyn_lds + 4 * PTB, slots);
+    }
+}
+
 }  // namespace
+
+int launch_cascade_split(const SplitArgs &pa0, const SplitArgs &sa, int32_t head_rounds, bool fp8, hipStream_t st) {
+    if (pa0.kind != 1 || sa.kind != 2) return SGL_ERR_INVALID;
+    if (pa0.D != 128 || sa.D != 128 || pa0.Hkv != sa.Hkv || pa0.Hq != sa.Hq) return SGL_ERR_UNSUPPORTED;
+    if (sa.Hkv % kRowsHeads != 0 || sa.Hkv > 16 || sa.Hq / sa.Hkv > 16) return SGL_ERR_UNSUPPORTED;
+    const int tk = fp8 ? TILE8 : TILE;
+    if (pa0.chunk % tk != 0 || sa.chunk % tk != 0 || sa.xcd_block < 1) return SGL_ERR_INVALID;
+    if (fp8 && (!sa.k_scale || !sa.v_scale || !pa0.k_scale || !pa0.v_scale)) return SGL_ERR_INVALID;
+    SplitArgs pa = pa0;
+    pa.row_blocks = (pa.max_members * (pa.Hq / pa.Hkv) + 15) / 16;
+    const int64_t n_rbg = (pa.row_blocks + 3) / 4;
+    const int64_t p_items = (int64_t)pa.n_sets * pa.max_splits * pa.Hkv;
+    const int64_t n_pre = ceil_div64(p_items, 8) * 8 * n_rbg;
+    // suffix workgroups per split round, as rows_split numbers them
+    const int rb = sa.xcd_block;
+    const int64_t n_v = (int64_t)sa.n_sets * (sa.Hkv / kRowsHeads);
+    const int64_t per_round = sa.n_sets > 0 ? 8 * (((n_v + rb - 1) / rb + 7) / 8) * rb : 0;
+    const int64_t n_suf = per_round * sa.max_splits;
+    const int64_t head = head_rounds < 0 ? 0 : (head_rounds > sa.max_splits ? sa.max_splits : head_rounds);
+    const int64_t n_head = per_round * head;
+    if (n_pre + n_suf == 0) return SGL_OK;
+    if (n_pre + n_suf > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+    const int64_t p_slots = fp8 ? pa.chunk : min(pa.chunk, kSlotTab);
+    const size_t dyn = 32768 + (size_t)(p_slots > sa.chunk ? p_slots : sa.chunk) * sizeof(int32_t);
+    const dim3 grid((unsigned)(n_pre + n_suf)), block(256);
+    if (fp8)
+        hipLaunchKernelGGL((cascade_split_kernel<128, true>), grid, block, dyn, st, pa, sa, (unsigned)n_head,
+                           (unsigned)n_pre);
+    else
+        hipLaunchKernelGGL((cascade_split_kernel<128, false>), grid, block, dyn, st, pa, sa, (unsigned)n_head,
+                           (unsigned)n_pre);
+    return hip_status(hipGetLastError());
+}
 
 int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
     if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
