@@ -308,7 +308,8 @@ size_t sgl_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq,
  * max_group_size * (Hq / Hkv) <= 4096.  Up to 64 query rows of a group
  * (request x query head) share one read of the prefix; larger groups read it
  * once per 64 rows.
- * workspace: sgl_cascade_workspace_size(...) bytes. */
+ * workspace: sgl_cascade_workspace_size(...) bytes (both stages' split states
+ * and each request's suffix start, written by the call before it reads them). */
 int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new,
                             void *k_pool, void *v_pool, int64_t num_slots,
                             const int32_t *r2t, int64_t num_rows, int64_t row_stride,
@@ -327,14 +328,15 @@ size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
  * memory: code under HIP graph capture, serving loops that must not call
  * hipMalloc, harnesses that forbid allocation.  Same arguments, semantics and
  * result as sgl_cascade_decode_attn, without the workspace: the split states
- * live in a static device array of sgl_static_scratch_bytes() = 128 MiB that
- * every GPU the library runs on holds from its first use until the process
- * ends.  The call allocates no device memory (and calls no allocating
+ * (and the requests' suffix starts) live in a static device array of
+ * sgl_static_scratch_bytes() = 128 MiB that every GPU the library runs on
+ * holds from its first use until the process ends.  The call allocates no device memory (and calls no allocating
  * library routine); with validation on (sgl_set_validate) it still copies
  * the index metadata into host memory first.  A call whose split states do
  * not fit 128 MiB -- the sizing rule of sgl_cascade_workspace_size with the
- * splits doubled up to 512 keys; e.g. 256 requests x 32 query heads x D 128
- * over contexts up to 8k fit -- returns SGL_ERR_WORKSPACE and enqueues
+ * prefix splits doubled up to 512 keys and the suffix splits up to 1024;
+ * e.g. 256 requests x 32 query heads x D 128 over contexts up to 8k fit --
+ * returns SGL_ERR_WORKSPACE and enqueues
  * nothing.  Every call on one GPU shares that GPU's array, and every state a
  * call reads it has written first, so nothing needs clearing between calls;
  * calls on one stream are ordered, but calls that can overlap on one GPU

@@ -13,7 +13,8 @@
 namespace {
 
 constexpr int kDecodeChunk = 1024;   // keys per split of the per-head kernels (flat, suffix)
-constexpr int kRowsChunk = 512;      // keys per split of the whole-row kernel (flat, suffix)
+constexpr int kRowsChunk = 512;      // keys per split of the whole-row kernel (flat fp8)
+constexpr int kSuffixChunk = 1024;   // keys per split of the cascade suffix (whole-row kernel), at most
 constexpr int kPrefixChunkMax = 512;
 constexpr int kPrefixChunkMin = 64;
 constexpr int64_t kPrefixWorkgroups = 1024;  // ~4 per compute unit
@@ -41,15 +42,20 @@ int prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int3
 }
 
 // Keys per split of the cascade suffix stage (the whole-row kernel, one
-// workgroup per (request, 4 KV heads, split)).  512 normally; halved (down to
-// 64) while the suffixes -- estimated as max_seq_len - max_prefix_len, which
-// only sizes the splits -- would give fewer than kPrefixWorkgroups
-// workgroups: a batch of a few dozen requests with short suffixes otherwise
-// leaves most compute units idle while each workgroup walks its suffix alone.
+// workgroup per (request, 4 KV heads, split)).  kSuffixChunk normally: on the
+// 256-request decode workload 1024-key splits take 641 us against 653 us with
+// 512 (each workgroup hand-off on a compute unit -- draining the finished
+// item's state stores, starting the next -- leaves its slot idle for a few
+// us, and the prefix items that follow the suffix rounds fill the longer
+// tail).  Halved (down to 64) while the suffixes -- estimated as
+// max_seq_len - max_prefix_len, which only sizes the splits -- would give
+// fewer than kPrefixWorkgroups workgroups: a batch of a few dozen requests
+// with short suffixes otherwise leaves most compute units idle while each
+// workgroup walks its suffix alone.
 int suffix_chunk(int32_t batch, int32_t max_seq_len, int32_t max_prefix_len, int32_t Hkv) {
     const int64_t units = (int64_t)batch * (Hkv > 4 ? Hkv / 4 : 1);
     const int64_t est = std::max<int64_t>(1, (int64_t)max_seq_len - std::max<int32_t>(max_prefix_len, 0));
-    int c = kRowsChunk;
+    int c = kSuffixChunk;
     while (c > kPrefixChunkMin && units * ceil_div64(est, c) < kPrefixWorkgroups) c /= 2;
     return c;
 }
@@ -400,9 +406,10 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     const bool rows_suffix = rows_ok;
     // Split sizes.  The cascade's preferred prefix and suffix splits depend on
     // the call's bounds (smaller bounds can prefer smaller splits, hence more
-    // split states), so they are doubled, up to 512 keys, while their states
-    // would not fit the caller's workspace: a workspace sized by
-    // sgl_cascade_workspace_size for larger bounds always holds 512-key splits.
+    // split states), so they are doubled, up to kPrefixChunkMax and
+    // kSuffixChunk keys, while their states would not fit the caller's
+    // workspace: a workspace sized by sgl_cascade_workspace_size for larger
+    // bounds always holds splits of those sizes.
     int pchunk = kPrefixChunkMax, fchunk = rows_flat ? kRowsChunk : kDecodeChunk;
     size_t need;
     if (cascade) {
@@ -410,10 +417,11 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
         fchunk = rows_suffix ? suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv) : kDecodeChunk;
         auto need_for = [&](int pc, int fc) {
             const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pc) : 1;
-            return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, ceil_div64(max_seq_len, fc), Hq, D);
+            return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, ceil_div64(max_seq_len, fc), Hq, D) +
+                   align_up((size_t)batch * sizeof(int32_t));
         };
         while (need_for(pchunk, fchunk) > workspace_bytes) {
-            if (fchunk < kRowsChunk && (fchunk <= pchunk || pchunk >= kPrefixChunkMax)) fchunk *= 2;
+            if (fchunk < kSuffixChunk && (fchunk <= pchunk || pchunk >= kPrefixChunkMax)) fchunk *= 2;
             else if (pchunk < kPrefixChunkMax) pchunk *= 2;
             else break;
         }
@@ -502,6 +510,12 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     SplitArgs sa = a;
     sa.kind = 2; sa.chunk = fchunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
     sa.part = carve(wp, batch, Ss, Hq, D);
+    // each request's suffix start, found once for every suffix item and the merge
+    int32_t *suffix_lo = (int32_t *)wp;
+    if ((rc = launch_suffix_start(group_ptr, group_prefix_len, seq_lens, G, batch, suffix_lo, st)) != SGL_OK)
+        return rc;
+    sa.suffix_lo = suffix_lo;
+    m.suffix_lo = suffix_lo;
 
     // Both stages in one grid when the shape allows it (D 128, KV heads in
     // groups of 4) and the suffix items are the longer ones: a suffix item
@@ -562,7 +576,8 @@ size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
                            ? ceil_div64(max_prefix_len, prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D))
                            : 1;
     const int64_t Ss = ceil_div64(max_seq_len, suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv));
-    return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, Ss, Hq, D);
+    // split states of both stages, then each request's suffix start
+    return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, Ss, Hq, D) + align_up((size_t)batch * sizeof(int32_t));
 }
 
 int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,

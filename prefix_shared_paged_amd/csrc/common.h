@@ -30,6 +30,22 @@ __device__ __forceinline__ int32_t safe_slot(int32_t s, int64_t num_slots) {
     return (s >= 0 && (int64_t)s < num_slots) ? s : 0;
 }
 
+// Prefix group of request r: the last g in [0, G) with group_ptr[g] <= r
+// (group_ptr ascends from 0).  The whole wave searches at once -- lane l
+// compares entry base + l, the ballot counts the entries <= r -- so the
+// answer costs one load round trip per 64 groups instead of a chain of
+// log2(G) dependent loads.  Every lane of the wave must be active; the result
+// lies in [0, G) whatever group_ptr holds.
+__device__ __forceinline__ int wave_find_group(const int32_t *group_ptr, int G, int r) {
+    const int lane = threadIdx.x & 63;
+    for (int base = 0;; base += 64) {
+        const int g = base + lane;
+        const bool le = g < G && group_ptr[g] <= r;
+        const int cnt = __popcll(__builtin_amdgcn_ballot_w64(le));
+        if (cnt < 64 || base + 64 >= G) return base + cnt > 0 ? base + cnt - 1 : 0;
+    }
+}
+
 // Wave-wide reductions (wave64) ------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -132,6 +148,8 @@ struct SplitArgs {
     const int64_t *q_off;          // kind 4: token offsets [batch + 1]
     const int32_t *prefix_lens;    // kind 4: cached keys per request
     int32_t n_spl;                 // kind 4: splits per request
+    const int32_t *suffix_lo;      // kind 2, optional: first suffix key of each request
+                                   // (launch_suffix_start); else found from the group arrays
     PartialBuf part;
 };
 
@@ -182,8 +200,14 @@ struct MergeArgs {
     int32_t n_req, n_spl;
     int32_t Hkv;           // kind 5: query rows of a tile follow from Hq / Hkv
     int64_t row_stride;    // kind 5: bound on a context (keys past it are not read)
+    const int32_t *suffix_lo;   // kind 3, optional: as SplitArgs::suffix_lo
 };
 int launch_merge(const MergeArgs &a, hipStream_t st);
+
+// Cascade: lo[r] = the group prefix length of request r clamped to [0,
+// seq_lens[r]] -- where its suffix starts -- for r in [0, batch).
+int launch_suffix_start(const int32_t *group_ptr, const int32_t *group_prefix_len, const int32_t *seq_lens,
+                        int32_t G, int32_t batch, int32_t *lo, hipStream_t st);
 
 // Row moves between a page-locked host tier and the pool (kernels_hicache.hip).
 // Row move i pairs host row host_rows[i] with pool slot slots[i]; tensor t

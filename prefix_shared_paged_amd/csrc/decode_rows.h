@@ -93,8 +93,7 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, unsigned
     const int64_t ref_row = a.req_rows[set];
     int64_t lo = 0, hi = L;
     if (a.kind == 2) {
-        const int grp = find_group_dec(a.group_ptr, a.G, set);
-        const int64_t P = a.group_prefix_len[grp];
+        const int64_t P = a.suffix_lo ? a.suffix_lo[set] : a.group_prefix_len[wave_find_group(a.group_ptr, a.G, set)];
         lo = P < 0 ? 0 : (P > L ? L : P);
     }
     if (ref_row < 0 || ref_row >= a.num_rows) return;

@@ -17,15 +17,6 @@ __device__ __forceinline__ int swz(int r) {
     return (r & 7) ^ ((r >> 3) & 1);                                // 8 chunks per row
 }
 
-__device__ __forceinline__ int find_group_dec(const int32_t *group_ptr, int G, int r) {
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (group_ptr[mid] <= r) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 ld_q(const __bf16 *p) {

@@ -109,8 +109,8 @@ __device__ __forceinline__ bool split_item(const SplitArgs &a, int w, unsigned i
         if (a.kind == 0) {
             lo = 0;
         } else {
-            const int grp = find_group_dec(a.group_ptr, a.G, set);
-            const int64_t P = a.group_prefix_len[grp];
+            const int64_t P =
+                a.suffix_lo ? a.suffix_lo[set] : a.group_prefix_len[wave_find_group(a.group_ptr, a.G, set)];
             lo = P < 0 ? 0 : (P > L ? L : P);
         }
         hi = L;

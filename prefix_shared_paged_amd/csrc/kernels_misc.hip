@@ -1,5 +1,7 @@
 // kernels_misc.hip -- req_to_token build, KV store, and the log-sum-exp merge
 // of partial softmax states.
+#include <climits>
+
 #include "common.h"
 
 // ---------------------------------------------------------------------------
@@ -246,20 +248,47 @@ int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new,
 }
 
 // ---------------------------------------------------------------------------
+// Suffix start of every request of a cascade call, computed once so that the
+// suffix split items and the merge read one value instead of searching the
+// group table themselves (a chain of dependent loads in every one of them,
+// including the split items past a request's last split).  Lane l of a wave
+// holds request r = 64 w + l; the wave loads 64 group_ptr entries at a time
+// and every lane counts those <= r (readlane broadcasts), so group(r) = count
+// - 1 for ascending group_ptr; any contents give a group in [0, G).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) suffix_start_kernel(const int32_t *__restrict__ group_ptr,
+                                                           const int32_t *__restrict__ group_prefix_len,
+                                                           const int32_t *__restrict__ seq_lens, int32_t G,
+                                                           int32_t batch, int32_t *__restrict__ lo) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int cnt = 0;
+    for (int base = 0; base < G; base += 64) {
+        const int gp = base + lane < G ? group_ptr[base + lane] : INT_MAX;
+        const int n = G - base < 64 ? G - base : 64;
+        for (int j = 0; j < n; j++) cnt += __builtin_amdgcn_readlane(gp, j) <= r ? 1 : 0;
+    }
+    if (r >= batch) return;
+    const int64_t P = group_prefix_len[cnt > 0 ? cnt - 1 : 0], L = seq_lens[r];
+    lo[r] = (int32_t)(P < 0 ? 0 : (P > L ? L : P));
+}
+
+int launch_suffix_start(const int32_t *group_ptr, const int32_t *group_prefix_len, const int32_t *seq_lens,
+                        int32_t G, int32_t batch, int32_t *lo, hipStream_t st) {
+    if (batch <= 0) return SGL_OK;
+    if (G < 1) return SGL_ERR_INVALID;
+    hipLaunchKernelGGL(suffix_start_kernel, dim3((unsigned)ceil_div64(batch, 256)), dim3(256), 0, st, group_ptr,
+                       group_prefix_len, seq_lens, G, batch, lo);
+    return hip_status(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
 // Merge of partial softmax states.  The pages give the one-key online-softmax
 // update (rescale what was accumulated by e^(m_old - m_new), chenxutan.com
 // section 3.2 PagedPrefill); applied to whole blocks it is
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s o_s 2^(m_s - M) / L
 // (m in log2 units).  One wave per (request, q head); lanes own dims.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int find_group(const int32_t *group_ptr, int G, int r) {
-    int lo = 0, hi = G - 1;  // last g with group_ptr[g] <= r
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (group_ptr[mid] <= r) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
 
 template <int D, bool OUT_BF16>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
@@ -294,8 +323,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     } else {
         const int64_t L = a.seq_lens[r];
         if (a.kind == 3) {
-            const int g = find_group(a.group_ptr, a.G, r);
-            int64_t P = a.group_prefix_len[g];
+            int64_t P = a.suffix_lo ? a.suffix_lo[r] : a.group_prefix_len[wave_find_group(a.group_ptr, a.G, r)];
             P = P < 0 ? 0 : (P > L ? L : P);
             np = (int)ceil_div64(P, a.chunk_prefix);
             ns = (int)ceil_div64(L - P, a.chunk_flat);

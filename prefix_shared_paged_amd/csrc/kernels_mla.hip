@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(256 * RBW) split_mla_kernel(SplitArgs a) {
         ref_row = a.req_rows[set];
         lo = 0;
         if (a.kind == 2) {
-            const int grp = find_group_dec(a.group_ptr, a.G, set);
+            const int grp = wave_find_group(a.group_ptr, a.G, set);
             const int64_t P = a.group_prefix_len[grp];
             lo = P < 0 ? 0 : (P > L ? L : P);
         }
@@ -355,7 +355,7 @@ __global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
         ref_row = a.req_rows[set];
         lo = 0;
         if (a.kind == 2) {
-            const int grp = find_group_dec(a.group_ptr, a.G, set);
+            const int grp = wave_find_group(a.group_ptr, a.G, set);
             const int64_t P = a.group_prefix_len[grp];
             lo = P < 0 ? 0 : (P > L ? L : P);
         }
