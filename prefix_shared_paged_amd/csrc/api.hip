@@ -459,17 +459,39 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
         }
     }
 
+    // Workspace: [flat splits] or [prefix splits][suffix splits][suffix starts]
+    char *wp = (char *)workspace;
+    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pchunk) : 1;
+    const int64_t Ss = ceil_div64(max_seq_len, fchunk);
+    PartialBuf flat_part{}, pre_part{}, suf_part{};
+    int32_t *suffix_lo = nullptr;
+    if (!cascade) {
+        flat_part = carve(wp, batch, ceil_div64(max_seq_len, fchunk), Hq, D);
+    } else {
+        pre_part = carve(wp, batch, Sp, Hq, D);
+        suf_part = carve(wp, batch, Ss, Hq, D);
+        suffix_lo = (int32_t *)wp;
+    }
+    // The current token's K/V, and (cascade) each request's suffix start,
+    // found once for every suffix item and the merge: one kernel when there
+    // is a token to store.
+    SuffixStartArgs ss;
+    ss.group_ptr = group_ptr; ss.group_prefix_len = group_prefix_len; ss.seq_lens = seq_lens;
+    ss.G = G; ss.batch = batch; ss.lo = suffix_lo;
     int rc = SGL_OK;
     if (k_new) {
+        const SuffixStartArgs *ssp = cascade ? &ss : nullptr;
         rc = fp8 ? launch_store_kv_fp8(2, elt_size(dtype), k_new, v_new, batch, nullptr, k_pool, v_pool,
                                        num_slots, Hkv, D, k_scale, v_scale, r2t, num_rows, row_stride,
-                                       req_rows, seq_lens, nullptr, batch, 0, st)
+                                       req_rows, seq_lens, nullptr, batch, 0, st, ssp)
                  : launch_store_kv(2, elt_size(dtype), k_new, v_new, batch, nullptr, k_pool, v_pool, num_slots,
-                                   Hkv, D, r2t, num_rows, row_stride, req_rows, seq_lens, nullptr, batch, 0, st);
-        if (rc != SGL_OK) return rc;
+                                   Hkv, D, r2t, num_rows, row_stride, req_rows, seq_lens, nullptr, batch, 0, st,
+                                   ssp);
+    } else if (cascade) {
+        rc = launch_suffix_start(ss, st);
     }
+    if (rc != SGL_OK) return rc;
 
-    char *wp = (char *)workspace;
     SplitArgs a;
     std::memset(&a, 0, sizeof a);
     a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.num_slots = num_slots; a.r2t = r2t;
@@ -493,27 +515,20 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     m.chunk_flat = fchunk; m.chunk_prefix = pchunk;
 
     if (!cascade) {
-        const int64_t S = ceil_div64(max_seq_len, fchunk);
-        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)S; a.chunk = fchunk;
-        a.part = carve(wp, batch, S, Hq, D);
+        a.kind = 0; a.n_sets = batch; a.max_splits = (int32_t)flat_part.S; a.chunk = fchunk;
+        a.part = flat_part;
         if ((rc = run_split(a, rows_flat)) != SGL_OK) return rc;
         m.kind = 0; m.flat_or_suffix = a.part;
         return launch_merge(m, st);
     }
-    const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pchunk) : 1;
-    const int64_t Ss = ceil_div64(max_seq_len, fchunk);
     SplitArgs pa = a;
     pa.kind = 1; pa.chunk = pchunk; pa.max_splits = (int32_t)Sp; pa.max_members = max_group_size;
-    pa.part = carve(wp, batch, Sp, Hq, D);
+    pa.part = pre_part;
     // the f32 path walks (request, head, split) for every kind; the bf16 path one wave per group
     pa.n_sets = dtype == SGL_F32 ? batch : G;
     SplitArgs sa = a;
     sa.kind = 2; sa.chunk = fchunk; sa.max_splits = (int32_t)Ss; sa.n_sets = batch;
-    sa.part = carve(wp, batch, Ss, Hq, D);
-    // each request's suffix start, found once for every suffix item and the merge
-    int32_t *suffix_lo = (int32_t *)wp;
-    if ((rc = launch_suffix_start(group_ptr, group_prefix_len, seq_lens, G, batch, suffix_lo, st)) != SGL_OK)
-        return rc;
+    sa.part = suf_part;
     sa.suffix_lo = suffix_lo;
     m.suffix_lo = suffix_lo;
 

@@ -82,12 +82,24 @@ int launch_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride
                               const int64_t *prefix_off, const int32_t *new_slots,
                               const int64_t *new_off, const int32_t *new_col0, hipStream_t st);
 
-// mode 0: slots[i];  mode 1: extend (r2t at prefix_lens[r] + i);  mode 2: decode (r2t at seq_lens[r]-1)
+// Cascade: lo[r] = the group prefix length of request r clamped to [0,
+// seq_lens[r]] -- where its suffix starts -- for r in [0, batch).
+struct SuffixStartArgs {
+    const int32_t *group_ptr;
+    const int32_t *group_prefix_len;
+    const int32_t *seq_lens;
+    int32_t G, batch;
+    int32_t *lo;
+};
+int launch_suffix_start(const SuffixStartArgs &a, hipStream_t st);
+
+// mode 0: slots[i];  mode 1: extend (r2t at prefix_lens[r] + i);  mode 2: decode (r2t at seq_lens[r]-1).
+// Mode 2 also writes the suffix starts of *ss when ss is not null (one launch for both).
 int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
                     const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
                     int32_t Hkv, int32_t D, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                     const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
-                    int32_t batch, int32_t max_extend_len, hipStream_t st);
+                    int32_t batch, int32_t max_extend_len, hipStream_t st, const SuffixStartArgs *ss = nullptr);
 
 // The same three modes, quantising to e4m3fn codes with per-KV-head factors.
 int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
@@ -95,7 +107,7 @@ int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new,
                         int32_t Hkv, int32_t D, const float *k_scale, const float *v_scale,
                         const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                         const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
-                        int32_t batch, int32_t max_extend_len, hipStream_t st);
+                        int32_t batch, int32_t max_extend_len, hipStream_t st, const SuffixStartArgs *ss = nullptr);
 
 int launch_extend_f32(const float *q, const float *k_pool, const float *v_pool, int64_t num_slots,
                       const int32_t *r2t, int64_t num_rows, int64_t row_stride,
@@ -203,11 +215,6 @@ struct MergeArgs {
     const int32_t *suffix_lo;   // kind 3, optional: as SplitArgs::suffix_lo
 };
 int launch_merge(const MergeArgs &a, hipStream_t st);
-
-// Cascade: lo[r] = the group prefix length of request r clamped to [0,
-// seq_lens[r]] -- where its suffix starts -- for r in [0, batch).
-int launch_suffix_start(const int32_t *group_ptr, const int32_t *group_prefix_len, const int32_t *seq_lens,
-                        int32_t G, int32_t batch, int32_t *lo, hipStream_t st);
 
 // Row moves between a page-locked host tier and the pool (kernels_hicache.hip).
 // Row move i pairs host row host_rows[i] with pool slot slots[i]; tensor t

@@ -1,6 +1,7 @@
 // kernels_misc.hip -- req_to_token build, KV store, and the log-sum-exp merge
 // of partial softmax states.
 #include <climits>
+#include <cstring>
 
 #include "common.h"
 
@@ -51,13 +52,52 @@ int launch_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride
 // V into the pools at their slots ("SGLang 深度解读" module 5: write the
 // current K, V at cache_loc before attending).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Suffix start of every request of a cascade call, computed once so that the
+// suffix split items and the merge read one value instead of searching the
+// group table themselves (a chain of dependent loads in every one of them,
+// including the split items past a request's last split).  Thread t of the
+// grid takes requests t, t + grid size, ...; the 64 lanes of a wave load 64
+// group_ptr entries at a time and every lane counts those <= its request
+// (readlane broadcasts), so group(r) = count - 1 for ascending group_ptr;
+// any contents give a group in [0, G).  Every thread of the grid must run
+// it (whole waves take part in the search).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void suffix_starts(const SuffixStartArgs &a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t r0 = (int64_t)blockIdx.x * blockDim.x; r0 < a.batch; r0 += step) {   // uniform per workgroup
+        const int64_t r = r0 + threadIdx.x;
+        int cnt = 0;
+        for (int base = 0; base < a.G; base += 64) {
+            const int gp = base + lane < a.G ? a.group_ptr[base + lane] : INT_MAX;
+            const int n = a.G - base < 64 ? a.G - base : 64;
+            for (int j = 0; j < n; j++) cnt += __builtin_amdgcn_readlane(gp, j) <= r ? 1 : 0;
+        }
+        if (r < a.batch) {
+            const int64_t P = a.group_prefix_len[cnt > 0 ? cnt - 1 : 0], L = a.seq_lens[r];
+            a.lo[r] = (int32_t)(P < 0 ? 0 : (P > L ? L : P));
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) suffix_start_kernel(SuffixStartArgs a) { suffix_starts(a); }
+
+int launch_suffix_start(const SuffixStartArgs &a, hipStream_t st) {
+    if (a.batch <= 0) return SGL_OK;
+    if (a.G < 1 || !a.lo) return SGL_ERR_INVALID;
+    hipLaunchKernelGGL(suffix_start_kernel, dim3((unsigned)ceil_div64(a.batch, 256)), dim3(256), 0, st, a);
+    return hip_status(hipGetLastError());
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(256) store_kv_kernel(
     const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_new, uint4 *__restrict__ k_pool,
     uint4 *__restrict__ v_pool, int64_t num_slots, int32_t row_chunks, int64_t n_tokens,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ r2t, int64_t num_rows,
     int64_t stride, const int32_t *__restrict__ req_rows, const int32_t *__restrict__ lens,
-    const int64_t *__restrict__ q_off) {
+    const int64_t *__restrict__ q_off, SuffixStartArgs ss) {
+    if (MODE == 2 && ss.lo) suffix_starts(ss);
     if (MODE == 1) {
         // extend: blockIdx.y = request; tokens q_off[r] .. q_off[r+1]
         const int r = blockIdx.y;
@@ -101,8 +141,11 @@ int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int
                     const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
                     int32_t Hkv, int32_t D, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                     const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
-                    int32_t batch, int32_t max_extend_len, hipStream_t st) {
+                    int32_t batch, int32_t max_extend_len, hipStream_t st, const SuffixStartArgs *ss) {
     const int64_t row_bytes = (int64_t)Hkv * D * elt;
+    SuffixStartArgs sx;
+    std::memset(&sx, 0, sizeof sx);
+    if (ss && mode == 2) sx = *ss;
     const int32_t row_chunks = (int32_t)(row_bytes / 16);
     if (n_tokens == 0) return SGL_OK;
     const uint4 *kn = (const uint4 *)k_new;
@@ -115,17 +158,17 @@ int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int
         if (gx < 1) gx = 1;
         hipLaunchKernelGGL(store_kv_kernel<1>, dim3(gx, batch), dim3(256), 0, st, kn, vn, kp, vp,
                            num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
-                           req_rows, lens, q_off);
+                           req_rows, lens, q_off, sx);
     } else {
         int gx = (int)std::min<int64_t>(ceil_div64(n_tokens * row_chunks, 256), 8192);
         if (mode == 0)
             hipLaunchKernelGGL(store_kv_kernel<0>, dim3(gx), dim3(256), 0, st, kn, vn, kp, vp,
                                num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
-                               req_rows, lens, q_off);
+                               req_rows, lens, q_off, sx);
         else
             hipLaunchKernelGGL(store_kv_kernel<2>, dim3(gx), dim3(256), 0, st, kn, vn, kp, vp,
                                num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
-                               req_rows, lens, q_off);
+                               req_rows, lens, q_off, sx);
     }
     return hip_status(hipGetLastError());
 }
@@ -178,7 +221,8 @@ __global__ void __launch_bounds__(256) store_kv_fp8_kernel(
     const float *__restrict__ k_scale, const float *__restrict__ v_scale, int64_t n_tokens,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ r2t, int64_t num_rows,
     int64_t stride, const int32_t *__restrict__ req_rows, const int32_t *__restrict__ lens,
-    const int64_t *__restrict__ q_off) {
+    const int64_t *__restrict__ q_off, SuffixStartArgs ss) {
+    if (MODE == 2 && ss.lo) suffix_starts(ss);
     constexpr int IN_CHUNK = 16 * ELT;   // input bytes per 16 codes
     int64_t t0 = 0, n = n_tokens * row_chunks, row = 0, P = 0;
     if (MODE == 1) {
@@ -219,9 +263,12 @@ int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new,
                         int32_t Hkv, int32_t D, const float *k_scale, const float *v_scale,
                         const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                         const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
-                        int32_t batch, int32_t max_extend_len, hipStream_t st) {
+                        int32_t batch, int32_t max_extend_len, hipStream_t st, const SuffixStartArgs *ss) {
     if (n_tokens == 0) return SGL_OK;
     const int32_t row_chunks = Hkv * D / 16, head_chunks = D / 16;
+    SuffixStartArgs sx;
+    std::memset(&sx, 0, sizeof sx);
+    if (ss && mode == 2) sx = *ss;
     const char *kn = (const char *)k_new;
     const char *vn = (const char *)v_new;
     uint4 *kp = (uint4 *)k_pool;
@@ -237,48 +284,13 @@ int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new,
 #define SGL_STORE8(M, E)                                                                                    \
     hipLaunchKernelGGL((store_kv_fp8_kernel<M, E>), grid, dim3(256), 0, st, kn, vn, kp, vp, num_slots,     \
                        row_chunks, head_chunks, k_scale, v_scale, n_tokens, slots, r2t, num_rows,          \
-                       row_stride, req_rows, lens, q_off)
+                       row_stride, req_rows, lens, q_off, sx)
     if (elt == 2) {
         if (mode == 0) SGL_STORE8(0, 2); else if (mode == 1) SGL_STORE8(1, 2); else SGL_STORE8(2, 2);
     } else {
         if (mode == 0) SGL_STORE8(0, 4); else if (mode == 1) SGL_STORE8(1, 4); else SGL_STORE8(2, 4);
     }
 #undef SGL_STORE8
-    return hip_status(hipGetLastError());
-}
-
-// ---------------------------------------------------------------------------
-// Suffix start of every request of a cascade call, computed once so that the
-// suffix split items and the merge read one value instead of searching the
-// group table themselves (a chain of dependent loads in every one of them,
-// including the split items past a request's last split).  Lane l of a wave
-// holds request r = 64 w + l; the wave loads 64 group_ptr entries at a time
-// and every lane counts those <= r (readlane broadcasts), so group(r) = count
-// - 1 for ascending group_ptr; any contents give a group in [0, G).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) suffix_start_kernel(const int32_t *__restrict__ group_ptr,
-                                                           const int32_t *__restrict__ group_prefix_len,
-                                                           const int32_t *__restrict__ seq_lens, int32_t G,
-                                                           int32_t batch, int32_t *__restrict__ lo) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int cnt = 0;
-    for (int base = 0; base < G; base += 64) {
-        const int gp = base + lane < G ? group_ptr[base + lane] : INT_MAX;
-        const int n = G - base < 64 ? G - base : 64;
-        for (int j = 0; j < n; j++) cnt += __builtin_amdgcn_readlane(gp, j) <= r ? 1 : 0;
-    }
-    if (r >= batch) return;
-    const int64_t P = group_prefix_len[cnt > 0 ? cnt - 1 : 0], L = seq_lens[r];
-    lo[r] = (int32_t)(P < 0 ? 0 : (P > L ? L : P));
-}
-
-int launch_suffix_start(const int32_t *group_ptr, const int32_t *group_prefix_len, const int32_t *seq_lens,
-                        int32_t G, int32_t batch, int32_t *lo, hipStream_t st) {
-    if (batch <= 0) return SGL_OK;
-    if (G < 1) return SGL_ERR_INVALID;
-    hipLaunchKernelGGL(suffix_start_kernel, dim3((unsigned)ceil_div64(batch, 256)), dim3(256), 0, st, group_ptr,
-                       group_prefix_len, seq_lens, G, batch, lo);
     return hip_status(hipGetLastError());
 }
 
