@@ -11,7 +11,9 @@
 // query heads that share the KV head are packed into the tile, so every K/V
 // tile brought into LDS serves 128 rows.  Workgroup ids are ordered so that
 // id % 8 (the XCD a workgroup lands on) follows the KV head: all tiles of one
-// KV head share an XCD and its L2 holds that head's prefix.
+// KV head share an XCD and its L2 holds that head's prefix.  Within a
+// request the query tiles go last to first (the causal tiles with the most
+// keys start first; 1 % shorter on the 64 x 256 over 2048 workload).
 //
 // Keys are gathered by slot id straight from HBM into LDS with
 // global_load_lds_dwordx4 (no register staging), 32 keys at a time, into rings
@@ -142,7 +144,7 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
     const int id = blockIdx.x;
     const int kvh = id % Hkv;
     const int rest = id / Hkv;
-    const int qt = rest % n_qtiles;
+    const int qt = n_qtiles - 1 - rest % n_qtiles;   // the tiles with the most keys first
     const int r = SPLIT ? (rest / n_qtiles) % batch : rest / n_qtiles;
     const int sp = SPLIT ? rest / n_qtiles / batch : 0;   // split of the key range
     const int g = Hq / Hkv;
