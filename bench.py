@@ -85,16 +85,14 @@ def parse():
 
 # the sources each traffic record depends on (a change to any of them makes
 # the record stale)
+DECODE_SOURCES = ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_rows.h", "decode_util.h",
+                  "kernels_misc.hip", "api.hip", "common.h"]
 KERNEL_SOURCES = {
     "extend_bf16_kernel": ["kernels_extend.hip", "common.h"],
-    "cascade_decode_call": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
-                            "kernels_misc.hip", "api.hip", "common.h"],
-    "cascade_decode_call_fp8": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
-                                "kernels_misc.hip", "api.hip", "common.h"],
-    "flat_decode_call": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
-                         "kernels_misc.hip", "api.hip", "common.h"],
-    "flat_decode_call_fp8": ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_util.h",
-                             "kernels_misc.hip", "api.hip", "common.h"],
+    "cascade_decode_call": DECODE_SOURCES,
+    "cascade_decode_call_fp8": DECODE_SOURCES,
+    "flat_decode_call": DECODE_SOURCES,
+    "flat_decode_call_fp8": DECODE_SOURCES,
 }
 
 
