@@ -269,3 +269,19 @@ def f32_rel_err(got, want):
     num = np.max(np.abs(got.astype(np.float64) - want), axis=-1)
     den = np.max(np.abs(want), axis=-1)
     return float(np.max(num / np.maximum(den, 1e-30)))
+
+
+def late_rounds_workload(seed, Hq=32, Hkv=8, D=128):
+    """One group with a 4000-token prefix and short suffixes beside groups
+    with short prefixes and suffixes of up to 4080 keys: max_seq_len -
+    max_prefix_len is 96, so the one-grid cascade puts only the first few
+    suffix split rounds before the prefix items, and the long suffixes' later
+    splits run in the rounds dispatched after them."""
+    spec = W.Spec("late_rounds", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed)
+    members = [3, 2, 1, 4]
+    prefixes = [4000, 16, 0, 2000]
+    grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
+    sib = np.concatenate([np.arange(m) for m in members]).astype(np.int64)
+    L = np.array([4001, 4050, 4096, 4096, 3000, 2500, 2001, 2600, 4000, 4096], np.int64)
+    assert len(L) == len(grp)
+    return W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, sib, L)

@@ -14,7 +14,7 @@ import torch
 import oracle.fp8 as F8
 import workloads as W
 from prefix_shared_paged_amd import store_kv_fp8
-from scenarios import GroupCase, bf16_err, oracle_decode, run_decode
+from scenarios import GroupCase, bf16_err, late_rounds_workload, oracle_decode, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -110,6 +110,21 @@ def test_decode_fp8_small_flat_and_cascade(Hq, Hkv, D, q_scale=1.0):
         err = bf16_err(o[reqs], O)
         lerr = float(np.max(np.abs(l[reqs] - LSE)))
         _print(f"decode fp8 small {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+        assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+def test_cascade_fp8_late_suffix_rounds():
+    # the workload of test_cascade_late_suffix_rounds over an FP8 cache
+    wl = late_rounds_workload(31)
+    case = GroupCase(wl, fp8=True)
+    res = run_decode(case, wl.ctx_len.copy(), cascade=False, both=True)
+    case.check_r2t()
+    _check_pools(case, res, range(wl.B))
+    reqs, O, LSE = oracle_decode(case, res)
+    for tag, o, l in (("flat", res["o"], res["lse"]), ("cascade", res["o_c"], res["lse_c"])):
+        err = bf16_err(o[reqs], O)
+        lerr = float(np.max(np.abs(l[reqs] - LSE)))
+        _print(f"decode fp8 late suffix rounds {tag}: max abs err {err:.3e}, lse err {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= LSE_TOL
 
 

@@ -12,8 +12,8 @@ import torch
 import oracle
 import workloads as W
 from prefix_shared_paged_amd import decode_attn, extend_attn
-from scenarios import (GroupCase, bf16_err, dev, dev_i, f32_rel_err, oracle_decode,
-                       oracle_extend, run_decode, run_extend)
+from scenarios import (GroupCase, bf16_err, dev, dev_i, f32_rel_err, late_rounds_workload,
+                       oracle_decode, oracle_extend, run_decode, run_extend)
 
 pytestmark = pytest.mark.gpu
 
@@ -404,6 +404,19 @@ def test_decode_split_and_group_edges(Hq, Hkv, D):
         err = bf16_err(o[reqs], O)
         lerr = float(np.max(np.abs(l[reqs] - LSE)))
         _print(f"decode split edges {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+        assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+def test_cascade_late_suffix_rounds():
+    wl = late_rounds_workload(29)
+    case = GroupCase(wl)
+    res = run_decode(case, wl.ctx_len.copy(), cascade=False, both=True)
+    case.check_r2t()
+    reqs, O, LSE = oracle_decode(case, res)
+    for tag, o, l in (("flat", res["o"], res["lse"]), ("cascade", res["o_c"], res["lse_c"])):
+        err = bf16_err(o[reqs], O)
+        lerr = float(np.max(np.abs(l[reqs] - LSE)))
+        _print(f"decode late suffix rounds {tag}: max abs err {err:.3e}, lse err {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
