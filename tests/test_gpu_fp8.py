@@ -98,7 +98,8 @@ def _small_decode_workload(seed, Hq, Hkv, D, q_scale=1.0):
     return W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, sib, L)
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64), (16, 4, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64), (16, 4, 64), (16, 4, 128),
+                                     (32, 16, 128)])
 def test_decode_fp8_small_flat_and_cascade(Hq, Hkv, D, q_scale=1.0):
     wl = _small_decode_workload(21, Hq, Hkv, D, q_scale)
     case = GroupCase(wl, fp8=True)

@@ -346,10 +346,11 @@ def _small_decode_workload(seed, Hq=32, Hkv=8, D=128, q_scale=1.0):
 
 
 @pytest.mark.parametrize("cascade", [False, True])
-@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 128), (8, 8, 64), (16, 4, 128), (32, 16, 128)])
 def test_decode_small(cascade, Hq, Hkv, D):
     # the 16-member group gives 16 * Hq/Hkv query rows per KV head: 128 rows
-    # (two 64-row waves) for Hq/Hkv = 8
+    # (two 64-row waves) for Hq/Hkv = 8; 4 and 16 KV heads at D 128 put one
+    # and four groups of 4 KV heads in the cascade's whole-row suffix items
     wl = _small_decode_workload(7, Hq, Hkv, D)
     case = GroupCase(wl)
     res = run_decode(case, wl.ctx_len.copy(), cascade)
