@@ -86,7 +86,7 @@ def parse():
 # the sources each traffic record depends on (a change to any of them makes
 # the record stale)
 DECODE_SOURCES = ["kernels_decode.hip", "kernels_decode_rows.hip", "decode_rows.h", "decode_util.h",
-                  "kernels_misc.hip", "api.hip", "common.h"]
+                  "store_util.h", "kernels_misc.hip", "api.hip", "common.h"]
 KERNEL_SOURCES = {
     "extend_bf16_kernel": ["kernels_extend.hip", "common.h"],
     "cascade_decode_call": DECODE_SOURCES,

@@ -304,7 +304,12 @@ size_t sgl_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t Hq,
  * Precondition: within a group all req_to_token rows hold the same slots in
  * columns [0, group_prefix_len[g]) (the prefix slots are read from the row
  * of the group's first request) and group_prefix_len[g] <= seq_lens[r] for
- * its requests.  max_group_size, max_prefix_len: host bounds (grid sizing);
+ * its requests; when the call stores the current token (k_new given), the
+ * prefix ends before it: group_prefix_len[g] < seq_lens[r], and the slot of
+ * position seq_lens[r]-1 is none of the group's prefix slots (the store may
+ * run while the prefix is being read).  Validation mode returns
+ * SGL_ERR_INVALID for a call that breaks either.
+ * max_group_size, max_prefix_len: host bounds (grid sizing);
  * max_group_size * (Hq / Hkv) <= 4096.  Up to 64 query rows of a group
  * (request x query head) share one read of the prefix; larger groups read it
  * once per 64 rows.

@@ -450,10 +450,19 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
                 if (b <= a || b - a > max_group_size) return SGL_ERR_INVALID;
                 if (gpl[gg] < 0 || gpl[gg] > max_prefix_len) return SGL_ERR_INVALID;
                 for (int r = a; r < b; r++) {
-                    if (gpl[gg] > lens[r]) return SGL_ERR_INVALID;
+                    if (gpl[gg] > lens[r] || (k_new && gpl[gg] >= lens[r])) return SGL_ERR_INVALID;
                     if (std::memcmp(&tab[(size_t)rows[r] * row_stride], &tab[(size_t)rows[a] * row_stride],
                                     sizeof(int32_t) * (size_t)gpl[gg]) != 0)
                         return SGL_ERR_INVALID;
+                }
+                if (k_new && gpl[gg] > 0) {   // the stored tokens' slots lie outside the prefix
+                    const int32_t *pre = &tab[(size_t)rows[a] * row_stride];
+                    std::vector<int32_t> sorted(pre, pre + gpl[gg]);
+                    std::sort(sorted.begin(), sorted.end());
+                    for (int r = a; r < b; r++)
+                        if (std::binary_search(sorted.begin(), sorted.end(),
+                                               tab[(size_t)rows[r] * row_stride + lens[r] - 1]))
+                            return SGL_ERR_INVALID;
                 }
             }
         }
@@ -472,14 +481,34 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
         suf_part = carve(wp, batch, Ss, Hq, D);
         suffix_lo = (int32_t *)wp;
     }
+    // Both cascade stages in one grid when the shape allows it (D 128, KV
+    // heads in groups of 4) and the suffix items are the longer ones: a
+    // suffix item walks fchunk / 16 tiles one at a time, a prefix item
+    // pchunk / 16 tiles with three in flight, so that is 3 fchunk > pchunk.
+    // The suffix rounds that suffixes of about max_seq_len - max_prefix_len
+    // keys need (twice that, for groups with shorter prefixes) go first, the
+    // prefix items fill the compute units as they run out, and the rest of
+    // the Ss rounds (mostly empty) go last.  Measured: the 256-request decode
+    // workload takes 651 us this way against 666 us in two launches; on the
+    // 8-branch fork (prefix items longer) one grid with the prefix items
+    // first loses to two launches as the suffixes grow (139 against 129 us at
+    // 512 keys), so such calls keep one launch per stage.
+    const bool one_grid = cascade && max_prefix_len > 0 && rows_suffix && D == 128 && Hkv % 4 == 0 &&
+                          3 * fchunk > pchunk;
     // The current token's K/V, and (cascade) each request's suffix start,
-    // found once for every suffix item and the merge: one kernel when there
-    // is a token to store.
+    // found once for every suffix item and the merge.  A bf16-query cascade
+    // call in two launches hands both to the leading workgroups of its
+    // prefix-stage launch (the prefix items never read a current token:
+    // every group prefix ends before its requests' current positions);
+    // otherwise they take a kernel of their own before the attention.
     SuffixStartArgs ss;
     ss.group_ptr = group_ptr; ss.group_prefix_len = group_prefix_len; ss.seq_lens = seq_lens;
     ss.G = G; ss.batch = batch; ss.lo = suffix_lo;
+    const bool carry_store = cascade && max_prefix_len > 0 && !one_grid && dtype == SGL_BF16;
     int rc = SGL_OK;
-    if (k_new) {
+    if (carry_store) {
+        // launched with the prefix stage below
+    } else if (k_new) {
         const SuffixStartArgs *ssp = cascade ? &ss : nullptr;
         rc = fp8 ? launch_store_kv_fp8(2, elt_size(dtype), k_new, v_new, batch, nullptr, k_pool, v_pool,
                                        num_slots, Hkv, D, k_scale, v_scale, r2t, num_rows, row_stride,
@@ -532,19 +561,9 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     sa.suffix_lo = suffix_lo;
     m.suffix_lo = suffix_lo;
 
-    // Both stages in one grid when the shape allows it (D 128, KV heads in
-    // groups of 4) and the suffix items are the longer ones: a suffix item
-    // walks fchunk / 16 tiles one at a time, a prefix item pchunk / 16 tiles
-    // with three in flight, so that is 3 fchunk > pchunk.  The suffix rounds
-    // that suffixes of about max_seq_len - max_prefix_len keys need (twice
-    // that, for groups with shorter prefixes) go first, the prefix items
-    // fill the compute units as they run out, and the rest of the Ss rounds
-    // (mostly empty) go last.  Measured: the 256-request decode workload
-    // takes 651 us this way against 666 us in two launches; on the 8-branch
-    // fork (prefix items longer) one grid with the prefix items first loses
-    // to two launches as the suffixes grow (139 against 129 us at 512 keys),
-    // so such calls keep one launch per stage.
-    const bool one_grid = max_prefix_len > 0 && rows_suffix && D == 128 && Hkv % 4 == 0 && 3 * fchunk > pchunk;
+    if (carry_store)
+        pa.store = decode_store_args(elt_size(dtype), fp8, k_new, v_new, batch, k_pool, v_pool, num_slots, Hkv, D,
+                                     k_scale, v_scale, r2t, num_rows, row_stride, req_rows, seq_lens, &ss);
     if (one_grid) {
         SplitArgs sx = sa;
         sx.xcd_block = 1;

@@ -93,6 +93,39 @@ struct SuffixStartArgs {
 };
 int launch_suffix_start(const SuffixStartArgs &a, hipStream_t st);
 
+// The decode store as a job for the workgroups of some launch: token i of
+// n_tokens (row i of k_new / v_new) goes to the slot at position lens[i] - 1
+// of table row req_rows[i]; with fp8 set the rows are quantised to e4m3fn
+// codes from elt-byte inputs with the per-KV-head factors.  ss.lo, when set,
+// also receives the suffix starts.  n_wg: workgroups the carrying launch gives
+// the job (decode_store_wgs).
+struct DecodeStoreArgs {
+    const char *k_new, *v_new;
+    uint4 *k_pool, *v_pool;
+    int64_t num_slots;
+    int32_t row_chunks;     // 16-byte chunks of a pool row
+    int32_t head_chunks;    // fp8: 16-byte chunks of one head's codes
+    const float *k_scale, *v_scale;
+    const int32_t *r2t;
+    int64_t num_rows, stride;
+    const int32_t *req_rows, *lens;
+    int64_t n_tokens;
+    int32_t elt;            // input bytes per element (2 bf16, 4 fp32)
+    int32_t fp8;
+    int32_t n_wg;
+    SuffixStartArgs ss;
+};
+DecodeStoreArgs decode_store_args(int elt, bool fp8, const void *k_new, const void *v_new, int64_t n_tokens,
+                                  void *k_pool, void *v_pool, int64_t num_slots, int32_t Hkv, int32_t D,
+                                  const float *k_scale, const float *v_scale, const int32_t *r2t,
+                                  int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                                  const int32_t *lens, const SuffixStartArgs *ss);
+// Workgroups of `threads` threads for the job: about four chunks per thread,
+// at most 256, a multiple of 8 (so workgroups numbered after them in the
+// same grid keep the XCD they would have without them); 0 for no tokens and
+// no suffix starts.
+int32_t decode_store_wgs(const DecodeStoreArgs &d, int threads);
+
 // mode 0: slots[i];  mode 1: extend (r2t at prefix_lens[r] + i);  mode 2: decode (r2t at seq_lens[r]-1).
 // Mode 2 also writes the suffix starts of *ss when ss is not null (one launch for both).
 int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
@@ -163,6 +196,8 @@ struct SplitArgs {
     const int32_t *suffix_lo;      // kind 2, optional: first suffix key of each request
                                    // (launch_suffix_start); else found from the group arrays
     PartialBuf part;
+    DecodeStoreArgs store;         // kind 1 (launch_split_bf16 / _fp8), optional: a decode
+                                   // store run by leading workgroups of the launch
 };
 
 // Keys per split of a small-q extend request with L keys cut into n_spl

@@ -39,6 +39,7 @@
 #include "common.h"
 #include "decode_rows.h"
 #include "decode_util.h"
+#include "store_util.h"
 
 namespace {
 
@@ -629,12 +630,24 @@ __device__ __forceinline__ void fp8_split(const SplitArgs &a, unsigned id, unsig
     if (kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
 }
 
+// a.store.n_wg > 0 (a cascade prefix stage): the first a.store.n_wg
+// workgroups run the decode store of the call's current tokens and the
+// suffix starts instead (the prefix items read positions below every
+// request's group prefix length, which stays below its current token's
+// position, and the suffix stage and the merge that read the token and the
+// starts are later launches); the split items follow, numbered from 0, and
+// n_wg is a multiple of 8, so each keeps its XCD.
 template <int D, int DEPTH, int WPG>
 __global__ void __launch_bounds__(64 * WPG) split_bf16_kernel(SplitArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TILE * 2 * D];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TILE * 2 * D];
     extern __shared__ int32_t slot_lds[];  // [min(chunk, kSlotTab)]
-    bf16_split<D, DEPTH, WPG>(a, blockIdx.x, k_lds, v_lds, slot_lds);
+    const unsigned nst = (unsigned)a.store.n_wg;
+    if (blockIdx.x < nst) {
+        decode_store_job<2, false>(a.store, blockIdx.x, nst);
+        return;
+    }
+    bf16_split<D, DEPTH, WPG>(a, blockIdx.x - nst, k_lds, v_lds, slot_lds);
 }
 
 template <int D, int DEPTH, int WPG>
@@ -642,7 +655,12 @@ __global__ void __launch_bounds__(64 * WPG) split_fp8_kernel(SplitArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[DEPTH * TILE8 * D];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds[DEPTH * TILE8 * D];
     extern __shared__ int32_t slot_lds[];  // [chunk]
-    fp8_split<D, DEPTH, WPG>(a, blockIdx.x, k_lds, v_lds, slot_lds);
+    const unsigned nst = (unsigned)a.store.n_wg;
+    if (blockIdx.x < nst) {                  // bf16 inputs (the launcher checks)
+        decode_store_job<2, true>(a.store, blockIdx.x, nst);
+        return;
+    }
+    fp8_split<D, DEPTH, WPG>(a, blockIdx.x - nst, k_lds, v_lds, slot_lds);
 }
 
 // ---- cascade: prefix and suffix stages in one grid ----------------------------
@@ -715,8 +733,21 @@ int launch_cascade_split(const SplitArgs &pa0, const SplitArgs &sa, int32_t head
     return hip_status(hipGetLastError());
 }
 
+// The decode store carried by a prefix-stage launch: its workgroup count for
+// `threads`-thread workgroups (0 when there is none); rejects a store the
+// kernels do not carry.
+static int carried_store(SplitArgs &a, bool fp8, int threads) {
+    const bool any = a.store.n_tokens > 0 || a.store.ss.lo;
+    a.store.n_wg = 0;
+    if (!any) return SGL_OK;
+    if (a.kind != 1 || a.store.fp8 != (fp8 ? 1 : 0) || (fp8 && a.store.elt != 2)) return SGL_ERR_INVALID;
+    if (fp8 && a.store.n_tokens > 0 && (!a.store.k_scale || !a.store.v_scale)) return SGL_ERR_INVALID;
+    a.store.n_wg = decode_store_wgs(a.store, threads);
+    return SGL_OK;
+}
+
 int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
-    if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
+    if ((a0.n_sets == 0 || a0.max_splits == 0) && a0.store.n_tokens == 0 && !a0.store.ss.lo) return SGL_OK;
     if (a0.chunk % TILE != 0) return SGL_ERR_INVALID;
     SplitArgs a = a0;
     const bool multi = a.kind == 1 || a.kind == 4;   // several query rows per (set, KV head)
@@ -732,7 +763,9 @@ int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
     if (a.D == 64 && wpg > 2) wpg = 2;               // 2 load instructions per 64-dim tile
     const int n_rbg = (a.row_blocks + wpg - 1) / wpg;
     const int64_t items = (int64_t)a.n_sets * a.max_splits * a.Hkv;
-    const int64_t n_wg = ceil_div64(items, 8) * 8 * n_rbg;
+    int rc = carried_store(a, false, 64 * wpg);
+    if (rc != SGL_OK) return rc;
+    const int64_t n_wg = ceil_div64(items, 8) * 8 * n_rbg + a.store.n_wg;
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const size_t dyn = (size_t)(a.kind == 4 ? kSlotTab : min(a.chunk, kSlotTab)) * sizeof(int32_t);
     const dim3 grid((unsigned)n_wg), block(64 * wpg);
@@ -751,7 +784,7 @@ int launch_split_bf16(const SplitArgs &a0, hipStream_t st) {
 
 int launch_split_fp8(const SplitArgs &a0, hipStream_t st) {
     if (a0.kind == 4) return SGL_ERR_UNSUPPORTED;   // small-q extend runs on bf16 caches only
-    if (a0.n_sets == 0 || a0.max_splits == 0) return SGL_OK;
+    if ((a0.n_sets == 0 || a0.max_splits == 0) && a0.store.n_tokens == 0 && !a0.store.ss.lo) return SGL_OK;
     if (a0.chunk % TILE8 != 0 || !a0.k_scale || !a0.v_scale) return SGL_ERR_INVALID;
     SplitArgs a = a0;
     const int rows = (a.kind == 1 ? a.max_members : 1) * (a.Hq / a.Hkv);
@@ -762,7 +795,9 @@ int launch_split_fp8(const SplitArgs &a0, hipStream_t st) {
     if (a.D == 64 && wpg > 2) wpg = 2;               // 2 load instructions per 64-dim tile
     const int n_rbg = (a.row_blocks + wpg - 1) / wpg;
     const int64_t items = (int64_t)a.n_sets * a.max_splits * a.Hkv;
-    const int64_t n_wg = ceil_div64(items, 8) * 8 * n_rbg;
+    int rc = carried_store(a, true, 64 * wpg);
+    if (rc != SGL_OK) return rc;
+    const int64_t n_wg = ceil_div64(items, 8) * 8 * n_rbg + a.store.n_wg;
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
     const dim3 grid((unsigned)n_wg), block(64 * wpg);

@@ -1,9 +1,8 @@
 // kernels_misc.hip -- req_to_token build, KV store, and the log-sum-exp merge
 // of partial softmax states.
-#include <climits>
 #include <cstring>
 
-#include "common.h"
+#include "store_util.h"
 
 // ---------------------------------------------------------------------------
 // req_to_token build: one workgroup per request, columns strided over threads.
@@ -50,38 +49,14 @@ int launch_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride
 // ---------------------------------------------------------------------------
 // KV store: copy token rows (Hkv * D elements = row_chunks * 16 bytes) of K and
 // V into the pools at their slots ("SGLang 深度解读" module 5: write the
-// current K, V at cache_loc before attending).
+// current K, V at cache_loc before attending).  Modes 0 (given slots) and 1
+// (extend: the slots of positions prefix_lens[r] + i) here; mode 2 (decode)
+// is decode_store_job (store_util.h), which a cascade call may instead hand
+// to the leading workgroups of its prefix-stage launch.
 // ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
-// Suffix start of every request of a cascade call, computed once so that the
-// suffix split items and the merge read one value instead of searching the
-// group table themselves (a chain of dependent loads in every one of them,
-// including the split items past a request's last split).  Thread t of the
-// grid takes requests t, t + grid size, ...; the 64 lanes of a wave load 64
-// group_ptr entries at a time and every lane counts those <= its request
-// (readlane broadcasts), so group(r) = count - 1 for ascending group_ptr;
-// any contents give a group in [0, G).  Every thread of the grid must run
-// it (whole waves take part in the search).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void suffix_starts(const SuffixStartArgs &a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t step = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t r0 = (int64_t)blockIdx.x * blockDim.x; r0 < a.batch; r0 += step) {   // uniform per workgroup
-        const int64_t r = r0 + threadIdx.x;
-        int cnt = 0;
-        for (int base = 0; base < a.G; base += 64) {
-            const int gp = base + lane < a.G ? a.group_ptr[base + lane] : INT_MAX;
-            const int n = a.G - base < 64 ? a.G - base : 64;
-            for (int j = 0; j < n; j++) cnt += __builtin_amdgcn_readlane(gp, j) <= r ? 1 : 0;
-        }
-        if (r < a.batch) {
-            const int64_t P = a.group_prefix_len[cnt > 0 ? cnt - 1 : 0], L = a.seq_lens[r];
-            a.lo[r] = (int32_t)(P < 0 ? 0 : (P > L ? L : P));
-        }
-    }
+__global__ void __launch_bounds__(256) suffix_start_kernel(SuffixStartArgs a) {
+    suffix_starts(a, blockIdx.x, gridDim.x);
 }
-
-__global__ void __launch_bounds__(256) suffix_start_kernel(SuffixStartArgs a) { suffix_starts(a); }
 
 int launch_suffix_start(const SuffixStartArgs &a, hipStream_t st) {
     if (a.batch <= 0) return SGL_OK;
@@ -96,8 +71,7 @@ __global__ void __launch_bounds__(256) store_kv_kernel(
     uint4 *__restrict__ v_pool, int64_t num_slots, int32_t row_chunks, int64_t n_tokens,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ r2t, int64_t num_rows,
     int64_t stride, const int32_t *__restrict__ req_rows, const int32_t *__restrict__ lens,
-    const int64_t *__restrict__ q_off, SuffixStartArgs ss) {
-    if (MODE == 2 && ss.lo) suffix_starts(ss);
+    const int64_t *__restrict__ q_off) {
     if (MODE == 1) {
         // extend: blockIdx.y = request; tokens q_off[r] .. q_off[r+1]
         const int r = blockIdx.y;
@@ -121,15 +95,7 @@ __global__ void __launch_bounds__(256) store_kv_kernel(
         for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
              idx += (int64_t)gridDim.x * blockDim.x) {
             const int64_t i = idx / row_chunks, c = idx % row_chunks;
-            int32_t s;
-            if (MODE == 0) {
-                s = slots[i];
-            } else {  // decode: token i of request i at position seq_lens[i] - 1
-                const int64_t row = req_rows[i];
-                const int64_t col = (int64_t)lens[i] - 1;
-                if (row < 0 || row >= num_rows || col < 0 || col >= stride) continue;
-                s = r2t[row * stride + col];
-            }
+            const int32_t s = slots[i];
             if (s < 0 || s >= num_slots) continue;
             k_pool[(int64_t)s * row_chunks + c] = k_new[i * row_chunks + c];
             v_pool[(int64_t)s * row_chunks + c] = v_new[i * row_chunks + c];
@@ -137,17 +103,64 @@ __global__ void __launch_bounds__(256) store_kv_kernel(
     }
 }
 
+template <int ELT, bool FP8>
+__global__ void __launch_bounds__(256) decode_store_kernel(DecodeStoreArgs d) {
+    decode_store_job<ELT, FP8>(d, blockIdx.x, gridDim.x);
+}
+
+DecodeStoreArgs decode_store_args(int elt, bool fp8, const void *k_new, const void *v_new, int64_t n_tokens,
+                                  void *k_pool, void *v_pool, int64_t num_slots, int32_t Hkv, int32_t D,
+                                  const float *k_scale, const float *v_scale, const int32_t *r2t,
+                                  int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                                  const int32_t *lens, const SuffixStartArgs *ss) {
+    DecodeStoreArgs d;
+    std::memset(&d, 0, sizeof d);
+    d.k_new = (const char *)k_new; d.v_new = (const char *)v_new;
+    d.k_pool = (uint4 *)k_pool; d.v_pool = (uint4 *)v_pool;
+    d.num_slots = num_slots;
+    d.row_chunks = fp8 ? Hkv * D / 16 : (int32_t)((int64_t)Hkv * D * elt / 16);
+    d.head_chunks = D / 16;
+    d.k_scale = k_scale; d.v_scale = v_scale;
+    d.r2t = r2t; d.num_rows = num_rows; d.stride = row_stride;
+    d.req_rows = req_rows; d.lens = lens;
+    d.n_tokens = k_new ? n_tokens : 0;
+    d.elt = elt; d.fp8 = fp8 ? 1 : 0;
+    if (ss) d.ss = *ss;
+    return d;
+}
+
+int32_t decode_store_wgs(const DecodeStoreArgs &d, int threads) {
+    const int64_t chunks = d.n_tokens * d.row_chunks;
+    const int64_t starts = d.ss.lo ? d.ss.batch : 0;
+    if (chunks <= 0 && starts <= 0) return 0;
+    int64_t n = std::max(ceil_div64(chunks, 4 * (int64_t)threads), ceil_div64(starts, threads));
+    n = std::min<int64_t>(std::max<int64_t>(n, 1), 256);
+    return (int32_t)ceil_div64(n, 8) * 8;
+}
+
+// the decode store (and suffix starts) in a launch of its own
+static int launch_decode_store(const DecodeStoreArgs &d, hipStream_t st) {
+    if (d.n_tokens == 0) return SGL_OK;
+    if (d.fp8 && (!d.k_scale || !d.v_scale)) return SGL_ERR_INVALID;
+    const dim3 grid((unsigned)std::min<int64_t>(ceil_div64(d.n_tokens * d.row_chunks, 256), 8192));
+    if (!d.fp8) hipLaunchKernelGGL((decode_store_kernel<2, false>), grid, dim3(256), 0, st, d);
+    else if (d.elt == 2) hipLaunchKernelGGL((decode_store_kernel<2, true>), grid, dim3(256), 0, st, d);
+    else hipLaunchKernelGGL((decode_store_kernel<4, true>), grid, dim3(256), 0, st, d);
+    return hip_status(hipGetLastError());
+}
+
 int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int64_t n_tokens,
                     const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
                     int32_t Hkv, int32_t D, const int32_t *r2t, int64_t num_rows, int64_t row_stride,
                     const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
                     int32_t batch, int32_t max_extend_len, hipStream_t st, const SuffixStartArgs *ss) {
-    const int64_t row_bytes = (int64_t)Hkv * D * elt;
-    SuffixStartArgs sx;
-    std::memset(&sx, 0, sizeof sx);
-    if (ss && mode == 2) sx = *ss;
-    const int32_t row_chunks = (int32_t)(row_bytes / 16);
     if (n_tokens == 0) return SGL_OK;
+    if (mode == 2)
+        return launch_decode_store(decode_store_args(elt, false, k_new, v_new, n_tokens, k_pool, v_pool, num_slots,
+                                                     Hkv, D, nullptr, nullptr, r2t, num_rows, row_stride,
+                                                     req_rows, lens, ss),
+                                   st);
+    const int32_t row_chunks = (int32_t)((int64_t)Hkv * D * elt / 16);
     const uint4 *kn = (const uint4 *)k_new;
     const uint4 *vn = (const uint4 *)v_new;
     uint4 *kp = (uint4 *)k_pool;
@@ -158,62 +171,21 @@ int launch_store_kv(int mode, int elt, const void *k_new, const void *v_new, int
         if (gx < 1) gx = 1;
         hipLaunchKernelGGL(store_kv_kernel<1>, dim3(gx, batch), dim3(256), 0, st, kn, vn, kp, vp,
                            num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
-                           req_rows, lens, q_off, sx);
+                           req_rows, lens, q_off);
     } else {
         int gx = (int)std::min<int64_t>(ceil_div64(n_tokens * row_chunks, 256), 8192);
-        if (mode == 0)
-            hipLaunchKernelGGL(store_kv_kernel<0>, dim3(gx), dim3(256), 0, st, kn, vn, kp, vp,
-                               num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
-                               req_rows, lens, q_off, sx);
-        else
-            hipLaunchKernelGGL(store_kv_kernel<2>, dim3(gx), dim3(256), 0, st, kn, vn, kp, vp,
-                               num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
-                               req_rows, lens, q_off, sx);
+        hipLaunchKernelGGL(store_kv_kernel<0>, dim3(gx), dim3(256), 0, st, kn, vn, kp, vp,
+                           num_slots, row_chunks, n_tokens, slots, r2t, num_rows, row_stride,
+                           req_rows, lens, q_off);
     }
     return hip_status(hipGetLastError());
 }
 
 // ---------------------------------------------------------------------------
 // FP8 KV store: the same rows as store_kv_kernel, quantised to e4m3fn codes on
-// the way ("SGLang 深度拆解" section 4.3 keeps the KV cache in FP8 to halve
-// it).  For head kv: y = x / scale[kv] (fp32, IEEE division), clamped to
-// [-448, 448], rounded to the nearest e4m3fn value with ties to even
-// (v_cvt_pk_fp8_f32).  One thread writes one 16-byte chunk of codes.
+// the way by quant16 (store_util.h).  One thread writes one 16-byte chunk of
+// codes.
 // ---------------------------------------------------------------------------
-template <int ELT>
-__device__ __forceinline__ uint4 quant16(const char *src, float sc) {
-    float x[16];
-    if (ELT == 2) {
-        const uint4 a = ((const uint4 *)src)[0], b = ((const uint4 *)src)[1];
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float4 f = ((const float4 *)src)[i];
-            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
-        }
-    }
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        float y[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float v = x[4 * i + j] / sc;
-            y[j] = v > 448.f ? 448.f : (v < -448.f ? -448.f : v);   // NaN stays NaN
-        }
-        int t = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        t = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], t, true);
-        w[i] = (uint32_t)t;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 template <int MODE, int ELT>
 __global__ void __launch_bounds__(256) store_kv_fp8_kernel(
     const char *__restrict__ k_new, const char *__restrict__ v_new, uint4 *__restrict__ k_pool,
@@ -221,8 +193,7 @@ __global__ void __launch_bounds__(256) store_kv_fp8_kernel(
     const float *__restrict__ k_scale, const float *__restrict__ v_scale, int64_t n_tokens,
     const int32_t *__restrict__ slots, const int32_t *__restrict__ r2t, int64_t num_rows,
     int64_t stride, const int32_t *__restrict__ req_rows, const int32_t *__restrict__ lens,
-    const int64_t *__restrict__ q_off, SuffixStartArgs ss) {
-    if (MODE == 2 && ss.lo) suffix_starts(ss);
+    const int64_t *__restrict__ q_off) {
     constexpr int IN_CHUNK = 16 * ELT;   // input bytes per 16 codes
     int64_t t0 = 0, n = n_tokens * row_chunks, row = 0, P = 0;
     if (MODE == 1) {
@@ -240,15 +211,10 @@ __global__ void __launch_bounds__(256) store_kv_fp8_kernel(
         int32_t s;
         if (MODE == 0) {
             s = slots[i];
-        } else if (MODE == 1) {
+        } else {
             const int64_t col = P + i;
             if (col >= stride) continue;
             s = r2t[row * stride + col];
-        } else {
-            const int64_t rw = req_rows[i];
-            const int64_t col = (int64_t)lens[i] - 1;
-            if (rw < 0 || rw >= num_rows || col < 0 || col >= stride) continue;
-            s = r2t[rw * stride + col];
         }
         if (s < 0 || s >= num_slots) continue;
         const int h = (int)(c / head_chunks);
@@ -265,10 +231,12 @@ int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new,
                         const int32_t *req_rows, const int32_t *lens, const int64_t *q_off,
                         int32_t batch, int32_t max_extend_len, hipStream_t st, const SuffixStartArgs *ss) {
     if (n_tokens == 0) return SGL_OK;
+    if (mode == 2)
+        return launch_decode_store(decode_store_args(elt, true, k_new, v_new, n_tokens, k_pool, v_pool, num_slots,
+                                                     Hkv, D, k_scale, v_scale, r2t, num_rows, row_stride,
+                                                     req_rows, lens, ss),
+                                   st);
     const int32_t row_chunks = Hkv * D / 16, head_chunks = D / 16;
-    SuffixStartArgs sx;
-    std::memset(&sx, 0, sizeof sx);
-    if (ss && mode == 2) sx = *ss;
     const char *kn = (const char *)k_new;
     const char *vn = (const char *)v_new;
     uint4 *kp = (uint4 *)k_pool;
@@ -284,11 +252,11 @@ int launch_store_kv_fp8(int mode, int elt, const void *k_new, const void *v_new,
 #define SGL_STORE8(M, E)                                                                                    \
     hipLaunchKernelGGL((store_kv_fp8_kernel<M, E>), grid, dim3(256), 0, st, kn, vn, kp, vp, num_slots,     \
                        row_chunks, head_chunks, k_scale, v_scale, n_tokens, slots, r2t, num_rows,          \
-                       row_stride, req_rows, lens, q_off, sx)
+                       row_stride, req_rows, lens, q_off)
     if (elt == 2) {
-        if (mode == 0) SGL_STORE8(0, 2); else if (mode == 1) SGL_STORE8(1, 2); else SGL_STORE8(2, 2);
+        if (mode == 0) SGL_STORE8(0, 2); else SGL_STORE8(1, 2);
     } else {
-        if (mode == 0) SGL_STORE8(0, 4); else if (mode == 1) SGL_STORE8(1, 4); else SGL_STORE8(2, 4);
+        if (mode == 0) SGL_STORE8(0, 4); else SGL_STORE8(1, 4);
     }
 #undef SGL_STORE8
     return hip_status(hipGetLastError());

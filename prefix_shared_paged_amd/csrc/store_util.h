@@ -1,0 +1,112 @@
+// store_util.h -- device side of the decode store (the current token's K/V
+// into the pool, "SGLang 深度解读" module 5: the current K, V are written at
+// their cache location before attending) and of the cascade's suffix starts,
+// as jobs that any workgroups can run: the store's own launch, or the
+// leading workgroups of the cascade's prefix-stage launch.
+#pragma once
+
+#include <climits>
+
+#include "common.h"
+
+// ---------------------------------------------------------------------------
+// Suffix start of every request of a cascade call, computed once so that the
+// suffix split items and the merge read one value instead of searching the
+// group table themselves (a chain of dependent loads in every one of them,
+// including the split items past a request's last split).  Workgroup wg of
+// the n_wg that run the job takes requests wg * blockDim + t, then steps by
+// n_wg * blockDim; the 64 lanes of a wave load 64 group_ptr entries at a time
+// and every lane counts those <= its request (readlane broadcasts), so
+// group(r) = count - 1 for ascending group_ptr; any contents give a group in
+// [0, G).  Every thread of those workgroups must run it (whole waves take
+// part in the search).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void suffix_starts(const SuffixStartArgs &a, unsigned wg, unsigned n_wg) {
+    const int lane = threadIdx.x & 63;
+    const int64_t step = (int64_t)n_wg * blockDim.x;
+    for (int64_t r0 = (int64_t)wg * blockDim.x; r0 < a.batch; r0 += step) {   // uniform per workgroup
+        const int64_t r = r0 + threadIdx.x;
+        int cnt = 0;
+        for (int base = 0; base < a.G; base += 64) {
+            const int gp = base + lane < a.G ? a.group_ptr[base + lane] : INT_MAX;
+            const int n = a.G - base < 64 ? a.G - base : 64;
+            for (int j = 0; j < n; j++) cnt += __builtin_amdgcn_readlane(gp, j) <= r ? 1 : 0;
+        }
+        if (r < a.batch) {
+            const int64_t P = a.group_prefix_len[cnt > 0 ? cnt - 1 : 0], L = a.seq_lens[r];
+            a.lo[r] = (int32_t)(P < 0 ? 0 : (P > L ? L : P));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 codes of 16 inputs (ELT bytes each: 2 = bf16, 4 = fp32) with the factor
+// sc of their KV head ("SGLang 深度拆解" section 4.3 keeps the KV cache in FP8):
+// y = x / sc (fp32, IEEE division), clamped to [-448, 448], rounded to the
+// nearest e4m3fn value with ties to even (v_cvt_pk_fp8_f32).
+// ---------------------------------------------------------------------------
+template <int ELT>
+__device__ __forceinline__ uint4 quant16(const char *src, float sc) {
+    float x[16];
+    if (ELT == 2) {
+        const uint4 a = ((const uint4 *)src)[0], b = ((const uint4 *)src)[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 f = ((const float4 *)src)[i];
+            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+        }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float v = x[4 * i + j] / sc;
+            y[j] = v > 448.f ? 448.f : (v < -448.f ? -448.f : v);   // NaN stays NaN
+        }
+        int t = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        t = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], t, true);
+        w[i] = (uint32_t)t;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Decode store: token i (row i of k_new / v_new) goes to the slot at
+// position lens[i] - 1 of table row req_rows[i], one 16-byte chunk of the
+// pool row per thread and step (FP8: 16 codes from 16 inputs of ELT bytes);
+// rows, positions and slots outside their ranges are skipped.  Then, when
+// d.ss.lo is set, the suffix starts.  Run by workgroups wg = 0 .. n_wg-1 of
+// any size (whole waves).
+// ---------------------------------------------------------------------------
+template <int ELT, bool FP8>
+__device__ __forceinline__ void decode_store_job(const DecodeStoreArgs &d, unsigned wg, unsigned n_wg) {
+    const int64_t n = d.n_tokens * d.row_chunks;
+    for (int64_t idx = (int64_t)wg * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)n_wg * blockDim.x) {
+        const int64_t i = idx / d.row_chunks, c = idx % d.row_chunks;
+        const int64_t row = d.req_rows[i];
+        const int64_t col = (int64_t)d.lens[i] - 1;
+        if (row < 0 || row >= d.num_rows || col < 0 || col >= d.stride) continue;
+        const int32_t s = d.r2t[row * d.stride + col];
+        if (s < 0 || s >= d.num_slots) continue;
+        const int64_t dst = (int64_t)s * d.row_chunks + c;
+        if constexpr (FP8) {
+            const int h = (int)(c / d.head_chunks);
+            const int64_t src = idx * (16 * ELT);
+            d.k_pool[dst] = quant16<ELT>(d.k_new + src, d.k_scale[h]);
+            d.v_pool[dst] = quant16<ELT>(d.v_new + src, d.v_scale[h]);
+        } else {
+            d.k_pool[dst] = ((const uint4 *)d.k_new)[idx];
+            d.v_pool[dst] = ((const uint4 *)d.v_new)[idx];
+        }
+    }
+    if (d.ss.lo) suffix_starts(d.ss, wg, n_wg);
+}

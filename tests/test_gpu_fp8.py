@@ -114,6 +114,36 @@ def test_decode_fp8_small_flat_and_cascade(Hq, Hkv, D, q_scale=1.0):
         assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 64), (16, 4, 64)])
+def test_decode_fp8_cascade_stores_current_token(Hq, Hkv, D):
+    # the cascade call stores the current tokens itself (in the leading
+    # workgroups of its prefix-stage launch when it runs in two launches,
+    # D 64 here; in a kernel of its own before the one-grid cascade)
+    wl = _small_decode_workload(25, Hq, Hkv, D)
+    case = GroupCase(wl, fp8=True)
+    res = run_decode(case, wl.ctx_len.copy(), cascade=True)
+    _check_pools(case, res, range(wl.B))
+    reqs, O, LSE = oracle_decode(case, res)
+    err = bf16_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"decode fp8 cascade with store Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+def test_fork_cascade_fp8_stores_current_token():
+    wl = W.fork(seed=2)
+    case = GroupCase(wl, fp8=True)
+    L = np.full(wl.B, 4096 + 40, np.int64)
+    res = run_decode(case, L, cascade=True)
+    sample = list(range(0, wl.B, 9))
+    _check_pools(case, res, sample)
+    reqs, O, LSE = oracle_decode(case, res, reqs=sample)
+    err = bf16_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"fork fp8 cascade with store: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
 def test_cascade_fp8_late_suffix_rounds():
     # the workload of test_cascade_late_suffix_rounds over an FP8 cache
     wl = late_rounds_workload(31)

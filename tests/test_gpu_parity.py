@@ -447,6 +447,45 @@ def test_fork_cascade(s):
     assert err <= BF16_TOL and err_c <= BF16_TOL
 
 
+def _check_current_rows(case, res):
+    """The pool rows at every request's current position hold the token the
+    call stored (bf16 values, exactly)."""
+    cur = [int(st.slots[int(res["L"][r]) - 1]) for r, st in enumerate(case.rows)]
+    idx = torch.tensor(cur, dtype=torch.long, device="cuda")
+    kg = case.cache.k_pool[idx].float().cpu().numpy()
+    vg = case.cache.v_pool[idx].float().cpu().numpy()
+    for r in range(len(cur)):
+        n = int(res["L"][r] - res["P"][r])
+        Ks, Vs = case.suffix_kv(r)
+        np.testing.assert_array_equal(kg[r], Ks[n - 1])
+        np.testing.assert_array_equal(vg[r], Vs[n - 1])
+
+
+@pytest.mark.parametrize("wl_name,s", [("fork", 1), ("fork", 64), ("small_8_8_64", 0), ("small_16_2_128", 0)])
+def test_cascade_stores_current_token(wl_name, s):
+    # the cascade call itself stores the current tokens.  On these shapes it
+    # runs its stages in two launches (the fork's prefix items are the longer
+    # ones; D 64; 2 KV heads), so the store and the suffix starts run in
+    # leading workgroups of the prefix-stage launch
+    if wl_name == "fork":
+        wl = W.fork(seed=1)
+        L = np.full(wl.B, 4096 + s, np.int64)
+        sample = list(range(0, wl.B, 4))
+    else:
+        Hq, Hkv, D = (int(x) for x in wl_name.split("_")[1:])
+        wl = _small_decode_workload(23, Hq, Hkv, D)
+        L = wl.ctx_len.copy()
+        sample = None
+    case = GroupCase(wl)
+    res = run_decode(case, L, cascade=True)
+    _check_current_rows(case, res)
+    reqs, O, LSE = oracle_decode(case, res, reqs=sample)
+    err = bf16_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"cascade with store {wl_name} s={s}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
 @pytest.mark.parametrize("P,E", [(12000, 100), (3000, 2)])
 def test_extend_without_workspace_runs_unsplit(P, E):
     # key splits (one long request) and the small-q split-K path (2 new tokens)

@@ -138,6 +138,25 @@ def test_cascade_group_arrays(validating):
     _expect_invalid(lambda o: _decode(c, True, o=o), c)
 
 
+def test_cascade_prefix_reaching_the_current_token(validating):
+    # a call that stores the current tokens needs every group prefix to end
+    # before its requests' current positions; with no token to store the
+    # prefix may cover a whole context
+    c = _case(9)
+    c["r2t"][:, :100] = c["r2t"][0, :100].clone()
+    c["gpl"][0] = 100                         # request 3's whole context (100), its current token included
+    _expect_invalid(lambda o: _decode(c, True, o=o), c)
+    o = torch.full((B, HQ, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    sp.cascade_decode_attn(c["q"], c["kp"], c["vp"], c["r2t"], c["rows"], c["seq"], c["gptr"], c["gpl"],
+                           256, B, 100, o=o)
+    torch.cuda.synchronize()
+    assert not bool((o == 7.0).any())
+    # a current token whose slot is one of the group's prefix slots
+    c["gpl"][0] = 64
+    c["r2t"][1, 179] = c["r2t"][0, 5]         # request 1's current position (seq 180)
+    _expect_invalid(lambda o: _decode(c, True, o=o), c)
+
+
 def test_extend_invalid_metadata(validating):
     c = _case(8)
     E = 8
