@@ -564,15 +564,24 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     if (carry_store)
         pa.store = decode_store_args(elt_size(dtype), fp8, k_new, v_new, batch, k_pool, v_pool, num_slots, Hkv, D,
                                      k_scale, v_scale, r2t, num_rows, row_stride, req_rows, seq_lens, &ss);
+    // Suffix split rounds for suffixes of about max_seq_len - max_prefix_len
+    // keys, twice that for groups with shorter prefixes: the rest of the Ss
+    // rounds, mostly empty, go after the prefix items in one grid; in two
+    // launches (whole-row suffix kernel) the grid holds only these rounds
+    // and its workgroups take the later rounds' items that have keys (on the
+    // fork, 65 rounds of 64-key splits for suffixes of one key otherwise
+    // dispatch some 16,000 empty workgroups).
+    const int64_t est = std::max<int64_t>(1, (int64_t)max_seq_len - max_prefix_len);
+    const int32_t head = (int32_t)std::min<int64_t>(Ss, 2 * ceil_div64(est, fchunk));
     if (one_grid) {
         SplitArgs sx = sa;
         sx.xcd_block = 1;
-        const int64_t est = std::max<int64_t>(1, (int64_t)max_seq_len - max_prefix_len);
-        const int32_t head = (int32_t)std::min<int64_t>(Ss, 2 * ceil_div64(est, fchunk));
         if ((rc = launch_cascade_split(pa, sx, head, fp8, st)) != SGL_OK) return rc;
     } else {
         if (max_prefix_len > 0 && (rc = run_split(pa, false)) != SGL_OK) return rc;
-        if ((rc = run_split(sa, rows_suffix)) != SGL_OK) return rc;
+        SplitArgs sx = sa;
+        if (rows_suffix && dtype != SGL_F32) sx.rounds = head;
+        if ((rc = run_split(sx, rows_suffix)) != SGL_OK) return rc;
     }
     m.kind = 3; m.prefix = pa.part; m.flat_or_suffix = sa.part;
     if (max_prefix_len == 0) m.kind = 0, m.flat_or_suffix = sa.part;

@@ -195,6 +195,10 @@ struct SplitArgs {
     int32_t n_spl;                 // kind 4: splits per request
     const int32_t *suffix_lo;      // kind 2, optional: first suffix key of each request
                                    // (launch_suffix_start); else found from the group arrays
+    int32_t rounds;                // launch_split_rows, kind 2 with suffix_lo: split rounds in the
+                                   // grid (0: all max_splits); each workgroup then also runs the
+                                   // non-empty items of the later rounds that share its id modulo
+                                   // the grid
     PartialBuf part;
     DecodeStoreArgs store;         // kind 1 (launch_split_bf16 / _fp8), optional: a decode
                                    // store run by leading workgroups of the launch

@@ -34,17 +34,45 @@ __device__ __forceinline__ int rsw(int r) {
     return f & (CR - 1);
 }
 
+// Work item of id bid: split round s and work set v (below).
+__device__ __forceinline__ void rows_item(const SplitArgs &a, int HPW, int bid, int &s, int &v) {
+    const int n_v = a.n_sets * (a.Hkv / HPW);
+    const int rb = a.xcd_block;
+    const int bpx = ((n_v + rb - 1) / rb + 7) / 8;        // blocks per XCD and round
+    const int xcd = (int)((unsigned)bid & 7u);
+    const int local = (int)((unsigned)bid >> 3);
+    s = local / (bpx * rb);
+    const int sl = local % (bpx * rb);
+    const int b = (sl / rb) * 8 + ((xcd - s) & 7);
+    v = b * rb + sl % rb;
+}
+
+// Whether item bid of a suffix stage (kind 2 with suffix starts) has keys:
+// the test rows_split makes before its work, for one item per lane.
+__device__ __forceinline__ bool rows_item_live(const SplitArgs &a, int HPW, int bid) {
+    int s, v;
+    rows_item(a, HPW, bid, s, v);
+    if (s >= a.max_splits || s >= a.part.S || v >= a.n_sets * (a.Hkv / HPW)) return false;
+    const int set = v % a.n_sets;
+    const int64_t L = a.seq_lens[set], P = a.suffix_lo[set], row = a.req_rows[set];
+    if (row < 0 || row >= a.num_rows) return false;
+    const int64_t lo = P < 0 ? 0 : (P > L ? L : P), hi = L < a.row_stride ? L : a.row_stride;
+    return s < ceil_div64(hi - lo, a.chunk);
+}
+
 // HPW waves per workgroup, one per KV head of the head group hg: the
 // workgroup loads the group's HPW * D * elt bytes of every row (the whole row
 // when HPW = Hkv).
 //
 // bid is the work item's id (the workgroup id, less the workgroups of other
 // stages that precede it in a shared grid, which come in multiples of 8, so
-// bid % 8 is still the XCD); k_lds and v_lds hold one tile each (T * R
-// bytes), slot_lds a.chunk slot ids.
+// bid % 8 is still the XCD); tid is threadIdx.x (a caller that runs several
+// items in a loop passes a copy the compiler cannot see through, so that
+// nothing derived from it is kept live across the loop); k_lds and v_lds
+// hold one tile each (T * R bytes), slot_lds a.chunk slot ids.
 template <int D, bool FP8, int HPW>
-__device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, unsigned char *k_lds, unsigned char *v_lds,
-                                           int32_t *slot_lds) {
+__device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, int tid, unsigned char *k_lds,
+                                           unsigned char *v_lds, int32_t *slot_lds) {
     constexpr int ELT = FP8 ? 1 : 2;
     constexpr int T = FP8 ? 32 : 16;        // keys per tile
     constexpr int R = HPW * D * ELT;        // bytes of one tile row (the group's heads of a slot)
@@ -58,8 +86,8 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, unsigned
     constexpr int DB = D / 16;              // 16-dim output blocks
     constexpr int KCH = D / 64;             // fp8: K chunks per lane per 16-key block
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // head of this wave in its group
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // head of this wave in its group
     auto barrier = [&]() {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -78,14 +106,8 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, unsigned
     // are in order, so every set's first split starts before any second one.
     const int ng = a.Hkv / HPW;
     const int n_v = a.n_sets * ng;
-    const int rb = a.xcd_block;
-    const int bpx = ((n_v + rb - 1) / rb + 7) / 8;        // blocks per XCD and round
-    const int xcd = (int)((unsigned)bid & 7u);
-    const int local = (int)((unsigned)bid >> 3);
-    const int s = local / (bpx * rb);
-    const int sl = local % (bpx * rb);
-    const int b = (sl / rb) * 8 + ((xcd - s) & 7);
-    const int v = b * rb + sl % rb;
+    int s, v;
+    rows_item(a, HPW, bid, s, v);
     if (s >= a.max_splits || v >= n_v) return;
     const int set = v % a.n_sets, hg = v / a.n_sets;
     const int kvh = hg * HPW + w;                   // KV head of this wave
@@ -106,7 +128,7 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, unsigned
     const int g = a.Hq / a.Hkv;                     // query rows of this wave (<= 16)
 
     const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
-    for (int j = threadIdx.x; j < nk; j += 64 * HPW) slot_lds[j] = safe_slot(row[j], a.num_slots);
+    for (int j = tid; j < nk; j += 64 * HPW) slot_lds[j] = safe_slot(row[j], a.num_slots);
 
     const int n16 = lane & 15, kq = lane >> 4;
 

@@ -690,7 +690,8 @@ __global__ void __launch_bounds__(256) cascade_split_kernel(SplitArgs pa, SplitA
     const unsigned id = blockIdx.x;
     if (id < n_head || id - n_head >= n_pre) {
         const unsigned sid = id < n_head ? id : id - n_pre;
-        rows_split<D, FP8, kRowsHeads>(sa, (int)sid, dyn_lds, dyn_lds + STB, (int32_t *)(dyn_lds + 2 * STB));
+        rows_split<D, FP8, kRowsHeads>(sa, (int)sid, (int)threadIdx.x, dyn_lds, dyn_lds + STB,
+                                        (int32_t *)(dyn_lds + 2 * STB));
     } else {
         int32_t *slots = (int32_t *)(dyn_lds + 8 * PTB);
         if constexpr (FP8) fp8_split<D, 4, 4>(pa, id - n_head, dyn_lds, dyn_lds + 4 * PTB, slots);

@@ -144,9 +144,11 @@ def test_fork_cascade_fp8_stores_current_token():
     assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
-def test_cascade_fp8_late_suffix_rounds():
-    # the workload of test_cascade_late_suffix_rounds over an FP8 cache
-    wl = late_rounds_workload(31)
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 4, 64)])
+def test_cascade_fp8_late_suffix_rounds(Hq, Hkv, D):
+    # the workloads of test_cascade_late_suffix_rounds over an FP8 cache (one
+    # grid; two launches)
+    wl = late_rounds_workload(31, Hq, Hkv, D)
     case = GroupCase(wl, fp8=True)
     res = run_decode(case, wl.ctx_len.copy(), cascade=False, both=True)
     case.check_r2t()
@@ -155,7 +157,7 @@ def test_cascade_fp8_late_suffix_rounds():
     for tag, o, l in (("flat", res["o"], res["lse"]), ("cascade", res["o_c"], res["lse_c"])):
         err = bf16_err(o[reqs], O)
         lerr = float(np.max(np.abs(l[reqs] - LSE)))
-        _print(f"decode fp8 late suffix rounds {tag}: max abs err {err:.3e}, lse err {lerr:.2e}")
+        _print(f"decode fp8 late suffix rounds {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= LSE_TOL
 
 

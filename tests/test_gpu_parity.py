@@ -408,8 +408,12 @@ def test_decode_split_and_group_edges(Hq, Hkv, D):
         assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
-def test_cascade_late_suffix_rounds():
-    wl = late_rounds_workload(29)
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 128), (16, 4, 64)])
+def test_cascade_late_suffix_rounds(Hq, Hkv, D):
+    # (32, 8, 128): one grid, the long suffixes' later rounds after the prefix
+    # items; (16, 2, 128) and (16, 4, 64): two launches, the suffix grid sized
+    # for the short suffixes and its workgroups running the later rounds
+    wl = late_rounds_workload(29, Hq, Hkv, D)
     case = GroupCase(wl)
     res = run_decode(case, wl.ctx_len.copy(), cascade=False, both=True)
     case.check_r2t()
@@ -417,7 +421,7 @@ def test_cascade_late_suffix_rounds():
     for tag, o, l in (("flat", res["o"], res["lse"]), ("cascade", res["o_c"], res["lse_c"])):
         err = bf16_err(o[reqs], O)
         lerr = float(np.max(np.abs(l[reqs] - LSE)))
-        _print(f"decode late suffix rounds {tag}: max abs err {err:.3e}, lse err {lerr:.2e}")
+        _print(f"decode late suffix rounds {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
