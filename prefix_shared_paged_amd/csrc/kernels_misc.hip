@@ -327,6 +327,52 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
         return pb.o + (((int64_t)r * pb.S + ss) * a.Hq + h) * D;
     };
 
+    constexpr int PER = D / 64;
+    const int64_t obase = ((int64_t)r * a.Hq + h) * D + lane * PER;
+    // Up to FAST parts (head dims up to 128): every part's (m, l) -- lane j
+    // holds part j's -- and o row are loaded at once, so the merge waits for
+    // one round of loads instead of one per pass over the states.
+    constexpr int FAST = PER <= 2 ? 32 : 0;
+    if (FAST > 0 && total <= FAST) {
+        float2 v = make_float2(-INFINITY, 0.f);
+        if (lane < total) v = ml_of(lane);
+        float ov[FAST > 0 ? FAST : 1][PER];
+#pragma unroll
+        for (int u = 0; u < FAST; u++) {
+            if (u < total) {
+                const float *op = o_of(u);
+#pragma unroll
+                for (int i = 0; i < PER; i++) ov[u][i] = op[lane * PER + i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < PER; i++) ov[u][i] = 0.f;
+            }
+        }
+        const float M = wave_max(v.y > 0.f ? v.x : -INFINITY);
+        const float f = v.y > 0.f ? exp2f(v.x - M) : 0.f;
+        const float Lsum = wave_sum(v.y > 0.f ? v.y * f : 0.f);
+        float acc[PER];
+#pragma unroll
+        for (int i = 0; i < PER; i++) acc[i] = 0.f;
+#pragma unroll
+        for (int u = 0; u < FAST; u++) {
+            const float fu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u));
+#pragma unroll
+            for (int i = 0; i < PER; i++) acc[i] += fu == 0.f ? 0.f : ov[u][i] * fu;
+        }
+        const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            if (OUT_BF16)
+                ((__bf16 *)a.o)[obase + i] = (__bf16)(acc[i] * inv);
+            else
+                ((float *)a.o)[obase + i] = acc[i] * inv;
+        }
+        if (a.lse && lane == 0)
+            a.lse[(int64_t)r * a.Hq + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+        return;
+    }
+
     // lane j holds the state of parts j, j + 64, ...: the maximum first, then
     // each part's weight 2^(m - M) (0 for an empty part), broadcast by
     // readlane while the o rows of eight parts are in flight at once
@@ -340,7 +386,6 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
         }
         M = fmaxf(M, wave_max(m));
     }
-    constexpr int PER = D / 64;
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) acc[i] = 0.f;
@@ -374,7 +419,6 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     }
     const float Lsum = wave_sum(Lpart);
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    const int64_t obase = ((int64_t)r * a.Hq + h) * D + lane * PER;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
         if (OUT_BF16)
