@@ -133,7 +133,9 @@ int32_t decode_store_wgs(const DecodeStoreArgs &d, int threads) {
     const int64_t chunks = d.n_tokens * d.row_chunks;
     const int64_t starts = d.ss.lo ? d.ss.batch : 0;
     if (chunks <= 0 && starts <= 0) return 0;
-    int64_t n = std::max(ceil_div64(chunks, 4 * (int64_t)threads), ceil_div64(starts, threads));
+    // about four chunks per thread, and (decode_store_job) as many more
+    // workgroups for the suffix starts
+    int64_t n = ceil_div64(chunks, 4 * (int64_t)threads) + ceil_div64(starts, threads);
     n = std::min<int64_t>(std::max<int64_t>(n, 1), 256);
     return (int32_t)ceil_div64(n, 8) * 8;
 }
@@ -142,7 +144,8 @@ int32_t decode_store_wgs(const DecodeStoreArgs &d, int threads) {
 static int launch_decode_store(const DecodeStoreArgs &d, hipStream_t st) {
     if (d.n_tokens == 0) return SGL_OK;
     if (d.fp8 && (!d.k_scale || !d.v_scale)) return SGL_ERR_INVALID;
-    const dim3 grid((unsigned)std::min<int64_t>(ceil_div64(d.n_tokens * d.row_chunks, 256), 8192));
+    const int64_t store_wgs = std::min<int64_t>(ceil_div64(d.n_tokens * d.row_chunks, 256), 8192);
+    const dim3 grid((unsigned)(store_wgs + (d.ss.lo ? ceil_div64(d.ss.batch, 256) : 0)));
     if (!d.fp8) hipLaunchKernelGGL((decode_store_kernel<2, false>), grid, dim3(256), 0, st, d);
     else if (d.elt == 2) hipLaunchKernelGGL((decode_store_kernel<2, true>), grid, dim3(256), 0, st, d);
     else hipLaunchKernelGGL((decode_store_kernel<4, true>), grid, dim3(256), 0, st, d);
@@ -331,8 +334,11 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     const int64_t obase = ((int64_t)r * a.Hq + h) * D + lane * PER;
     // Up to FAST parts (head dims up to 128): every part's (m, l) -- lane j
     // holds part j's -- and o row are loaded at once, so the merge waits for
-    // one round of loads instead of one per pass over the states.
-    constexpr int FAST = PER <= 2 ? 32 : 0;
+    // one round of loads instead of one per pass over the states.  16 parts
+    // cover the decode and cascade splits of contexts up to 8k keys; 32
+    // measured slower (their 64 o registers cost the kernel occupancy: 11.7
+    // against 9.0 us per merge on the 256-request decode workload).
+    constexpr int FAST = PER <= 2 ? 16 : 0;
     if (FAST > 0 && total <= FAST) {
         float2 v = make_float2(-INFINITY, 0.f);
         if (lane < total) v = ml_of(lane);

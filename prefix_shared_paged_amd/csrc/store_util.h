@@ -83,15 +83,22 @@ __device__ __forceinline__ uint4 quant16(const char *src, float sc) {
 // Decode store: token i (row i of k_new / v_new) goes to the slot at
 // position lens[i] - 1 of table row req_rows[i], one 16-byte chunk of the
 // pool row per thread and step (FP8: 16 codes from 16 inputs of ELT bytes);
-// rows, positions and slots outside their ranges are skipped.  Then, when
-// d.ss.lo is set, the suffix starts.  Run by workgroups wg = 0 .. n_wg-1 of
-// any size (whole waves).
+// rows, positions and slots outside their ranges are skipped.  A thread
+// loads its inputs before it looks the slot up, so the two round trips
+// overlap.  Run by workgroups wg = 0 .. n_wg-1 of any size.
 // ---------------------------------------------------------------------------
 template <int ELT, bool FP8>
-__device__ __forceinline__ void decode_store_job(const DecodeStoreArgs &d, unsigned wg, unsigned n_wg) {
+__device__ __forceinline__ void store_rows(const DecodeStoreArgs &d, unsigned wg, unsigned n_wg) {
+    constexpr int NIN = FP8 ? ELT : 1;   // 16-byte input pieces per pool chunk
     const int64_t n = d.n_tokens * d.row_chunks;
     for (int64_t idx = (int64_t)wg * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)n_wg * blockDim.x) {
         const int64_t i = idx / d.row_chunks, c = idx % d.row_chunks;
+        uint4 kin[NIN], vin[NIN];
+#pragma unroll
+        for (int j = 0; j < NIN; j++) {
+            kin[j] = ((const uint4 *)d.k_new)[idx * NIN + j];
+            vin[j] = ((const uint4 *)d.v_new)[idx * NIN + j];
+        }
         const int64_t row = d.req_rows[i];
         const int64_t col = (int64_t)d.lens[i] - 1;
         if (row < 0 || row >= d.num_rows || col < 0 || col >= d.stride) continue;
@@ -100,13 +107,34 @@ __device__ __forceinline__ void decode_store_job(const DecodeStoreArgs &d, unsig
         const int64_t dst = (int64_t)s * d.row_chunks + c;
         if constexpr (FP8) {
             const int h = (int)(c / d.head_chunks);
-            const int64_t src = idx * (16 * ELT);
-            d.k_pool[dst] = quant16<ELT>(d.k_new + src, d.k_scale[h]);
-            d.v_pool[dst] = quant16<ELT>(d.v_new + src, d.v_scale[h]);
+            d.k_pool[dst] = quant16<ELT>((const char *)kin, d.k_scale[h]);
+            d.v_pool[dst] = quant16<ELT>((const char *)vin, d.v_scale[h]);
         } else {
-            d.k_pool[dst] = ((const uint4 *)d.k_new)[idx];
-            d.v_pool[dst] = ((const uint4 *)d.v_new)[idx];
+            d.k_pool[dst] = kin[0];
+            d.v_pool[dst] = vin[0];
         }
     }
-    if (d.ss.lo) suffix_starts(d.ss, wg, n_wg);
+}
+
+// Workgroups of the n_wg running a decode store job that compute the suffix
+// starts (the rest store the tokens, so the two chains of loads run side by
+// side); 0 when there are none to compute or only one workgroup, which then
+// does both in turn.
+__device__ __forceinline__ unsigned suffix_start_wgs(const DecodeStoreArgs &d, unsigned n_wg) {
+    if (!d.ss.lo || n_wg < 2) return 0;
+    const unsigned need = (unsigned)((d.ss.batch + blockDim.x - 1) / blockDim.x);
+    return need < n_wg / 2 ? need : n_wg / 2;
+}
+
+// The decode store and, when d.ss.lo is set, the suffix starts, by
+// workgroups wg = 0 .. n_wg-1 (whole waves).
+template <int ELT, bool FP8>
+__device__ __forceinline__ void decode_store_job(const DecodeStoreArgs &d, unsigned wg, unsigned n_wg) {
+    const unsigned n_ss = suffix_start_wgs(d, n_wg);
+    if (wg < n_ss) {
+        suffix_starts(d.ss, wg, n_ss);
+        return;
+    }
+    store_rows<ELT, FP8>(d, wg - n_ss, n_wg - n_ss);
+    if (d.ss.lo && n_ss == 0) suffix_starts(d.ss, wg, n_wg);
 }
