@@ -271,6 +271,21 @@ def f32_rel_err(got, want):
     return float(np.max(num / np.maximum(den, 1e-30)))
 
 
+def many_rounds_workload(seed, Hq=16, Hkv=2, D=128):
+    """A group whose prefix covers nearly all of a 9,000-key context beside a
+    request with no prefix at all: max_seq_len - max_prefix_len is 10, so the
+    suffix splits are 64 keys and a two-launch cascade's suffix grid holds 2
+    split rounds, while the prefix-less request needs 141 -- each suffix
+    workgroup then runs up to 70 later items, found 64 per ballot."""
+    spec = W.Spec("many_rounds", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed)
+    members = [2, 1]
+    prefixes = [8990, 0]
+    grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
+    sib = np.concatenate([np.arange(m) for m in members]).astype(np.int64)
+    L = np.array([8995, 9000, 9000], np.int64)
+    return W.GroupWorkload(spec, np.array(prefixes, np.int64), grp, sib, L)
+
+
 def late_rounds_workload(seed, Hq=32, Hkv=8, D=128):
     """One group with a 4000-token prefix and short suffixes beside groups
     with short prefixes and suffixes of up to 4080 keys: max_seq_len -

@@ -14,7 +14,7 @@ import torch
 import oracle.fp8 as F8
 import workloads as W
 from prefix_shared_paged_amd import store_kv_fp8
-from scenarios import GroupCase, bf16_err, late_rounds_workload, oracle_decode, run_decode
+from scenarios import GroupCase, bf16_err, late_rounds_workload, many_rounds_workload, oracle_decode, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -159,6 +159,20 @@ def test_cascade_fp8_late_suffix_rounds(Hq, Hkv, D):
         lerr = float(np.max(np.abs(l[reqs] - LSE)))
         _print(f"decode fp8 late suffix rounds {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+def test_cascade_fp8_many_later_rounds():
+    # the workload of test_cascade_many_later_rounds over an FP8 cache (D 64,
+    # two launches): the suffix workgroups' later items, 64 per ballot
+    wl = many_rounds_workload(39, 16, 4, 64)
+    case = GroupCase(wl, fp8=True)
+    res = run_decode(case, wl.ctx_len.copy(), cascade=True)
+    _check_pools(case, res, range(wl.B))
+    reqs, O, LSE = oracle_decode(case, res)
+    err = bf16_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"decode fp8 many later rounds: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
 def test_decode_fp8_peaky():

@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads as W
 from prefix_shared_paged_amd import decode_attn, extend_attn
-from scenarios import (GroupCase, bf16_err, dev, dev_i, f32_rel_err, late_rounds_workload,
+from scenarios import (GroupCase, bf16_err, dev, dev_i, f32_rel_err, late_rounds_workload, many_rounds_workload,
                        oracle_decode, oracle_extend, run_decode, run_extend)
 
 pytestmark = pytest.mark.gpu
@@ -423,6 +423,19 @@ def test_cascade_late_suffix_rounds(Hq, Hkv, D):
         lerr = float(np.max(np.abs(l[reqs] - LSE)))
         _print(f"decode late suffix rounds {tag} Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
         assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 2, 128), (16, 4, 64)])
+def test_cascade_many_later_rounds(Hq, Hkv, D):
+    wl = many_rounds_workload(37, Hq, Hkv, D)
+    case = GroupCase(wl)
+    res = run_decode(case, wl.ctx_len.copy(), cascade=True)
+    case.check_r2t()
+    reqs, O, LSE = oracle_decode(case, res)
+    err = bf16_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"cascade many later rounds Hq={Hq} Hkv={Hkv} D={D}: max abs err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= BF16_TOL and lerr <= LSE_TOL
 
 
 def test_decode_full_size_flat_and_cascade():
