@@ -16,7 +16,7 @@ constexpr int kDecodeChunk = 1024;   // keys per split of the per-head kernels (
 constexpr int kRowsChunk = 512;      // keys per split of the whole-row kernel (flat fp8)
 constexpr int kSuffixChunk = 1024;   // keys per split of the cascade suffix (whole-row kernel), at most
 constexpr int kPrefixChunkMax = 512;
-constexpr int kPrefixChunkMin = 64;
+constexpr int kPrefixChunkMin = 128;
 constexpr int64_t kPrefixWorkgroups = 1024;  // ~4 per compute unit
 constexpr int kFlatXcdBlock = 16;    // consecutive requests per XCD block (flat fp8 decode)
 constexpr size_t kAlign = 256;
@@ -28,9 +28,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Keys per split of the cascade prefix stage.  The stage runs one workgroup
 // per (group, KV head, split, block of up to 4 x 16 query rows) -- often far
 // fewer than the flat call has work items -- and a workgroup walks its
-// split's tiles one after another, so the splits are halved (down to 64
-// keys) until about kPrefixWorkgroups workgroups run.  The row-block rule
-// matches the launcher in kernels_decode.hip.
+// split's tiles one after another, so the splits are halved (down to
+// kPrefixChunkMin keys) until about kPrefixWorkgroups workgroups run.  The
+// row-block rule matches the launcher in kernels_decode.hip.  Splits shorter
+// than 128 keys cost more in per-workgroup start-up (slot table, queries,
+// state writes) than their parallelism gains: the extend step's decode (64
+// requests over one 2,048-key prefix, 257-key suffixes) takes 40 us with
+// 128-key prefix and suffix splits against 50 us with 64 and 44 us with 256.
 int prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq, int32_t Hkv, int32_t D) {
     const int64_t rb = ceil_div64((int64_t)max_group_size * (Hq / Hkv), 16);
     int64_t wpg = rb >= 3 ? 4 : rb;
@@ -47,7 +51,7 @@ int prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int3
 // 512 (each workgroup hand-off on a compute unit -- draining the finished
 // item's state stores, starting the next -- leaves its slot idle for a few
 // us, and the prefix items that follow the suffix rounds fill the longer
-// tail).  Halved (down to 64) while the suffixes -- estimated as
+// tail).  Halved (down to kPrefixChunkMin) while the suffixes -- estimated as
 // max_seq_len - max_prefix_len, which only sizes the splits -- would give
 // fewer than kPrefixWorkgroups workgroups: a batch of a few dozen requests
 // with short suffixes otherwise leaves most compute units idle while each
@@ -164,7 +168,7 @@ int32_t extend_splits(int32_t batch, int32_t Hkv) {
 }
 
 // MLA latent decode: keys per split of the flat call and the suffix, and
-// the prefix split (halved down to 64 keys until about kPrefixWorkgroups
+// the prefix split (halved down to kPrefixChunkMin keys until about kPrefixWorkgroups
 // workgroups run; the row-block rule matches launch_split_mla).
 // Keys per flat / suffix split of the latent decode: 1024 when each split
 // has 64 or more query rows (one wave per 16-row block), where the split
