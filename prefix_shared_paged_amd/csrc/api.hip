@@ -403,7 +403,11 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     //  - flat fp8: whole-row loads with blocks of kFlatXcdBlock consecutive
     //    requests per XCD, so siblings share prefix rows through one L2;
     //  - flat bf16: the per-head kernel, whose head-per-XCD order already gets
-    //    that reuse with every XCD holding an equal share of each request;
+    //    that reuse with every XCD holding an equal share of each request (the
+    //    whole-row kernel here measured mixed: faster on the fork, 241 -> 214
+    //    us, and on chunked-prefill decode with 16-token pages, 7.61 -> 7.52 ms
+    //    per run, slower on 256 requests with no shared prefix, 1,028 -> 1,061
+    //    us, and within noise on the decode workload);
     //  - other shapes, and the cascade prefix stage: the per-head kernels.
     const bool rows_ok = dtype != SGL_F32 && (Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16) && g <= 16;
     const bool rows_flat = rows_ok && fp8;
