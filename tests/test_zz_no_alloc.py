@@ -21,11 +21,12 @@ BF16_TOL = 2e-2
 LSE_TOL = 1e-3
 
 
-def _case(seed, G, per_group, p_hi, l_hi):
-    wl = W.decode(seed=seed, G=G, per_group=per_group, p_lo=64, p_hi=p_hi, l_lo=p_hi // 2, l_hi=l_hi,
-                  num_slots=1 << 20)
+def _case(seed, G, per_group, p_hi, l_hi, wl=None, L=None):
+    if wl is None:
+        wl = W.decode(seed=seed, G=G, per_group=per_group, p_lo=64, p_hi=p_hi, l_lo=p_hi // 2, l_hi=l_hi,
+                      num_slots=1 << 20)
     case = GroupCase(wl)
-    L = wl.ctx_len.copy()
+    L = wl.ctx_len.copy() if L is None else L
     P = np.array([wl.prefix_len[wl.grp[r]] for r in range(wl.B)], np.int64)
     rows = case.admit_requests(L - P)
     case.cache.append(rows, L - P)
@@ -73,6 +74,15 @@ def test_static_scratch_two_calls_second_smaller():
     _run_both(case, res, args, kv)
     case2, res2, args2, kv2 = _case(seed=4, G=3, per_group=5, p_hi=700, l_hi=1500)
     _run_both(case2, res2, args2, kv2)
+
+
+def test_static_scratch_fork_two_launches():
+    # the fork shape (prefix items longer than the suffix items) runs the two
+    # stages in two launches, the first also computing the suffix starts
+    wl = W.fork(seed=5, G=16, branches=8, prompt=4096, max_suffix=40, num_slots=1 << 17)
+    L = np.full(wl.B, 4096 + 40, np.int64)
+    case, res, args, kv = _case(5, 0, 0, 0, 0, wl=wl, L=L)
+    _run_both(case, res, args, kv)
 
 
 def test_static_scratch_rejects_oversized_call():
