@@ -17,7 +17,8 @@
 //     reduction across waves; the waves of a workgroup (1, 2 or 4 row blocks)
 //     share each 16-key latent tile (18 KiB) in LDS, gathered by slot with
 //     non-temporal direct loads into a ring of 2 (one or two blocks: four
-//     workgroups per CU) or 4 tiles (four blocks);
+//     workgroups per CU) or 4 tiles (four blocks, whose value contraction
+//     takes the tiles in pairs);
 //   split_mla_kernel (the cascade's prefix stage, up to 4 blocks): every
 //     16-row block gets four waves: wave q computes the partial S^T = K Q^T
 //     of the block over its share of the 576 score dims (5, 5, 4, 4 MFMA
@@ -311,18 +312,22 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &
 
 // One wave per 16-row block over all 576 score dims and all 512 value dims:
 // no reduction across waves.  The RBW waves of a workgroup (RBW row blocks)
-// share each latent tile; a ring of DEPTH tiles (DEPTH - 1 in flight) lets one
-// barrier per tile both publish the tile's direct loads and retire the
-// buffer they refill.  Four blocks take a ring of four (72 KiB, two
-// workgroups per CU); one or two blocks a ring of two (36 KiB: four
-// workgroups per CU keep more rows in flight than a deeper ring would).
-// A wave keeps its block's Q operand (72 VGPRs) and O^T accumulators (128).
+// share each latent tile; a ring of DEPTH tiles lets one barrier per tile
+// both publish the tile's direct loads and retire the buffer they refill.
+// Four blocks take a ring of four (72 KiB, two workgroups per CU) and run the
+// value contraction over pairs of tiles (32 keys per 16x16x32 MFMA); one or
+// two blocks a ring of two (36 KiB: four workgroups per CU keep more rows in
+// flight than a deeper ring would) and 16-key steps.  A wave keeps its
+// block's Q operand (72 VGPRs) and O^T accumulators (128); with four or two
+// blocks the kernel fits 256 VGPRs, two waves per SIMD.
 template <int RBW, int DEPTH>
-__global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
+__global__ void __launch_bounds__(64 * RBW, DEPTH >= 4 ? 2 : 1) split_mla_full_kernel(SplitArgs a) {
     constexpr int QS = DQK / 32;                   // 18 S^T steps
     constexpr int DB = DV / 16;                    // 32 output blocks of 16 dims
     constexpr int KB = 3;                          // K operand reads per batch
     constexpr int VB = 8;                          // V^T reads per batch
+    constexpr int TPS = DEPTH >= 4 ? 2 : 1;        // tiles per O^T step
+    constexpr int VB2 = 4;                         // output blocks per batch of paired V^T reads
     __shared__ __attribute__((aligned(16))) unsigned char t_lds[DEPTH * TBM];
     extern __shared__ int32_t slot_lds[];          // [chunk]
 
@@ -390,21 +395,26 @@ __global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
     // ---- direct loads: instruction ii covers tile bytes [1024 ii, 1024 ii + 1024);
     // wave w issues ii = w, w + RBW, ...
     constexpr int MAXI = (NIM + RBW - 1) / RBW;
-    int lrow[MAXI], lsrc[MAXI];
-#pragma unroll
-    for (int u = 0; u < MAXI; u++) {
-        const int ii = w + RBW * u;
-        const int off = (ii < NIM ? ii : 0) * 1024 + 16 * lane;
-        lrow[u] = off / RB;
-        const int c = (off % RB) / 16;
-        lsrc[u] = 16 * (c ^ msw(lrow[u]));
-    }
     const int n_mine = (NIM - w + RBW - 1) / RBW;
     const char *pool = (const char *)a.k_pool;
 
     __syncthreads();   // slot table visible
 
     auto issue = [&](int n, unsigned char *dst) {
+        // tile row and source byte offset of each of this lane's pieces;
+        // with several waves (two per SIMD) they are recomputed per tile from
+        // a lane id the compiler cannot see through, since kept live across
+        // the loop they would cost registers the MFMA operands need
+        int ln = lane;
+        if constexpr (RBW > 1) asm volatile("" : "+v"(ln));
+        int lrow[MAXI], lsrc[MAXI];
+#pragma unroll
+        for (int u = 0; u < MAXI; u++) {
+            const int ii = w + RBW * u;
+            const int off = (ii < NIM ? ii : 0) * 1024 + 16 * ln;
+            lrow[u] = off / RB;
+            lsrc[u] = 16 * ((off % RB) / 16 ^ msw(lrow[u]));
+        }
         int32_t sl[MAXI];                          // all look-ups first: one LDS wait
 #pragma unroll
         for (int u = 0; u < MAXI; u++) sl[u] = slot_lds[min(n * MT + lrow[u], nk - 1)];
@@ -438,11 +448,10 @@ __global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
 #pragma unroll
     for (int d = 0; d < 4; d++) voff[d] = vr * RB + 16 * ((2 * d + (qq >> 1)) ^ mv) + 8 * (qq & 1);
 
-    auto tile = [&](int n, const unsigned char *tb) {
-        const uint32_t base = lds_addr(tb);
+    // S^T of one 16-key tile (KB independent accumulators: step t feeds t % KB,
+    // so consecutive MFMAs do not wait on each other)
+    auto scores = [&](uint32_t base) -> f32x4 {
         const uint32_t kb0 = base + koff0, kb1 = base + koff1;
-        // KB independent accumulators (step t feeds t % KB), so consecutive
-        // MFMAs do not wait on each other
         f32x4 sp[KB];
 #pragma unroll
         for (int i = 0; i < KB; i++) sp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -462,15 +471,20 @@ __global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
         f32x4 sacc = sp[0];
 #pragma unroll
         for (int i = 1; i < KB; i++) sacc += sp[i];
-        // online softmax over the tile's 16 keys (lazy reference maximum)
-        float sv[4];
+        return sacc;
+    };
+    // online softmax over NT * 16 keys from tile n0 on (lazy reference
+    // maximum); p[4 t + j] is key 16 (n0 + t) + 4 kq + j of row n16
+    auto softmax = [&](int n0, const f32x4 (&s)[TPS], float (&p)[4 * TPS]) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float x = n * MT + kq * 4 + j < nk ? sacc[j] * qscale : -INFINITY;
-            sv[j] = x;
-            mx = fmaxf(mx, x);
-        }
+        for (int t = 0; t < TPS; t++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float x = (n0 + t) * MT + kq * 4 + j < nk ? s[t][j] * qscale : -INFINITY;
+                p[4 * t + j] = x;
+                mx = fmaxf(mx, x);
+            }
         mx = max_across_kq(mx);
         const bool move = mx > m_run + 8.f;
         if (__builtin_amdgcn_ballot_w64(move)) {
@@ -481,42 +495,113 @@ __global__ void __launch_bounds__(64 * RBW) split_mla_full_kernel(SplitArgs a) {
             for (int db = 0; db < DB; db++) oacc[db] *= alpha;
             m_run = m_new;
         }
-        bf16x4 pf;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const float pj = __builtin_amdgcn_exp2f(sv[j] - m_run);
-            l_run += pj;
-            pf[j] = (__bf16)pj;
+        for (int j = 0; j < 4 * TPS; j++) {
+            p[j] = __builtin_amdgcn_exp2f(p[j] - m_run);
+            l_run += p[j];
         }
-        const i16x4 pb = __builtin_bit_cast(i16x4, pf);
-        static_for(std::make_integer_sequence<int, DB / VB>{}, [&](auto bi) {
-            constexpr int D0 = decltype(bi)::value * VB;
-            i32x2 vt[VB];
-            static_for(std::make_integer_sequence<int, VB>{}, [&](auto di) {
-                constexpr int DBI = D0 + decltype(di)::value;
-                ds_tr16<128 * (DBI >> 2)>(vt[decltype(di)::value], base + voff[DBI & 3]);
-            });
-            lgkm_wait_tied(vt);
-#pragma unroll
-            for (int i = 0; i < VB; i++)
-                oacc[D0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt[i]), pb,
-                                                                         oacc[D0 + i], 0, 0, 0);
-        });
     };
 
-    // ring of DEPTH tiles, DEPTH - 1 in flight: at the top of step n this
-    // wave's loads of tile n have landed when only those of tiles n+1 ..
-    // n+DEPTH-2 remain; after the barrier every wave has also finished tile
-    // n-1, whose buffer takes tile n+DEPTH-1
-    for (int t = 0; t < DEPTH - 1 && t < N; t++) issue(t, t_lds + t * TBM);
-    for (int n = 0; n < N; n++) {
-        const int later = min(DEPTH - 2, N - 1 - n);
-        vm_wait_upto<MAXI * (DEPTH - 2)>(n_mine * later);
-        lgkm_wait0();
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (n + DEPTH - 1 < N) issue(n + DEPTH - 1, t_lds + ((n + DEPTH - 1) % DEPTH) * TBM);
-        tile(n, t_lds + (n % DEPTH) * TBM);
+    if constexpr (TPS == 1) {
+        // one tile per step: O^T += V^T P^T over its 16 keys (16x16x16 MFMAs)
+        auto tile = [&](int n, const unsigned char *tb) {
+            const uint32_t base = lds_addr(tb);
+            const f32x4 s[1] = {scores(base)};
+            float p[4];
+            softmax(n, s, p);
+            bf16x4 pf;
+#pragma unroll
+            for (int j = 0; j < 4; j++) pf[j] = (__bf16)p[j];
+            const i16x4 pb = __builtin_bit_cast(i16x4, pf);
+            static_for(std::make_integer_sequence<int, DB / VB>{}, [&](auto bi) {
+                constexpr int D0 = decltype(bi)::value * VB;
+                i32x2 vt[VB];
+                static_for(std::make_integer_sequence<int, VB>{}, [&](auto di) {
+                    constexpr int DBI = D0 + decltype(di)::value;
+                    ds_tr16<128 * (DBI >> 2)>(vt[decltype(di)::value], base + voff[DBI & 3]);
+                });
+                lgkm_wait_tied(vt);
+#pragma unroll
+                for (int i = 0; i < VB; i++)
+                    oacc[D0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vt[i]), pb,
+                                                                             oacc[D0 + i], 0, 0, 0);
+            });
+        };
+        // ring of DEPTH tiles, DEPTH - 1 in flight: at the top of step n this
+        // wave's loads of tile n have landed when only those of tiles n+1 ..
+        // n+DEPTH-2 remain; after the barrier every wave has also finished tile
+        // n-1, whose buffer takes tile n+DEPTH-1
+        for (int t = 0; t < DEPTH - 1 && t < N; t++) issue(t, t_lds + t * TBM);
+        for (int n = 0; n < N; n++) {
+            const int later = min(DEPTH - 2, N - 1 - n);
+            vm_wait_upto<MAXI * (DEPTH - 2)>(n_mine * later);
+            lgkm_wait0();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (n + DEPTH - 1 < N) issue(n + DEPTH - 1, t_lds + ((n + DEPTH - 1) % DEPTH) * TBM);
+            tile(n, t_lds + (n % DEPTH) * TBM);
+        }
+    } else {
+        // tiles in pairs: the scores of an even tile are kept until the next
+        // (odd) tile's, then one softmax covers both and O^T += V^T P^T runs
+        // over their 32 keys with 16x16x32 MFMAs (half the instructions of
+        // two 16-key steps).  Contraction slot 8 kq + j of a lane is key
+        // 4 kq + j of the even tile for j < 4 and key 4 kq + j - 4 of the odd
+        // one: the V^T operand is the two tiles' transposed reads side by
+        // side, the P^T operand the two score fragments.  With no odd tile
+        // (N odd) the even tile's buffer stands in for it under zero weights.
+        auto pair = [&](int n0, const f32x4 &sa, uint32_t ba, const f32x4 &sb, uint32_t bb) {
+            const f32x4 s[2] = {sa, sb};
+            float p[8];
+            softmax(n0, s, p);
+            bf16x8 pb;
+#pragma unroll
+            for (int j = 0; j < 8; j++) pb[j] = (__bf16)p[j];
+            static_for(std::make_integer_sequence<int, DB / VB2>{}, [&](auto bi) {
+                constexpr int D0 = decltype(bi)::value * VB2;
+                i32x2 vt[2 * VB2];
+                static_for(std::make_integer_sequence<int, VB2>{}, [&](auto di) {
+                    constexpr int DBI = D0 + decltype(di)::value;
+                    ds_tr16<128 * (DBI >> 2)>(vt[2 * decltype(di)::value], ba + voff[DBI & 3]);
+                    ds_tr16<128 * (DBI >> 2)>(vt[2 * decltype(di)::value + 1], bb + voff[DBI & 3]);
+                });
+                lgkm_wait_tied(vt);
+#pragma unroll
+                for (int i = 0; i < VB2; i++) {
+                    const u32x4 v = {(unsigned)vt[2 * i][0], (unsigned)vt[2 * i][1], (unsigned)vt[2 * i + 1][0],
+                                     (unsigned)vt[2 * i + 1][1]};
+                    oacc[D0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pb,
+                                                                           oacc[D0 + i], 0, 0, 0);
+                }
+            });
+        };
+        // ring of DEPTH tiles, F = DEPTH - 2 in flight: at the top of step n
+        // this wave's loads of tile n have landed when only those of tiles
+        // n+1 .. n+F-1 remain; after the barrier every wave is past step
+        // n-1, so tile n-2 (scored at step n-2, its values read by step n-1
+        // at the latest) is done and its buffer takes tile n+F, while tile
+        // n-1 (still to be read when n is odd) keeps its own.
+        constexpr int F = DEPTH - 2;
+        static_assert(F >= 2, "pairs of tiles take a ring of four or more");
+        for (int t = 0; t < F && t < N; t++) issue(t, t_lds + t * TBM);
+        f32x4 s_even = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint32_t b_even = lds_addr(t_lds);
+        for (int n = 0; n < N; n++) {
+            vm_wait_upto<MAXI * (F - 1)>(n_mine * min(F - 1, N - 1 - n));
+            lgkm_wait0();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (n + F < N) issue(n + F, t_lds + ((n + F) % DEPTH) * TBM);
+            const uint32_t base = lds_addr(t_lds + (n % DEPTH) * TBM);
+            const f32x4 s = scores(base);
+            if (n & 1) {
+                pair(n - 1, s_even, b_even, s, base);
+            } else {
+                s_even = s;
+                b_even = base;
+            }
+        }
+        if (N & 1) pair(N - 1, s_even, b_even, f32x4{0.f, 0.f, 0.f, 0.f}, b_even);
     }
 
     // ---- the split's state -----------------------------------------------------
