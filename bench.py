@@ -468,6 +468,47 @@ def time_events(fn, n, warm=3):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def box_peaks():
+    """The chip's sustained ceilings, measured in the same process with the
+    library's probes (sgl_probe.h): the dense bf16 MFMA rate (2,048
+    workgroups x 4 waves x 2,048 rounds of 8 independent 32x32x16 MFMAs) and
+    the streaming copy bandwidth (1 GiB read and written once, bytes moved =
+    read + written); medians of 5 event-timed launches after 3 untimed.  The
+    probe's output is checked against its closed form, so the work was done."""
+    import torch
+    import prefix_shared_paged_amd as sp
+    out = torch.empty(2048 * sp.PROBE_THREADS, dtype=torch.float32, device="cuda")
+    iters = 2048
+    flop = sp.probe_mfma_bf16(out, iters)
+    t_mfma = float(np.median(time_events(lambda: sp.probe_mfma_bf16(out, iters), 5)))
+    ok = bool((out == 8 * 16 * iters).all().item())
+    del out
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    moved = sp.probe_copy(src, dst)
+    t_copy = float(np.median(time_events(lambda: sp.probe_copy(src, dst), 5)))
+    ok = ok and bool(torch.equal(src[:1 << 20], dst[:1 << 20]))
+    del src, dst
+    torch.cuda.empty_cache()
+    tflops = flop / (t_mfma * 1e-3) / 1e12
+    gbps = moved / (t_copy * 1e-3) / 1e9
+    return {"mfma_bf16_tflops": tflops, "mfma_frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+            "copy_gbps": gbps, "copy_frac_of_peak": gbps / PEAK_HBM_GBPS, "probe_ms": [t_mfma, t_copy],
+            "checked": ok}
+
+
+def with_box(roof, box):
+    """A roofline object with its fraction of the box's measured ceiling."""
+    if not roof or not box:
+        return roof
+    meas = box["mfma_bf16_tflops"] if roof.get("unit") == "TFLOP/s" else box["copy_gbps"] if roof.get(
+        "unit") == "GB/s" and roof.get("bound") == "hbm" else None
+    if meas:
+        roof["box_peak"] = meas
+        roof["frac_of_box_peak"] = roof["achieved"] / meas
+    return roof
+
+
 def base_line(metric_value, ms, args, config, roofline, extra):
     line = {"metric": "decode attn tokens/s + HBM GB/s; extend attn TFLOP/s (frac of roofline)",
             "value": metric_value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -1290,6 +1331,11 @@ def main():
         line = {"tiny": bench_tiny, "decode": bench_decode, "fork": bench_fork, "verify": bench_verify,
                 "mla": bench_mla, "hicache": bench_hicache,
                 "multiturn": bench_multiturn}[args.config](args, flush)
+    torch.cuda.empty_cache()
+    box = box_peaks()
+    line["box"] = box
+    with_box(line.get("roofline"), box)
+    log(f"box probes done: {box['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, {box['copy_gbps']:.0f} GB/s copy")
     print(json.dumps(line, default=lambda x: x.item() if hasattr(x, "item") else str(x)), flush=True)
 
 

@@ -103,6 +103,8 @@ def load():
         "sgl_mla_cascade_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32]),
         "sgl_hicache_prefetch": (ctypes.c_int, [P, P, I64, P, P, I64, P, P, I64, I64, P]),
         "sgl_hicache_write_back": (ctypes.c_int, [P, P, I64, P, P, I64, P, P, I64, I64, P]),
+        "sgl_probe_mfma_bf16": (ctypes.c_int, [I32, I32, F, P, P]),
+        "sgl_probe_copy": (ctypes.c_int, [P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         if alt and not hasattr(lib, name):
@@ -124,7 +126,8 @@ EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_set_validate", "sgl_kv_p
            "sgl_cascade_decode_attn_static", "sgl_static_scratch_bytes",
            "sgl_store_kv_fp8", "sgl_decode_attn_fp8kv", "sgl_cascade_decode_attn_fp8kv",
            "sgl_mla_decode_attn", "sgl_mla_decode_workspace_size", "sgl_mla_cascade_decode_attn",
-           "sgl_mla_cascade_workspace_size", "sgl_hicache_prefetch", "sgl_hicache_write_back"]
+           "sgl_mla_cascade_workspace_size", "sgl_hicache_prefetch", "sgl_hicache_write_back",
+           "sgl_probe_mfma_bf16", "sgl_probe_copy"]
 
 
 def status_string(status: int) -> str:
@@ -659,3 +662,29 @@ def hicache_write_back(k_pool, v_pool, slots, host_rows, host_k, host_v=None, st
     _check("sgl_hicache_write_back", load().sgl_hicache_write_back(
         kp, vp, k_pool.shape[0], _dev_ptr(slots, "slots", torch.int32), _dev_ptr(host_rows, "host_rows", torch.int64),
         slots.numel(), hk, hv, host_k.shape[0], row_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# measurement helpers (sgl_probe.h): the chip's sustained MFMA rate and copy
+# bandwidth, reported beside the published peaks
+# ---------------------------------------------------------------------------
+PROBE_THREADS = 256
+
+
+def probe_mfma_bf16(out, iters, x=1.0, stream=None):
+    """Enqueue the dense bf16 MFMA probe over out.numel() // 256 workgroups;
+    returns the floating-point operations the launch performs."""
+    torch = _torch()
+    n_wg = out.numel() // PROBE_THREADS
+    _check("sgl_probe_mfma_bf16", load().sgl_probe_mfma_bf16(
+        n_wg, int(iters), float(x), _dev_ptr(out, "out", torch.float32), _stream(stream)))
+    return n_wg * 4 * int(iters) * 8 * 32768
+
+
+def probe_copy(src, dst, stream=None):
+    """Enqueue dst <- src (same byte size, 16-byte multiple); returns the bytes moved (read + written)."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must have the same byte size")
+    _check("sgl_probe_copy", load().sgl_probe_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), nb, _stream(stream)))
+    return 2 * nb

@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["host_cache.cpp", "api.hip", "kernels_misc.hip", "kernels_f32.hip",
            "kernels_decode.hip", "kernels_decode_rows.hip", "kernels_mla.hip", "kernels_extend.hip",
-           "kernels_hicache.hip"]
+           "kernels_hicache.hip", "kernels_probe.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -2,6 +2,7 @@
 and rejects bad arguments before any GPU work (these calls never reach HIP,
 so they run without a GPU)."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -12,12 +13,15 @@ import prefix_shared_paged_amd as sp
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgl_attn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(sgl_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(sgl_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_hot_path_calls():
@@ -41,7 +45,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_header_compiles_as_c():
-    src = '#include "sgl_attn.h"\nint main(void) { return sgl_abi_version() > 0 ? 0 : 1; }\n'
+    src = ('#include "sgl_attn.h"\n#include "sgl_probe.h"\n'
+           'int main(void) { return sgl_abi_version() > 0 ? 0 : 1; }\n')
     res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I",
                           os.path.dirname(HEADER), "-x", "c", "-"], input=src, text=True,
                          capture_output=True)
@@ -126,6 +131,16 @@ def test_device_calls_reject_bad_arguments_before_gpu_work():
     assert wb(q, None, 8, q, q, 4, q, q, 8, 16, None) == sp.SGL_ERR_INVALID
     assert wb(q, q, 8, q, q, 0, q, q, 8, 16, None) == sp.SGL_OK
     assert pf(None, None, 8, None, None, 0, None, None, 8, 16, None) == sp.SGL_OK
+    # measurement helpers: bad sizes, counts and pointers
+    assert lib.sgl_probe_copy(q, _fake(4), 24, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_probe_copy(q, _fake(4), -16, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_probe_copy(mis, _fake(4), 16, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_probe_copy(q, None, 16, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_probe_copy(q, ctypes.c_void_p(q.value + 16), 64, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_probe_copy(None, None, 0, None) == sp.SGL_OK
+    assert lib.sgl_probe_mfma_bf16(0, 1, 1.0, q, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_probe_mfma_bf16(1, 0, 1.0, q, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_probe_mfma_bf16(1, 1, 1.0, None, None) == sp.SGL_ERR_INVALID
 
 
 def test_workspace_sizes_grow_with_the_problem():
