@@ -319,8 +319,10 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &
 // two blocks a ring of two (36 KiB: four workgroups per CU keep more rows in
 // flight than a deeper ring would) and 16-key steps.  A wave keeps its
 // block's Q operand (72 VGPRs) and O^T accumulators (128); with four or two
-// blocks the kernel fits 256 VGPRs, two waves per SIMD.
-template <int RBW, int DEPTH>
+// blocks the kernel fits 256 VGPRs, two waves per SIMD.  SHARED: an item
+// (request, split) has several row-block groups, which then read each tile
+// through the same XCD's L2.
+template <int RBW, int DEPTH, bool SHARED>
 __global__ void __launch_bounds__(64 * RBW, DEPTH >= 4 ? 2 : 1) split_mla_full_kernel(SplitArgs a) {
     constexpr int QS = DQK / 32;                   // 18 S^T steps
     constexpr int DB = DV / 16;                    // 32 output blocks of 16 dims
@@ -337,8 +339,12 @@ __global__ void __launch_bounds__(64 * RBW, DEPTH >= 4 ? 2 : 1) split_mla_full_k
     // ---- work item (as split_mla_kernel) -----------------------------------------
     const int n_rbg = (a.row_blocks + RBW - 1) / RBW;
     const int id = blockIdx.x;
-    const int rbg = id % n_rbg;
-    const int64_t item = id / n_rbg;
+    // SHARED (several row-block groups per item): the groups of one item sit
+    // 8 ids apart, on the same XCD and dispatched together, so the later
+    // groups' tile loads find the first group's in that XCD's L2 (the grid is
+    // a multiple of 8 * n_rbg; ids past the last item exit below)
+    const int rbg = SHARED ? (id / 8) % n_rbg : id % n_rbg;
+    const int64_t item = SHARED ? (int64_t)(id / (8 * n_rbg)) * 8 + id % 8 : id / n_rbg;
     const int set = (int)(item % a.n_sets);
     const int s = (int)(item / a.n_sets);
     if (s >= a.max_splits) return;
@@ -422,8 +428,11 @@ __global__ void __launch_bounds__(64 * RBW, DEPTH >= 4 ? 2 : 1) split_mla_full_k
         for (int u = 0; u < MAXI; u++) {
             if (u < n_mine) {
                 const char *src = pool + (int64_t)sl[u] * RB + lsrc[u];
+                // tiles that another row-block group reads too stay in L2;
+                // otherwise non-temporal
                 __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                                 (SGL_LDS void *)(dst + (w + RBW * u) * 1024), 16, 0, 2 /* nt */);
+                                                 (SGL_LDS void *)(dst + (w + RBW * u) * 1024), 16, 0,
+                                                 SHARED ? 0 : 2 /* nt */);
             }
         }
     };
@@ -631,26 +640,31 @@ int launch_split_mla(const SplitArgs &a0, hipStream_t st) {
     a.row_blocks = (rows + 15) / 16;
     const int rbw = a.row_blocks >= 4 ? 4 : (a.row_blocks >= 2 ? 2 : 1);
     const int n_rbg = (a.row_blocks + rbw - 1) / rbw;
-    const int64_t n_wg = (int64_t)a.n_sets * a.max_splits * n_rbg;
+    const int64_t n_items = (int64_t)a.n_sets * a.max_splits;   // (set, split) pairs
+    const int64_t n_wg = n_items * n_rbg;
     if (n_wg > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
     const size_t dyn = (size_t)a.chunk * sizeof(int32_t);
     if (a.row_blocks >= 4 && a.kind != 1) {
         // 64 or more query rows per split: one wave per 16-row block
         constexpr int FR = 4;
-        const int64_t n_wf = (int64_t)a.n_sets * a.max_splits * ((a.row_blocks + FR - 1) / FR);
+        const int64_t nr = (a.row_blocks + FR - 1) / FR;
+        const int64_t n_wf = (nr > 1 ? ceil_div64(n_items, 8) * 8 : n_items) * nr;
         if (n_wf > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((split_mla_full_kernel<FR, 4>), dim3((unsigned)n_wf), dim3(64 * FR), dyn, st, a);
+        if (nr > 1) hipLaunchKernelGGL((split_mla_full_kernel<FR, 4, true>), dim3((unsigned)n_wf), dim3(64 * FR), dyn, st, a);
+        else hipLaunchKernelGGL((split_mla_full_kernel<FR, 4, false>), dim3((unsigned)n_wf), dim3(64 * FR), dyn, st, a);
         return hip_status(hipGetLastError());
     }
     if (a.kind != 1) {
         // fewer than 64 query rows per split: one wave per 16-row block, one or
         // two blocks per workgroup sharing a two-tile ring
         if (a.row_blocks == 1) {
-            hipLaunchKernelGGL((split_mla_full_kernel<1, 2>), dim3((unsigned)n_wg), dim3(64), dyn, st, a);
+            hipLaunchKernelGGL((split_mla_full_kernel<1, 2, false>), dim3((unsigned)n_wg), dim3(64), dyn, st, a);
         } else {
-            const int64_t n_w2 = (int64_t)a.n_sets * a.max_splits * ((a.row_blocks + 1) / 2);
+            const int64_t nr = (a.row_blocks + 1) / 2;
+            const int64_t n_w2 = (nr > 1 ? ceil_div64(n_items, 8) * 8 : n_items) * nr;
             if (n_w2 > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
-            hipLaunchKernelGGL((split_mla_full_kernel<2, 2>), dim3((unsigned)n_w2), dim3(128), dyn, st, a);
+            if (nr > 1) hipLaunchKernelGGL((split_mla_full_kernel<2, 2, true>), dim3((unsigned)n_w2), dim3(128), dyn, st, a);
+            else hipLaunchKernelGGL((split_mla_full_kernel<2, 2, false>), dim3((unsigned)n_w2), dim3(128), dyn, st, a);
         }
         return hip_status(hipGetLastError());
     }
