@@ -741,8 +741,12 @@ int mla_common(bool cascade, const void *q, const void *kv_new, void *kv_pool, i
     // prefix once for them; a group with more rows would read it once per 64
     // rows from workgroups of 16 waves, which measured slower than reading it
     // once per request (128 requests in groups of 8 over 2-8k keys: 16 heads
-    // 253 vs 208 us, 128 heads 885 vs 805 us).  Such groups run the flat
-    // splits (same result) and need only the flat call's workspace.
+    // 253 vs 208 us, 128 heads 885 vs 805 us), and so did a prefix item per
+    // group whose 64-row workgroups share each tile through one XCD's L2
+    // (16 heads 196-214 vs 188 us, 128 heads 479-507 vs 405-413 us: the
+    // per-request prefix states and the merge cost more than the re-reads).
+    // Such groups run the flat splits (same result) and need only the flat
+    // call's workspace.
     const bool flat_path = !cascade || (int64_t)max_group_size * Hq > 64;
     const int chunk = mla_chunk(Hq);
     const int64_t Ss = ceil_div64(max_seq_len, chunk);
