@@ -170,11 +170,13 @@ int32_t extend_splits(int32_t batch, int32_t Hkv) {
 // MLA latent decode: keys per split of the flat call and the suffix, and
 // the prefix split (halved down to kPrefixChunkMin keys until about kPrefixWorkgroups
 // workgroups run; the row-block rule matches launch_split_mla).
-// Keys per flat / suffix split of the latent decode: 1024 when each split
-// has 64 or more query rows (one wave per 16-row block), where the split
-// states (512 fp32 per row and split) would otherwise cost as much traffic
-// as the latents; 512 otherwise.
-int mla_chunk(int32_t Hq) { return Hq >= 64 ? 1024 : 512; }
+// Keys per flat / suffix split of the latent decode: 512 below 64 query rows
+// per split; from 64 rows on the split states (512 fp32 per row and split)
+// would otherwise cost as much traffic as the latents, so 2048 at exactly 64
+// rows (one workgroup per split; 258 -> 244 us on the latent workload) and
+// 1024 above, where two or more workgroups share each split and the grid
+// would be too small with 2048 (398 -> 421 us at 128 heads).
+int mla_chunk(int32_t Hq) { return Hq > 64 ? 1024 : (Hq == 64 ? 2048 : 512); }
 constexpr int kMlaDqk = 576, kMlaDv = 512;
 int mla_prefix_chunk(int32_t G, int32_t max_group_size, int32_t max_prefix_len, int32_t Hq) {
     const int64_t rb = ceil_div64((int64_t)max_group_size * Hq, 16);

@@ -126,17 +126,18 @@ def test_mla_small(Hq):
     _check(c, list(range(c["B"])), f"small Hq={Hq}")
 
 
-@pytest.mark.parametrize("Hq", [16, 128])
+@pytest.mark.parametrize("Hq", [16, 64, 128])
 def test_mla_decode_shape_sampled(Hq):
     # the benchmark's shape: 128 requests in 16 groups of 8, prefixes
     # ~U[512, 4096], contexts ~U[max(1024, P+1), 8192]; 128 heads (all of
-    # them, 1024-key splits, four 16-row blocks per workgroup) and 16 heads
-    # (one tensor-parallel share of 128); sampled requests, all heads
+    # them, 1024-key splits, two workgroups of four 16-row blocks per split),
+    # 64 heads (2048-key splits, one workgroup per split) and 16 heads (one
+    # tensor-parallel share of 128); sampled requests, all heads
     rng = np.random.default_rng(9)
     members = [8] * 16
     prefixes = [int(x) for x in rng.integers(512, 4097, 16)]
     L = [int(rng.integers(max(1024, P + 1), 8193)) for P in prefixes for _ in range(8)]
-    c = _case(21 if Hq == 16 else 23, Hq, members, prefixes, L, num_slots=1 << 20)
+    c = _case({16: 21, 64: 22, 128: 23}[Hq], Hq, members, prefixes, L, num_slots=1 << 20)
     reqs = sorted(set(rng.choice(c["B"], 24, replace=False).tolist() + [0, c["B"] - 1]
                       + [int(np.argmax(L))]))
     _check(c, reqs, f"decode shape Hq={Hq}")
