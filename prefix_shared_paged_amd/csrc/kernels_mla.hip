@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(64 * RBW, DEPTH >= 4 ? 2 : 1) split_mla_full_k
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // ---- work item (as split_mla_kernel) -----------------------------------------
+    // ---- work item (as split_mla_kernel, ids ordered as below) --------------------
     const int n_rbg = (a.row_blocks + RBW - 1) / RBW;
     const int id = blockIdx.x;
     // SHARED (several row-block groups per item): the groups of one item sit
