@@ -44,10 +44,12 @@
 // MFMAs exactly as given (a negative scale negates it, which is exact), the
 // scores s = q.k come out of the MFMAs in fp32, and the scale joins them in
 // fp32 inside the exponent: p = 2^(s*c - reference) with c = |scale|*log2(e),
-// one FMA per score; the row maximum is found on s and scaled once.  The
-// reference maximum is moved lazily, only when a row's tile maximum exceeds
-// it by more than 2^8 (the exact result is unchanged: the reference is only
-// a scaling point), and the mask is applied only to tiles that may cross the
+// one FMA per score.  The reference maximum is moved lazily, only when a
+// row's tile maximum exceeds it by more than 2^8 (the exact result is
+// unchanged: the reference is only a scaling point): each lane compares the
+// maximum of its half of the row's scores, unscaled, with that threshold
+// divided by the factor, and only when some lane passes it are the two halves
+// combined and scaled; the mask is applied only to tiles that may cross the
 // diagonal.  p is rounded to bf16 for the PV MFMAs (the only reduced-
 // precision step); the row sum l adds the fp32 p, so the log-sum-exp is that
 // of the fp32 scores.
@@ -187,6 +189,7 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
         }
     }
     const float cs = fabsf(qscale);   // |scale| * log2(e): scores -> log2 units
+    const float inv_cs = 1.f / cs;
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -197,6 +200,7 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
     float m_sub = 0.f;           // the reference as subtracted before 2^x (0 while none)
     float l_run = 0.f;           // this lane's part of the row sum
     float thr = -INFINITY;       // a tile maximum above this moves the reference
+    float thr_s = -INFINITY;     // the same threshold in raw score units (thr / cs)
 
     // ---- slot ids: a table in LDS holds the ids of keys [c*TABH, (c+1)*TABH)
     // in half c % 2, so the loop reads them from LDS instead of HBM.  The
@@ -244,9 +248,12 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
     // pool byte offsets of this lane's rows of tile `tile` (a K tile and the V
     // tile of the same keys share them)
     auto offsets = [&](int tile, Off (&dst)[NB]) {
+        // tile * BN is a multiple of BN and jl[i] < BN, so the wrap of the
+        // table index touches only the uniform part
+        const TabT *tab = slot_tab + ((tile * BN) & (2 * TABH - 1));
 #pragma unroll
         for (int i = 0; i < NB; i++) {
-            const TabT e = slot_tab[(tile * BN + jl[i]) & (2 * TABH - 1)];
+            const TabT e = tab[jl[i]];
             if (OFF32) dst[i] = e + lp[i];
             else dst[i] = (int64_t)safe_slot(e, num_slots) * rowstride_el * 2 + (kvh * D * 2 + lp[i]);
         }
@@ -302,8 +309,7 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
         return s;
     };
     // causal mask of tile n (absolute key of accumulator element j:
-    // 32n + 8*(j/4) + 4*h2 + j%4) and the row maximum of the scaled scores
-    // (the maximum of s times the positive factor cs)
+    // 32n + 8*(j/4) + 4*h2 + j%4) and the maximum of this lane's 16 scores
     auto mask_max = [&](f32x16 &s, int n, auto mask_tag) {
         if (decltype(mask_tag)::value) {
             const int lim = pos - n * BN - 4 * h2;
@@ -314,13 +320,14 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
         float mx = s[0];
 #pragma unroll
         for (int j = 1; j < 16; j++) mx = fmaxf(mx, s[j]);
-        return max_xor32(mx) * cs;
+        return mx;               // this lane's half of the row, raw score units
     };
-    // lazy move of the reference (mx is the tile's row maximum); rescales O
-    // and l, so it runs after the PV MFMAs issued before it
-    auto move_ref = [&](float mx) {
-        const bool need = mx > thr;
-        if (__builtin_amdgcn_ballot_w64(need)) {
+    // lazy move of the reference (mx_half: this lane's half-row maximum of
+    // the tile); rescales O and l, so it runs after the PV MFMAs issued before it
+    auto move_ref = [&](float mx_half) {
+        if (__builtin_amdgcn_ballot_w64(mx_half > thr_s)) {
+            const float mx = max_xor32(mx_half) * cs;   // the whole row's maximum, log2 units
+            const bool need = mx > thr;
             const float m_new = need ? mx : m_run;
             const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
@@ -329,6 +336,7 @@ __global__ void __launch_bounds__(NT, 3) extend_bf16_kernel(
             m_run = m_new;
             m_sub = m_new == -INFINITY ? 0.f : m_new;
             thr = m_new + kLazy;
+            thr_s = thr * inv_cs;
         }
     };
     // p = 2^(s*cs - reference) in fp32, rounded to bf16 for the B operands of
