@@ -6,6 +6,10 @@ replays the same bookkeeping on the brute-force model (oracle/radix_model.py)
 to produce the expected req_to_token rows.  Expected attention values come
 from the fp64 oracle over the LOGICAL sequences drawn by workloads/.
 """
+import os
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -238,6 +242,25 @@ def run_decode(case, L, cascade, both=False, workspace=None):
     return out
 
 
+_FP8_LOCK = threading.Lock()
+
+
+def _fp8_logical_kv(case, r, n_suffix):
+    """The oracle's own FP8 codes of request r's logical K/V, decoded exactly.
+    Coding is elementwise (per-head factors), so a group's prefix is coded
+    once and reused by its members."""
+    deq = lambda x, sc: F8.decode(F8.quantize(x, sc)).astype(np.float32)
+    cache = case.__dict__.setdefault("_fp8_prefix_codes", {})
+    g = int(case.wl.grp[r])
+    with _FP8_LOCK:
+        if g not in cache:
+            Kp, Vp = case.prefix_kv[g]
+            cache[g] = (deq(Kp, case.kv_scale[0]), deq(Vp, case.kv_scale[1]))
+    Ks, Vs = case.suffix_kv(r)
+    return (np.concatenate([cache[g][0], deq(Ks[:n_suffix], case.kv_scale[0])]),
+            np.concatenate([cache[g][1], deq(Vs[:n_suffix], case.kv_scale[1])]))
+
+
 def oracle_decode(case, res, reqs=None, heads=None, batch=16):
     wl = case.wl
     s = wl.spec
@@ -245,14 +268,16 @@ def oracle_decode(case, res, reqs=None, heads=None, batch=16):
     Os, LSEs = [], []
     for b0 in range(0, len(reqs), batch):
         part = reqs[b0:b0 + batch]
-        Ks, Vs = [], []
-        for r in part:
-            K, V = case.logical_kv(r, int(res["L"][r] - res["P"][r]))
-            if case.fp8:   # the oracle's own codes of the same values, decoded exactly
-                K = F8.decode(F8.quantize(K, case.kv_scale[0])).astype(np.float32)
-                V = F8.decode(F8.quantize(V, case.kv_scale[1])).astype(np.float32)
-            Ks.append(K)
-            Vs.append(V)
+        n_suf = [int(res["L"][r] - res["P"][r]) for r in part]
+        if case.fp8:   # the coding runs in numpy, which releases the GIL: one thread per request
+            for r in part:
+                case.suffix_kv(r)
+            with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+                KV = list(ex.map(lambda a: _fp8_logical_kv(case, *a), zip(part, n_suf)))
+        else:
+            KV = [case.logical_kv(r, n) for r, n in zip(part, n_suf)]
+        Ks = [k for k, _ in KV]
+        Vs = [v for _, v in KV]
         O, M, Ls, LSE = oracle.attention(Ks, Vs, np.arange(len(part)), [int(res["L"][r]) - 1 for r in part],
                                          res["q"][part], s.Hq, s.Hkv, heads=heads, kv_scale=case.kv_scale)
         Os.append(O)
