@@ -1,8 +1,12 @@
 // kernels_f32.hip -- fp32 attention (extend, and split partial states for
-// decode / cascade).  One wave per (query row, q head): lanes own head_dim
-// elements, every key is a wave-wide dot product followed by the one-key
-// online-softmax update (running maximum, rescaled sum and accumulator;
-// "SGLang 深度拆解" (chenxutan.com) section 3.2, PagedPrefill).  Full fp32
+// decode / cascade).  One wave per (query row, q head) walks its keys in
+// blocks of 64 with the online softmax ("SGLang 深度拆解" (chenxutan.com)
+// section 3.2, PagedPrefill: running maximum, rescaled sum and accumulator),
+// one block at a time instead of one key at a time, so that a block costs a
+// few memory round trips rather than one per key: lane j owns key j of the
+// block for the scores (its whole K row, against the query broadcast from
+// LDS), then for P V lane d owns head dims d (and d + 64) and adds the 64
+// keys' V rows, whose loads all go out before the sums.  Full fp32
 // arithmetic throughout; this path serves small fp32 workloads, the bf16
 // path is the tuned one.
 #include "common.h"
@@ -13,8 +17,9 @@ struct RangeState {
     float acc[PER];
 };
 
-// Attend one query vector (lane holds PER elements) to keys [lo, hi) of a
-// req_to_token row.  m is in log2 units of the scaled score.
+// Attend one query vector (lane holds elements lane*PER .. lane*PER+PER-1) to
+// keys [lo, hi) of a req_to_token row.  m is in log2 units of the scaled
+// score.  Every lane of the wave must be active.
 template <int PER>
 __device__ RangeState<PER> attend_range_f32(const float *qv, const float *__restrict__ k_pool,
                                             const float *__restrict__ v_pool, int64_t num_slots,
@@ -22,25 +27,60 @@ __device__ RangeState<PER> attend_range_f32(const float *qv, const float *__rest
                                             int kvh, int Hkv, float qscale) {
     constexpr int D = PER * 64;
     const int lane = threadIdx.x & 63;
+    __shared__ float q_lds[D];
+#pragma unroll
+    for (int i = 0; i < PER; i++) q_lds[lane * PER + i] = qv[i];
+    __syncthreads();
     RangeState<PER> st;
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; i++) st.acc[i] = 0.f;
-    for (int64_t j = lo; j < hi; j++) {
-        const int64_t s = safe_slot(row[j], num_slots);
-        const float *kr = k_pool + (s * Hkv + kvh) * D + lane * PER;
-        const float *vr = v_pool + (s * Hkv + kvh) * D + lane * PER;
-        float part = 0.f;
+    constexpr int VC = 32;                                            // V rows in flight per lane
+    for (int64_t j0 = lo; j0 < hi; j0 += 64) {
+        const int nv = (int)(hi - j0 < 64 ? hi - j0 : 64);           // keys in this block (uniform)
+        const bool valid = lane < nv;
+        const int32_t slot = valid ? safe_slot(row[j0 + lane], num_slots) : 0;
+        // this lane's key: s = q . k over the whole row
+        const float4 *kr = (const float4 *)(k_pool + ((int64_t)slot * Hkv + kvh) * D);
+        float sc = 0.f;
 #pragma unroll
-        for (int i = 0; i < PER; i++) part = fmaf(qv[i], kr[i], part);
-        const float sc = wave_sum(part) * qscale;
-        const float m_new = fmaxf(st.m, sc);
+        for (int c = 0; c < D / 4; c++) {
+            const float4 k4 = kr[c];
+            const float4 q4 = *(const float4 *)(q_lds + 4 * c);
+            sc = fmaf(q4.x, k4.x, sc);
+            sc = fmaf(q4.y, k4.y, sc);
+            sc = fmaf(q4.z, k4.z, sc);
+            sc = fmaf(q4.w, k4.w, sc);
+        }
+        sc = valid ? sc * qscale : -INFINITY;
+        const float m_new = fmaxf(st.m, wave_max(sc));               // finite: the block has a key
         const float alpha = exp2f(st.m - m_new);
-        const float p = exp2f(sc - m_new);
-        st.l = st.l * alpha + p;
+        const float p = valid ? exp2f(sc - m_new) : 0.f;
+        st.l = st.l * alpha + wave_sum(p);
 #pragma unroll
-        for (int i = 0; i < PER; i++) st.acc[i] = st.acc[i] * alpha + p * vr[i];
+        for (int i = 0; i < PER; i++) st.acc[i] *= alpha;
+        // P V: VC keys at a time, their V rows loaded before any is added
+        for (int c0 = 0; c0 < nv; c0 += VC) {
+            float vv[VC][PER];
+#pragma unroll
+            for (int u = 0; u < VC; u++) {
+                if (c0 + u < nv) {
+                    const int64_t sj = __builtin_amdgcn_readlane(slot, c0 + u);
+                    const float *vr = v_pool + (sj * Hkv + kvh) * D + lane * PER;
+#pragma unroll
+                    for (int i = 0; i < PER; i++) vv[u][i] = vr[i];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < VC; u++) {
+                if (c0 + u < nv) {
+                    const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), c0 + u));
+#pragma unroll
+                    for (int i = 0; i < PER; i++) st.acc[i] = fmaf(pj, vv[u][i], st.acc[i]);
+                }
+            }
+        }
         st.m = m_new;
     }
     return st;

@@ -331,8 +331,9 @@ def test_pool_over_4gib_extend_and_decode():
 # ---------------------------------------------------------------------------
 # decode and cascade decode
 # ---------------------------------------------------------------------------
-def _small_decode_workload(seed, Hq=32, Hkv=8, D=128, q_scale=1.0):
-    spec = W.Spec("small_dec", "bf16", Hq, Hkv, D, 1, 1 << 15, 0.5, seed, extra={"q_scale": q_scale})
+def _small_decode_workload(seed, Hq=32, Hkv=8, D=128, q_scale=1.0, dtype="bf16"):
+    spec = W.Spec("small_dec", dtype, Hq, Hkv, D, 1, 1 << 15, 0.5 if dtype == "bf16" else 1.0, seed,
+                  extra={"q_scale": q_scale})
     members = [1, 3, 5, 16]
     prefixes = [0, 1, 300, 256]
     grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
@@ -360,6 +361,26 @@ def test_decode_small(cascade, Hq, Hkv, D):
     lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
     _print(f"decode small cascade={cascade} Hq={Hq}: max abs err {err:.3e}, lse err {lerr:.2e}")
     assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("cascade", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 64), (16, 4, 128)])
+def test_decode_fp32_small(cascade, Hq, Hkv, D):
+    # the fp32 kernels walk keys in blocks of 64: lengths on and beside the
+    # block edges, suffixes of one and 64 keys, a prefix of one key
+    wl = _small_decode_workload(9, Hq, Hkv, D, dtype="f32")
+    L = wl.ctx_len.copy()
+    L[2], L[3], L[5], L[6], L[7] = 64, 65, 364, 365, 300 + 128
+    L[10], L[11], L[12] = 256 + 1, 256 + 63, 256 + 64
+    wl = W.GroupWorkload(wl.spec, wl.prefix_len, wl.grp, wl.sib, L)
+    case = GroupCase(wl)
+    res = run_decode(case, wl.ctx_len.copy(), cascade)
+    case.check_r2t()
+    reqs, O, LSE = oracle_decode(case, res)
+    err = f32_rel_err(res["o"][reqs], O)
+    lerr = float(np.max(np.abs(res["lse"][reqs] - LSE)))
+    _print(f"decode fp32 small cascade={cascade} Hq={Hq} D={D}: max rel err {err:.3e}, lse err {lerr:.2e}")
+    assert err <= F32_TOL and lerr <= 1e-4
 
 
 @pytest.mark.parametrize("cascade", [False, True])
