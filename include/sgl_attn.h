@@ -45,7 +45,8 @@
  *   - Index safety: device kernels never access memory outside the arrays
  *     the arguments describe.  A slot id outside [0, num_slots) read from
  *     req_to_token is replaced by slot 0 (its result is then meaningless but
- *     no fault occurs).  With the environment variable SGL_ATTN_VALIDATE=1
+ *     no fault occurs); sgl_count_bad_slots counts such ids on the device,
+ *     stream-ordered.  With the environment variable SGL_ATTN_VALIDATE=1
  *     the device calls first copy the index metadata to the host (a
  *     synchronising step), check it, and return SGL_ERR_INVALID on any
  *     out-of-range slot, row or length, enqueuing nothing; sgl_set_validate
@@ -227,6 +228,23 @@ int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
                            const int32_t *prefix_slots, const int64_t *prefix_off,
                            const int32_t *new_slots, const int64_t *new_off,
                            const int32_t *new_col0, void *stream);
+
+/* Device-side index check, stream-ordered (no host round trip, unlike the
+ * validation switch): adds to *count (a device uint32 that the caller zeroes
+ * beforehand) the number of slot ids req_to_token[req_rows[r], j],
+ * 0 <= j < seq_lens[r], that lie outside [0, num_slots), plus one for every
+ * request whose row lies outside [0, num_rows) or whose length lies outside
+ * [0, min(row_stride, max_seq_len)].  These are exactly the ids the
+ * attention calls would replace by slot 0 (see "Index safety" above); the
+ * rows a call reads are the request's first seq_lens[r] columns (for an
+ * extend call, prefix_lens[r] plus its new tokens).  All arrays are device
+ * arrays; the count is read and written by one vector atomic per wave, so
+ * several checks may add to one counter.  The pages say nothing of malformed
+ * tables: this is a safety aid for callers that build their own
+ * req_to_token, not part of the method. */
+int sgl_count_bad_slots(const int32_t *r2t, int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                        const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, int64_t num_slots,
+                        uint32_t *count, void *stream);
 
 /* Store K/V rows into the pools: token i's K row (Hkv*D elements) goes to
  * k_pool[slots[i]], likewise V ("token_to_kv_pool.write(cache_loc, k, v)",

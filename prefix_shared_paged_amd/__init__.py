@@ -74,6 +74,7 @@ def load():
         "sgl_radix_lock_batch": (ctypes.c_int, [P, P, I32, I32]),
         "sgl_kv_pool_alloc_batch": (ctypes.c_int, [P, P, P, P, I32, P]),
         "sgl_build_req_to_token": (ctypes.c_int, [P, I64, I64, P, I32, P, P, P, P, P, P]),
+        "sgl_count_bad_slots": (ctypes.c_int, [P, I64, I64, P, P, I32, I32, I64, P, P]),
         "sgl_store_kv": (ctypes.c_int, [ctypes.c_int, P, P, I64, P, P, P, I64, I32, I32, P]),
         "sgl_extend_attn": (ctypes.c_int, [ctypes.c_int, P, P, P, P, P, I64, P, I64, I64, P, P, P,
                                            I32, I64, I32, I32, I32, I32, F, P, P, P, SZ, P]),
@@ -120,7 +121,8 @@ EXPORTS = ["sgl_status_string", "sgl_abi_version", "sgl_set_validate", "sgl_kv_p
            "sgl_kv_pool_alloc", "sgl_kv_pool_free", "sgl_kv_pool_available", "sgl_radix_create",
            "sgl_radix_destroy", "sgl_radix_match", "sgl_radix_insert", "sgl_radix_lock",
            "sgl_radix_evict", "sgl_radix_stats", "sgl_radix_match_batch", "sgl_radix_insert_batch",
-           "sgl_radix_lock_batch", "sgl_kv_pool_alloc_batch", "sgl_build_req_to_token", "sgl_store_kv",
+           "sgl_radix_lock_batch", "sgl_kv_pool_alloc_batch", "sgl_build_req_to_token", "sgl_count_bad_slots",
+           "sgl_store_kv",
            "sgl_extend_attn", "sgl_extend_workspace_size", "sgl_decode_attn",
            "sgl_decode_workspace_size", "sgl_cascade_decode_attn", "sgl_cascade_workspace_size",
            "sgl_cascade_decode_attn_static", "sgl_static_scratch_bytes",
@@ -341,6 +343,18 @@ def build_req_to_token(r2t, req_rows, new_slots, new_off, prefix_slots=None, pre
         _dev_ptr(prefix_off, "prefix_off", torch.int64, True),
         _dev_ptr(new_slots, "new_slots", torch.int32), _dev_ptr(new_off, "new_off", torch.int64),
         _dev_ptr(new_col0, "new_col0", torch.int32, True), _stream(stream)))
+
+
+def count_bad_slots(r2t, req_rows, seq_lens, max_seq_len, num_slots, count, stream=None):
+    """Adds to count (a device uint32 tensor of one element, zeroed by the
+    caller) the out-of-range slot ids of the requests' rows, stream-ordered."""
+    torch = _torch()
+    if count.numel() != 1:
+        raise ValueError("count: one int32 element (read as uint32)")
+    _check("sgl_count_bad_slots", load().sgl_count_bad_slots(
+        _dev_ptr(r2t, "r2t", torch.int32), r2t.shape[0], r2t.shape[1], _dev_ptr(req_rows, "req_rows", torch.int32),
+        _dev_ptr(seq_lens, "seq_lens", torch.int32), req_rows.numel(), int(max_seq_len), int(num_slots),
+        _dev_ptr(count, "count", torch.int32), _stream(stream)))
 
 
 def store_kv(k_new, v_new, slots, k_pool, v_pool, stream=None):

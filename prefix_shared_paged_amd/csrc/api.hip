@@ -230,6 +230,16 @@ int sgl_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride,
                                      prefix_off, new_slots, new_off, new_col0, st);
 }
 
+int sgl_count_bad_slots(const int32_t *r2t, int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                        const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, int64_t num_slots,
+                        uint32_t *count, void *stream) {
+    if (batch < 0 || num_rows < 0 || row_stride < 0 || num_slots < 0 || max_seq_len < 0) return SGL_ERR_INVALID;
+    if (batch == 0) return SGL_OK;
+    if (!r2t || !req_rows || !seq_lens || !count) return SGL_ERR_INVALID;
+    return launch_count_bad_slots(r2t, num_rows, row_stride, req_rows, seq_lens, batch, max_seq_len, num_slots,
+                                  count, (hipStream_t)stream);
+}
+
 int sgl_store_kv(int dtype, const void *k_new, const void *v_new, int64_t n_tokens,
                  const int32_t *slots, void *k_pool, void *v_pool, int64_t num_slots,
                  int32_t Hkv, int32_t D, void *stream) {

@@ -82,6 +82,10 @@ int launch_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride
                               const int64_t *prefix_off, const int32_t *new_slots,
                               const int64_t *new_off, const int32_t *new_col0, hipStream_t st);
 
+int launch_count_bad_slots(const int32_t *r2t, int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, int64_t num_slots,
+                           uint32_t *count, hipStream_t st);
+
 // Cascade: lo[r] = the group prefix length of request r clamped to [0,
 // seq_lens[r]] -- where its suffix starts -- for r in [0, batch).
 struct SuffixStartArgs {

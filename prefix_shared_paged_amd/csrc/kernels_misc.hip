@@ -47,6 +47,48 @@ int launch_build_req_to_token(int32_t *r2t, int64_t num_rows, int64_t row_stride
 }
 
 // ---------------------------------------------------------------------------
+// Index check on the device: count the slot ids of the requests' rows that lie
+// outside the pool (the attention kernels read slot 0 in their place), and
+// the requests whose row or length is out of range.  Grid (key chunks,
+// batch); a wave counts its 64 ids by ballot and adds the count with one
+// vector atomic.
+// ---------------------------------------------------------------------------
+constexpr int kCheckChunk = 4096;   // keys per workgroup
+
+__global__ void __launch_bounds__(256) count_bad_slots_kernel(
+    const int32_t *__restrict__ r2t, int64_t num_rows, int64_t stride, const int32_t *__restrict__ req_rows,
+    const int32_t *__restrict__ seq_lens, int64_t max_len, int64_t num_slots, uint32_t *__restrict__ count) {
+    const int r = blockIdx.y;
+    const int64_t row = req_rows[r];
+    const int64_t L = seq_lens[r];
+    const int lane = threadIdx.x & 63;
+    if (row < 0 || row >= num_rows || L < 0 || L > stride || L > max_len) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicAdd(count, 1u);
+        return;
+    }
+    const int32_t *src = r2t + row * stride;
+    const int64_t k0 = (int64_t)blockIdx.x * kCheckChunk;
+    const int64_t k1 = k0 + kCheckChunk < L ? k0 + kCheckChunk : L;
+    uint32_t bad = 0;
+    for (int64_t j = k0 + threadIdx.x; j - threadIdx.x < k1; j += blockDim.x) {
+        const bool out = j < k1 && (src[j] < 0 || (int64_t)src[j] >= num_slots);
+        bad += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(out));
+    }
+    if (lane == 0 && bad) atomicAdd(count, bad);
+}
+
+int launch_count_bad_slots(const int32_t *r2t, int64_t num_rows, int64_t row_stride, const int32_t *req_rows,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, int64_t num_slots,
+                           uint32_t *count, hipStream_t st) {
+    if (batch == 0) return SGL_OK;
+    const int64_t chunks = max_seq_len > 0 ? ceil_div64(max_seq_len, kCheckChunk) : 1;
+    if (chunks > 65535 || batch > 65535) return SGL_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(count_bad_slots_kernel, dim3((unsigned)chunks, (unsigned)batch), dim3(256), 0, st, r2t,
+                       num_rows, row_stride, req_rows, seq_lens, (int64_t)max_seq_len, num_slots, count);
+    return hip_status(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
 // KV store: copy token rows (Hkv * D elements = row_chunks * 16 bytes) of K and
 // V into the pools at their slots ("SGLang 深度解读" module 5: write the
 // current K, V at cache_loc before attending).  Modes 0 (given slots) and 1

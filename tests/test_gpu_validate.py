@@ -184,3 +184,66 @@ def test_extend_invalid_metadata(validating):
                                                         device="cuda")), c, shape)    # q_off[B] != n_tokens
     _expect_invalid(lambda o: ext(o, rows=torch.tensor([0, 1, 2, -1], dtype=torch.int32, device="cuda")),
                     c, shape)
+
+
+# ---------------------------------------------------------------------------
+# device-side index check (sgl_count_bad_slots): stream-ordered, no host copy
+# ---------------------------------------------------------------------------
+def _count_bad(r2t, rows, seq, max_seq, num_slots):
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sp.count_bad_slots(r2t, rows, seq, max_seq, num_slots, cnt)
+    torch.cuda.synchronize()
+    return int(cnt.item()) & 0xFFFFFFFF
+
+
+def _count_bad_host(r2t, rows, seq, max_seq, num_slots):
+    t, rs, ls = r2t.cpu().numpy(), rows.cpu().numpy(), seq.cpu().numpy()
+    n = 0
+    for r, L in zip(rs, ls):
+        if r < 0 or r >= t.shape[0] or L < 0 or L > min(t.shape[1], max_seq):
+            n += 1
+            continue
+        ids = t[r, :L]
+        n += int(np.count_nonzero((ids < 0) | (ids >= num_slots)))
+    return n
+
+
+def test_count_bad_slots_clean_table_counts_zero():
+    c = _case()
+    assert _count_bad(c["r2t"], c["rows"], c["seq"], 256, S) == 0
+    # the same table against a smaller pool: every id >= 1000 in the rows counts
+    want = _count_bad_host(c["r2t"], c["rows"], c["seq"], 256, 1000)
+    assert want > 0 and _count_bad(c["r2t"], c["rows"], c["seq"], 256, 1000) == want
+
+
+def test_count_bad_slots_marked_ids_rows_and_lengths():
+    c = _case(3)
+    r2t = c["r2t"].clone()
+    r2t[0, 5] = -1                 # inside row 0's 200 keys
+    r2t[1, 179] = S                # the last key of row 1
+    r2t[1, 180] = -7               # past row 1's length: not read, not counted
+    r2t[2, 0] = 1 << 30
+    rows = torch.tensor([0, 1, 2, 3, 9, 1], dtype=torch.int32, device="cuda")       # row 9 is outside the table
+    seq = torch.tensor([200, 180, 256, 100, 10, 300], dtype=torch.int32, device="cuda")   # 300 > stride
+    want = _count_bad_host(r2t, rows, seq, 256, S)
+    assert want == 5
+    assert _count_bad(r2t, rows, seq, 256, S) == want
+    # a length above max_seq_len counts as well, and adds to what the counter holds
+    cnt = torch.full((1,), 4, dtype=torch.int32, device="cuda")
+    sp.count_bad_slots(r2t, rows[:4], seq[:4], 199, S, cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 4 + _count_bad_host(r2t, rows[:4], seq[:4], 199, S)
+
+
+def test_count_bad_slots_long_rows_span_several_chunks():
+    # rows of 9,000 keys (three 4,096-key chunks), bad ids near each chunk edge
+    n_rows, stride, slots = 3, 9000, 1 << 16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    r2t = torch.randint(0, slots, (n_rows, stride), generator=gen, device="cuda", dtype=torch.int32)
+    for col in (0, 4095, 4096, 8191, 8192, 8999):
+        r2t[1, col] = slots + col
+    r2t[2, 4096] = -3
+    rows = torch.arange(n_rows, dtype=torch.int32, device="cuda")
+    seq = torch.tensor([9000, 9000, 4096], dtype=torch.int32, device="cuda")   # row 2 stops before its bad id
+    assert _count_bad(r2t, rows, seq, 9000, slots) == 6

@@ -98,6 +98,10 @@ def test_device_calls_reject_bad_arguments_before_gpu_work():
                                        None) == sp.SGL_ERR_INVALID
     # r2t build: prefix slots without offsets
     assert lib.sgl_build_req_to_token(p, 4, 8, p, 1, p, None, p, p, None, None) == sp.SGL_ERR_INVALID
+    # device index check: missing counter, negative bounds; empty batch is a no-op
+    assert lib.sgl_count_bad_slots(p, 4, 8, p, p, 1, 8, 16, None, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_count_bad_slots(p, 4, 8, p, p, 1, -1, 16, p, None) == sp.SGL_ERR_INVALID
+    assert lib.sgl_count_bad_slots(p, 4, 8, p, p, 0, 8, 16, p, None) == sp.SGL_OK
     # empty batches are a no-op
     assert lib.sgl_decode_attn(sp.SGL_BF16, p, None, None, p, p, 16, p, 1, 8, p, p, 0, 8, 32, 8, 128,
                                0.1, p, None, None, 0, None) == sp.SGL_OK
