@@ -100,6 +100,20 @@ size_t part_bytes(int64_t B, int64_t S, int64_t Hq, int64_t D) {
     return align_up((size_t)(B * S * Hq * D) * sizeof(float)) + align_up((size_t)(B * S * Hq * 2) * sizeof(float));
 }
 
+// Workgroups per head group of the balanced suffix stage: four per compute
+// unit over the whole grid.
+#ifndef SGL_BALANCED_SUFFIX
+#define SGL_BALANCED_SUFFIX 1
+#endif
+constexpr int kBalancedWorkgroups = 1024;
+int64_t balanced_wgs(int32_t Hkv) { return kBalancedWorkgroups / (Hkv >= 4 ? Hkv / 4 : 1); }
+
+// Bytes of the cascade's suffix states: Ss splits per request, or the rows
+// of the balanced suffix stage, whichever is larger (one region serves both).
+size_t suffix_part_bytes(int64_t B, int64_t Ss, int64_t Hq, int64_t Hkv, int64_t D) {
+    return std::max(part_bytes(B, Ss, Hq, D), part_bytes(sk_state_rows(B, balanced_wgs((int32_t)Hkv)), 1, Hq, D));
+}
+
 PartialBuf carve(char *&p, int64_t B, int64_t S, int64_t Hq, int64_t D) {
     PartialBuf pb;
     pb.o = (float *)p;
@@ -424,6 +438,16 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     const bool rows_ok = dtype != SGL_F32 && (Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16) && g <= 16;
     const bool rows_flat = rows_ok && fp8;
     const bool rows_suffix = rows_ok;
+    // Cascade suffix stage in equal runs of the concatenated suffixes
+    // (launch_split_rows_balanced) for bf16 caches with suffixes of about a
+    // suffix split or more: on the 256-request decode workload 582 against
+    // 621 us for the call (one grid); shorter suffixes would cut a run into
+    // many one-request pieces, each paying its own start (the 8-branch fork:
+    // 122 against 75 us at one key), and the FP8 cache measured slower this
+    // way (355 against 343 us), so those keep the split items.
+    const bool balanced = SGL_BALANCED_SUFFIX && cascade && rows_suffix && !fp8 && Hkv % 4 == 0 &&
+                          max_prefix_len > 0 && (int64_t)max_seq_len - max_prefix_len >= kSuffixChunk;
+    const int32_t sk_wgs = (int32_t)balanced_wgs(Hkv);
     // Split sizes.  The cascade's preferred prefix and suffix splits depend on
     // the call's bounds (smaller bounds can prefer smaller splits, hence more
     // split states), so they are doubled, up to kPrefixChunkMax and
@@ -437,8 +461,8 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
         fchunk = rows_suffix ? suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv) : kDecodeChunk;
         auto need_for = [&](int pc, int fc) {
             const int64_t Sp = max_prefix_len > 0 ? ceil_div64(max_prefix_len, pc) : 1;
-            return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, ceil_div64(max_seq_len, fc), Hq, D) +
-                   align_up((size_t)batch * sizeof(int32_t));
+            return part_bytes(batch, Sp, Hq, D) + suffix_part_bytes(batch, ceil_div64(max_seq_len, fc), Hq, Hkv, D) +
+                   align_up((size_t)batch * sizeof(int32_t)) + align_up((size_t)(batch + 2) * sizeof(int64_t));
         };
         while (need_for(pchunk, fchunk) > workspace_bytes) {
             if (fchunk < kSuffixChunk && (fchunk <= pchunk || pchunk >= kPrefixChunkMax)) fchunk *= 2;
@@ -494,12 +518,21 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     const int64_t Ss = ceil_div64(max_seq_len, fchunk);
     PartialBuf flat_part{}, pre_part{}, suf_part{};
     int32_t *suffix_lo = nullptr;
+    int64_t *sk_plan = nullptr;
     if (!cascade) {
         flat_part = carve(wp, batch, ceil_div64(max_seq_len, fchunk), Hq, D);
     } else {
         pre_part = carve(wp, batch, Sp, Hq, D);
+        char *suf_base = wp;
         suf_part = carve(wp, batch, Ss, Hq, D);
+        wp = suf_base + suffix_part_bytes(batch, Ss, Hq, Hkv, D);
         suffix_lo = (int32_t *)wp;
+        wp += align_up((size_t)batch * sizeof(int32_t));
+        sk_plan = (int64_t *)wp;
+        if (balanced) {   // the same bytes as batch + sk_wgs state rows of one split each
+            char *b = suf_base;
+            suf_part = carve(b, sk_state_rows(batch, sk_wgs), 1, Hq, D);
+        }
     }
     // Both cascade stages in one grid when the shape allows it (D 128, KV
     // heads in groups of 4) and the suffix items are the longer ones: a
@@ -513,7 +546,7 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     // 8-branch fork (prefix items longer) one grid with the prefix items
     // first loses to two launches as the suffixes grow (139 against 129 us at
     // 512 keys), so such calls keep one launch per stage.
-    const bool one_grid = cascade && max_prefix_len > 0 && rows_suffix && D == 128 && Hkv % 4 == 0 &&
+    const bool one_grid = !balanced && cascade && max_prefix_len > 0 && rows_suffix && D == 128 && Hkv % 4 == 0 &&
                           3 * fchunk > pchunk;
     // The current token's K/V, and (cascade) each request's suffix start,
     // found once for every suffix item and the merge.  A bf16-query cascade
@@ -593,7 +626,14 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     // dispatch some 16,000 empty workgroups).
     const int64_t est = std::max<int64_t>(1, (int64_t)max_seq_len - max_prefix_len);
     const int32_t head = (int32_t)std::min<int64_t>(Ss, 2 * ceil_div64(est, fchunk));
-    if (one_grid) {
+    if (balanced) {
+        if (max_prefix_len > 0 && (rc = run_split(pa, false)) != SGL_OK) return rc;
+        SplitArgs sx = sa;
+        sx.sk_wgs = sk_wgs;
+        sx.chunk = kSuffixChunk;
+        if ((rc = launch_split_rows_balanced(sx, fp8, sk_plan, st)) != SGL_OK) return rc;
+        m.sk_plan = sk_plan;
+    } else if (one_grid) {
         SplitArgs sx = sa;
         sx.xcd_block = 1;
         if ((rc = launch_cascade_split(pa, sx, head, fp8, st)) != SGL_OK) return rc;
@@ -639,8 +679,9 @@ size_t sgl_cascade_workspace_size(int32_t batch, int32_t G, int32_t max_seq_len,
                            ? ceil_div64(max_prefix_len, prefix_chunk(G, max_group_size, max_prefix_len, Hq, Hkv, D))
                            : 1;
     const int64_t Ss = ceil_div64(max_seq_len, suffix_chunk(batch, max_seq_len, max_prefix_len, Hkv));
-    // split states of both stages, then each request's suffix start
-    return part_bytes(batch, Sp, Hq, D) + part_bytes(batch, Ss, Hq, D) + align_up((size_t)batch * sizeof(int32_t));
+    // split states of both stages, each request's suffix start, the balanced suffix stage's plan
+    return part_bytes(batch, Sp, Hq, D) + suffix_part_bytes(batch, Ss, Hq, Hkv, D) +
+           align_up((size_t)batch * sizeof(int32_t)) + align_up((size_t)(batch + 2) * sizeof(int64_t));
 }
 
 int sgl_cascade_decode_attn(int dtype, const void *q, const void *k_new, const void *v_new, void *k_pool,

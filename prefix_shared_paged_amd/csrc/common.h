@@ -204,9 +204,17 @@ struct SplitArgs {
                                    // non-empty items of the later rounds that share its id modulo
                                    // the grid
     PartialBuf part;
+    // Balanced suffix stage (launch_split_rows_balanced): plan[r] = first
+    // suffix key of request r in the concatenation of all requests' suffixes
+    // (r <= batch; plan[batch] = their total), plan[batch + 1] = keys per
+    // workgroup; sk_wgs workgroups per head group
+    const int64_t *sk_plan;
+    int32_t sk_wgs;
     DecodeStoreArgs store;         // kind 1 (launch_split_bf16 / _fp8), optional: a decode
                                    // store run by leading workgroups of the launch
 };
+
+int launch_split_rows_balanced(const SplitArgs &a, bool fp8, int64_t *plan, hipStream_t st);
 
 // Keys per split of a small-q extend request with L keys cut into n_spl
 // splits (whole 16-key tiles); the split kernel and the merge both use it.
@@ -256,7 +264,15 @@ struct MergeArgs {
     int32_t Hkv;           // kind 5: query rows of a tile follow from Hq / Hkv
     int64_t row_stride;    // kind 5: bound on a context (keys past it are not read)
     const int32_t *suffix_lo;   // kind 3, optional: as SplitArgs::suffix_lo
+    const int64_t *sk_plan;     // kind 3, optional: suffix states of a balanced suffix stage (SplitArgs::sk_plan)
 };
+
+// Balanced suffix stage: the piece of request r that workgroup w takes (its
+// run's part inside r) leaves its states in row r + w of the suffix buffer.
+// Runs and requests both follow the concatenated suffixes, so of two pieces
+// the later one has the larger r or the larger w and never a smaller one:
+// the rows are distinct, and below batch + workgroups.
+__host__ __device__ __forceinline__ int64_t sk_state_rows(int64_t batch, int64_t wgs) { return batch + wgs; }
 int launch_merge(const MergeArgs &a, hipStream_t st);
 
 // Row moves between a page-locked host tier and the pool (kernels_hicache.hip).

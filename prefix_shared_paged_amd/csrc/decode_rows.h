@@ -60,6 +60,11 @@ __device__ __forceinline__ bool rows_item_live(const SplitArgs &a, int HPW, int 
     return s < ceil_div64(hi - lo, a.chunk);
 }
 
+template <int D, bool FP8, int HPW, bool LONG = false>
+__device__ __forceinline__ void rows_segment(const SplitArgs &a, int tid, int set, int hg, int64_t ref_row,
+                                             int64_t k0, int nk, int64_t part_row, unsigned char *k_lds,
+                                             unsigned char *v_lds, int32_t *slot_lds);
+
 // HPW waves per workgroup, one per KV head of the head group hg: the
 // workgroup loads the group's HPW * D * elt bytes of every row (the whole row
 // when HPW = Hkv).
@@ -73,6 +78,49 @@ __device__ __forceinline__ bool rows_item_live(const SplitArgs &a, int HPW, int 
 template <int D, bool FP8, int HPW>
 __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, int tid, unsigned char *k_lds,
                                            unsigned char *v_lds, int32_t *slot_lds) {
+    // ---- work item (uniform over the workgroup): split s of (request, head group)
+    // The work sets are v = hg * n_sets + request; they form blocks of rb
+    // consecutive ones (one head group of rb consecutive requests).
+    // Workgroups go to the 8 XCDs round-robin by id (id % 8 is the XCD), and
+    // each XCD runs its workgroups in id order.  Split round s gives block b
+    // to XCD (b + s) % 8: the rotation spreads every set's splits over the
+    // XCDs (an XCD's total work does not hang on the lengths of a few
+    // requests), and with rb > 1 sibling requests (adjacent in the batch)
+    // still read the prefix rows of one split through one XCD's L2.  Rounds
+    // are in order, so every set's first split starts before any second one.
+    const int ng = a.Hkv / HPW;
+    const int n_v = a.n_sets * ng;
+    int s, v;
+    rows_item(a, HPW, bid, s, v);
+    if (s >= a.max_splits || v >= n_v) return;
+    const int set = v % a.n_sets, hg = v / a.n_sets;
+    const int64_t L = a.seq_lens[set];
+    const int64_t ref_row = a.req_rows[set];
+    int64_t lo = 0, hi = L;
+    if (a.kind == 2) {
+        const int64_t P = a.suffix_lo ? a.suffix_lo[set] : a.group_prefix_len[wave_find_group(a.group_ptr, a.G, set)];
+        lo = P < 0 ? 0 : (P > L ? L : P);
+    }
+    if (ref_row < 0 || ref_row >= a.num_rows) return;
+    if (hi > a.row_stride) hi = a.row_stride;
+    const int64_t n_split = ceil_div64(hi - lo, a.chunk);
+    if (s >= n_split || s >= a.part.S) return;
+    const int64_t k0 = lo + (int64_t)s * a.chunk;
+    const int nk = (int)((k0 + a.chunk < hi ? k0 + a.chunk : hi) - k0);
+    rows_segment<D, FP8, HPW>(a, tid, set, hg, ref_row, k0, nk, (int64_t)set * a.part.S + s, k_lds, v_lds,
+                              slot_lds);
+}
+
+// Keys [k0, k0 + nk) of request `set`'s row ref_row for the KV heads of head
+// group hg: the tile loop of one work item, writing the partial state of
+// every query row to state row `part_row` of a.part (index part_row * Hq +
+// query head).  Uniform over the workgroup.  The slot table holds a.chunk
+// ids (a multiple of the tile): nk <= a.chunk, or, with LONG, any nk, the
+// table then being refilled every a.chunk keys.
+template <int D, bool FP8, int HPW, bool LONG>
+__device__ __forceinline__ void rows_segment(const SplitArgs &a, int tid, int set, int hg, int64_t ref_row,
+                                             int64_t k0, int nk, int64_t part_row, unsigned char *k_lds,
+                                             unsigned char *v_lds, int32_t *slot_lds) {
     constexpr int ELT = FP8 ? 1 : 2;
     constexpr int T = FP8 ? 32 : 16;        // keys per tile
     constexpr int R = HPW * D * ELT;        // bytes of one tile row (the group's heads of a slot)
@@ -93,42 +141,18 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, int tid,
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-
-    // ---- work item (uniform over the workgroup): split s of (request, head group)
-    // The work sets are v = hg * n_sets + request; they form blocks of rb
-    // consecutive ones (one head group of rb consecutive requests).
-    // Workgroups go to the 8 XCDs round-robin by id (id % 8 is the XCD), and
-    // each XCD runs its workgroups in id order.  Split round s gives block b
-    // to XCD (b + s) % 8: the rotation spreads every set's splits over the
-    // XCDs (an XCD's total work does not hang on the lengths of a few
-    // requests), and with rb > 1 sibling requests (adjacent in the batch)
-    // still read the prefix rows of one split through one XCD's L2.  Rounds
-    // are in order, so every set's first split starts before any second one.
-    const int ng = a.Hkv / HPW;
-    const int n_v = a.n_sets * ng;
-    int s, v;
-    rows_item(a, HPW, bid, s, v);
-    if (s >= a.max_splits || v >= n_v) return;
-    const int set = v % a.n_sets, hg = v / a.n_sets;
     const int kvh = hg * HPW + w;                   // KV head of this wave
-    const int64_t L = a.seq_lens[set];
-    const int64_t ref_row = a.req_rows[set];
-    int64_t lo = 0, hi = L;
-    if (a.kind == 2) {
-        const int64_t P = a.suffix_lo ? a.suffix_lo[set] : a.group_prefix_len[wave_find_group(a.group_ptr, a.G, set)];
-        lo = P < 0 ? 0 : (P > L ? L : P);
-    }
-    if (ref_row < 0 || ref_row >= a.num_rows) return;
-    if (hi > a.row_stride) hi = a.row_stride;
-    const int64_t n_split = ceil_div64(hi - lo, a.chunk);
-    if (s >= n_split || s >= a.part.S) return;
-    const int64_t k0 = lo + (int64_t)s * a.chunk;
-    const int nk = (int)((k0 + a.chunk < hi ? k0 + a.chunk : hi) - k0);
     const int N = (nk + T - 1) / T;                 // tiles, >= 1
     const int g = a.Hq / a.Hkv;                     // query rows of this wave (<= 16)
 
     const int32_t *row = a.r2t + ref_row * a.row_stride + k0;
-    for (int j = tid; j < nk; j += 64 * HPW) slot_lds[j] = safe_slot(row[j], a.num_slots);
+    // LONG: the table holds keys [sub, sub + a.chunk) of the segment
+    int sub = 0;
+    auto fill = [&](int base) {
+        const int cnt = LONG ? min(nk - base, a.chunk) : nk;
+        for (int j = tid; j < cnt; j += 64 * HPW) slot_lds[j] = safe_slot(row[base + j], a.num_slots);
+    };
+    fill(0);
 
     const int n16 = lane & 15, kq = lane >> 4;
 
@@ -165,7 +189,7 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, int tid,
 #pragma unroll
         for (int u = 0; u < NIW; u++) {
             const int kk = min(n * T + lrow[u], nk - 1);   // past the split end: repeat the last key
-            const char *src = pool + (int64_t)slot_lds[kk] * pool_row + lsrc[u];
+            const char *src = pool + (int64_t)slot_lds[LONG ? kk - sub : kk] * pool_row + lsrc[u];
             __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
                                              (SGL_LDS void *)(dst + (u * HPW + w) * 1024), 16, 0, 2 /* nt */);
         }
@@ -292,6 +316,13 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, int tid,
         s_tile(sacc);
         if (n + 1 < N) {
             barrier();                               // every wave has read the K tile
+            if (LONG && (n + 1) * T - sub == a.chunk) {
+                // tile n + 1 starts the next a.chunk keys: every wave is done
+                // with this table (tile n's loads went out in the last pass)
+                sub += a.chunk;
+                fill(sub);
+                __syncthreads();
+            }
             issue(n + 1, kp, k_lds);
         }
         pv_tile(n, sacc);
@@ -308,7 +339,7 @@ __device__ __forceinline__ void rows_split(const SplitArgs &a, int bid, int tid,
     if (n16 >= g) return;
     const float vscale = FP8 ? a.v_scale[kvh] : 1.f;
     const int h = kvh * g + n16;
-    const int64_t idx = ((int64_t)set * a.part.S + s) * a.Hq + h;
+    const int64_t idx = part_row * a.Hq + h;
     float *op = a.part.o + idx * D;
 #pragma unroll
     for (int db = 0; db < DB; db++) *(f32x4 *)(op + db * 16 + kq * 4) = FP8 ? oacc[db] * vscale : oacc[db];

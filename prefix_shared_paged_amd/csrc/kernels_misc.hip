@@ -324,6 +324,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
 
     // parts: [prefix splits of r][suffix (or flat) splits of r]
     int np = 0, ns;
+    int64_t sk_w0 = 0;      // balanced suffix stage: the first run covering r
     if (a.kind == 4 || a.kind == 5) {
         // token r of request rq = the last rq with q_off[rq] <= r
         int lo = 0, hi = a.n_req - 1;
@@ -351,25 +352,37 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
             int64_t P = a.suffix_lo ? a.suffix_lo[r] : a.group_prefix_len[wave_find_group(a.group_ptr, a.G, r)];
             P = P < 0 ? 0 : (P > L ? L : P);
             np = (int)ceil_div64(P, a.chunk_prefix);
-            ns = (int)ceil_div64(L - P, a.chunk_flat);
+            if (a.sk_plan) {
+                // balanced suffix stage: the pieces of r are rows r + w of
+                // the runs w that cover its suffix keys
+                const int64_t off = a.sk_plan[r], nxt = a.sk_plan[r + 1], C = a.sk_plan[a.batch + 1];
+                sk_w0 = nxt > off ? off / C : 0;
+                ns = nxt > off ? (int)((nxt - 1) / C - sk_w0 + 1) : 0;
+            } else {
+                ns = (int)ceil_div64(L - P, a.chunk_flat);
+            }
         } else {
             ns = (int)ceil_div64(L, a.chunk_flat);
         }
     }
     if (np > a.prefix.S) np = a.prefix.S;
-    if (ns > a.flat_or_suffix.S) ns = a.flat_or_suffix.S;
+    const bool sk = a.kind == 3 && a.sk_plan;
+    if (!sk && ns > a.flat_or_suffix.S) ns = a.flat_or_suffix.S;
     const int total = np + ns;
 
+    // state row of part s
+    auto row_of = [&](int s) -> int64_t {
+        if (s < np) return (int64_t)r * a.prefix.S + s;
+        return sk ? r + sk_w0 + (s - np) : (int64_t)r * a.flat_or_suffix.S + (s - np);
+    };
     auto ml_of = [&](int s) -> float2 {
         const PartialBuf &pb = s < np ? a.prefix : a.flat_or_suffix;
-        const int ss = s < np ? s : s - np;
-        const float *p = pb.ml + (((int64_t)r * pb.S + ss) * a.Hq + h) * 2;
+        const float *p = pb.ml + (row_of(s) * a.Hq + h) * 2;
         return make_float2(p[0], p[1]);
     };
     auto o_of = [&](int s) -> const float * {
         const PartialBuf &pb = s < np ? a.prefix : a.flat_or_suffix;
-        const int ss = s < np ? s : s - np;
-        return pb.o + (((int64_t)r * pb.S + ss) * a.Hq + h) * D;
+        return pb.o + (row_of(s) * a.Hq + h) * D;
     };
 
     constexpr int PER = D / 64;

@@ -77,3 +77,44 @@ def test_cascade_random_shapes(seed, fp8):
     print(f"random cascade seed={seed} fp8={fp8} Hq={s.Hq} Hkv={s.Hkv} D={s.D} B={wl.B} G={wl.G}: "
           f"max abs err {err:.3e}, lse err {lerr:.2e}", flush=True)
     assert err <= BF16_TOL and lerr <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# balanced suffix stage: bf16 calls whose suffixes reach 1024 keys or more
+# (max_seq_len - max_prefix_len >= 1024) lay the suffixes end to end and give
+# every workgroup an equal run; runs cross requests, long suffixes span many
+# runs (the merge then has more parts than its one-round form holds), and
+# one-key suffixes sit between long ones
+# ---------------------------------------------------------------------------
+def _balanced_workload(seed, Hq, Hkv, D, n_req=48):
+    rng = np.random.default_rng(8100 + seed)
+    prefixes = np.array([0, 1, 300, 1000, 2047, 64], np.int64)
+    members = np.full(len(prefixes), n_req // len(prefixes))
+    grp = np.concatenate([np.full(m, g) for g, m in enumerate(members)]).astype(np.int64)
+    sib = np.concatenate([np.arange(m) for m in members]).astype(np.int64)
+    suf = rng.integers(1, 3200, size=len(grp))
+    suf[::7] = 1                                   # the current token only
+    suf[3::11] = int(rng.integers(3000, 4000))     # long suffixes over many runs
+    L = np.array([prefixes[g] + s for g, s in zip(grp, suf)], np.int64)
+    spec = W.Spec("balanced_suffix", "bf16", Hq, Hkv, D, 1, 1 << 18, 0.5, 8200 + seed)
+    return W.GroupWorkload(spec, prefixes, grp, sib, L)
+
+
+@pytest.mark.parametrize("store", [True, False])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 4, 128), (16, 16, 128), (16, 4, 64)])
+def test_cascade_balanced_suffix(Hq, Hkv, D, store):
+    wl = _balanced_workload(Hkv + D, Hq, Hkv, D)
+    assert int(wl.ctx_len.max() - wl.prefix_len.max()) >= 1024
+    case = GroupCase(wl)
+    # store: the cascade call stores the current tokens; else the flat call
+    # stores them and the cascade call (o_c) reads them from the pool
+    res = run_decode(case, wl.ctx_len.copy(), cascade=True, both=not store)
+    case.check_r2t()
+    _check_current_rows(case, res)
+    reqs, O, LSE = oracle_decode(case, res)
+    o, l = (res["o"], res["lse"]) if store else (res["o_c"], res["lse_c"])
+    err = bf16_err(o[reqs], O)
+    lerr = float(np.max(np.abs(l[reqs] - LSE)))
+    print(f"balanced suffix Hq={Hq} Hkv={Hkv} D={D} store={store} B={wl.B}: max abs err {err:.3e}, "
+          f"lse err {lerr:.2e}", flush=True)
+    assert err <= BF16_TOL and lerr <= LSE_TOL
