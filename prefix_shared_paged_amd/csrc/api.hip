@@ -102,9 +102,6 @@ size_t part_bytes(int64_t B, int64_t S, int64_t Hq, int64_t D) {
 
 // Workgroups per head group of the balanced suffix stage: four per compute
 // unit over the whole grid.
-#ifndef SGL_BALANCED_SUFFIX
-#define SGL_BALANCED_SUFFIX 1
-#endif
 constexpr int kBalancedWorkgroups = 1024;
 int64_t balanced_wgs(int32_t Hkv) { return kBalancedWorkgroups / (Hkv >= 4 ? Hkv / 4 : 1); }
 
@@ -438,15 +435,19 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     const bool rows_ok = dtype != SGL_F32 && (Hkv == 2 || Hkv == 4 || Hkv == 8 || Hkv == 16) && g <= 16;
     const bool rows_flat = rows_ok && fp8;
     const bool rows_suffix = rows_ok;
-    // Cascade suffix stage in equal runs of the concatenated suffixes
-    // (launch_split_rows_balanced) for bf16 caches with suffixes of about a
-    // suffix split or more: on the 256-request decode workload 582 against
-    // 621 us for the call (one grid); shorter suffixes would cut a run into
-    // many one-request pieces, each paying its own start (the 8-branch fork:
-    // 122 against 75 us at one key), and the FP8 cache measured slower this
-    // way (355 against 343 us), so those keep the split items.
-    const bool balanced = SGL_BALANCED_SUFFIX && cascade && rows_suffix && !fp8 && Hkv % 4 == 0 &&
-                          max_prefix_len > 0 && (int64_t)max_seq_len - max_prefix_len >= kSuffixChunk;
+    // Cascade suffix stage in equal runs of the concatenated suffixes, the
+    // prefix items behind them in the same grid (launch_cascade_balanced),
+    // for bf16 caches (D 128, KV heads in groups of 4) with suffixes of about
+    // a suffix split or more.  On the 256-request decode workload the call
+    // takes 576-580 us this way against 618-625 us with the one grid of split
+    // items, and 586 us with the prefix stage in a launch of its own before
+    // the runs (600 us with the prefix items first in the grid).  Shorter
+    // suffixes would cut a run into many one-request pieces, each paying its
+    // own start (the 8-branch fork: 122 against 75 us at one key), and the
+    // FP8 cache measured slower this way (355 against 343 us), so those keep
+    // the split items.
+    const bool balanced = cascade && rows_suffix && !fp8 && D == 128 && Hkv % 4 == 0 && max_prefix_len > 0 &&
+                          (int64_t)max_seq_len - max_prefix_len >= kSuffixChunk;
     const int32_t sk_wgs = (int32_t)balanced_wgs(Hkv);
     // Split sizes.  The cascade's preferred prefix and suffix splits depend on
     // the call's bounds (smaller bounds can prefer smaller splits, hence more
@@ -555,9 +556,14 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     // every group prefix ends before its requests' current positions);
     // otherwise they take a kernel of their own before the attention.
     SuffixStartArgs ss;
+    std::memset(&ss, 0, sizeof ss);
     ss.group_ptr = group_ptr; ss.group_prefix_len = group_prefix_len; ss.seq_lens = seq_lens;
     ss.G = G; ss.batch = batch; ss.lo = suffix_lo;
-    const bool carry_store = cascade && max_prefix_len > 0 && !one_grid && dtype == SGL_BF16;
+    if (balanced) {   // and the balanced stage's plan, by one more workgroup of the same launch
+        ss.plan = sk_plan; ss.plan_wgs = sk_wgs; ss.req_rows = req_rows; ss.num_rows = num_rows;
+        ss.row_stride = row_stride;
+    }
+    const bool carry_store = cascade && max_prefix_len > 0 && !one_grid && !balanced && dtype == SGL_BF16;
     int rc = SGL_OK;
     if (carry_store) {
         // launched with the prefix stage below
@@ -627,11 +633,11 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     const int64_t est = std::max<int64_t>(1, (int64_t)max_seq_len - max_prefix_len);
     const int32_t head = (int32_t)std::min<int64_t>(Ss, 2 * ceil_div64(est, fchunk));
     if (balanced) {
-        if (max_prefix_len > 0 && (rc = run_split(pa, false)) != SGL_OK) return rc;
         SplitArgs sx = sa;
         sx.sk_wgs = sk_wgs;
         sx.chunk = kSuffixChunk;
-        if ((rc = launch_split_rows_balanced(sx, fp8, sk_plan, st)) != SGL_OK) return rc;
+        sx.sk_plan = sk_plan;
+        if ((rc = launch_cascade_balanced(pa, sx, st)) != SGL_OK) return rc;
         m.sk_plan = sk_plan;
     } else if (one_grid) {
         SplitArgs sx = sa;

@@ -94,6 +94,15 @@ struct SuffixStartArgs {
     const int32_t *seq_lens;
     int32_t G, batch;
     int32_t *lo;
+    // Optional: the plan of a balanced suffix stage (launch_cascade_balanced),
+    // by one more workgroup of the launch that writes lo, from the same group
+    // arrays: plan[r] = suffix keys of the requests before r (r <= batch),
+    // plan[batch + 1] = keys per run of plan_wgs runs.  A request's suffix is
+    // [lo, min(seq_lens, row_stride)), empty if its row is outside the table.
+    int64_t *plan;
+    int32_t plan_wgs;
+    const int32_t *req_rows;
+    int64_t num_rows, row_stride;
 };
 int launch_suffix_start(const SuffixStartArgs &a, hipStream_t st);
 
@@ -204,7 +213,7 @@ struct SplitArgs {
                                    // non-empty items of the later rounds that share its id modulo
                                    // the grid
     PartialBuf part;
-    // Balanced suffix stage (launch_split_rows_balanced): plan[r] = first
+    // Balanced suffix stage (launch_cascade_balanced): plan[r] = first
     // suffix key of request r in the concatenation of all requests' suffixes
     // (r <= batch; plan[batch] = their total), plan[batch + 1] = keys per
     // workgroup; sk_wgs workgroups per head group
@@ -214,7 +223,7 @@ struct SplitArgs {
                                    // store run by leading workgroups of the launch
 };
 
-int launch_split_rows_balanced(const SplitArgs &a, bool fp8, int64_t *plan, hipStream_t st);
+int launch_cascade_balanced(const SplitArgs &pa, const SplitArgs &sa, hipStream_t st);
 
 // Keys per split of a small-q extend request with L keys cut into n_spl
 // splits (whole 16-key tiles); the split kernel and the merge both use it.

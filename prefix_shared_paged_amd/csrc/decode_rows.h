@@ -346,4 +346,47 @@ __device__ __forceinline__ void rows_segment(const SplitArgs &a, int tid, int se
     if (kq == 0) *(float2 *)(a.part.ml + idx * 2) = make_float2(m_run, l);
 }
 
+// Run w of the balanced suffix stage for head group hg (see
+// kernels_decode_rows.hip): the keys [w C, (w + 1) C) of the concatenated
+// suffixes (plan = a.sk_plan), piece by piece, each piece's states in row
+// request + w of a.part.  Uniform over the workgroup; each piece takes the
+// thread id and the arguments through values the compiler cannot see
+// through, so that nothing derived from them stays live across the loop.
+typedef const __attribute__((address_space(4))) SplitArgs *KArgs;   // arguments in the kernarg segment
+template <int D, bool FP8, int HPW>
+__device__ __forceinline__ void balanced_run(KArgs ap, int64_t w, int hg, unsigned char *k_lds,
+                                             unsigned char *v_lds, int32_t *slot_lds) {
+    const SplitArgs &a = *(const SplitArgs *)ap;
+    const int64_t *plan = a.sk_plan;
+    const int64_t total = plan[a.batch], C = plan[a.batch + 1];
+    int64_t p = w * C;
+    const int64_t end = p + C < total ? p + C : total;
+    if (p >= end) return;
+    // the request holding key p: the last r < batch with plan[r] <= p (plan
+    // ascends from plan[0] = 0); 64 entries per ballot
+    const int lane = threadIdx.x & 63;
+    int r = -1;
+    for (int base = 0; base < a.batch; base += 64) {
+        const int i = base + lane;
+        const int c = __popcll(__builtin_amdgcn_ballot_w64(i < a.batch && plan[i] <= p));
+        r += c;
+        if (c < 64) break;
+    }
+    for (;;) {
+        const int64_t r_off = plan[r], r_end = plan[r + 1];
+        const int64_t pe = end < r_end ? end : r_end;
+        const int64_t L = a.seq_lens[r], P = a.suffix_lo[r];
+        const int64_t lo = P < 0 ? 0 : (P > L ? L : P);
+        int tid = (int)threadIdx.x;
+        KArgs kp = ap;
+        asm volatile("" : "+v"(tid), "+s"(kp));
+        rows_segment<D, FP8, HPW, true>(*(const SplitArgs *)kp, tid, r, hg, a.req_rows[r], lo + (p - r_off),
+                                        (int)(pe - p), r + w, k_lds, v_lds, slot_lds);
+        p = pe;
+        if (p >= end) break;
+        while (plan[r + 1] <= p) r++;              // the next request with keys (plan[batch] > p)
+        __syncthreads();                            // tiles and slot table free for the next piece
+    }
+}
+
 }  // namespace sgl_decode

@@ -699,7 +699,54 @@ __global__ void __launch_bounds__(256) cascade_split_kernel(SplitArgs pa, SplitA
     }
 }
 
+// ---- cascade: balanced suffix runs, then the prefix items, in one grid ---------
+// The suffixes of all requests laid end to end, every workgroup of a head
+// group taking an equal run of them (balanced_run, 4 KV heads per
+// workgroup: all of them resident at once, so the grid does not drain as
+// split items of suffix-long work would), and behind them the prefix items
+// (bf16_split, four waves sharing a ring of four tiles), which take the
+// compute units as the runs finish.  The LDS budget is cascade_split_kernel's.
+// sa is the first argument: balanced_run reads it through the kernarg pointer.
+template <int D>
+__global__ void __launch_bounds__(256, 4) cascade_balanced_kernel(SplitArgs sa, SplitArgs pa, unsigned n_bal) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+    constexpr int PTB = TILE * 2 * D;                                   // prefix tile bytes
+    constexpr int STB = 16 * kRowsHeads * D * 2;                         // suffix tile bytes
+    static_assert(8 * PTB == 2 * STB, "one LDS budget");
+    const unsigned id = blockIdx.x;
+    if (id < n_bal) {
+        const unsigned ng = (unsigned)(sa.Hkv / kRowsHeads);
+        balanced_run<D, false, kRowsHeads>((KArgs)__builtin_amdgcn_kernarg_segment_ptr(), id / ng, (int)(id % ng),
+                                           dyn_lds, dyn_lds + STB, (int32_t *)(dyn_lds + 2 * STB));
+    } else {
+        bf16_split<D, 4, 4>(pa, id - n_bal, dyn_lds, dyn_lds + 4 * PTB, (int32_t *)(dyn_lds + 8 * PTB));
+    }
+}
+
 }  // namespace
+
+// bf16 cascade: one grid of the balanced suffix runs (sa.sk_wgs per head
+// group of 4 KV heads) and the prefix items.  The current tokens, the suffix
+// starts and the plan (SuffixStartArgs::plan) must already be written.
+int launch_cascade_balanced(const SplitArgs &pa0, const SplitArgs &sa, hipStream_t st) {
+    if (pa0.kind != 1 || sa.kind != 2 || !sa.suffix_lo || !sa.sk_plan || sa.sk_wgs < 1 || sa.part.S != 1)
+        return SGL_ERR_INVALID;
+    if (pa0.D != sa.D || pa0.Hkv != sa.Hkv || pa0.Hq != sa.Hq) return SGL_ERR_INVALID;
+    if (sa.D != 128 || sa.Hkv % kRowsHeads != 0 || sa.Hkv > 16 || sa.Hq / sa.Hkv > 16) return SGL_ERR_UNSUPPORTED;
+    if (pa0.chunk % TILE != 0 || sa.chunk % TILE != 0) return SGL_ERR_INVALID;
+    SplitArgs pa = pa0;
+    pa.row_blocks = (pa.max_members * (pa.Hq / pa.Hkv) + 15) / 16;
+    const int64_t n_rbg = (pa.row_blocks + 3) / 4;
+    const int64_t p_items = (int64_t)pa.n_sets * pa.max_splits * pa.Hkv;
+    const int64_t n_pre = ceil_div64(p_items, 8) * 8 * n_rbg;
+    const int64_t n_bal = (int64_t)sa.sk_wgs * (sa.Hkv / kRowsHeads);
+    if (n_pre + n_bal > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
+    const int64_t p_slots = min(pa.chunk, kSlotTab);
+    const size_t dyn = 32768 + (size_t)(p_slots > sa.chunk ? p_slots : sa.chunk) * sizeof(int32_t);
+    hipLaunchKernelGGL((cascade_balanced_kernel<128>), dim3((unsigned)(n_pre + n_bal)), dim3(256), dyn, st, sa, pa,
+                       (unsigned)n_bal);
+    return hip_status(hipGetLastError());
+}
 
 int launch_cascade_split(const SplitArgs &pa0, const SplitArgs &sa, int32_t head_rounds, bool fp8, hipStream_t st) {
     if (pa0.kind != 1 || sa.kind != 2) return SGL_ERR_INVALID;

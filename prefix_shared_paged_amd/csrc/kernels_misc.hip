@@ -96,14 +96,22 @@ int launch_count_bad_slots(const int32_t *r2t, int64_t num_rows, int64_t row_str
 // is decode_store_job (store_util.h), which a cascade call may instead hand
 // to the leading workgroups of its prefix-stage launch.
 // ---------------------------------------------------------------------------
+// The suffix starts; with a.plan the last workgroup computes the balanced
+// suffix stage's plan instead.
 __global__ void __launch_bounds__(256) suffix_start_kernel(SuffixStartArgs a) {
-    suffix_starts(a, blockIdx.x, gridDim.x);
+    const unsigned n = gridDim.x - (a.plan ? 1u : 0u);
+    if (blockIdx.x >= n) {
+        balanced_plan(a);
+        return;
+    }
+    suffix_starts(a, blockIdx.x, n);
 }
 
 int launch_suffix_start(const SuffixStartArgs &a, hipStream_t st) {
     if (a.batch <= 0) return SGL_OK;
-    if (a.G < 1 || !a.lo) return SGL_ERR_INVALID;
-    hipLaunchKernelGGL(suffix_start_kernel, dim3((unsigned)ceil_div64(a.batch, 256)), dim3(256), 0, st, a);
+    if (a.G < 1 || !a.lo || (a.plan && a.plan_wgs < 1)) return SGL_ERR_INVALID;
+    const unsigned n = (unsigned)ceil_div64(a.batch, 256) + (a.plan ? 1u : 0u);
+    hipLaunchKernelGGL(suffix_start_kernel, dim3(n), dim3(256), 0, st, a);
     return hip_status(hipGetLastError());
 }
 
@@ -147,7 +155,12 @@ __global__ void __launch_bounds__(256) store_kv_kernel(
 
 template <int ELT, bool FP8>
 __global__ void __launch_bounds__(256) decode_store_kernel(DecodeStoreArgs d) {
-    decode_store_job<ELT, FP8>(d, blockIdx.x, gridDim.x);
+    const unsigned n = gridDim.x - (d.ss.plan ? 1u : 0u);   // the last workgroup: the plan (launch_decode_store)
+    if (blockIdx.x >= n) {
+        balanced_plan(d.ss);
+        return;
+    }
+    decode_store_job<ELT, FP8>(d, blockIdx.x, n);
 }
 
 DecodeStoreArgs decode_store_args(int elt, bool fp8, const void *k_new, const void *v_new, int64_t n_tokens,
@@ -187,7 +200,8 @@ static int launch_decode_store(const DecodeStoreArgs &d, hipStream_t st) {
     if (d.n_tokens == 0) return SGL_OK;
     if (d.fp8 && (!d.k_scale || !d.v_scale)) return SGL_ERR_INVALID;
     const int64_t store_wgs = std::min<int64_t>(ceil_div64(d.n_tokens * d.row_chunks, 256), 8192);
-    const dim3 grid((unsigned)(store_wgs + (d.ss.lo ? ceil_div64(d.ss.batch, 256) : 0)));
+    if (d.ss.plan && (!d.ss.lo || d.ss.plan_wgs < 1)) return SGL_ERR_INVALID;
+    const dim3 grid((unsigned)(store_wgs + (d.ss.lo ? ceil_div64(d.ss.batch, 256) : 0) + (d.ss.plan ? 1 : 0)));
     if (!d.fp8) hipLaunchKernelGGL((decode_store_kernel<2, false>), grid, dim3(256), 0, st, d);
     else if (d.elt == 2) hipLaunchKernelGGL((decode_store_kernel<2, true>), grid, dim3(256), 0, st, d);
     else hipLaunchKernelGGL((decode_store_kernel<4, true>), grid, dim3(256), 0, st, d);

@@ -39,6 +39,57 @@ __device__ __forceinline__ void suffix_starts(const SuffixStartArgs &a, unsigned
     }
 }
 
+// The plan of a balanced suffix stage (a.plan; see SuffixStartArgs), by one
+// workgroup of any whole number of waves (at most 16): thread t takes a run
+// of consecutive requests, finds each one's group as suffix_starts does, and
+// the runs' sums are scanned within each wave and then over the waves.
+__device__ __forceinline__ int64_t plan_suffix_len(const SuffixStartArgs &a, int64_t r) {
+    const int lane = threadIdx.x & 63;
+    int cnt = 0;
+    for (int base = 0; base < a.G; base += 64) {
+        const int gp = base + lane < a.G ? a.group_ptr[base + lane] : INT_MAX;
+        const int n = a.G - base < 64 ? a.G - base : 64;
+        for (int j = 0; j < n; j++) cnt += __builtin_amdgcn_readlane(gp, j) <= r ? 1 : 0;
+    }
+    if (r >= a.batch) return 0;
+    const int64_t L = a.seq_lens[r], row = a.req_rows[r];
+    if (row < 0 || row >= a.num_rows || L <= 0) return 0;
+    const int64_t P = a.group_prefix_len[cnt > 0 ? cnt - 1 : 0];
+    const int64_t lo = P < 0 ? 0 : (P > L ? L : P), hi = L < a.row_stride ? L : a.row_stride;
+    return hi > lo ? hi - lo : 0;
+}
+
+__device__ __forceinline__ void balanced_plan(const SuffixStartArgs &a) {
+    __shared__ int64_t wave_tot[16];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, nw = blockDim.x >> 6;
+    const int64_t per = ceil_div64(a.batch, blockDim.x);
+    const int64_t r0 = (int64_t)t * per;
+    int64_t sum = 0;
+    for (int64_t i = 0; i < per; i++) sum += plan_suffix_len(a, r0 + i);   // every lane runs every step
+    int64_t x = sum;                                 // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_tot[wv] = x;
+    __syncthreads();
+    int64_t run = x - sum;
+    for (int i = 0; i < wv; i++) run += wave_tot[i];
+    for (int64_t i = 0; i < per; i++) {
+        const int64_t len = plan_suffix_len(a, r0 + i);
+        if (r0 + i < a.batch) a.plan[r0 + i] = run;
+        run += len;
+    }
+    if (t == 0) {
+        int64_t total = 0;
+        for (int i = 0; i < nw; i++) total += wave_tot[i];
+        a.plan[a.batch] = total;
+        const int64_t c = ceil_div64(total > 0 ? total : 1, a.plan_wgs);
+        a.plan[a.batch + 1] = ceil_div64(c, 16) * 16;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // FP8 codes of 16 inputs (ELT bytes each: 2 = bf16, 4 = fp32) with the factor
 // sc of their KV head ("SGLang 深度拆解" section 4.3 keeps the KV cache in FP8):
