@@ -437,16 +437,15 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
     const bool rows_suffix = rows_ok;
     // Cascade suffix stage in equal runs of the concatenated suffixes, the
     // prefix items behind them in the same grid (launch_cascade_balanced),
-    // for bf16 caches (D 128, KV heads in groups of 4) with suffixes of about
-    // a suffix split or more.  On the 256-request decode workload the call
-    // takes 576-580 us this way against 618-625 us with the one grid of split
-    // items, and 586 us with the prefix stage in a launch of its own before
-    // the runs (600 us with the prefix items first in the grid).  Shorter
-    // suffixes would cut a run into many one-request pieces, each paying its
-    // own start (the 8-branch fork: 122 against 75 us at one key), and the
-    // FP8 cache measured slower this way (355 against 343 us), so those keep
-    // the split items.
-    const bool balanced = cascade && rows_suffix && !fp8 && D == 128 && Hkv % 4 == 0 && max_prefix_len > 0 &&
+    // for D 128 with KV heads in groups of 4 and suffixes of about a suffix
+    // split or more.  On the 256-request decode workload the call takes
+    // 576-580 us this way against 618-625 us with the one grid of split items
+    // (FP8 cache: 336-337 against 343-345 us), and 586 us with the prefix
+    // stage in a launch of its own before the runs (600 us with the prefix
+    // items first in the grid).  Shorter suffixes would cut a run into many
+    // one-request pieces, each paying its own start (the 8-branch fork: 122
+    // against 75 us at one key), so those keep the split items.
+    const bool balanced = cascade && rows_suffix && D == 128 && Hkv % 4 == 0 && max_prefix_len > 0 &&
                           (int64_t)max_seq_len - max_prefix_len >= kSuffixChunk;
     const int32_t sk_wgs = (int32_t)balanced_wgs(Hkv);
     // Split sizes.  The cascade's preferred prefix and suffix splits depend on
@@ -637,7 +636,7 @@ int decode_common(bool cascade, bool fp8, int dtype, const void *q, const void *
         sx.sk_wgs = sk_wgs;
         sx.chunk = kSuffixChunk;
         sx.sk_plan = sk_plan;
-        if ((rc = launch_cascade_balanced(pa, sx, st)) != SGL_OK) return rc;
+        if ((rc = launch_cascade_balanced(pa, sx, fp8, st)) != SGL_OK) return rc;
         m.sk_plan = sk_plan;
     } else if (one_grid) {
         SplitArgs sx = sa;

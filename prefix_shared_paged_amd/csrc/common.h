@@ -223,7 +223,7 @@ struct SplitArgs {
                                    // store run by leading workgroups of the launch
 };
 
-int launch_cascade_balanced(const SplitArgs &pa, const SplitArgs &sa, hipStream_t st);
+int launch_cascade_balanced(const SplitArgs &pa, const SplitArgs &sa, bool fp8, hipStream_t st);
 
 // Keys per split of a small-q extend request with L keys cut into n_spl
 // splits (whole 16-key tiles); the split kernel and the merge both use it.

@@ -707,19 +707,21 @@ __global__ void __launch_bounds__(256) cascade_split_kernel(SplitArgs pa, SplitA
 // (bf16_split, four waves sharing a ring of four tiles), which take the
 // compute units as the runs finish.  The LDS budget is cascade_split_kernel's.
 // sa is the first argument: balanced_run reads it through the kernarg pointer.
-template <int D>
+template <int D, bool FP8>
 __global__ void __launch_bounds__(256, 4) cascade_balanced_kernel(SplitArgs sa, SplitArgs pa, unsigned n_bal) {
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
-    constexpr int PTB = TILE * 2 * D;                                   // prefix tile bytes
-    constexpr int STB = 16 * kRowsHeads * D * 2;                         // suffix tile bytes
+    constexpr int PTB = FP8 ? TILE8 * D : TILE * 2 * D;                 // prefix tile bytes
+    constexpr int STB = (FP8 ? 32 : 16) * kRowsHeads * D * (FP8 ? 1 : 2);   // suffix tile bytes
     static_assert(8 * PTB == 2 * STB, "one LDS budget");
     const unsigned id = blockIdx.x;
     if (id < n_bal) {
         const unsigned ng = (unsigned)(sa.Hkv / kRowsHeads);
-        balanced_run<D, false, kRowsHeads>((KArgs)__builtin_amdgcn_kernarg_segment_ptr(), id / ng, (int)(id % ng),
-                                           dyn_lds, dyn_lds + STB, (int32_t *)(dyn_lds + 2 * STB));
+        balanced_run<D, FP8, kRowsHeads>((KArgs)__builtin_amdgcn_kernarg_segment_ptr(), id / ng, (int)(id % ng),
+                                         dyn_lds, dyn_lds + STB, (int32_t *)(dyn_lds + 2 * STB));
     } else {
-        bf16_split<D, 4, 4>(pa, id - n_bal, dyn_lds, dyn_lds + 4 * PTB, (int32_t *)(dyn_lds + 8 * PTB));
+        int32_t *slots = (int32_t *)(dyn_lds + 8 * PTB);
+        if constexpr (FP8) fp8_split<D, 4, 4>(pa, id - n_bal, dyn_lds, dyn_lds + 4 * PTB, slots);
+        else bf16_split<D, 4, 4>(pa, id - n_bal, dyn_lds, dyn_lds + 4 * PTB, slots);
     }
 }
 
@@ -728,12 +730,14 @@ __global__ void __launch_bounds__(256, 4) cascade_balanced_kernel(SplitArgs sa, 
 // bf16 cascade: one grid of the balanced suffix runs (sa.sk_wgs per head
 // group of 4 KV heads) and the prefix items.  The current tokens, the suffix
 // starts and the plan (SuffixStartArgs::plan) must already be written.
-int launch_cascade_balanced(const SplitArgs &pa0, const SplitArgs &sa, hipStream_t st) {
+int launch_cascade_balanced(const SplitArgs &pa0, const SplitArgs &sa, bool fp8, hipStream_t st) {
     if (pa0.kind != 1 || sa.kind != 2 || !sa.suffix_lo || !sa.sk_plan || sa.sk_wgs < 1 || sa.part.S != 1)
         return SGL_ERR_INVALID;
     if (pa0.D != sa.D || pa0.Hkv != sa.Hkv || pa0.Hq != sa.Hq) return SGL_ERR_INVALID;
     if (sa.D != 128 || sa.Hkv % kRowsHeads != 0 || sa.Hkv > 16 || sa.Hq / sa.Hkv > 16) return SGL_ERR_UNSUPPORTED;
-    if (pa0.chunk % TILE != 0 || sa.chunk % TILE != 0) return SGL_ERR_INVALID;
+    const int tk = fp8 ? TILE8 : TILE;
+    if (pa0.chunk % tk != 0 || sa.chunk % tk != 0) return SGL_ERR_INVALID;
+    if (fp8 && (!sa.k_scale || !sa.v_scale || !pa0.k_scale || !pa0.v_scale)) return SGL_ERR_INVALID;
     SplitArgs pa = pa0;
     pa.row_blocks = (pa.max_members * (pa.Hq / pa.Hkv) + 15) / 16;
     const int64_t n_rbg = (pa.row_blocks + 3) / 4;
@@ -741,10 +745,14 @@ int launch_cascade_balanced(const SplitArgs &pa0, const SplitArgs &sa, hipStream
     const int64_t n_pre = ceil_div64(p_items, 8) * 8 * n_rbg;
     const int64_t n_bal = (int64_t)sa.sk_wgs * (sa.Hkv / kRowsHeads);
     if (n_pre + n_bal > 0x7fffffff) return SGL_ERR_UNSUPPORTED;
-    const int64_t p_slots = min(pa.chunk, kSlotTab);
+    const int64_t p_slots = fp8 ? pa.chunk : min(pa.chunk, kSlotTab);
     const size_t dyn = 32768 + (size_t)(p_slots > sa.chunk ? p_slots : sa.chunk) * sizeof(int32_t);
-    hipLaunchKernelGGL((cascade_balanced_kernel<128>), dim3((unsigned)(n_pre + n_bal)), dim3(256), dyn, st, sa, pa,
-                       (unsigned)n_bal);
+    if (fp8)
+        hipLaunchKernelGGL((cascade_balanced_kernel<128, true>), dim3((unsigned)(n_pre + n_bal)), dim3(256), dyn, st,
+                           sa, pa, (unsigned)n_bal);
+    else
+        hipLaunchKernelGGL((cascade_balanced_kernel<128, false>), dim3((unsigned)(n_pre + n_bal)), dim3(256), dyn, st,
+                           sa, pa, (unsigned)n_bal);
     return hip_status(hipGetLastError());
 }
 
